@@ -1,0 +1,359 @@
+"""fp64 reference of the quantized MoE layer (test infrastructure only).
+
+Every step is written from its definition, in float64, with NumPy; no blocking,
+fusion or reordering beyond what the definition states.  Page references:
+
+  [P2-Fitur]  page "Show HN: Menjalankan GLM 5.2 di komputer lambat",
+              section "Fitur utama yang diimplementasikan" (DeepSeek-V3-style
+              sigmoid router, noaux_tc, routed_scaling_factor, shared expert;
+              batch-union MoE; int4 kernels with dequant-on-use).
+  [P2-Cara]   same page, section "Cara kerja eksekusi MoE berbasis streaming
+              disk" (routed experts vs the always-resident shared expert).
+  [P5-Tech]   page "NVIDIA stellt neues GLM-5.2 NVFP4 Modell vor", section
+              "Technische Details und Quantisierungsansatz" (expert FFNs in
+              NVFP4 with FP8 scales per 16 elements; router kept in BF16/FP32).
+
+Readings taken where the pages are silent are listed in the repository's design
+notes; the ones that change results are repeated at the function that takes them.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+
+# ---------------------------------------------------------------------------
+# Number formats
+# ---------------------------------------------------------------------------
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) -> float64.  A bf16 number is the upper
+    half of an IEEE binary32, so widening is exact."""
+    b = np.asarray(bits).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def fp16_bits_to_f64(bits) -> np.ndarray:
+    """IEEE binary16 bit patterns -> float64 (exact)."""
+    return np.asarray(bits).astype(np.uint16).view(np.float16).astype(np.float64)
+
+
+def decode_e2m1(codes) -> np.ndarray:
+    """E2M1 (FP4) code -> value.  Bit 3 is the sign, bits 2..1 the exponent with
+    bias 1, bit 0 the mantissa; exponent 0 is subnormal (0 or 0.5).  Magnitudes
+    are therefore {0, 0.5, 1, 1.5, 2, 3, 4, 6}.  [P5-Tech: 4-bit elements]"""
+    c = np.asarray(codes).astype(np.int64)
+    sign = (c >> 3) & 1
+    e = (c >> 1) & 3
+    m = (c & 1).astype(np.float64)
+    mag = np.where(e == 0, 0.5 * m, np.ldexp(1.0 + 0.5 * m, (e - 1).astype(np.int64)))
+    return np.where(sign == 1, -mag, mag)
+
+
+def decode_e4m3fn(codes) -> np.ndarray:
+    """FP8 E4M3 ("fn": bias 7, no infinities, S.1111.111 is NaN) -> value.
+    [P5-Tech: FP8 scale per 16 elements]"""
+    c = np.asarray(codes).astype(np.int64)
+    sign = (c >> 7) & 1
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, np.ldexp(m / 8.0, -6),
+                   np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int64)))
+    mag = np.where((e == 15) & (c & 7 == 7), np.nan, mag)
+    return np.where(sign == 1, -mag, mag)
+
+
+# ---------------------------------------------------------------------------
+# Packed weight layouts
+# ---------------------------------------------------------------------------
+
+def unpack_int4_codes(q: np.ndarray) -> np.ndarray:
+    """uint8 [..., K/2] in the interleaved word layout -> codes [..., K].
+    Each group of 4 bytes is a little-endian 32-bit word covering inputs
+    8j..8j+7; input 8j+2i sits in bits [4i, 4i+4) and input 8j+2i+1 in bits
+    [16+4i, 16+4i+4)."""
+    q = np.asarray(q, dtype=np.uint8)
+    *lead, half = q.shape
+    K = half * 2
+    b = q.reshape(*lead, K // 8, 4).astype(np.uint32)
+    word = b[..., 0] | (b[..., 1] << 8) | (b[..., 2] << 16) | (b[..., 3] << 24)
+    out = np.empty((*lead, K // 8, 8), dtype=np.uint8)
+    for i in range(4):
+        out[..., 2 * i] = (word >> (4 * i)) & 15
+        out[..., 2 * i + 1] = (word >> (16 + 4 * i)) & 15
+    return out.reshape(*lead, K)
+
+
+def unpack_nvfp4_codes(q: np.ndarray) -> np.ndarray:
+    """uint8 [..., K/2] -> E2M1 codes [..., K]; byte j holds input 2j in the low
+    nibble and input 2j+1 in the high nibble."""
+    q = np.asarray(q, dtype=np.uint8)
+    *lead, half = q.shape
+    out = np.empty((*lead, half, 2), dtype=np.uint8)
+    out[..., 0] = q & 15
+    out[..., 1] = q >> 4
+    return out.reshape(*lead, half * 2)
+
+
+def dequant_int4(q: np.ndarray, scale_bits: np.ndarray) -> np.ndarray:
+    """Symmetric int4 with one fp16 scale per 32 inputs: w = (u - 8) * scale.
+    [P2-Fitur: packed int4, dequant-on-use; group-32 scales per the workload]
+    q: uint8 [N, K/2]; scale_bits: uint16/float16 [N, K/32] -> float64 [N, K]."""
+    u = unpack_int4_codes(q).astype(np.float64)
+    s = fp16_bits_to_f64(np.asarray(scale_bits).view(np.uint16))
+    N, K = u.shape
+    return ((u - 8.0).reshape(N, K // 32, 32) * s[:, :, None]).reshape(N, K)
+
+
+def dequant_nvfp4(q: np.ndarray, scale_e4m3: np.ndarray, gscale: float) -> np.ndarray:
+    """NVFP4: w = e2m1(code) * e4m3(block scale of 16 inputs) * fp32 per-tensor
+    scale.  [P5-Tech]  q: uint8 [N, K/2]; scale_e4m3: uint8 [N, K/16]."""
+    v = decode_e2m1(unpack_nvfp4_codes(q))
+    s = decode_e4m3fn(scale_e4m3)
+    N, K = v.shape
+    g = float(np.float32(gscale))
+    return (v.reshape(N, K // 16, 16) * s[:, :, None]).reshape(N, K) * g
+
+
+@dataclasses.dataclass
+class ExpertSource:
+    """Packed weights of E experts as NumPy arrays, decoded on demand.
+    proj -> (q uint8 [E,N,K/2], scale [E,N,K/g], gscale float32 [E] or None)."""
+    wfmt: str                      # "int4" or "nvfp4"
+    gate: tuple
+    up: tuple
+    down: tuple
+
+    def weight(self, proj: str, e: int) -> np.ndarray:
+        q, s, g = getattr(self, proj)
+        if self.wfmt == "int4":
+            return dequant_int4(q[e], s[e])
+        return dequant_nvfp4(q[e], s[e], g[e])
+
+    @property
+    def n_experts(self) -> int:
+        return self.gate[0].shape[0]
+
+
+# ---------------------------------------------------------------------------
+# Router  [P2-Fitur: DeepSeek-V3-style sigmoid router, noaux_tc,
+#          routed_scaling_factor]
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class RouterConfig:
+    n_experts: int
+    n_group: int
+    topk_group: int
+    top_k: int
+    routed_scaling_factor: float
+    group_top: int = 2          # reading: a group's score is the sum of its top-2 biased scores
+
+
+def _router_scores(x: np.ndarray, Wr: np.ndarray, b: np.ndarray):
+    logits = np.asarray(x, np.float64) @ np.asarray(Wr, np.float64).T
+    s = 1.0 / (1.0 + np.exp(-logits))
+    sb = s + np.asarray(b, np.float64)[None, :]
+    return logits, s, sb
+
+
+def _group_scores(sb: np.ndarray, cfg: RouterConfig) -> np.ndarray:
+    T, E = sb.shape
+    per = E // cfg.n_group
+    top = min(cfg.group_top, per)
+    desc = -np.sort(-sb.reshape(T, cfg.n_group, per), axis=-1)
+    return desc[..., :top].sum(-1)
+
+
+def route(x: np.ndarray, Wr: np.ndarray, b: np.ndarray, cfg: RouterConfig):
+    """Select top_k experts per token.
+
+    1. logits = x . Wr^T (float64; x is bf16 widened exactly, Wr fp32).
+    2. s = sigmoid(logits).
+    3. s' = s + b  (the score-correction bias steers selection only).
+    4. group j = experts [j*E/G, (j+1)*E/G); group score = sum of its top-2 s'.
+    5. keep the topk_group best groups (equal scores: lower group index first).
+    6. among experts of the kept groups, take the top_k by s' (equal: lower id);
+       experts of dropped groups are excluded outright (-inf), so exactly top_k
+       experts always come from the kept groups.
+    7. report ids in ascending expert id.
+    8. weights: w_i = s[id_i] / sum_j s[id_j] * routed_scaling_factor.
+    Returns (ids int64 [T,k], w float64 [T,k], info dict)."""
+    x = np.asarray(x, np.float64)
+    T = x.shape[0]
+    E, G, TG, k = cfg.n_experts, cfg.n_group, cfg.topk_group, cfg.top_k
+    logits, s, sb = _router_scores(x, Wr, b)
+    gscore = _group_scores(sb, cfg)
+    gorder = np.argsort(-gscore, axis=1, kind="stable")
+    keep = np.zeros((T, G), dtype=bool)
+    np.put_along_axis(keep, gorder[:, :TG], True, axis=1)
+    allowed = np.repeat(keep, E // G, axis=1)
+    masked = np.where(allowed, sb, -np.inf)
+    eorder = np.argsort(-masked, axis=1, kind="stable")
+    ids = np.sort(eorder[:, :k], axis=1)
+    w = route_weights(s, ids, cfg.routed_scaling_factor)
+    info = dict(logits=logits, s=s, sb=sb, gscore=gscore, keep=keep,
+                margin=route_margins(sb, gscore, keep, cfg))
+    return ids, w, info
+
+
+def route_weights(s: np.ndarray, ids: np.ndarray, rsf: float) -> np.ndarray:
+    """Renormalised unbiased sigmoid scores of the chosen experts times
+    routed_scaling_factor (no epsilon: every s > 0)."""
+    sel = np.take_along_axis(np.asarray(s, np.float64), np.asarray(ids), axis=1)
+    return sel / sel.sum(axis=1, keepdims=True) * float(rsf)
+
+
+def route_margins(sb, gscore, keep, cfg: RouterConfig) -> np.ndarray:
+    """Per token: the smallest gap at a selection boundary -- between the
+    topk_group-th and next group score, and between the top_k-th and next
+    allowed s'.  A decision whose margin is tiny may flip under rounding."""
+    T, G = gscore.shape
+    gdesc = -np.sort(-gscore, axis=1)
+    m = np.full(T, np.inf)
+    if cfg.topk_group < G:
+        m = np.minimum(m, gdesc[:, cfg.topk_group - 1] - gdesc[:, cfg.topk_group])
+    allowed = np.repeat(keep, cfg.n_experts // G, axis=1)
+    masked = np.where(allowed, sb, -np.inf)
+    edesc = -np.sort(-masked, axis=1)
+    n_allowed = allowed.sum(1)
+    k = cfg.top_k
+    has_next = n_allowed > k
+    if has_next.any():
+        gap = edesc[:, k - 1] - np.where(has_next, edesc[:, min(k, edesc.shape[1] - 1)], -np.inf)
+        m = np.minimum(m, np.where(has_next, gap, np.inf))
+    return m
+
+
+def valid_under_perturbation(ids_t: np.ndarray, sb_t: np.ndarray, cfg: RouterConfig,
+                             tau: float) -> bool:
+    """Whether `ids_t` (one token's chosen experts) is what the selection of
+    `route` returns for some biased scores within `tau` of `sb_t` -- the check
+    applied to tokens whose decision margin is below rounding level."""
+    E, G, TG, k = cfg.n_experts, cfg.n_group, cfg.topk_group, cfg.top_k
+    ids_t = np.asarray(ids_t)
+    if len(set(ids_t.tolist())) != k or ids_t.min() < 0 or ids_t.max() >= E:
+        return False
+    per = E // G
+    gscore = _group_scores(sb_t[None, :], cfg)[0]
+    chosen_groups = sorted(set((ids_t // per).tolist()))
+    if len(chosen_groups) > TG:
+        return False
+    rest = [g for g in np.argsort(-gscore, kind="stable") if g not in chosen_groups]
+    gsel = chosen_groups + rest[: TG - len(chosen_groups)]
+    out = [g for g in range(G) if g not in gsel]
+    # each s' may move by tau, so a group score (sum of two) by 2*tau
+    if out and min(gscore[gsel]) < max(gscore[out]) - 4 * tau:
+        return False
+    allowed = np.zeros(E, bool)
+    for g in gsel:
+        allowed[g * per:(g + 1) * per] = True
+    chosen = np.zeros(E, bool)
+    chosen[ids_t] = True
+    others = allowed & ~chosen
+    if others.any() and sb_t[chosen].min() < sb_t[others].max() - 2 * tau:
+        return False
+    return True
+
+
+# ---------------------------------------------------------------------------
+# Permutation  [P2-Fitur: batch-union MoE]
+# ---------------------------------------------------------------------------
+
+def permute(ids: np.ndarray, n_experts: int):
+    """Group the T*k picks by expert, keeping pick order (t*k+i) inside an
+    expert: a counting sort written out.
+    Returns expert_offsets [E+1], sorted_token [T*k] (token of the pick at each
+    sorted position), inv_perm [T*k] (sorted position of pick t*k+i),
+    active_experts (ascending ids with at least one pick)."""
+    ids = np.asarray(ids)
+    T, k = ids.shape
+    flat = ids.reshape(-1).tolist()
+    counts = [0] * n_experts
+    for e in flat:
+        counts[e] += 1
+    offsets = [0] * (n_experts + 1)
+    for e in range(n_experts):
+        offsets[e + 1] = offsets[e] + counts[e]
+    cursor = offsets[:-1]
+    cursor = list(cursor)
+    sorted_token = [0] * (T * k)
+    inv_perm = [0] * (T * k)
+    for p, e in enumerate(flat):
+        pos = cursor[e]
+        cursor[e] += 1
+        sorted_token[pos] = p // k
+        inv_perm[p] = pos
+    active = [e for e in range(n_experts) if counts[e] > 0]
+    return (np.array(offsets, np.int64), np.array(sorted_token, np.int64),
+            np.array(inv_perm, np.int64), np.array(active, np.int64))
+
+
+# ---------------------------------------------------------------------------
+# Expert FFN and layer  [P2-Fitur, P2-Cara, P5-Tech]
+# ---------------------------------------------------------------------------
+
+def swiglu_ffn(X: np.ndarray, Wg: np.ndarray, Wu: np.ndarray, Wd: np.ndarray) -> np.ndarray:
+    """FFN(x) = Wd ( silu(Wg x) * (Wu x) ),  silu(z) = z * sigmoid(z).
+    X: [M, H]; Wg, Wu: [I, H]; Wd: [H, I]; all float64."""
+    G = X @ Wg.T
+    U = X @ Wu.T
+    with np.errstate(over="ignore"):
+        h = G / (1.0 + np.exp(-G)) * U
+    return h @ Wd.T
+
+
+def _expert_weights(src: ExpertSource, e: int):
+    return src.weight("gate", e), src.weight("up", e), src.weight("down", e)
+
+
+def layer(x_bits, Wr, b, cfg: RouterConfig, routed: ExpertSource,
+          shared: Optional[ExpertSource] = None, ids: Optional[np.ndarray] = None,
+          token_idx: Optional[np.ndarray] = None):
+    """y_t = sum_{e in S_t} w_{t,e} FFN_e(x_t) + FFN_shared(x_t).
+
+    (S_t, w_t) come from `route` unless `ids` is given, in which case the
+    weights are recomputed for those ids.  `token_idx` restricts the evaluation
+    to a subset of tokens (rows of x_bits / ids are then those tokens).
+    The shared expert enters with weight 1 (routed_scaling_factor applies to the
+    routed experts only).  Each routed expert is dequantised once and applied to
+    the tokens that chose it; that only reorders the sum over experts.
+    Returns (y float64 [T', H], ids, w)."""
+    X = bf16_bits_to_f64(x_bits)
+    if token_idx is not None:
+        X = X[np.asarray(token_idx)]
+    _, s, _ = _router_scores(X, Wr, b)
+    if ids is None:
+        ids, w, _ = route(X, Wr, b, cfg)
+    else:
+        ids = np.asarray(ids)
+        w = route_weights(s, ids, cfg.routed_scaling_factor)
+    T, H = X.shape
+    y = np.zeros((T, H))
+    for e in np.unique(ids):
+        rows, slots = np.nonzero(ids == e)
+        Wg, Wu, Wd = _expert_weights(routed, int(e))
+        y[rows] += w[rows, slots][:, None] * swiglu_ffn(X[rows], Wg, Wu, Wd)
+    if shared is not None:
+        y += swiglu_ffn(X, *_expert_weights(shared, 0))
+    return y, ids, w
+
+
+def dense_layer(x_bits, Wr, b, cfg: RouterConfig, routed: ExpertSource,
+                shared: Optional[ExpertSource] = None):
+    """The same layer as a dense MoE: every expert on every token, multiplied by
+    a gate matrix that is w on the chosen experts and 0 elsewhere.  Small
+    shapes only."""
+    X = bf16_bits_to_f64(x_bits)
+    ids, w, _ = route(X, Wr, b, cfg)
+    T, H = X.shape
+    gate = np.zeros((T, cfg.n_experts))
+    np.put_along_axis(gate, ids, w, axis=1)
+    y = np.zeros((T, H))
+    for e in range(cfg.n_experts):
+        y += gate[:, e:e + 1] * swiglu_ffn(X, *_expert_weights(routed, e))
+    if shared is not None:
+        y += swiglu_ffn(X, *_expert_weights(shared, 0))
+    return y
