@@ -1,0 +1,159 @@
+"""ctypes binding of libqmoe (include/qmoe.h), argument marshalling only.
+
+Each function has the name of the C entry point it calls and takes torch
+tensors where the C function takes device pointers; torch supplies device
+memory and the current HIP stream and nothing else.  A non-zero status raises
+QmoeError.  The library must have been built (python -m
+quantized_moe_02_amd.build); there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqmoe.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP = range(5)
+MOE_WFMT_INT4_G32_F16, MOE_WFMT_NVFP4 = 0, 1
+MOE_OUT_F32, MOE_OUT_BF16 = 0, 1
+MOE_MAX_TOKENS = 262144
+WFMT = {"int4": MOE_WFMT_INT4_G32_F16, "nvfp4": MOE_WFMT_NVFP4}
+
+
+class QmoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+        self.status = status
+
+
+class MoeConfig(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("moe_inter", ctypes.c_int32),
+                ("n_routed_experts", ctypes.c_int32), ("n_group", ctypes.c_int32),
+                ("topk_group", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("n_shared_experts", ctypes.c_int32), ("shared_inter", ctypes.c_int32),
+                ("routed_scaling_factor", ctypes.c_float), ("wfmt", ctypes.c_int32)]
+
+
+class MoeQProj(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("gscale", ctypes.c_void_p)]
+
+
+class MoeQExperts(ctypes.Structure):
+    _fields_ = [("gate", MoeQProj), ("up", MoeQProj), ("down", MoeQProj)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libqmoe.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m quantized_moe_02_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        cfgp = ctypes.POINTER(MoeConfig)
+        exp = ctypes.POINTER(MoeQExperts)
+        sig = {
+            "moe_workspace_size": [cfgp, i32, ctypes.POINTER(sz)],
+            "moe_route": [cfgp, i32, vp, vp, vp, vp, vp, vp, sz, vp],
+            "moe_permute": [cfgp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+            "moe_expert_ffn_q4": [cfgp, i32, vp, exp, vp, vp, vp, vp, vp, vp, sz, vp],
+            "moe_combine": [cfgp, i32, vp, vp, vp, vp, vp, i32, vp],
+            "moe_layer": [cfgp, i32, vp, vp, vp, exp, exp, vp, i32, vp, vp, vp, sz, vp],
+        }
+        for name, args in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        L.moe_status_string.argtypes = [ctypes.c_int]
+        L.moe_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().moe_status_string(status).decode()
+
+
+def _check(status: int, where: str):
+    if status != MOE_OK:
+        raise QmoeError(status, where)
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def make_config(geom: dict, wfmt: str) -> MoeConfig:
+    return MoeConfig(geom["hidden"], geom["moe_inter"], geom["n_routed_experts"],
+                     geom["n_group"], geom["topk_group"], geom["top_k"],
+                     geom["n_shared_experts"], geom.get("shared_inter", 0),
+                     float(geom["routed_scaling_factor"]), WFMT.get(wfmt, wfmt))
+
+
+def qexperts(gate, up, down) -> MoeQExperts:
+    """Each argument: (q, scale, gscale-or-None) tensors."""
+    def proj(p):
+        return MoeQProj(p[0].data_ptr(), p[1].data_ptr(), None if p[2] is None else p[2].data_ptr())
+    return MoeQExperts(proj(gate), proj(up), proj(down))
+
+
+def moe_workspace_size(cfg: MoeConfig, T: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_workspace_size(ctypes.byref(cfg), T, ctypes.byref(n)), "moe_workspace_size")
+    return n.value
+
+
+def workspace(cfg: MoeConfig, T: int, device="cuda") -> torch.Tensor:
+    """A torch-allocated workspace of the size the library asks for."""
+    return torch.empty(max(moe_workspace_size(cfg, T), 1), dtype=torch.uint8, device=device)
+
+
+def moe_route(cfg, T, x, router_w, bias, topk_ids, topk_w, ws, stream=None):
+    _check(lib().moe_route(ctypes.byref(cfg), T, _p(x), _p(router_w), _p(bias), _p(topk_ids),
+                           _p(topk_w), _p(ws), 0 if ws is None else ws.numel(), _stream(stream)),
+           "moe_route")
+
+
+def moe_permute(cfg, T, topk_ids, expert_offsets, sorted_token, inv_perm, active_experts,
+                n_active, ws, stream=None):
+    _check(lib().moe_permute(ctypes.byref(cfg), T, _p(topk_ids), _p(expert_offsets),
+                             _p(sorted_token), _p(inv_perm), _p(active_experts), _p(n_active),
+                             _p(ws), 0 if ws is None else ws.numel(), _stream(stream)),
+           "moe_permute")
+
+
+def moe_expert_ffn_q4(cfg, T, x, w: MoeQExperts, expert_offsets, sorted_token, active_experts,
+                      n_active, out, ws, stream=None):
+    _check(lib().moe_expert_ffn_q4(ctypes.byref(cfg), T, _p(x), ctypes.byref(w),
+                                   _p(expert_offsets), _p(sorted_token), _p(active_experts),
+                                   _p(n_active), _p(out), _p(ws),
+                                   0 if ws is None else ws.numel(), _stream(stream)),
+           "moe_expert_ffn_q4")
+
+
+def moe_combine(cfg, T, expert_out, inv_perm, topk_w, shared_out, y, out_dtype=MOE_OUT_F32,
+                stream=None):
+    _check(lib().moe_combine(ctypes.byref(cfg), T, _p(expert_out), _p(inv_perm), _p(topk_w),
+                             _p(shared_out), _p(y), out_dtype, _stream(stream)), "moe_combine")
+
+
+def moe_layer(cfg, T, x, router_w, bias, routed: MoeQExperts, shared: Optional[MoeQExperts], y,
+              out_dtype=MOE_OUT_F32, topk_ids_out=None, topk_w_out=None, ws=None, stream=None):
+    _check(lib().moe_layer(ctypes.byref(cfg), T, _p(x), _p(router_w), _p(bias),
+                           ctypes.byref(routed), None if shared is None else ctypes.byref(shared),
+                           _p(y), out_dtype, _p(topk_ids_out), _p(topk_w_out), _p(ws),
+                           0 if ws is None else ws.numel(), _stream(stream)), "moe_layer")

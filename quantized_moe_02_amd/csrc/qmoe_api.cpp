@@ -1,0 +1,310 @@
+// C-ABI entry points of libqmoe (declared in include/qmoe.h): argument
+// validation, workspace layout and kernel dispatch.  Every check runs before
+// the first HIP call, so invalid calls leave the device untouched.
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+
+#include "qmoe_internal.h"
+
+namespace qmoe {
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+moe_status check_cfg(const moe_config* c) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  if (c->hidden <= 0 || c->hidden % 32 != 0) return MOE_ERR_INVALID_ARG;
+  if (c->moe_inter <= 0 || c->moe_inter % 32 != 0) return MOE_ERR_INVALID_ARG;
+  if (c->n_shared_experts != 0 && c->n_shared_experts != 1) return MOE_ERR_INVALID_ARG;
+  if (c->n_shared_experts == 1 && (c->shared_inter <= 0 || c->shared_inter % 32 != 0))
+    return MOE_ERR_INVALID_ARG;
+  if (c->n_routed_experts <= 0 || c->n_group <= 0) return MOE_ERR_INVALID_ARG;
+  if (c->n_routed_experts % c->n_group != 0) return MOE_ERR_INVALID_ARG;
+  if (c->topk_group < 1 || c->topk_group > c->n_group) return MOE_ERR_INVALID_ARG;
+  const int64_t allowed =
+      (int64_t)c->topk_group * (c->n_routed_experts / c->n_group);
+  if (c->top_k < 1 || c->top_k > allowed) return MOE_ERR_INVALID_ARG;
+  if (!std::isfinite(c->routed_scaling_factor) || !(c->routed_scaling_factor > 0.0f))
+    return MOE_ERR_INVALID_ARG;
+  if (c->wfmt != MOE_WFMT_INT4_G32_F16 && c->wfmt != MOE_WFMT_NVFP4) return MOE_ERR_INVALID_ARG;
+  // kernel limits
+  if (c->n_routed_experts > 256 || c->n_group > 64 || c->top_k > 16) return MOE_ERR_UNSUPPORTED;
+  if (c->hidden > 65536 || c->moe_inter > 65536) return MOE_ERR_UNSUPPORTED;
+  if (c->n_shared_experts == 1 && c->shared_inter > 65536) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status check_T(int32_t T) {
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T > MOE_MAX_TOKENS) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status check_proj(const moe_qproj& p, int wfmt) {
+  if (!p.q || !p.scale) return MOE_ERR_INVALID_ARG;
+  if (!aligned(p.q, 16) || !aligned(p.scale, 16)) return MOE_ERR_INVALID_ARG;
+  if (wfmt == MOE_WFMT_NVFP4) {
+    if (!p.gscale || !aligned(p.gscale, 4)) return MOE_ERR_INVALID_ARG;
+  } else if (p.gscale) {
+    return MOE_ERR_INVALID_ARG;
+  }
+  return MOE_OK;
+}
+
+moe_status check_experts(const moe_qexperts* w, int wfmt) {
+  if (!w) return MOE_ERR_INVALID_ARG;
+  moe_status s;
+  if ((s = check_proj(w->gate, wfmt)) != MOE_OK) return s;
+  if ((s = check_proj(w->up, wfmt)) != MOE_OK) return s;
+  return check_proj(w->down, wfmt);
+}
+
+moe_status check_ws(const moe_config& c, int T, const void* ws, size_t ws_bytes) {
+  const size_t need = carve_workspace(c, T, nullptr).total;
+  if (need == 0) return MOE_OK;
+  if (!ws) return MOE_ERR_INVALID_ARG;
+  if (!aligned(ws, kAlign)) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return MOE_OK;
+}
+
+ExpertSet expert_set(const moe_qexperts& w, int inter) {
+  ExpertSet s;
+  s.gate = {w.gate.q, w.gate.scale, w.gate.gscale};
+  s.up = {w.up.q, w.up.scale, w.up.gscale};
+  s.down = {w.down.q, w.down.scale, w.down.gscale};
+  s.inter = inter;
+  return s;
+}
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+Workspace carve_workspace(const moe_config& c, int T, void* base) {
+  Workspace w{};
+  if (T == 0) return w;
+  const size_t E = c.n_routed_experts, K = c.top_k, H = c.hidden;
+  const size_t P = (size_t)T * K;
+  const size_t imax = (size_t)std::max(c.moe_inter, c.n_shared_experts ? c.shared_inter : 0);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = round_up(off + bytes, kAlign);
+    return o;
+  };
+  const size_t o_logits = take((size_t)T * E * sizeof(double));
+  const size_t o_ids = take(P * sizeof(int32_t));
+  const size_t o_tw = take(P * sizeof(float));
+  const size_t o_off = take((E + 1) * sizeof(int32_t));
+  const size_t o_act = take(E * sizeof(int32_t));
+  const size_t o_na = take(4 * sizeof(int32_t));
+  const size_t o_st = take(P * sizeof(int32_t));
+  const size_t o_inv = take(P * sizeof(int32_t));
+  const size_t o_h = take((P + T) * imax * sizeof(uint16_t));
+  const size_t o_O = take((P + T) * H * sizeof(float));
+  w.total = off;
+  if (base) {
+    char* b = static_cast<char*>(base);
+    w.logits = reinterpret_cast<double*>(b + o_logits);
+    w.ids = reinterpret_cast<int32_t*>(b + o_ids);
+    w.tw = reinterpret_cast<float*>(b + o_tw);
+    w.offsets = reinterpret_cast<int32_t*>(b + o_off);
+    w.active = reinterpret_cast<int32_t*>(b + o_act);
+    w.n_active = reinterpret_cast<int32_t*>(b + o_na);
+    w.sorted_token = reinterpret_cast<int32_t*>(b + o_st);
+    w.inv_perm = reinterpret_cast<int32_t*>(b + o_inv);
+    w.h = reinterpret_cast<uint16_t*>(b + o_h);
+    w.O = reinterpret_cast<float*>(b + o_O);
+  }
+  return w;
+}
+
+}  // namespace qmoe
+
+using namespace qmoe;
+
+extern "C" {
+
+moe_status moe_workspace_size(const moe_config* cfg, int32_t T, size_t* bytes) {
+  moe_status s;
+  if ((s = check_cfg(cfg)) != MOE_OK) return s;
+  if ((s = check_T(T)) != MOE_OK) return s;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  *bytes = carve_workspace(*cfg, T, nullptr).total;
+  return MOE_OK;
+}
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+moe_status moe_route(const moe_config* cfg, int32_t T, const uint16_t* x, const float* router_w,
+                     const float* bias, int32_t* topk_ids, float* topk_w, void* ws,
+                     size_t ws_bytes, hipStream_t stream) {
+  moe_status s;
+  if ((s = check_cfg(cfg)) != MOE_OK) return s;
+  if ((s = check_T(T)) != MOE_OK) return s;
+  if (!x || !router_w || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(router_w, 16)) return MOE_ERR_INVALID_ARG;
+  if ((s = check_ws(*cfg, T, ws, ws_bytes)) != MOE_OK) return s;
+  if (T == 0) return MOE_OK;
+  const Workspace w = carve_workspace(*cfg, T, ws);
+  RouteArgs a{x, router_w, bias, topk_ids, topk_w, w.logits, T, cfg->hidden,
+              cfg->n_routed_experts, cfg->n_group, cfg->topk_group, cfg->top_k,
+              cfg->routed_scaling_factor};
+  return hip_status(launch_route(a, stream));
+}
+
+moe_status moe_permute(const moe_config* cfg, int32_t T, const int32_t* topk_ids,
+                       int32_t* expert_offsets, int32_t* sorted_token, int32_t* inv_perm,
+                       int32_t* active_experts, int32_t* n_active, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  moe_status s;
+  if ((s = check_cfg(cfg)) != MOE_OK) return s;
+  if ((s = check_T(T)) != MOE_OK) return s;
+  if (!topk_ids || !expert_offsets || !sorted_token || !inv_perm || !active_experts || !n_active)
+    return MOE_ERR_INVALID_ARG;
+  if ((s = check_ws(*cfg, T, ws, ws_bytes)) != MOE_OK) return s;
+  if (T == 0) return MOE_OK;
+  PermuteArgs a{topk_ids, expert_offsets, sorted_token, inv_perm, active_experts, n_active,
+                T, cfg->top_k, cfg->n_routed_experts};
+  return hip_status(launch_permute(a, stream));
+}
+
+moe_status moe_expert_ffn_q4(const moe_config* cfg, int32_t T, const uint16_t* x,
+                             const moe_qexperts* w, const int32_t* expert_offsets,
+                             const int32_t* sorted_token, const int32_t* active_experts,
+                             const int32_t* n_active, float* out, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
+  moe_status s;
+  if ((s = check_cfg(cfg)) != MOE_OK) return s;
+  if ((s = check_T(T)) != MOE_OK) return s;
+  if (!x || !out || !aligned(x, 16) || !aligned(out, 16)) return MOE_ERR_INVALID_ARG;
+  if ((s = check_experts(w, cfg->wfmt)) != MOE_OK) return s;
+  const bool routed = expert_offsets != nullptr;
+  if (routed) {
+    if (!sorted_token || !active_experts || !n_active) return MOE_ERR_INVALID_ARG;
+  } else {
+    if (sorted_token || active_experts || n_active) return MOE_ERR_INVALID_ARG;
+    if (cfg->n_shared_experts == 0) return MOE_ERR_INVALID_ARG;  // no shared_inter to use
+  }
+  if ((s = check_ws(*cfg, T, ws, ws_bytes)) != MOE_OK) return s;
+  if (T == 0) return MOE_OK;
+  const Workspace ws_ = carve_workspace(*cfg, T, ws);
+  const int ldh = std::max(cfg->moe_inter, cfg->n_shared_experts ? cfg->shared_inter : 0);
+  FfnArgs a{};
+  a.x = x;
+  a.T = T;
+  a.H = cfg->hidden;
+  a.K = cfg->top_k;
+  a.wfmt = cfg->wfmt;
+  a.ldh = ldh;
+  if (routed) {
+    a.has_routed = true;
+    a.routed = expert_set(*w, cfg->moe_inter);
+    a.max_slots = std::min<int64_t>(cfg->n_routed_experts, (int64_t)T * cfg->top_k);
+    a.offsets = expert_offsets;
+    a.sorted_token = sorted_token;
+    a.active = active_experts;
+    a.n_active = n_active;
+    a.h_routed = ws_.h;
+    a.o_routed = out;
+  } else {
+    a.has_dense = true;
+    a.dense = expert_set(*w, cfg->shared_inter);
+    a.h_dense = ws_.h;
+    a.o_dense = out;
+  }
+  return hip_status(launch_ffn(a, stream));
+}
+
+moe_status moe_combine(const moe_config* cfg, int32_t T, const float* expert_out,
+                       const int32_t* inv_perm, const float* topk_w, const float* shared_out,
+                       void* y, int32_t out_dtype, hipStream_t stream) {
+  moe_status s;
+  if ((s = check_cfg(cfg)) != MOE_OK) return s;
+  if ((s = check_T(T)) != MOE_OK) return s;
+  if (!expert_out || !inv_perm || !topk_w || !y) return MOE_ERR_INVALID_ARG;
+  if (out_dtype != MOE_OUT_F32 && out_dtype != MOE_OUT_BF16) return MOE_ERR_INVALID_ARG;
+  if (!aligned(expert_out, 16) || !aligned(y, 16) || (shared_out && !aligned(shared_out, 16)))
+    return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  CombineArgs a{expert_out, inv_perm, topk_w, shared_out, y, out_dtype == MOE_OUT_BF16,
+                T, cfg->hidden, cfg->top_k};
+  return hip_status(launch_combine(a, stream));
+}
+
+moe_status moe_layer(const moe_config* cfg, int32_t T, const uint16_t* x, const float* router_w,
+                     const float* bias, const moe_qexperts* routed, const moe_qexperts* shared,
+                     void* y, int32_t out_dtype, int32_t* topk_ids_out, float* topk_w_out,
+                     void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status s;
+  if ((s = check_cfg(cfg)) != MOE_OK) return s;
+  if ((s = check_T(T)) != MOE_OK) return s;
+  if (!x || !router_w || !y) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(router_w, 16) || !aligned(y, 16)) return MOE_ERR_INVALID_ARG;
+  if (out_dtype != MOE_OUT_F32 && out_dtype != MOE_OUT_BF16) return MOE_ERR_INVALID_ARG;
+  if ((s = check_experts(routed, cfg->wfmt)) != MOE_OK) return s;
+  if (cfg->n_shared_experts == 1) {
+    if ((s = check_experts(shared, cfg->wfmt)) != MOE_OK) return s;
+  } else if (shared) {
+    return MOE_ERR_INVALID_ARG;
+  }
+  if ((s = check_ws(*cfg, T, ws, ws_bytes)) != MOE_OK) return s;
+  if (T == 0) return MOE_OK;
+
+  const Workspace w = carve_workspace(*cfg, T, ws);
+  const size_t P = (size_t)T * cfg->top_k;
+  int32_t* ids = topk_ids_out ? topk_ids_out : w.ids;
+  float* tw = topk_w_out ? topk_w_out : w.tw;
+  hipError_t e;
+  RouteArgs ra{x, router_w, bias, ids, tw, w.logits, T, cfg->hidden, cfg->n_routed_experts,
+               cfg->n_group, cfg->topk_group, cfg->top_k, cfg->routed_scaling_factor};
+  if ((e = launch_route(ra, stream)) != hipSuccess) return MOE_ERR_HIP;
+  PermuteArgs pa{ids, w.offsets, w.sorted_token, w.inv_perm, w.active, w.n_active,
+                 T, cfg->top_k, cfg->n_routed_experts};
+  if ((e = launch_permute(pa, stream)) != hipSuccess) return MOE_ERR_HIP;
+
+  const bool has_shared = cfg->n_shared_experts == 1;
+  FfnArgs fa{};
+  fa.x = x;
+  fa.T = T;
+  fa.H = cfg->hidden;
+  fa.K = cfg->top_k;
+  fa.wfmt = cfg->wfmt;
+  fa.ldh = std::max(cfg->moe_inter, has_shared ? cfg->shared_inter : 0);
+  fa.has_routed = true;
+  fa.routed = expert_set(*routed, cfg->moe_inter);
+  fa.max_slots = (int)std::min<int64_t>(cfg->n_routed_experts, (int64_t)P);
+  fa.offsets = w.offsets;
+  fa.sorted_token = w.sorted_token;
+  fa.active = w.active;
+  fa.n_active = w.n_active;
+  fa.h_routed = w.h;
+  fa.o_routed = w.O;
+  if (has_shared) {
+    fa.has_dense = true;
+    fa.dense = expert_set(*shared, cfg->shared_inter);
+    fa.h_dense = w.h + P * fa.ldh;
+    fa.o_dense = w.O + P * cfg->hidden;
+  }
+  if ((e = launch_ffn(fa, stream)) != hipSuccess) return MOE_ERR_HIP;
+  CombineArgs ca{w.O, w.inv_perm, tw, has_shared ? w.O + P * cfg->hidden : nullptr, y,
+                 out_dtype == MOE_OUT_BF16, T, cfg->hidden, cfg->top_k};
+  return hip_status(launch_combine(ca, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,99 @@
+// Internal interfaces between the C-ABI layer (qmoe_api.cpp) and the kernel
+// launchers (*.hip).  Not installed; the public interface is include/qmoe.h.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "../../include/qmoe.h"
+
+namespace qmoe {
+
+struct ProjPtr {
+  const uint8_t* q;
+  const void* s;
+  const float* g;
+};
+
+struct ExpertSet {
+  ProjPtr gate, up, down;
+  int inter;
+};
+
+// Pieces of the caller's workspace.  Every piece starts on a 256-byte boundary.
+struct Workspace {
+  double* logits;         // [T][E]   router logits (fp64)
+  int32_t* ids;           // [T][k]   routing when the caller keeps none
+  float* tw;              // [T][k]
+  int32_t* offsets;       // [E+1]
+  int32_t* active;        // [E]
+  int32_t* n_active;      // [4]
+  int32_t* sorted_token;  // [P]
+  int32_t* inv_perm;      // [P]
+  uint16_t* h;            // [P+T][Imax] fp16 SwiGLU outputs
+  float* O;               // [P+T][H]   per-pick expert outputs (fp32)
+  size_t total;
+};
+
+// Lays the workspace out from `base` (nullptr: only sizes it).
+Workspace carve_workspace(const moe_config& c, int T, void* base);
+
+struct RouteArgs {
+  const uint16_t* x;
+  const float* router_w;
+  const float* bias;  // nullable
+  int32_t* ids;
+  float* tw;
+  double* logits;
+  int T, H, E, G, TG, K;
+  float rsf;
+};
+hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+
+struct PermuteArgs {
+  const int32_t* ids;
+  int32_t* offsets;
+  int32_t* sorted_token;
+  int32_t* inv_perm;
+  int32_t* active;
+  int32_t* n_active;
+  int T, K, E;
+};
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
+
+struct FfnArgs {
+  const uint16_t* x;
+  int T, H, K, wfmt;
+  // routed experts (grouped by the permutation)
+  bool has_routed;
+  ExpertSet routed;
+  int max_slots;  // upper bound on the number of active experts
+  const int32_t* offsets;
+  const int32_t* sorted_token;
+  const int32_t* active;
+  const int32_t* n_active;
+  uint16_t* h_routed;  // [P][ldh]
+  float* o_routed;     // [P][H]
+  // one expert applied to all T tokens (the shared expert, or dense mode)
+  bool has_dense;
+  ExpertSet dense;
+  uint16_t* h_dense;   // [T][ldh]
+  float* o_dense;      // [T][H]
+  int ldh;
+};
+hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
+
+struct CombineArgs {
+  const float* expert_out;  // [P][H]
+  const int32_t* inv_perm;
+  const float* tw;
+  const float* shared_out;  // nullable, [T][H]
+  void* y;
+  int out_bf16;
+  int T, H, K;
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+
+}  // namespace qmoe
