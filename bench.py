@@ -1,0 +1,322 @@
+#!/usr/bin/env python3
+"""Benchmark of one quantized MoE layer (GLM-5.2 shape) on one MI355X.
+
+A step is one moe_layer call -- router, permutation, routed and shared expert
+FFNs, combine -- over one batch of synthetic inputs resident in HBM.  The
+headline workload is single-token decode (hidden 6144, moe_inter 2048, 256
+experts, top-8 of 4 kept groups out of 8, one shared expert, int4 weights with
+fp16 scales per 32 inputs).  Weight sets are replicated and rotated so that no
+step reads weights another step left in the 256 MB Infinity Cache.
+
+Prints one JSON line.  Usage:
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads a,b,...]
+    python bench.py --copy-calibration      (plain copy kernel, for PMC scaling)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + weight-stream HBM GB/s (% peak); prefill MFMA util"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_F16_TFLOPS = 2500.0       # MI355X dense fp16/bf16 MFMA
+ALL_WORKLOADS = ["decode", "verify4", "verify64", "prefill4k", "prefill16k", "nvfp4_512"]
+HEADLINE = "decode"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workloads", default=",".join(ALL_WORKLOADS))
+    ap.add_argument("--replicas", type=int, default=0, help="weight replicas (0: automatic)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-trace", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--json-out", default=None)
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# algorithmic bytes and flops
+# ---------------------------------------------------------------------------
+
+def proj_bytes(N, K, wfmt):
+    if wfmt == "int4":
+        return N * K // 2 + (N * K // 32) * 2
+    return N * K // 2 + N * K // 16 + 4
+
+
+def expert_bytes(H, I, wfmt):
+    return {"gate": proj_bytes(I, H, wfmt), "up": proj_bytes(I, H, wfmt),
+            "down": proj_bytes(H, I, wfmt)}
+
+
+def algorithmic(geom, wfmt, T, n_active):
+    """Bytes the method must move and flops it must do for one layer call,
+    and per kernel of the current launch sequence."""
+    H, I, E, k = geom["hidden"], geom["moe_inter"], geom["n_routed_experts"], geom["top_k"]
+    Is = geom["shared_inter"] if geom["n_shared_experts"] else 0
+    P = T * k
+    eb = expert_bytes(H, I, wfmt)
+    sb = expert_bytes(H, Is, wfmt) if Is else {"gate": 0, "up": 0, "down": 0}
+    x_b, y_b = T * H * 2, T * H * 4
+    router_b = E * H * 4 + E * 4
+    layer_bytes = n_active * sum(eb.values()) + sum(sb.values()) + router_b + x_b + y_b
+    layer_flops = P * 2 * H * I * 3 + T * 2 * H * Is * 3 + T * 2 * H * E
+    ldh_rows = P + (T if Is else 0)
+    kern = {
+        "route_logits": dict(bytes=router_b + x_b + T * E * 8, flops=T * 2 * H * E),
+        "route_select": dict(bytes=T * E * 8 + E * 4 + P * 8, flops=0),
+        "permute": dict(bytes=P * 4 * 3 + (E + 1) * 4, flops=0),
+        "gateup_gemv": dict(bytes=n_active * (eb["gate"] + eb["up"]) + sb["gate"] + sb["up"]
+                            + x_b + ldh_rows * I * 2,
+                            flops=P * 2 * H * I * 2 + T * 2 * H * Is * 2),
+        "down_gemv": dict(bytes=n_active * eb["down"] + sb["down"] + ldh_rows * I * 2
+                          + ldh_rows * H * 4,
+                          flops=P * 2 * H * I + T * 2 * H * Is),
+        "combine": dict(bytes=ldh_rows * H * 4 + P * 8 + y_b, flops=2 * P * H),
+    }
+    return layer_bytes, layer_flops, kern
+
+
+# ---------------------------------------------------------------------------
+# layer set-up
+# ---------------------------------------------------------------------------
+
+def clone_experts(qe):
+    import synth
+    c = lambda p: synth.QProj(p.q.clone(), p.scale.clone(), None if p.gscale is None else p.gscale.clone())
+    return synth.QExperts(c(qe.gate), c(qe.up), c(qe.down))
+
+
+class Bench:
+    def __init__(self, name, replicas):
+        import quantized_moe_02_amd as q
+        import synth
+        self.q = q
+        self.name = name
+        self.L = L = synth.make_layer(name, "cuda")
+        self.geom, self.T, self.wfmt = L.geom, L.T, L.wfmt
+        g = self.geom
+        self.cfg = q.make_config(g, L.wfmt)
+        self.sets = [(L.router_w, L.bias, L.routed, L.shared)]
+        for _ in range(replicas - 1):
+            self.sets.append((L.router_w.clone(), L.bias.clone(), clone_experts(L.routed),
+                              clone_experts(L.shared) if L.shared is not None else None))
+        torch.cuda.synchronize()
+
+        def qx(qe):
+            t = lambda p: (p.q, p.scale, p.gscale)
+            return q.qexperts(t(qe.gate), t(qe.up), t(qe.down))
+        self.qsets = [(rw, b, qx(r), qx(s) if s is not None else None) for rw, b, r, s in self.sets]
+        self.ws = q.workspace(self.cfg, self.T)
+        self.y = torch.empty(self.T, g["hidden"], device="cuda", dtype=torch.float32)
+        self.ids = torch.empty(self.T, g["top_k"], device="cuda", dtype=torch.int32)
+        self.tw = torch.empty(self.T, g["top_k"], device="cuda", dtype=torch.float32)
+
+    def step(self, i, stream=None):
+        rw, b, r, s = self.qsets[i % len(self.qsets)]
+        self.q.moe_layer(self.cfg, self.T, self.L.x, rw, b, r, s, self.y, self.q.MOE_OUT_F32,
+                         self.ids, self.tw, self.ws, stream=stream)
+
+    def step_traced(self, i, trace):
+        rw, b, r, s = self.qsets[i % len(self.qsets)]
+        self.q.moe_layer_trace(self.cfg, self.T, self.L.x, rw, b, r, s, self.y, trace,
+                               self.q.MOE_OUT_F32, self.ids, self.tw, self.ws)
+
+    def n_active(self):
+        return int(torch.unique(self.ids).numel())
+
+
+def time_steps(B: Bench, steps, warmup, use_graph):
+    """Whole-step throughput.  Decode-sized steps replay a captured HIP graph of
+    one step per replica, so that Python launch overhead does not idle the GPU."""
+    R = len(B.qsets)
+    for i in range(warmup):
+        B.step(i)
+    torch.cuda.synchronize()
+    if use_graph:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for i in range(R):
+                    B.step(i)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, steps // R)
+        n = reps * R
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        return n, (t1 - t0)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        B.step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return steps, (t1 - t0)
+
+
+def trace_kernels(B: Bench, steps):
+    """Average duration of each kernel of moe_layer, from HIP events recorded
+    by the library at kernel boundaries on the launch stream.  The steps are
+    queued behind a sleep kernel so that host launch gaps do not enter the
+    intervals."""
+    q = B.q
+    per = {}
+    traces = []
+    evs = []
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2.4e9 * 0.02 + steps * 2.4e9 * 150e-6))   # ~20 ms + 150 us/step of cycles
+    for i in range(steps):
+        tr = q.MoeTrace()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(q.MOE_TRACE_MAX + 1)]
+        for j, ev in enumerate(e):
+            ev.record()   # materialise the event object
+            tr.events[j] = ev.cuda_event
+        B.step_traced(i, tr)
+        traces.append(tr)
+        evs.append(e)
+    torch.cuda.synchronize()
+    for tr, e in zip(traces, evs):
+        for j in range(tr.n_kernels):
+            name = tr.names[j].decode()
+            per.setdefault(name, []).append(e[j].elapsed_time(e[j + 1]) * 1e3)   # us
+    return {k: float(np.mean(v)) for k, v in per.items()}
+
+
+def run_workload(name, args):
+    T = __import__("synth").WORKLOADS[name]["tokens"]
+    decode_like = T <= 64
+    replicas = args.replicas or (8 if decode_like else 2)
+    B = Bench(name, replicas)
+    steps = args.steps or (400 if decode_like else (40 if T <= 4096 else 12))
+    warmup = args.warmup if args.warmup is not None else (20 if decode_like else 3)
+    n, dt = time_steps(B, steps, warmup, use_graph=decode_like)
+    B.step(0)
+    torch.cuda.synchronize()
+    n_active = B.n_active()
+    lb, lf, kern = algorithmic(B.geom, B.wfmt, B.T, n_active)
+    s_per_step = dt / n
+    res = dict(workload=name, tokens=B.T, steps=n, warmup=warmup, replicas=replicas,
+               ms_per_step=s_per_step * 1e3, tokens_per_s=B.T / s_per_step,
+               hbm_gbs=lb / s_per_step / 1e9, hbm_pct_peak=100 * lb / s_per_step / 1e9 / PEAK_HBM_GBS,
+               tflops=lf / s_per_step / 1e12, active_experts=n_active,
+               algorithmic_bytes=lb, algorithmic_flops=lf, graph=decode_like)
+    if not args.no_trace:
+        ksteps = min(steps, 64 if decode_like else 8)
+        kt = trace_kernels(B, ksteps)
+        res["kernels_us"] = kt
+        dom = max(kt, key=kt.get)
+        kb = kern.get(dom, dict(bytes=0, flops=0))
+        dur = kt[dom] * 1e-6
+        if "gemm" in dom:
+            ach = kb["flops"] / dur / 1e12
+            res["roofline"] = dict(kernel=dom, bound="mfma", achieved=ach, peak=PEAK_F16_TFLOPS,
+                                   unit="TFLOP/s", frac=ach / PEAK_F16_TFLOPS, traffic=None,
+                                   algorithmic=kb["flops"], avg_us=kt[dom])
+        else:
+            ach = kb["bytes"] / dur / 1e9
+            res["roofline"] = dict(kernel=dom, bound="hbm", achieved=ach, peak=PEAK_HBM_GBS,
+                                   unit="GB/s", frac=ach / PEAK_HBM_GBS, traffic=None,
+                                   algorithmic=kb["bytes"], avg_us=kt[dom])
+    del B
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(name):
+    """The fp64 oracle on one token of the workload, on this host's cores."""
+    import oracle
+    import synth
+    from threadpoolctl import threadpool_info
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from helpers import oracle_inputs
+    L = synth.make_layer(name, "cuda")
+    x, Wr, b, cfg, routed, shared = oracle_inputs(L, lazy=True)
+    t0 = time.perf_counter()
+    oracle.layer(x, Wr, b, cfg, routed, shared, token_idx=np.array([0]))
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return dict(value=1.0 / dt, unit="tokens/s", cores=int(threads), kind="oracle",
+                sample=f"1 token of the {name} workload (fp64 route + 8 routed + shared "
+                       f"expert FFNs incl. dequant), {dt:.1f} s")
+
+
+def copy_calibration():
+    """A plain streaming kernel of known traffic (read 1 GiB, write 1 GiB) whose
+    FETCH_SIZE / WRITE_SIZE readings scale the layer kernels' counters."""
+    n = 1 << 28
+    src = torch.randn(n, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps(dict(copy_kernel="torch.neg fp32", bytes_read=n * 4, bytes_written=n * 4,
+                          launches=5)))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the path has no multi-GPU mode); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    names = [w for w in args.workloads.split(",") if w]
+    results = {}
+    for name in names:
+        results[name] = run_workload(name, args)
+        print(f"# {name}: {results[name]['tokens_per_s']:.1f} tok/s "
+              f"{results[name]['ms_per_step']:.4f} ms/step", file=sys.stderr, flush=True)
+    head = HEADLINE if HEADLINE in results else names[0]
+    h = results[head]
+    import synth
+    geom = synth.WORKLOADS[head]["geom"]
+    line = {
+        "metric": METRIC, "value": h["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": h["steps"], "warmup": h["warmup"], "ms_per_step": h["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int4*bf16->f32" if synth.WORKLOADS[head]["wfmt"] == "int4" else "fp4*bf16->f32",
+        "data": "synthetic",
+        "config": {"workload": head, "tokens": h["tokens"], "hidden": geom["hidden"],
+                   "moe_inter": geom["moe_inter"], "experts": geom["n_routed_experts"],
+                   "top_k": geom["top_k"], "n_group": geom["n_group"],
+                   "topk_group": geom["topk_group"], "shared_inter": geom["shared_inter"],
+                   "weights": synth.WORKLOADS[head]["wfmt"], "replicas": h["replicas"]},
+        "roofline": h.get("roofline"),
+        "hbm_gbs": h["hbm_gbs"], "hbm_pct_peak": h["hbm_pct_peak"], "tflops": h["tflops"],
+        "workloads": results,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(head)
+    out = json.dumps(line)
+    print(out, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(out + "\n")
+
+
+if __name__ == "__main__":
+    main()

@@ -189,6 +189,29 @@ moe_status moe_layer(const moe_config* cfg, int32_t T, const uint16_t* x,
                      int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
                      hipStream_t stream);
 
+/* Kernel-boundary timing of moe_layer, for profiling and benchmarks.
+ * events[0..MOE_TRACE_MAX] are caller-created HIP events (hipEventCreate,
+ * timing enabled), all non-NULL; the library records events[0] on `stream`
+ * before its first kernel and events[i] right after its i-th kernel, sets
+ * n_kernels to the number of kernels it launched (<= MOE_TRACE_MAX) and
+ * names[i-1] to a static name of kernel i.  The interval between events[i-1]
+ * and events[i] is then kernel i's time on the stream.  Events beyond
+ * n_kernels are not touched. */
+#define MOE_TRACE_MAX 16
+typedef struct {
+  hipEvent_t events[MOE_TRACE_MAX + 1];
+  int32_t n_kernels;
+  const char* names[MOE_TRACE_MAX];
+} moe_trace;
+
+/* moe_layer, recording kernel-boundary events into `trace` (non-NULL; a
+ * NULL event returns MOE_ERR_INVALID_ARG).  Same results as moe_layer. */
+moe_status moe_layer_trace(const moe_config* cfg, int32_t T, const uint16_t* x,
+                           const float* router_w, const float* bias,
+                           const moe_qexperts* routed, const moe_qexperts* shared, void* y,
+                           int32_t out_dtype, int32_t* topk_ids_out, float* topk_w_out,
+                           void* ws, size_t ws_bytes, hipStream_t stream, moe_trace* trace);
+
 #ifdef __cplusplus
 }
 #endif

@@ -3,7 +3,7 @@ in include/qmoe.h) and its thin ctypes binding."""
 from .binding import (  # noqa: F401
     MoeConfig, MoeQExperts, MoeQProj, QmoeError, lib, make_config, qexperts, status_string,
     moe_workspace_size, workspace, moe_route, moe_permute, moe_expert_ffn_q4, moe_combine,
-    moe_layer, MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL,
+    moe_layer, moe_layer_trace, MoeTrace, MOE_TRACE_MAX, MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL,
     MOE_ERR_HIP, MOE_WFMT_INT4_G32_F16, MOE_WFMT_NVFP4, MOE_OUT_F32, MOE_OUT_BF16,
     MOE_MAX_TOKENS, WFMT,
 )

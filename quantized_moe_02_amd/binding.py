@@ -15,7 +15,8 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libqmoe.so")
+# QMOE_LIBRARY may name another build of the same library (e.g. a tuning variant)
+LIB_PATH = os.environ.get("QMOE_LIBRARY") or os.path.join(_HERE, "libqmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP = range(5)
 MOE_WFMT_INT4_G32_F16, MOE_WFMT_NVFP4 = 0, 1
@@ -46,6 +47,14 @@ class MoeQExperts(ctypes.Structure):
     _fields_ = [("gate", MoeQProj), ("up", MoeQProj), ("down", MoeQProj)]
 
 
+MOE_TRACE_MAX = 16
+
+
+class MoeTrace(ctypes.Structure):
+    _fields_ = [("events", ctypes.c_void_p * (MOE_TRACE_MAX + 1)), ("n_kernels", ctypes.c_int32),
+                ("names", ctypes.c_char_p * MOE_TRACE_MAX)]
+
+
 _lib = None
 
 
@@ -67,6 +76,8 @@ def lib() -> ctypes.CDLL:
             "moe_expert_ffn_q4": [cfgp, i32, vp, exp, vp, vp, vp, vp, vp, vp, sz, vp],
             "moe_combine": [cfgp, i32, vp, vp, vp, vp, vp, i32, vp],
             "moe_layer": [cfgp, i32, vp, vp, vp, exp, exp, vp, i32, vp, vp, vp, sz, vp],
+            "moe_layer_trace": [cfgp, i32, vp, vp, vp, exp, exp, vp, i32, vp, vp, vp, sz, vp,
+                                ctypes.POINTER(MoeTrace)],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -157,3 +168,16 @@ def moe_layer(cfg, T, x, router_w, bias, routed: MoeQExperts, shared: Optional[M
                            ctypes.byref(routed), None if shared is None else ctypes.byref(shared),
                            _p(y), out_dtype, _p(topk_ids_out), _p(topk_w_out), _p(ws),
                            0 if ws is None else ws.numel(), _stream(stream)), "moe_layer")
+
+
+def moe_layer_trace(cfg, T, x, router_w, bias, routed: MoeQExperts, shared: Optional[MoeQExperts],
+                    y, trace: MoeTrace, out_dtype=MOE_OUT_F32, topk_ids_out=None, topk_w_out=None,
+                    ws=None, stream=None):
+    """moe_layer recording kernel-boundary events into `trace` (whose events
+    the caller created, e.g. from torch.cuda.Event(enable_timing=True).cuda_event)."""
+    _check(lib().moe_layer_trace(ctypes.byref(cfg), T, _p(x), _p(router_w), _p(bias),
+                                 ctypes.byref(routed),
+                                 None if shared is None else ctypes.byref(shared), _p(y),
+                                 out_dtype, _p(topk_ids_out), _p(topk_w_out), _p(ws),
+                                 0 if ws is None else ws.numel(), _stream(stream),
+                                 ctypes.byref(trace)), "moe_layer_trace")

@@ -1,0 +1,602 @@
+// Small-batch path of the quantized MoE layer (T <= 4 tokens per call):
+// decode and short speculative-verify batches.  Every byte of the selected
+// experts' packed weights is streamed from HBM once; the work is memory
+// bound, so the kernels are built around keeping many independent 128-bit
+// loads in flight and doing as little else as possible.
+//
+//   K1 dec_router_shared   router logits (float64, one wave per expert) and,
+//                          in the same launch, the shared expert's gate/up
+//                          GEMV, which does not depend on the routing
+//   K2 dec_select_permute  one workgroup: per-token selection (one wave per
+//                          token) and the batch-union permutation of the
+//                          <= 64 picks
+//   K3 dec_gateup          gate/up GEMV of the selected experts with SwiGLU
+//   K4 dec_down_combine    down GEMV of every selected expert and the shared
+//                          expert for a block of output rows, with the
+//                          weighted combine done in registers
+//
+// Pages: "Show HN: Menjalankan GLM 5.2 di komputer lambat" (sections "Cara
+// kerja eksekusi MoE" -- routed experts vs resident shared expert -- and
+// "Fitur utama" -- DeepSeek-V3 router, batch-union MoE, int4
+// dequant-on-use); "NVIDIA stellt neues GLM-5.2 NVFP4 Modell vor" (section
+// "Technische Details": NVFP4 expert weights).
+#include "select_token.h"
+
+namespace qmoe {
+namespace {
+
+#ifndef QMOE_DEC_RPW
+#define QMOE_DEC_RPW 2
+#endif
+#ifndef QMOE_DEC_ITEMS
+#define QMOE_DEC_ITEMS 4
+#endif
+#ifndef QMOE_DEC_DOWN_ROWS
+#define QMOE_DEC_DOWN_ROWS 4
+#endif
+constexpr int kGPL = 3;                      // 32-input groups per lane per pass
+constexpr int kChunk = 64 * kGPL;            // groups covered by one pass of a wave
+constexpr int kRPW = QMOE_DEC_RPW;           // gate/up row pairs per pipeline item
+constexpr int kItems = QMOE_DEC_ITEMS;       // pipeline items per wave (even)
+constexpr int kPairsPerWave = kRPW * kItems;
+constexpr int kPairsPerBlock = 4 * kPairsPerWave;
+constexpr int kSharedPairsPerBlock = 4 * 2 * kRPW;  // K1: two items per wave
+static_assert(kItems % 2 == 0, "items are double-buffered in pairs");
+static_assert(32 % kPairsPerWave == 0 && 32 % (2 * kRPW) == 0, "a wave never straddles inter (a multiple of 32)");
+constexpr int kDownRows = QMOE_DEC_DOWN_ROWS; // down/combine output rows per block
+constexpr int kMaxT = kDecodeMaxTokens;
+constexpr int kRouterUnroll = 6;             // 16-byte router-weight loads per lane per pass
+
+__device__ __forceinline__ void load16(uint32_t (&d)[4], const void* p) {
+  const uint4 v = *reinterpret_cast<const uint4*>(p);
+  d[0] = v.x;
+  d[1] = v.y;
+  d[2] = v.z;
+  d[3] = v.w;
+}
+
+// sum_k w_k * a_k over one 32-input group.  wq: the group's 16 code bytes;
+// sc: its scale word (int4: fp16 bits; nvfp4: two E4M3 bytes); act: 16 pairs
+// of 16-bit activations; asum: sum of the 32 activations (int4 only).
+template <int FMT, bool F16ACT>
+__device__ __forceinline__ float group_dot(const uint32_t (&wq)[4], uint32_t sc,
+                                           const uint32_t (&act)[16], float asum, float gs) {
+  if constexpr (FMT == MOE_WFMT_INT4_G32_F16) {
+    float d = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        d = F16ACT ? dot2_f16(int4_pair_f16(wq[j], k), act[4 * j + k], d)
+                   : dot2_bf16(int4_pair_bf16(wq[j], k), act[4 * j + k], d);
+    return 16.0f * half_bits_to_f32(sc & 0xffffu) * fmaf(-1.5f, asum, d);
+  } else {
+    float d0 = 0.0f, d1 = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        d0 = F16ACT ? dot2_f16(fp4_pair_f16(wq[j], k), act[4 * j + k], d0)
+                    : dot2_bf16(fp4_pair_bf16(wq[j], k), act[4 * j + k], d0);
+#pragma unroll
+    for (int j = 2; j < 4; ++j)
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        d1 = F16ACT ? dot2_f16(fp4_pair_f16(wq[j], k), act[4 * j + k], d1)
+                    : dot2_bf16(fp4_pair_bf16(wq[j], k), act[4 * j + k], d1);
+    return fmaf(e4m3_to_f32(sc, 0), d0, e4m3_to_f32(sc, 1) * d1) * gs;
+  }
+}
+
+// Sum of the 32 activations of a group, for the int4 offset correction.
+template <bool F16ACT>
+__device__ __forceinline__ float act_sum(const uint32_t (&act)[16]) {
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    s = F16ACT ? dot2_f16(act[i], 0x3C003C00u, s) : dot2_bf16(act[i], 0x3F803F80u, s);
+  return s;
+}
+
+// ---------------------------------------------------------------------------
+// Double-buffered gate/up GEMV of one wave.  The wave owns kPairsPerWave
+// consecutive row pairs (gate row i, up row i), processed as kItems items of
+// kRPW pairs; item i+1's loads are in flight while item i is dequantised and
+// reduced, so the memory pipe stays busy.  Lane l owns the 32-input groups
+// l, l+64, ... (GPL of them); x (one token) lives in registers.
+// ---------------------------------------------------------------------------
+template <int GPL>
+struct GateUpItem {
+  uint32_t wg[kRPW][GPL][4], wu[kRPW][GPL][4], sg[kRPW][GPL], su[kRPW][GPL];
+};
+
+// Buffers of one expert's gate and up projections (codes and scales).
+struct GateUpBufs {
+  rsrc_t qg, qu, sg, su;
+  uint32_t rowBytes, scaleRowBytes;
+};
+
+template <int GPL>
+__device__ __forceinline__ void gu_load(GateUpItem<GPL>& it, const GateUpBufs& b,
+                                        const uint32_t (&off)[GPL], int pair0) {
+#pragma unroll
+  for (int r = 0; r < kRPW; ++r) {
+    const uint32_t row = (uint32_t)(pair0 + r);
+#pragma unroll
+    for (int j = 0; j < GPL; ++j) {
+      bload16(it.wg[r][j], b.qg, off[j] * 16u, row * b.rowBytes);
+      bload16(it.wu[r][j], b.qu, off[j] * 16u, row * b.rowBytes);
+      it.sg[r][j] = bload_u16(b.sg, off[j] * 2u, row * b.scaleRowBytes);
+      it.su[r][j] = bload_u16(b.su, off[j] * 2u, row * b.scaleRowBytes);
+    }
+  }
+}
+
+template <int FMT, int GPL>
+__device__ __forceinline__ void gu_compute(const GateUpItem<GPL>& it, const uint32_t (&xw)[GPL][16],
+                                           const float (&xs)[GPL], const bool (&ok)[GPL], float gg,
+                                           float gu, int pair0, uint16_t* __restrict__ hrow) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int r = 0; r < kRPW; ++r) {
+    float g = 0.0f, u = 0.0f;
+#pragma unroll
+    for (int j = 0; j < GPL; ++j) {
+      const float vg = group_dot<FMT, false>(it.wg[r][j], it.sg[r][j], xw[j], xs[j], gg);
+      const float vu = group_dot<FMT, false>(it.wu[r][j], it.su[r][j], xw[j], xs[j], gu);
+      g += ok[j] ? vg : 0.0f;
+      u += ok[j] ? vu : 0.0f;
+      // bound the number of dequantised pairs the scheduler keeps live
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    g = wave_sum(g);
+    u = wave_sum(u);
+    if (lane == r) {
+      const _Float16 hv = (_Float16)silu_mul(g, u);
+      hrow[pair0 + r] = __builtin_bit_cast(uint16_t, hv);
+    }
+  }
+}
+
+// Gate/up for row pairs [pair_begin, pair_begin + kPairsPerWave) of one
+// expert (rows [row_base, row_base + inter) of the projections) and one token
+// x; h written to hrow.
+template <int FMT, int GPL, int ITEMS = kItems>
+__device__ __forceinline__ void gateup_wave(const uint16_t* __restrict__ x, int H,
+                                            const ProjPtr& Pg, const ProjPtr& Pu, size_t row_base,
+                                            int inter, int pair_begin, float gg, float gu,
+                                            uint16_t* __restrict__ hrow) {
+  const int lane = threadIdx.x & 63;
+  const int nG = H / 32;
+  GateUpBufs b;
+  b.rowBytes = (uint32_t)H / 2;
+  b.scaleRowBytes = (uint32_t)nG * 2;
+  b.qg = make_rsrc(Pg.q + row_base * b.rowBytes, (uint32_t)inter * b.rowBytes);
+  b.qu = make_rsrc(Pu.q + row_base * b.rowBytes, (uint32_t)inter * b.rowBytes);
+  b.sg = make_rsrc(reinterpret_cast<const uint16_t*>(Pg.s) + row_base * nG, (uint32_t)inter * b.scaleRowBytes);
+  b.su = make_rsrc(reinterpret_cast<const uint16_t*>(Pu.s) + row_base * nG, (uint32_t)inter * b.scaleRowBytes);
+  const rsrc_t xr = make_rsrc(x, (uint32_t)H * 2u);
+  uint32_t cc[GPL];
+  bool ok[GPL];
+#pragma unroll
+  for (int j = 0; j < GPL; ++j) {
+    const int c = lane + 64 * j;
+    ok[j] = c < nG;
+    cc[j] = ok[j] ? c : nG - 1;
+  }
+  GateUpItem<GPL> A, B;
+  gu_load<GPL>(A, b, cc, pair_begin);
+  gu_load<GPL>(B, b, cc, pair_begin + kRPW);
+  uint32_t xw[GPL][16];
+  float xs[GPL];
+#pragma unroll
+  for (int j = 0; j < GPL; ++j) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t t4[4];
+      bload16(t4, xr, cc[j] * 64u + 16u * q, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xw[j][4 * q + i] = t4[i];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < GPL; ++j)
+    xs[j] = (FMT == MOE_WFMT_INT4_G32_F16) ? act_sum<false>(xw[j]) : 0.0f;
+#pragma unroll
+  for (int i = 0; i < ITEMS; i += 2) {
+    const int p = pair_begin + i * kRPW;
+    gu_compute<FMT, GPL>(A, xw, xs, ok, gg, gu, p, hrow);
+    __builtin_amdgcn_sched_barrier(0);
+    if (i + 2 < ITEMS) gu_load<GPL>(A, b, cc, p + 2 * kRPW);
+    __builtin_amdgcn_sched_barrier(0);
+    gu_compute<FMT, GPL>(B, xw, xs, ok, gg, gu, p + kRPW, hrow);
+    __builtin_amdgcn_sched_barrier(0);
+    if (i + 3 < ITEMS) gu_load<GPL>(B, b, cc, p + 3 * kRPW);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K1: router logits (blocks [0, nrb)) and shared-expert gate/up (the rest)
+// ---------------------------------------------------------------------------
+template <int FMT, int GPL>
+__global__ void __launch_bounds__(256) dec_router_shared_kernel(DecodeArgs a, int nrb) {
+  __shared__ double rpart[4][kMaxT];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if ((int)blockIdx.x < nrb) {
+    // expert e's logits: the four waves take quarters of the hidden dimension
+    const int e = blockIdx.x;
+    const int H = a.H, T = a.T;
+    const int q0 = wv * (H / 4), q1 = q0 + H / 4;
+    const float* wrow = a.router_w + (size_t)e * H;
+    double acc[kMaxT];
+#pragma unroll
+    for (int t = 0; t < kMaxT; ++t) acc[t] = 0.0;
+    for (int h0 = q0; h0 < q1; h0 += 256 * kRouterUnroll) {
+      float4 w4[kRouterUnroll];
+      uint2 xv[kRouterUnroll][kMaxT];
+      bool ok[kRouterUnroll];
+#pragma unroll
+      for (int i = 0; i < kRouterUnroll; ++i) {
+        const int h_raw = h0 + 256 * i + lane * 4;
+        ok[i] = h_raw < q1;
+        const int h = ok[i] ? h_raw : q0;
+        w4[i] = *reinterpret_cast<const float4*>(wrow + h);
+#pragma unroll
+        for (int t = 0; t < kMaxT; ++t)
+          xv[i][t] = *reinterpret_cast<const uint2*>(a.x + (size_t)(t < T ? t : 0) * H + h);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < kRouterUnroll; ++i) {
+        if (!ok[i]) continue;
+#pragma unroll
+        for (int t = 0; t < kMaxT; ++t) {
+          double s2 = acc[t];
+          s2 = fma((double)bf16_lo(xv[i][t].x), (double)w4[i].x, s2);
+          s2 = fma((double)bf16_hi(xv[i][t].x), (double)w4[i].y, s2);
+          s2 = fma((double)bf16_lo(xv[i][t].y), (double)w4[i].z, s2);
+          s2 = fma((double)bf16_hi(xv[i][t].y), (double)w4[i].w, s2);
+          acc[t] = s2;
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kMaxT; ++t) {
+      const double v = wave_sum(acc[t]);
+      if (lane == 0) rpart[wv][t] = v;
+    }
+    __syncthreads();
+    if (threadIdx.x < T)
+      a.logits[(size_t)threadIdx.x * a.E + e] =
+          ((rpart[0][threadIdx.x] + rpart[1][threadIdx.x]) + rpart[2][threadIdx.x]) +
+          rpart[3][threadIdx.x];
+    return;
+  }
+  // shared expert: all T tokens
+  const ExpertSet& S = a.shared;
+  const int pair0 = ((int)blockIdx.x - nrb) * kSharedPairsPerBlock + wv * (2 * kRPW);
+  if (pair0 >= S.inter) return;
+  const float gg = (FMT == MOE_WFMT_NVFP4) ? S.gate.g[0] : 1.0f;
+  const float gu = (FMT == MOE_WFMT_NVFP4) ? S.up.g[0] : 1.0f;
+  for (int t = 0; t < a.T; ++t)
+    gateup_wave<FMT, GPL, 2>(a.x + (size_t)t * a.H, a.H, S.gate, S.up, 0, S.inter, pair0, gg, gu,
+                             a.h_shared + (size_t)t * a.ldh);
+}
+
+// ---------------------------------------------------------------------------
+// K2: selection of every token, then the permutation of the P <= 64 picks
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) dec_select_permute_kernel(DecodeArgs a) {
+  __shared__ SelectScratch sc[4];
+  __shared__ int pid[64];
+  __shared__ float pw[64];
+  __shared__ int spid[64];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int K = a.K, P = a.T * a.K;
+  if (wv < a.T) {
+    int id, rank;
+    float w;
+    select_token(a.logits + (size_t)wv * a.E, a.bias, a.E, a.G, a.TG, K, a.rsf, sc[wv], id, w,
+                 rank);
+    if (lane < K) {
+      a.ids[wv * K + rank] = id;
+      a.tw[wv * K + rank] = w;
+      pid[wv * K + rank] = id;
+      pw[wv * K + rank] = w;
+    }
+  }
+  __syncthreads();
+  if (wv != 0) return;
+  // stable sort of the picks by expert: rank = #picks with a smaller id, or the
+  // same id and a smaller pick index
+  int e = 0, pos = 0;
+  if (lane < P) {
+    e = pid[lane];
+    for (int q = 0; q < P; ++q) {
+      const int o = pid[q];
+      pos += (o < e || (o == e && q < lane)) ? 1 : 0;
+    }
+    a.sorted_token[pos] = lane / K;
+    a.inv_perm[lane] = pos;
+    a.sorted_w[pos] = pw[lane];
+    spid[pos] = e;
+  }
+  wave_lds_sync();
+  const int se = lane < P ? spid[lane] : -1;
+  const bool first = lane < P && (lane == 0 || spid[lane - 1] != se);
+  const uint64_t firsts = __ballot(first);
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  if (first) a.active[__popcll(firsts & lt)] = se;
+  if (lane == 0) a.n_active[0] = __popcll(firsts);
+  for (int x = lane; x <= a.E; x += 64) {
+    int c = 0;
+    for (int q = 0; q < P; ++q) c += (spid[q] < x) ? 1 : 0;
+    a.offsets[x] = c;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K3: gate/up of the selected experts.  Block = (row block, slot); each wave
+// runs the double-buffered GEMV over its row pairs, once per token routed to
+// the expert (a second token re-reads the rows, mostly from cache).
+// ---------------------------------------------------------------------------
+template <int FMT, int GPL>
+__global__ void __launch_bounds__(256) dec_gateup_kernel(DecodeArgs a) {
+  const int slot = blockIdx.y;
+  if (slot >= *a.n_active) return;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const ExpertSet& R = a.routed;
+  const int pair0 = blockIdx.x * kPairsPerBlock + wv * kPairsPerWave;
+  if (pair0 >= R.inter) return;
+  const int e = a.active[slot];
+  const int p0 = a.offsets[e], M = a.offsets[e + 1] - p0;
+  const float gg = (FMT == MOE_WFMT_NVFP4) ? R.gate.g[e] : 1.0f;
+  const float gu = (FMT == MOE_WFMT_NVFP4) ? R.up.g[e] : 1.0f;
+  for (int m = 0; m < M; ++m) {
+    const int t = a.sorted_token[p0 + m];
+    gateup_wave<FMT, GPL>(a.x + (size_t)t * a.H, a.H, R.gate, R.up, (size_t)e * R.inter, R.inter,
+                          pair0, gg, gu, a.h_routed + (size_t)(p0 + m) * a.ldh);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K4: down projection of every selected expert and the shared expert for
+// kDownRows output rows, combined into y in registers.  The four waves of a
+// block take expert slots round-robin; each wave keeps the next slot's rows
+// in flight while it dequantises the current one.  Partial sums meet in LDS
+// in wave order, so the result does not depend on timing.
+// ---------------------------------------------------------------------------
+struct DownItem {
+  uint32_t w[kDownRows][4];
+  uint32_t sc[kDownRows];
+  uint32_t h[16];
+};
+
+struct SlotInfo {
+  rsrc_t q, s, h;
+  int p0, M, nG;
+  float g;
+  bool routed;
+};
+
+template <int FMT>
+__device__ __forceinline__ SlotInfo slot_info(const DecodeArgs& a, int s, int n_routed, int row0) {
+  SlotInfo d;
+  d.routed = s < n_routed;
+  const ExpertSet& X = d.routed ? a.routed : a.shared;
+  const int e = d.routed ? a.active[s] : 0;
+  d.p0 = d.routed ? a.offsets[e] : 0;
+  d.M = d.routed ? a.offsets[e + 1] - d.p0 : a.T;
+  d.nG = X.inter / 32;
+  const uint32_t rowBytes = (uint32_t)X.inter / 2;
+  const size_t rb = (size_t)e * a.H + row0;
+  d.q = make_rsrc(X.down.q + rb * rowBytes, kDownRows * rowBytes);
+  d.s = make_rsrc(reinterpret_cast<const uint16_t*>(X.down.s) + rb * d.nG, kDownRows * d.nG * 2u);
+  const uint16_t* hp = d.routed ? a.h_routed + (size_t)d.p0 * a.ldh : a.h_shared;
+  d.h = make_rsrc(hp, (uint32_t)d.M * a.ldh * 2u);
+  d.g = (FMT == MOE_WFMT_NVFP4) ? X.down.g[e] : 1.0f;
+  return d;
+}
+
+__device__ __forceinline__ void down_load(DownItem& it, const SlotInfo& d, uint32_t c) {
+  const uint32_t rowBytes = (uint32_t)d.nG * 16u;
+#pragma unroll
+  for (int r = 0; r < kDownRows; ++r) {
+    bload16(it.w[r], d.q, c * 16u, r * rowBytes);
+    it.sc[r] = bload_u16(d.s, c * 2u, r * (uint32_t)d.nG * 2u);
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t t4[4];
+    bload16(t4, d.h, c * 64u + 16u * q, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) it.h[4 * q + i] = t4[i];
+  }
+}
+
+template <int FMT, int MT>
+__device__ __forceinline__ void down_compute(const DownItem& it, const SlotInfo& d, uint32_t c,
+                                             bool valid, const DecodeArgs& a,
+                                             float (&acc)[MT][kDownRows]) {
+  const bool ok = valid && (int)c < d.nG;
+  for (int m = 0; m < d.M; ++m) {
+    uint32_t hm[16];
+    if (m == 0) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) hm[i] = it.h[i];
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t t4[4];
+        bload16(t4, d.h, c * 64u + 16u * q, (uint32_t)m * a.ldh * 2u);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hm[4 * q + i] = t4[i];
+      }
+    }
+    const float hs = (FMT == MOE_WFMT_INT4_G32_F16) ? act_sum<true>(hm) : 0.0f;
+    const int t = d.routed ? a.sorted_token[d.p0 + m] : m;
+    const float wpick = ok ? (d.routed ? a.sorted_w[d.p0 + m] : 1.0f) : 0.0f;
+#pragma unroll
+    for (int r = 0; r < kDownRows; ++r) {
+      const float v = wpick * group_dot<FMT, true>(it.w[r], it.sc[r], hm, hs, d.g);
+#pragma unroll
+      for (int tt = 0; tt < MT; ++tt)
+        if (tt == t) acc[tt][r] += v;
+    }
+  }
+}
+
+template <int FMT, int MT>
+__global__ void __launch_bounds__(256) dec_down_combine_kernel(DecodeArgs a) {
+  __shared__ float part[4][MT][kDownRows];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int H = a.H, T = a.T;
+  const int row0 = blockIdx.x * kDownRows;
+  const int n_routed = *a.n_active;
+  const int nslots = n_routed + (a.has_shared ? 1 : 0);
+  const int nG_max = max(a.routed.inter, a.has_shared ? a.shared.inter : 0) / 32;
+  float acc[MT][kDownRows];
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int r = 0; r < kDownRows; ++r) acc[t][r] = 0.0f;
+
+  if (wv < nslots) {
+    const int last = nslots - 1;
+    for (int c0 = 0; c0 < nG_max; c0 += 64) {
+      const uint32_t c = (uint32_t)(c0 + lane);
+      // slots wv, wv+4, ... with two in flight: A holds slot sa, B slot sb.  A
+      // prefetch past the last slot reads the last slot again (in bounds) and
+      // is never computed.
+      int sa = wv, sb = wv + 4;
+      SlotInfo da = slot_info<FMT>(a, sa, n_routed, row0);
+      SlotInfo db = slot_info<FMT>(a, min(sb, last), n_routed, row0);
+      DownItem A, B;
+      down_load(A, da, c);
+      down_load(B, db, c);
+      while (true) {
+        __builtin_amdgcn_sched_barrier(0);
+        down_compute<FMT, MT>(A, da, c, true, a, acc);  // sa <= last here
+        __builtin_amdgcn_sched_barrier(0);
+        if (sb > last) break;
+        sa = sb + 4;
+        da = slot_info<FMT>(a, min(sa, last), n_routed, row0);
+        down_load(A, da, c);
+        __builtin_amdgcn_sched_barrier(0);
+        down_compute<FMT, MT>(B, db, c, true, a, acc);  // sb <= last here
+        __builtin_amdgcn_sched_barrier(0);
+        if (sa > last) break;
+        sb = sa + 4;
+        db = slot_info<FMT>(a, min(sb, last), n_routed, row0);
+        down_load(B, db, c);
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    if (t < T) {
+#pragma unroll
+      for (int r = 0; r < kDownRows; ++r) {
+        const float v = wave_sum(acc[t][r]);
+        if (lane == 0) part[wv][t][r] = v;
+      }
+    }
+  }
+  __syncthreads();
+  const int t = threadIdx.x / kDownRows, r = threadIdx.x % kDownRows;
+  if (t < T) {
+    const float v = ((part[0][t][r] + part[1][t][r]) + part[2][t][r]) + part[3][t][r];
+    if (a.out_bf16) {
+      uint32_t u = __float_as_uint(v);
+      if ((u & 0x7fffffffu) > 0x7f800000u) {
+        u = (u >> 16) | 0x40u;
+      } else {
+        u += 0x7fffu + ((u >> 16) & 1u);
+        u >>= 16;
+      }
+      reinterpret_cast<uint16_t*>(a.y)[(size_t)t * H + row0 + r] = (uint16_t)u;
+    } else {
+      reinterpret_cast<float*>(a.y)[(size_t)t * H + row0 + r] = v;
+    }
+  }
+}
+
+template <int GPL>
+hipError_t launch_k1(const DecodeArgs& a, hipStream_t s, int nrb, int nsb) {
+  if (a.wfmt == MOE_WFMT_NVFP4)
+    hipLaunchKernelGGL((dec_router_shared_kernel<MOE_WFMT_NVFP4, GPL>), dim3(nrb + nsb), dim3(256),
+                       0, s, a, nrb);
+  else
+    hipLaunchKernelGGL((dec_router_shared_kernel<MOE_WFMT_INT4_G32_F16, GPL>), dim3(nrb + nsb),
+                       dim3(256), 0, s, a, nrb);
+  return hipGetLastError();
+}
+
+template <int GPL>
+hipError_t launch_k3(const DecodeArgs& a, hipStream_t s, dim3 grid) {
+  if (a.wfmt == MOE_WFMT_NVFP4)
+    hipLaunchKernelGGL((dec_gateup_kernel<MOE_WFMT_NVFP4, GPL>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((dec_gateup_kernel<MOE_WFMT_INT4_G32_F16, GPL>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool decode_supported(int H) { return H / 32 <= 64 * kDecodeMaxGPL; }
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
+  if (a.T == 0) return hipSuccess;
+  hipError_t e;
+  const int gpl = (a.H / 32 + 63) / 64;
+  const int nrb = a.E;
+  const int nsb =
+      a.has_shared ? (a.shared.inter + kSharedPairsPerBlock - 1) / kSharedPairsPerBlock : 0;
+  const bool f4 = a.wfmt == MOE_WFMT_NVFP4;
+  switch (gpl) {
+    case 1: e = launch_k1<1>(a, s, nrb, nsb); break;
+    case 2: e = launch_k1<2>(a, s, nrb, nsb); break;
+    case 3: e = launch_k1<3>(a, s, nrb, nsb); break;
+    default: e = launch_k1<4>(a, s, nrb, nsb); break;
+  }
+  if (e != hipSuccess) return e;
+  if (tr && (e = tr->mark("dec_router_shared")) != hipSuccess) return e;
+
+  hipLaunchKernelGGL(dec_select_permute_kernel, dim3(1), dim3(256), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (tr && (e = tr->mark("dec_select_permute")) != hipSuccess) return e;
+
+  const int slots = a.E < a.T * a.K ? a.E : a.T * a.K;
+  dim3 g3((a.routed.inter + kPairsPerBlock - 1) / kPairsPerBlock, slots);
+  switch (gpl) {
+    case 1: e = launch_k3<1>(a, s, g3); break;
+    case 2: e = launch_k3<2>(a, s, g3); break;
+    case 3: e = launch_k3<3>(a, s, g3); break;
+    default: e = launch_k3<4>(a, s, g3); break;
+  }
+  if (e != hipSuccess) return e;
+  if (tr && (e = tr->mark("dec_gateup")) != hipSuccess) return e;
+
+  dim3 g4(a.H / kDownRows);
+  if (a.T == 1) {
+    if (f4)
+      hipLaunchKernelGGL((dec_down_combine_kernel<MOE_WFMT_NVFP4, 1>), g4, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((dec_down_combine_kernel<MOE_WFMT_INT4_G32_F16, 1>), g4, dim3(256), 0, s, a);
+  } else {
+    if (f4)
+      hipLaunchKernelGGL((dec_down_combine_kernel<MOE_WFMT_NVFP4, kMaxT>), g4, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((dec_down_combine_kernel<MOE_WFMT_INT4_G32_F16, kMaxT>), g4, dim3(256), 0, s,
+                         a);
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (tr && (e = tr->mark("dec_down_combine")) != hipSuccess) return e;
+  return hipSuccess;
+}
+
+}  // namespace qmoe

@@ -283,7 +283,7 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
 
 }  // namespace
 
-hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
+hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, Tracer* tr) {
   if (a.T == 0) return hipSuccess;
   const int slots = (a.has_routed ? a.max_slots : 0) + (a.has_dense ? 1 : 0);
   if (slots == 0) return hipSuccess;
@@ -292,20 +292,28 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
   if (a.has_dense && a.dense.inter > max_inter) max_inter = a.dense.inter;
   dim3 g1((max_inter + kRowsPerBlock - 1) / kRowsPerBlock, slots);
   dim3 g2((a.H + kRowsPerBlock - 1) / kRowsPerBlock, slots);
-  if (a.wfmt == MOE_WFMT_INT4_G32_F16) {
+  hipError_t e;
+  if (a.wfmt == MOE_WFMT_INT4_G32_F16)
     hipLaunchKernelGGL(gateup_gemv_kernel<MOE_WFMT_INT4_G32_F16>, g1, dim3(256), 0, s, a);
-    hipLaunchKernelGGL(down_gemv_kernel<MOE_WFMT_INT4_G32_F16>, g2, dim3(256), 0, s, a);
-  } else {
+  else
     hipLaunchKernelGGL(gateup_gemv_kernel<MOE_WFMT_NVFP4>, g1, dim3(256), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (tr && (e = tr->mark("gateup_gemv")) != hipSuccess) return e;
+  if (a.wfmt == MOE_WFMT_INT4_G32_F16)
+    hipLaunchKernelGGL(down_gemv_kernel<MOE_WFMT_INT4_G32_F16>, g2, dim3(256), 0, s, a);
+  else
     hipLaunchKernelGGL(down_gemv_kernel<MOE_WFMT_NVFP4>, g2, dim3(256), 0, s, a);
-  }
-  return hipGetLastError();
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (tr && (e = tr->mark("down_gemv")) != hipSuccess) return e;
+  return hipSuccess;
 }
 
-hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s, Tracer* tr) {
   if (a.T == 0) return hipSuccess;
   hipLaunchKernelGGL(combine_kernel, dim3(a.T), dim3(256), 0, s, a);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && tr) e = tr->mark("combine");
+  return e;
 }
 
 }  // namespace qmoe

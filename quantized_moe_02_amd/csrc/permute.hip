@@ -81,11 +81,13 @@ __global__ void __launch_bounds__(kPermThreads) permute_kernel(
 
 }  // namespace
 
-hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t s, Tracer* tr) {
   if (a.T == 0) return hipSuccess;
   hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), 0, s, a.ids, a.offsets,
                      a.sorted_token, a.inv_perm, a.active, a.n_active, a.T * a.K, a.K, a.E);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && tr) e = tr->mark("permute");
+  return e;
 }
 
 }  // namespace qmoe

@@ -106,6 +106,7 @@ Workspace carve_workspace(const moe_config& c, int T, void* base) {
   const size_t o_na = take(4 * sizeof(int32_t));
   const size_t o_st = take(P * sizeof(int32_t));
   const size_t o_inv = take(P * sizeof(int32_t));
+  const size_t o_sw = take(P * sizeof(float));
   const size_t o_h = take((P + T) * imax * sizeof(uint16_t));
   const size_t o_O = take((P + T) * H * sizeof(float));
   w.total = off;
@@ -119,6 +120,7 @@ Workspace carve_workspace(const moe_config& c, int T, void* base) {
     w.n_active = reinterpret_cast<int32_t*>(b + o_na);
     w.sorted_token = reinterpret_cast<int32_t*>(b + o_st);
     w.inv_perm = reinterpret_cast<int32_t*>(b + o_inv);
+    w.sorted_w = reinterpret_cast<float*>(b + o_sw);
     w.h = reinterpret_cast<uint16_t*>(b + o_h);
     w.O = reinterpret_cast<float*>(b + o_O);
   }
@@ -247,10 +249,14 @@ moe_status moe_combine(const moe_config* cfg, int32_t T, const float* expert_out
   return hip_status(launch_combine(a, stream));
 }
 
-moe_status moe_layer(const moe_config* cfg, int32_t T, const uint16_t* x, const float* router_w,
-                     const float* bias, const moe_qexperts* routed, const moe_qexperts* shared,
-                     void* y, int32_t out_dtype, int32_t* topk_ids_out, float* topk_w_out,
-                     void* ws, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+moe_status layer_impl(const moe_config* cfg, int32_t T, const uint16_t* x, const float* router_w,
+                      const float* bias, const moe_qexperts* routed, const moe_qexperts* shared,
+                      void* y, int32_t out_dtype, int32_t* topk_ids_out, float* topk_w_out,
+                      void* ws, size_t ws_bytes, hipStream_t stream, moe_trace* trace) {
   moe_status s;
   if ((s = check_cfg(cfg)) != MOE_OK) return s;
   if ((s = check_T(T)) != MOE_OK) return s;
@@ -264,28 +270,73 @@ moe_status moe_layer(const moe_config* cfg, int32_t T, const uint16_t* x, const 
     return MOE_ERR_INVALID_ARG;
   }
   if ((s = check_ws(*cfg, T, ws, ws_bytes)) != MOE_OK) return s;
-  if (T == 0) return MOE_OK;
+  if (trace) {
+    for (int i = 0; i <= MOE_TRACE_MAX; ++i)
+      if (!trace->events[i]) return MOE_ERR_INVALID_ARG;
+  }
+  if (T == 0) {
+    if (trace) trace->n_kernels = 0;
+    return MOE_OK;
+  }
 
   const Workspace w = carve_workspace(*cfg, T, ws);
   const size_t P = (size_t)T * cfg->top_k;
+  Tracer tracer;
+  tracer.t = trace;
+  tracer.s = stream;
+  Tracer* tr = trace ? &tracer : nullptr;
+  if (tr && tr->begin() != hipSuccess) return MOE_ERR_HIP;
   int32_t* ids = topk_ids_out ? topk_ids_out : w.ids;
   float* tw = topk_w_out ? topk_w_out : w.tw;
   hipError_t e;
+  const bool has_shared = cfg->n_shared_experts == 1;
+  const int ldh = std::max(cfg->moe_inter, has_shared ? cfg->shared_inter : 0);
+  if (T <= kDecodeMaxTokens && decode_supported(cfg->hidden)) {
+    DecodeArgs d{};
+    d.x = x;
+    d.T = T;
+    d.H = cfg->hidden;
+    d.E = cfg->n_routed_experts;
+    d.G = cfg->n_group;
+    d.TG = cfg->topk_group;
+    d.K = cfg->top_k;
+    d.rsf = cfg->routed_scaling_factor;
+    d.router_w = router_w;
+    d.bias = bias;
+    d.logits = w.logits;
+    d.ids = ids;
+    d.tw = tw;
+    d.offsets = w.offsets;
+    d.sorted_token = w.sorted_token;
+    d.inv_perm = w.inv_perm;
+    d.active = w.active;
+    d.n_active = w.n_active;
+    d.sorted_w = w.sorted_w;
+    d.routed = expert_set(*routed, cfg->moe_inter);
+    d.has_shared = has_shared;
+    if (has_shared) d.shared = expert_set(*shared, cfg->shared_inter);
+    d.h_routed = w.h;
+    d.h_shared = w.h + P * ldh;
+    d.ldh = ldh;
+    d.y = y;
+    d.out_bf16 = out_dtype == MOE_OUT_BF16;
+    d.wfmt = cfg->wfmt;
+    return hip_status(launch_decode(d, stream, tr));
+  }
   RouteArgs ra{x, router_w, bias, ids, tw, w.logits, T, cfg->hidden, cfg->n_routed_experts,
                cfg->n_group, cfg->topk_group, cfg->top_k, cfg->routed_scaling_factor};
-  if ((e = launch_route(ra, stream)) != hipSuccess) return MOE_ERR_HIP;
+  if ((e = launch_route(ra, stream, tr)) != hipSuccess) return MOE_ERR_HIP;
   PermuteArgs pa{ids, w.offsets, w.sorted_token, w.inv_perm, w.active, w.n_active,
                  T, cfg->top_k, cfg->n_routed_experts};
-  if ((e = launch_permute(pa, stream)) != hipSuccess) return MOE_ERR_HIP;
+  if ((e = launch_permute(pa, stream, tr)) != hipSuccess) return MOE_ERR_HIP;
 
-  const bool has_shared = cfg->n_shared_experts == 1;
   FfnArgs fa{};
   fa.x = x;
   fa.T = T;
   fa.H = cfg->hidden;
   fa.K = cfg->top_k;
   fa.wfmt = cfg->wfmt;
-  fa.ldh = std::max(cfg->moe_inter, has_shared ? cfg->shared_inter : 0);
+  fa.ldh = ldh;
   fa.has_routed = true;
   fa.routed = expert_set(*routed, cfg->moe_inter);
   fa.max_slots = (int)std::min<int64_t>(cfg->n_routed_experts, (int64_t)P);
@@ -301,10 +352,32 @@ moe_status moe_layer(const moe_config* cfg, int32_t T, const uint16_t* x, const 
     fa.h_dense = w.h + P * fa.ldh;
     fa.o_dense = w.O + P * cfg->hidden;
   }
-  if ((e = launch_ffn(fa, stream)) != hipSuccess) return MOE_ERR_HIP;
+  if ((e = launch_ffn(fa, stream, tr)) != hipSuccess) return MOE_ERR_HIP;
   CombineArgs ca{w.O, w.inv_perm, tw, has_shared ? w.O + P * cfg->hidden : nullptr, y,
                  out_dtype == MOE_OUT_BF16, T, cfg->hidden, cfg->top_k};
-  return hip_status(launch_combine(ca, stream));
+  return hip_status(launch_combine(ca, stream, tr));
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_layer(const moe_config* cfg, int32_t T, const uint16_t* x, const float* router_w,
+                     const float* bias, const moe_qexperts* routed, const moe_qexperts* shared,
+                     void* y, int32_t out_dtype, int32_t* topk_ids_out, float* topk_w_out,
+                     void* ws, size_t ws_bytes, hipStream_t stream) {
+  return layer_impl(cfg, T, x, router_w, bias, routed, shared, y, out_dtype, topk_ids_out,
+                    topk_w_out, ws, ws_bytes, stream, nullptr);
+}
+
+moe_status moe_layer_trace(const moe_config* cfg, int32_t T, const uint16_t* x,
+                           const float* router_w, const float* bias, const moe_qexperts* routed,
+                           const moe_qexperts* shared, void* y, int32_t out_dtype,
+                           int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                           hipStream_t stream, moe_trace* trace) {
+  if (!trace) return MOE_ERR_INVALID_ARG;
+  return layer_impl(cfg, T, x, router_w, bias, routed, shared, y, out_dtype, topk_ids_out,
+                    topk_w_out, ws, ws_bytes, stream, trace);
 }
 
 }  // extern "C"

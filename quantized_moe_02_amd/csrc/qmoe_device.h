@@ -33,17 +33,41 @@ __device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
 // exactly.  A group sum of such values times x is then
 //   sum (u-8) x = 16 * sum (1+u/16) x - 24 * sum x.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t int4_pair_bf16(uint32_t w, int k) {
+// (x & mask) | one in a single v_and_or_b32.  gfx9 VOP3 encodings cannot hold
+// 32-bit literals, so left alone the compiler splits this into v_and + v_or;
+// here the mask comes from an SGPR and `one` from a VGPR (one constant-bus read).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t one) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(one));
+  return r;
+}
+// A VGPR holding `c`, opaque to the optimiser so it stays a register operand.
+__device__ __forceinline__ uint32_t vreg(uint32_t c) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "s"(c));
+  return r;
+}
+// One-constants for the two 16-bit float flavours (1.0 in both halves).
+struct Int4Consts {
+  uint32_t one_bf16, one_f16;
+};
+__device__ __forceinline__ Int4Consts int4_consts() { return {vreg(0x3F803F80u), vreg(0x3C003C00u)}; }
+
+__device__ __forceinline__ uint32_t int4_pair_bf16(uint32_t w, int k, uint32_t one) {
   // bf16: 7 mantissa bits, code goes to bits [3,7) of each half
-  const uint32_t m = 0x00780078u, one = 0x3F803F80u;
-  uint32_t s = (k == 0) ? (w << 3) : (w >> (4 * k - 3));
-  return (s & m) | one;
+  const uint32_t s = (k == 0) ? (w << 3) : (w >> (4 * k - 3));
+  return and_or(s, 0x00780078u, one);
+}
+__device__ __forceinline__ uint32_t int4_pair_f16(uint32_t w, int k, uint32_t one) {
+  // fp16: 10 mantissa bits, code goes to bits [6,10) of each half
+  const uint32_t s = (k == 0) ? (w << 6) : (k == 1) ? (w << 2) : (w >> (4 * k - 6));
+  return and_or(s, 0x03C003C0u, one);
+}
+__device__ __forceinline__ uint32_t int4_pair_bf16(uint32_t w, int k) {
+  return int4_pair_bf16(w, k, 0x3F803F80u);
 }
 __device__ __forceinline__ uint32_t int4_pair_f16(uint32_t w, int k) {
-  // fp16: 10 mantissa bits, code goes to bits [6,10) of each half
-  const uint32_t m = 0x03C003C0u, one = 0x3C003C00u;
-  uint32_t s = (k == 0) ? (w << 6) : (k == 1) ? (w << 2) : (w >> (4 * k - 6));
-  return (s & m) | one;
+  return int4_pair_f16(w, k, 0x3C003C00u);
 }
 
 // ---------------------------------------------------------------------------
@@ -81,22 +105,148 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t w, int j) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Buffer loads: a 128-bit resource descriptor in SGPRs (base, size in bytes;
+// word 3 = 0x00020000 for the gfx9 family), a per-lane 32-bit VGPR offset and
+// a wave-uniform SGPR offset.  Rows of one matrix then share a single VGPR
+// offset, and reads past `bytes` return zero.
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void bload16(uint32_t (&d)[4], rsrc_t r, uint32_t voff, uint32_t soff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  d[0] = v[0];
+  d[1] = v[1];
+  d[2] = v[2];
+  d[3] = v[3];
+}
+__device__ __forceinline__ uint32_t bload_u16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+
 __device__ __forceinline__ float half_bits_to_f32(uint32_t bits16) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
 }
 
 // ---------------------------------------------------------------------------
-// Wave reductions
+// Wave-wide reductions on the VALU cross-lane paths (no LDS round trip):
+// DPP quad_perm xor1 / xor2, row_half_mirror (i <-> 7-i in 8) and row_mirror
+// (i <-> 15-i in 16) combine lanes within a row of 16; v_permlane16_swap and
+// v_permlane32_swap then exchange rows.  Called with (v, v), the swaps return
+// {v[i & ~16], v[i | 16]} and {v[i & 31], v[i | 32]}, so combining the two
+// halves symmetrically gives every lane the same result.  Every step pairs
+// lanes symmetrically, so all 64 lanes end with bit-identical values.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
 }
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+  return __uint_as_float(dpp<CTRL>(__float_as_uint(v)));
+}
+__device__ __forceinline__ float swap16_sum(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap32_sum(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dppf<kDppXor1>(v);
+  v += dppf<kDppXor2>(v);
+  v += dppf<kDppHalfMirror>(v);
+  v += dppf<kDppMirror>(v);
+  v = swap16_sum(v);
+  return swap32_sum(v);
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dppd(double v) {
+  const uint64_t b = __double_as_longlong(v);
+  const uint32_t lo = dpp<CTRL>((uint32_t)b), hi = dpp<CTRL>((uint32_t)(b >> 32));
+  return __longlong_as_double(((uint64_t)hi << 32) | lo);
+}
+// {value at lane i & ~M, value at lane i | M} for M = 16 or 32
+template <int M>
+__device__ __forceinline__ void swap_pair(double v, double& a, double& b) {
+  const uint64_t x = __double_as_longlong(v);
+  const uint32_t lo = (uint32_t)x, hi = (uint32_t)(x >> 32);
+  uint32_t alo, ahi, blo, bhi;
+  if constexpr (M == 16) {
+    auto rl = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    auto rh = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    alo = rl[0]; blo = rl[1]; ahi = rh[0]; bhi = rh[1];
+  } else {
+    auto rl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    auto rh = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    alo = rl[0]; blo = rl[1]; ahi = rh[0]; bhi = rh[1];
+  }
+  a = __longlong_as_double(((uint64_t)ahi << 32) | alo);
+  b = __longlong_as_double(((uint64_t)bhi << 32) | blo);
+}
+template <int M>
+__device__ __forceinline__ void swap_pair(int v, int& a, int& b) {
+  if constexpr (M == 16) {
+    auto r = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+    a = (int)r[0]; b = (int)r[1];
+  } else {
+    auto r = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+    a = (int)r[0]; b = (int)r[1];
+  }
+}
+
 __device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+  v += dppd<kDppXor1>(v);
+  v += dppd<kDppXor2>(v);
+  v += dppd<kDppHalfMirror>(v);
+  v += dppd<kDppMirror>(v);
+  double a, b;
+  swap_pair<16>(v, a, b);
+  v = a + b;
+  swap_pair<32>(v, a, b);
+  return a + b;
+}
+
+// (value, index) arg-max across the wave: larger value wins, equal values go
+// to the lower index.  Symmetric, so all lanes agree.
+__device__ __forceinline__ void better_of(double& v, int& i, double ov, int oi) {
+  if (ov > v || (ov == v && oi < i)) {
+    v = ov;
+    i = oi;
+  }
+}
+template <int CTRL>
+__device__ __forceinline__ void argmax_dpp(double& v, int& i) {
+  better_of(v, i, dppd<CTRL>(v), (int)dpp<CTRL>((uint32_t)i));
+}
+template <int M>
+__device__ __forceinline__ void argmax_swap(double& v, int& i) {
+  double a, b;
+  int ia, ib;
+  swap_pair<M>(v, a, b);
+  swap_pair<M>(i, ia, ib);
+  v = a;
+  i = ia;
+  better_of(v, i, b, ib);
+}
+__device__ __forceinline__ void wave_argmax(double& v, int& i) {
+  argmax_dpp<kDppXor1>(v, i);
+  argmax_dpp<kDppXor2>(v, i);
+  argmax_dpp<kDppHalfMirror>(v, i);
+  argmax_dpp<kDppMirror>(v, i);
+  argmax_swap<16>(v, i);
+  argmax_swap<32>(v, i);
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) {

@@ -32,9 +32,30 @@ struct Workspace {
   int32_t* n_active;      // [4]
   int32_t* sorted_token;  // [P]
   int32_t* inv_perm;      // [P]
+  float* sorted_w;        // [P]     routing weight of the pick at each sorted slot
   uint16_t* h;            // [P+T][Imax] fp16 SwiGLU outputs
   float* O;               // [P+T][H]   per-pick expert outputs (fp32)
   size_t total;
+};
+
+// Records caller-owned events at kernel boundaries (moe_layer_trace).
+struct Tracer {
+  moe_trace* t = nullptr;
+  hipStream_t s = nullptr;
+  int n = 0;
+  hipError_t begin() {
+    if (!t) return hipSuccess;
+    t->n_kernels = 0;
+    return hipEventRecord(t->events[0], s);
+  }
+  // Call right after launching a kernel on the traced stream.
+  hipError_t mark(const char* name) {
+    if (!t || n >= MOE_TRACE_MAX) return hipSuccess;
+    t->names[n] = name;
+    ++n;
+    t->n_kernels = n;
+    return hipEventRecord(t->events[n], s);
+  }
 };
 
 // Lays the workspace out from `base` (nullptr: only sizes it).
@@ -50,7 +71,7 @@ struct RouteArgs {
   int T, H, E, G, TG, K;
   float rsf;
 };
-hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+hipError_t launch_route(const RouteArgs& a, hipStream_t s, Tracer* tr = nullptr);
 
 struct PermuteArgs {
   const int32_t* ids;
@@ -61,7 +82,7 @@ struct PermuteArgs {
   int32_t* n_active;
   int T, K, E;
 };
-hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t s, Tracer* tr = nullptr);
 
 struct FfnArgs {
   const uint16_t* x;
@@ -83,7 +104,7 @@ struct FfnArgs {
   float* o_dense;      // [T][H]
   int ldh;
 };
-hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
+hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, Tracer* tr = nullptr);
 
 struct CombineArgs {
   const float* expert_out;  // [P][H]
@@ -94,6 +115,40 @@ struct CombineArgs {
   int out_bf16;
   int T, H, K;
 };
-hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s, Tracer* tr = nullptr);
+
+// Small-batch path of moe_layer (T <= kDecodeMaxTokens): four kernels --
+// router logits with the shared expert's gate/up, selection + permutation,
+// routed gate/up, down with the weighted combine.
+constexpr int kDecodeMaxTokens = 4;
+constexpr int kDecodeMaxGPL = 4;   // hidden <= 64 lanes * 4 groups * 32 = 8192
+bool decode_supported(int hidden);
+
+struct DecodeArgs {
+  const uint16_t* x;
+  int T, H, E, G, TG, K;
+  float rsf;
+  const float* router_w;
+  const float* bias;
+  double* logits;
+  int32_t* ids;
+  float* tw;
+  int32_t* offsets;
+  int32_t* sorted_token;
+  int32_t* inv_perm;
+  int32_t* active;
+  int32_t* n_active;
+  float* sorted_w;
+  ExpertSet routed;
+  bool has_shared;
+  ExpertSet shared;
+  uint16_t* h_routed;  // [P][ldh]
+  uint16_t* h_shared;  // [T][ldh]
+  int ldh;
+  void* y;
+  int out_bf16;
+  int wfmt;
+};
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, Tracer* tr = nullptr);
 
 }  // namespace qmoe
