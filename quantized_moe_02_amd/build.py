@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libqmoe.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["qmoe_api.cpp", "route.hip", "permute.hip", "gemv.hip", "decode.hip"]
+SOURCES = ["qmoe_api.cpp", "route.hip", "permute.hip", "gemv.hip", "decode.hip", "gemm.hip"]
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

@@ -40,7 +40,8 @@ constexpr int kRPW = QMOE_DEC_RPW;           // gate/up row pairs per pipeline i
 constexpr int kItems = QMOE_DEC_ITEMS;       // pipeline items per wave (even)
 constexpr int kPairsPerWave = kRPW * kItems;
 constexpr int kPairsPerBlock = 4 * kPairsPerWave;
-constexpr int kSharedPairsPerBlock = 4 * 2 * kRPW;  // K1: two items per wave
+constexpr int kSharedRP = 1;                              // K1: row pairs per item
+constexpr int kSharedPairsPerBlock = 4 * 2 * kSharedRP;   // K1: two items per wave
 static_assert(kItems % 2 == 0, "items are double-buffered in pairs");
 static_assert(32 % kPairsPerWave == 0 && 32 % (2 * kRPW) == 0, "a wave never straddles inter (a multiple of 32)");
 constexpr int kDownRows = QMOE_DEC_DOWN_ROWS; // down/combine output rows per block
@@ -105,9 +106,9 @@ __device__ __forceinline__ float act_sum(const uint32_t (&act)[16]) {
 // reduced, so the memory pipe stays busy.  Lane l owns the 32-input groups
 // l, l+64, ... (GPL of them); x (one token) lives in registers.
 // ---------------------------------------------------------------------------
-template <int GPL>
+template <int GPL, int RP>
 struct GateUpItem {
-  uint32_t wg[kRPW][GPL][4], wu[kRPW][GPL][4], sg[kRPW][GPL], su[kRPW][GPL];
+  uint32_t wg[RP][GPL][4], wu[RP][GPL][4], sg[RP][GPL], su[RP][GPL];
 };
 
 // Buffers of one expert's gate and up projections (codes and scales).
@@ -116,11 +117,11 @@ struct GateUpBufs {
   uint32_t rowBytes, scaleRowBytes;
 };
 
-template <int GPL>
-__device__ __forceinline__ void gu_load(GateUpItem<GPL>& it, const GateUpBufs& b,
+template <int GPL, int RP>
+__device__ __forceinline__ void gu_load(GateUpItem<GPL, RP>& it, const GateUpBufs& b,
                                         const uint32_t (&off)[GPL], int pair0) {
 #pragma unroll
-  for (int r = 0; r < kRPW; ++r) {
+  for (int r = 0; r < RP; ++r) {
     const uint32_t row = (uint32_t)(pair0 + r);
 #pragma unroll
     for (int j = 0; j < GPL; ++j) {
@@ -132,13 +133,14 @@ __device__ __forceinline__ void gu_load(GateUpItem<GPL>& it, const GateUpBufs& b
   }
 }
 
-template <int FMT, int GPL>
-__device__ __forceinline__ void gu_compute(const GateUpItem<GPL>& it, const uint32_t (&xw)[GPL][16],
-                                           const float (&xs)[GPL], const bool (&ok)[GPL], float gg,
-                                           float gu, int pair0, uint16_t* __restrict__ hrow) {
+template <int FMT, int GPL, int RP>
+__device__ __forceinline__ void gu_compute(const GateUpItem<GPL, RP>& it,
+                                           const uint32_t (&xw)[GPL][16], const float (&xs)[GPL],
+                                           const bool (&ok)[GPL], float gg, float gu, int pair0,
+                                           uint16_t* __restrict__ hrow) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int r = 0; r < kRPW; ++r) {
+  for (int r = 0; r < RP; ++r) {
     float g = 0.0f, u = 0.0f;
 #pragma unroll
     for (int j = 0; j < GPL; ++j) {
@@ -161,7 +163,7 @@ __device__ __forceinline__ void gu_compute(const GateUpItem<GPL>& it, const uint
 // Gate/up for row pairs [pair_begin, pair_begin + kPairsPerWave) of one
 // expert (rows [row_base, row_base + inter) of the projections) and one token
 // x; h written to hrow.
-template <int FMT, int GPL, int ITEMS = kItems>
+template <int FMT, int GPL, int ITEMS = kItems, int RP = kRPW>
 __device__ __forceinline__ void gateup_wave(const uint16_t* __restrict__ x, int H,
                                             const ProjPtr& Pg, const ProjPtr& Pu, size_t row_base,
                                             int inter, int pair_begin, float gg, float gu,
@@ -184,9 +186,9 @@ __device__ __forceinline__ void gateup_wave(const uint16_t* __restrict__ x, int 
     ok[j] = c < nG;
     cc[j] = ok[j] ? c : nG - 1;
   }
-  GateUpItem<GPL> A, B;
-  gu_load<GPL>(A, b, cc, pair_begin);
-  gu_load<GPL>(B, b, cc, pair_begin + kRPW);
+  GateUpItem<GPL, RP> A, B;
+  gu_load<GPL, RP>(A, b, cc, pair_begin);
+  gu_load<GPL, RP>(B, b, cc, pair_begin + RP);
   uint32_t xw[GPL][16];
   float xs[GPL];
 #pragma unroll
@@ -204,14 +206,14 @@ __device__ __forceinline__ void gateup_wave(const uint16_t* __restrict__ x, int 
     xs[j] = (FMT == MOE_WFMT_INT4_G32_F16) ? act_sum<false>(xw[j]) : 0.0f;
 #pragma unroll
   for (int i = 0; i < ITEMS; i += 2) {
-    const int p = pair_begin + i * kRPW;
-    gu_compute<FMT, GPL>(A, xw, xs, ok, gg, gu, p, hrow);
+    const int p = pair_begin + i * RP;
+    gu_compute<FMT, GPL, RP>(A, xw, xs, ok, gg, gu, p, hrow);
     __builtin_amdgcn_sched_barrier(0);
-    if (i + 2 < ITEMS) gu_load<GPL>(A, b, cc, p + 2 * kRPW);
+    if (i + 2 < ITEMS) gu_load<GPL, RP>(A, b, cc, p + 2 * RP);
     __builtin_amdgcn_sched_barrier(0);
-    gu_compute<FMT, GPL>(B, xw, xs, ok, gg, gu, p + kRPW, hrow);
+    gu_compute<FMT, GPL, RP>(B, xw, xs, ok, gg, gu, p + RP, hrow);
     __builtin_amdgcn_sched_barrier(0);
-    if (i + 3 < ITEMS) gu_load<GPL>(B, b, cc, p + 3 * kRPW);
+    if (i + 3 < ITEMS) gu_load<GPL, RP>(B, b, cc, p + 3 * RP);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -276,13 +278,13 @@ __global__ void __launch_bounds__(256) dec_router_shared_kernel(DecodeArgs a, in
   }
   // shared expert: all T tokens
   const ExpertSet& S = a.shared;
-  const int pair0 = ((int)blockIdx.x - nrb) * kSharedPairsPerBlock + wv * (2 * kRPW);
+  const int pair0 = ((int)blockIdx.x - nrb) * kSharedPairsPerBlock + wv * (2 * kSharedRP);
   if (pair0 >= S.inter) return;
   const float gg = (FMT == MOE_WFMT_NVFP4) ? S.gate.g[0] : 1.0f;
   const float gu = (FMT == MOE_WFMT_NVFP4) ? S.up.g[0] : 1.0f;
   for (int t = 0; t < a.T; ++t)
-    gateup_wave<FMT, GPL, 2>(a.x + (size_t)t * a.H, a.H, S.gate, S.up, 0, S.inter, pair0, gg, gu,
-                             a.h_shared + (size_t)t * a.ldh);
+    gateup_wave<FMT, GPL, 2, kSharedRP>(a.x + (size_t)t * a.H, a.H, S.gate, S.up, 0, S.inter,
+                                        pair0, gg, gu, a.h_shared + (size_t)t * a.ldh);
 }
 
 // ---------------------------------------------------------------------------
@@ -292,7 +294,6 @@ __global__ void __launch_bounds__(256) dec_select_permute_kernel(DecodeArgs a) {
   __shared__ SelectScratch sc[4];
   __shared__ int pid[64];
   __shared__ float pw[64];
-  __shared__ int spid[64];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int K = a.K, P = a.T * a.K;
@@ -310,32 +311,47 @@ __global__ void __launch_bounds__(256) dec_select_permute_kernel(DecodeArgs a) {
   }
   __syncthreads();
   if (wv != 0) return;
-  // stable sort of the picks by expert: rank = #picks with a smaller id, or the
-  // same id and a smaller pick index
-  int e = 0, pos = 0;
-  if (lane < P) {
-    e = pid[lane];
-    for (int q = 0; q < P; ++q) {
-      const int o = pid[q];
-      pos += (o < e || (o == e && q < lane)) ? 1 : 0;
-    }
+  // Stable sort of the P <= 64 picks by expert, one pick per lane: a pick's
+  // slot = #picks with a smaller id, or the same id and a smaller pick index.
+  const bool have = lane < P;
+  const int e = have ? pid[lane] : 0x7fffffff;
+  const float pwv = have ? pw[lane] : 0.0f;
+  int pos = 0;
+  for (int q = 0; q < P; ++q) {
+    const int o = __builtin_amdgcn_readlane(e, q);
+    pos += (o < e || (o == e && q < lane)) ? 1 : 0;
+  }
+  if (have) {
     a.sorted_token[pos] = lane / K;
     a.inv_perm[lane] = pos;
-    a.sorted_w[pos] = pw[lane];
-    spid[pos] = e;
+    a.sorted_w[pos] = pwv;
   }
-  wave_lds_sync();
-  const int se = lane < P ? spid[lane] : -1;
-  const bool first = lane < P && (lane == 0 || spid[lane - 1] != se);
+  // distinct experts in ascending order: a pick is the first of its expert
+  // if no pick has the same id and a smaller slot
+  int dup = 0;
+  for (int q = 0; q < P; ++q) {
+    const int o = __builtin_amdgcn_readlane(e, q);
+    dup |= (o == e && q < lane) ? 1 : 0;
+  }
+  const bool first = have && !dup;
+  int arank = 0;  // #distinct experts with a smaller id
   const uint64_t firsts = __ballot(first);
-  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  if (first) a.active[__popcll(firsts & lt)] = se;
-  if (lane == 0) a.n_active[0] = __popcll(firsts);
-  for (int x = lane; x <= a.E; x += 64) {
-    int c = 0;
-    for (int q = 0; q < P; ++q) c += (spid[q] < x) ? 1 : 0;
-    a.offsets[x] = c;
+  for (int q = 0; q < P; ++q) {
+    const int o = __builtin_amdgcn_readlane(e, q);
+    arank += (((firsts >> q) & 1ull) && o < e) ? 1 : 0;
   }
+  if (first) a.active[arank] = e;
+  if (lane == 0) a.n_active[0] = __popcll(firsts);
+  // offsets[x] = #picks with id < x, for x = 0..E
+  int cnt[5] = {0, 0, 0, 0, 0};
+  for (int q = 0; q < P; ++q) {
+    const int o = __builtin_amdgcn_readlane(e, q);
+#pragma unroll
+    for (int j = 0; j < 5; ++j) cnt[j] += (o < lane + 64 * j) ? 1 : 0;
+  }
+#pragma unroll
+  for (int j = 0; j < 5; ++j)
+    if (lane + 64 * j <= a.E) a.offsets[lane + 64 * j] = cnt[j];
 }
 
 // ---------------------------------------------------------------------------
@@ -401,7 +417,10 @@ __device__ __forceinline__ SlotInfo slot_info(const DecodeArgs& a, int s, int n_
   return d;
 }
 
-__device__ __forceinline__ void down_load(DownItem& it, const SlotInfo& d, uint32_t c) {
+// Buffer loads range-check only the per-lane offset, so lanes past the row's
+// last group (small inter) load group 0 instead and are masked in compute.
+__device__ __forceinline__ void down_load(DownItem& it, const SlotInfo& d, uint32_t c_raw) {
+  const uint32_t c = (int)c_raw < d.nG ? c_raw : 0u;
   const uint32_t rowBytes = (uint32_t)d.nG * 16u;
 #pragma unroll
   for (int r = 0; r < kDownRows; ++r) {
@@ -431,7 +450,7 @@ __device__ __forceinline__ void down_compute(const DownItem& it, const SlotInfo&
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         uint32_t t4[4];
-        bload16(t4, d.h, c * 64u + 16u * q, (uint32_t)m * a.ldh * 2u);
+        bload16(t4, d.h, (ok ? c : 0u) * 64u + 16u * q, (uint32_t)m * a.ldh * 2u);
 #pragma unroll
         for (int i = 0; i < 4; ++i) hm[4 * q + i] = t4[i];
       }

@@ -1,0 +1,406 @@
+// Grouped GEMM for prefill-shaped calls: the SwiGLU expert FFN over 4-bit
+// weights on the matrix cores (page "Show HN: Menjalankan GLM 5.2 di komputer
+// lambat", sections "Cara kerja eksekusi MoE" and "Fitur utama": int4
+// dequant-on-use, batch-union MoE; NVFP4 per page "NVIDIA stellt neues
+// GLM-5.2 NVFP4 Modell vor", section "Technische Details").
+//
+// Work unit = (m tile of up to 128 tokens of one expert, n tile of weight
+// rows).  Each wave dequantises its own weight rows straight from HBM into
+// fp16 A operands (scale folded in, one rounding) and multiplies them against
+// the unit's activations, staged in LDS as fp16, with
+// v_mfma_f32_16x16x32_f16 (fp32 accumulate).
+//   gate/up: 128 row pairs per unit; each wave holds 32 gate rows and the 32
+//            matching up rows, so the SwiGLU epilogue pairs them in registers
+//            and writes h (fp16).
+//   down:    256 output rows per unit over K = inter; writes fp32 per pick.
+//
+// Operand layouts of v_mfma_f32_16x16x32_f16 (wave64): A lane l holds row
+// l%16, K 8*(l/16)..+7; B lane l holds column l%16, the same K; D lane l holds
+// rows 4*(l/16)..+3 of column l%16.  K is summed, so any K order shared by A
+// and B is valid: within a 128-input block a lane loads one 16-byte chunk of
+// its row (a whole 32-input group, one scale) and feeds its four 32-bit words
+// to four consecutive MFMA K steps; the B reads from LDS use the same order.
+#include "qmoe_device.h"
+
+namespace qmoe {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+constexpr int kBM = 128;          // tokens per unit
+constexpr int kBK = 128;          // inputs per K block
+constexpr int kXS = kBK + 8;      // LDS row stride in fp16 (16-byte pad against bank conflicts)
+constexpr int kCT = kBM / 16;     // 16-token column tiles
+constexpr int kGateUpPairs = 128; // row pairs per gate/up unit
+constexpr int kDownRows = 256;    // output rows per down unit
+
+__device__ __forceinline__ uint32_t pk_fma_f16(uint32_t a, uint32_t b, uint32_t c) {
+  const half2v r = __builtin_bit_cast(half2v, a) * __builtin_bit_cast(half2v, b) +
+                   __builtin_bit_cast(half2v, c);
+  return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ uint32_t pk_mul_f16(uint32_t a, uint32_t b) {
+  const half2v r = __builtin_bit_cast(half2v, a) * __builtin_bit_cast(half2v, b);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// One 32-bit word (8 consecutive inputs of one row) -> fp16 A operand.
+//   int4:  (u - 8) * scale, exact integer first, then one rounding.
+//   nvfp4: e2m1 * e4m3 (exact in fp16); the per-tensor fp32 scale is applied
+//          to the accumulator in the epilogue.
+template <int FMT>
+__device__ __forceinline__ half8 dequant_word(uint32_t w, uint32_t scale2) {
+  uint32_t p[4];
+  if constexpr (FMT == MOE_WFMT_INT4_G32_F16) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t v = int4_pair_f16(w, k);                   // 1 + u/16
+      const uint32_t q = pk_fma_f16(v, 0x4C004C00u, 0xCE00CE00u);  // *16 - 24 = u - 8
+      p[k] = pk_mul_f16(q, scale2);
+    }
+  } else {
+    // natural nibble order: byte k holds inputs 2k, 2k+1
+#pragma unroll
+    for (int k = 0; k < 4; ++k) p[k] = pk_mul_f16(fp4_pair_f16(w, k), scale2);
+  }
+  half8 r;
+  __builtin_memcpy(&r, p, 16);
+  return r;
+}
+
+struct Unit {
+  int e;        // expert index in its weight set (0 for the shared expert)
+  int p0;       // first row of the unit in the h / O buffers
+  int M;        // tokens in the unit (<= kBM)
+  int tok0;     // routed: first sorted slot (index into sorted_token); shared: first token
+  bool routed;
+};
+
+__device__ __forceinline__ Unit load_unit(const GemmArgs& g, int idx) {
+  const int4 t = g.tiles[idx];
+  Unit u;
+  u.routed = t.x >= 0;
+  u.e = u.routed ? t.x : 0;
+  u.p0 = t.y;
+  u.M = t.z;
+  u.tok0 = t.w;
+  return u;
+}
+
+// Activation rows of the unit -> registers -> LDS (fp16), zero rows past M.
+// Each thread moves 8 x 16 bytes: token m = tid / 2, half of the 128-input
+// block = tid % 2.  Loads are unconditional (rows and inputs clamped into
+// range) and masked afterwards, so that they all stay in flight together.
+template <int PROJ>
+__device__ __forceinline__ void load_act(const rsrc_t& ar, uint32_t rowoff, int kb, int K, bool mok,
+                                         uint4 (&reg)[8]) {
+  const int half = threadIdx.x & 1;
+  const int k0 = kb * kBK + half * 64;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int k = k0 + 8 * i;
+    const bool ok = mok && k < K;
+    uint32_t t4[4];
+    bload16(t4, ar, rowoff + (uint32_t)(k < K ? k : 0) * 2u, 0);
+    uint4 v = make_uint4(t4[0], t4[1], t4[2], t4[3]);
+    opaque(v);
+    reg[i] = ok ? v : make_uint4(0, 0, 0, 0);
+  }
+}
+
+// Byte offset, within the activation tensor, of the row this thread stages
+// (clamped into range), and the tensor's buffer descriptor.
+template <int PROJ>
+__device__ __forceinline__ uint32_t act_rowoff(const GemmArgs& g, const Unit& u, int K) {
+  const int m = min((int)(threadIdx.x >> 1), u.M - 1);
+  if constexpr (PROJ == 0) {
+    const int t = u.routed ? g.sorted_token[u.tok0 + m] : u.tok0 + m;
+    return (uint32_t)t * (uint32_t)K * 2u;
+  } else {
+    return (uint32_t)(u.p0 + m) * (uint32_t)g.ldh * 2u;
+  }
+}
+
+__device__ __forceinline__ void store_act(uint16_t* xs, const uint4 (&reg)[8]) {
+  const int tid = threadIdx.x;
+  const int m = tid >> 1, half = tid & 1;
+  uint4* dst = reinterpret_cast<uint4*>(xs + m * kXS + half * 64);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) dst[i] = reg[i];
+}
+
+// PROJ 0: gate/up (+SwiGLU), PROJ 1: down.
+template <int FMT, int PROJ>
+__global__ void __launch_bounds__(256, 2) moe_gemm_kernel(GemmArgs g) {
+  constexpr int RT = 4;  // 16-row tiles per wave
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][kBM * kXS];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int uidx = blockIdx.x;
+  if (uidx >= *g.n_tiles) return;
+  const Unit u = load_unit(g, uidx);
+  const ExpertSet& X = u.routed ? g.routed : g.shared;
+  const int inter = X.inter;
+  const int K = PROJ == 0 ? g.H : inter;
+  const int nrow_out = PROJ == 0 ? inter : g.H;
+  const int nt = blockIdx.y;
+  // first output row of this wave (gate/up: row pairs)
+  const int wrow = PROJ == 0 ? nt * kGateUpPairs + wv * 32 : nt * kDownRows + wv * 64;
+  if (nt * (PROJ == 0 ? kGateUpPairs : kDownRows) >= nrow_out) return;
+  const int nG = K / 32;
+  const uint32_t rowBytes = (uint32_t)K / 2;
+  const int sgpr = FMT == MOE_WFMT_INT4_G32_F16 ? 32 : 16;   // inputs per scale
+  const uint32_t scaleRowBytes = (uint32_t)(K / sgpr) * (FMT == MOE_WFMT_INT4_G32_F16 ? 2 : 1);
+
+  // weight buffers of this wave's row tiles: rt 0,1 gate (or down) rows,
+  // rt 2,3 the matching up rows (gate/up) or further down rows
+  rsrc_t qb[RT], sb[RT];
+  int rbase[RT];
+  float gsc[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const ProjPtr& P = PROJ == 0 ? (rt < 2 ? X.gate : X.up) : X.down;
+    const int r = PROJ == 0 ? wrow + 16 * (rt & 1) : wrow + 16 * rt;
+    rbase[rt] = r;
+    const int rows_valid = max(0, min(16, nrow_out - r));
+    const size_t row0 = (size_t)u.e * nrow_out + r;
+    qb[rt] = make_rsrc(P.q + row0 * rowBytes, (uint32_t)rows_valid * rowBytes);
+    sb[rt] = make_rsrc(reinterpret_cast<const uint8_t*>(P.s) + row0 * scaleRowBytes,
+                       (uint32_t)rows_valid * scaleRowBytes);
+    gsc[rt] = FMT == MOE_WFMT_NVFP4 ? P.g[u.e] : 1.0f;
+  }
+  const int lrow = lane & 15, lq = lane >> 4;
+  const int nkb = (K + kBK - 1) / kBK;
+  const int nct = (u.M + 15) >> 4;
+
+  float4v acc[RT][kCT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int c = 0; c < kCT; ++c) acc[rt][c] = float4v{0.f, 0.f, 0.f, 0.f};
+
+  // weights of one K block: lane (lrow, lq) loads group 4*kb + lq of its row
+  uint32_t wcode[2][RT][4], wsc[2][RT];
+  auto load_w = [&](int buf, int kb) {
+    const int grp = kb * 4 + lq;
+    const bool ok = grp < nG;
+    const uint32_t gc = ok ? (uint32_t)grp : 0u;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      bload16(wcode[buf][rt], qb[rt], gc * 16u, (uint32_t)lrow * rowBytes);
+      uint32_t sc = bload_u16(sb[rt], gc * 2u, (uint32_t)lrow * scaleRowBytes);
+      opaque(sc);
+      wsc[buf][rt] = ok ? sc : 0u;  // a zero scale zeroes the group
+    }
+  };
+
+  uint4 areg[8];
+  const rsrc_t ar = PROJ == 0 ? make_rsrc(g.x16, (uint32_t)g.T * (uint32_t)g.H * 2u)
+                              : make_rsrc(g.hin, (uint32_t)(g.P + g.T) * (uint32_t)g.ldh * 2u);
+  const uint32_t arowoff = act_rowoff<PROJ>(g, u, K);
+  const bool amok = (int)(threadIdx.x >> 1) < u.M;
+  load_act<PROJ>(ar, arowoff, 0, K, amok, areg);
+  load_w(0, 0);
+  store_act(xs[0], areg);
+  __syncthreads();
+
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int cur = kb & 1;
+    const bool more = kb + 1 < nkb;
+    if (more) {
+      load_act<PROJ>(ar, arowoff, kb + 1, K, amok, areg);
+      load_w(cur ^ 1, kb + 1);
+    }
+    const uint16_t* xb = xs[cur];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      half8 A[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        uint32_t s2;
+        if constexpr (FMT == MOE_WFMT_INT4_G32_F16) {
+          s2 = (wsc[cur][rt] & 0xffffu) * 0x00010001u;
+        } else {
+          // inputs 0-15 of the group use scale byte 0, 16-31 byte 1
+          const _Float16 sh = (_Float16)e4m3_to_f32(wsc[cur][rt], ks >> 1);
+          const uint32_t b = __builtin_bit_cast(uint16_t, sh);
+          s2 = b * 0x00010001u;
+        }
+        A[rt] = dequant_word<FMT>(wcode[cur][rt][ks], s2);
+      }
+#pragma unroll
+      for (int c0 = 0; c0 < kCT; c0 += 4) {
+        half8 B[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          B[c] = *reinterpret_cast<const half8*>(xb + (16 * (c0 + c) + lrow) * kXS + lq * 32 + ks * 8);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          if (c0 + c < nct) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+              acc[rt][c0 + c] =
+                  __builtin_amdgcn_mfma_f32_16x16x32_f16(A[rt], B[c], acc[rt][c0 + c], 0, 0, 0);
+          }
+        }
+      }
+    }
+    if (more) {
+      // xs[cur ^ 1] was last read in block kb-1, which every wave finished
+      // before the barrier that ended it
+      store_act(xs[cur ^ 1], areg);
+      __syncthreads();
+    }
+  }
+
+  // epilogue
+#pragma unroll
+  for (int c = 0; c < kCT; ++c) {
+    if (c >= nct) break;
+    const int m = 16 * c + lrow;
+    if (m >= u.M) continue;
+    const int orow = u.p0 + m;
+    if constexpr (PROJ == 0) {
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        uint32_t packed[2];
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+          const float h0 = silu_mul(acc[rt][c][i] * gsc[rt], acc[rt + 2][c][i] * gsc[rt + 2]);
+          const float h1 = silu_mul(acc[rt][c][i + 1] * gsc[rt], acc[rt + 2][c][i + 1] * gsc[rt + 2]);
+          const _Float16 a0 = (_Float16)h0, a1 = (_Float16)h1;
+          packed[i / 2] = (uint32_t)__builtin_bit_cast(uint16_t, a0) |
+                          ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
+        }
+        const int col = rbase[rt] + 4 * lq;
+        if (col < inter)
+          *reinterpret_cast<uint2*>(g.h_out + (size_t)orow * g.ldh + col) = make_uint2(packed[0], packed[1]);
+      }
+    } else {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const int col = rbase[rt] + 4 * lq;
+        if (col < g.H) {
+          float4 o;
+          o.x = acc[rt][c][0] * gsc[rt];
+          o.y = acc[rt][c][1] * gsc[rt];
+          o.z = acc[rt][c][2] * gsc[rt];
+          o.w = acc[rt][c][3] * gsc[rt];
+          *reinterpret_cast<float4*>(g.o_out + (size_t)orow * g.H + col) = o;
+        }
+      }
+    }
+  }
+}
+
+// bf16 -> fp16 copy of the activations (exact for |x| in the fp16 normal range)
+__global__ void __launch_bounds__(256) x_to_f16_kernel(const uint16_t* __restrict__ x,
+                                                       uint16_t* __restrict__ y, size_t n8) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (size_t)gridDim.x * 256) {
+    const uint4 v = reinterpret_cast<const uint4*>(x)[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const _Float16 lo = (_Float16)bf16_lo(w[j]), hi = (_Float16)bf16_hi(w[j]);
+      o[j] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+    reinterpret_cast<uint4*>(y)[i] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+// Work units: for each active expert (ascending) its sorted slots in slices of
+// kBM, then the shared expert's tokens in slices of kBM.
+// tiles[i] = {expert or -1, first h/O row, tokens, first sorted slot or token}.
+__global__ void __launch_bounds__(64) build_units_kernel(const int32_t* __restrict__ offsets,
+                                                         const int32_t* __restrict__ active,
+                                                         const int32_t* __restrict__ n_active,
+                                                         int4* __restrict__ tiles,
+                                                         int32_t* __restrict__ n_tiles, int T, int P,
+                                                         int has_shared) {
+  const int lane = threadIdx.x;
+  const int na = n_active ? *n_active : 0;
+  int base = 0;
+  for (int a0 = 0; a0 < na; a0 += 64) {
+    const int a = a0 + lane;
+    int e = 0, o = 0, M = 0, nm = 0;
+    if (a < na) {
+      e = active[a];
+      o = offsets[e];
+      M = offsets[e + 1] - o;
+      nm = (M + kBM - 1) / kBM;
+    }
+    // exclusive prefix of nm across the wave
+    int pre = nm;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(pre, d, 64);
+      if (lane >= d) pre += v;
+    }
+    const int excl = base + pre - nm;
+    for (int i = 0; i < nm; ++i) {
+      const int m0 = i * kBM;
+      tiles[excl + i] = make_int4(e, o + m0, min(kBM, M - m0), o + m0);
+    }
+    base += __shfl(pre, 63, 64);
+  }
+  if (has_shared) {
+    const int ns = (T + kBM - 1) / kBM;
+    for (int i = lane; i < ns; i += 64) {
+      const int t0 = i * kBM;
+      tiles[base + i] = make_int4(-1, P + t0, min(kBM, T - t0), t0);
+    }
+    base += ns;
+  }
+  if (lane == 0) *n_tiles = base;
+}
+
+}  // namespace
+
+hipError_t launch_build_units(const int32_t* offsets, const int32_t* active,
+                              const int32_t* n_active, int4* tiles, int32_t* n_tiles, int T, int P,
+                              bool has_shared, hipStream_t s) {
+  hipLaunchKernelGGL(build_units_kernel, dim3(1), dim3(64), 0, s, offsets, active, n_active, tiles,
+                     n_tiles, T, P, has_shared ? 1 : 0);
+  return hipGetLastError();
+}
+
+int gemm_max_units(int T, int K, int E, bool has_shared) {
+  const long P = (long)T * K;
+  const long routed = (P + kBM - 1) / kBM + (P < E ? P : E);
+  const long shared = has_shared ? (T + kBM - 1) / kBM : 0;
+  return (int)(routed + shared);
+}
+int gemm_unit_tokens() { return kBM; }
+
+hipError_t launch_x_to_f16(const uint16_t* x, uint16_t* y, size_t n, hipStream_t s) {
+  const size_t n8 = n / 8;
+  const int blocks = (int)std::min<size_t>((n8 + 255) / 256, 4096);
+  hipLaunchKernelGGL(x_to_f16_kernel, dim3(blocks), dim3(256), 0, s, x, y, n8);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm(const GemmArgs& g, int max_units, hipStream_t s, Tracer* tr) {
+  hipError_t e;
+  int max_inter = g.routed.inter;
+  if (g.has_shared && g.shared.inter > max_inter) max_inter = g.shared.inter;
+  dim3 g1(max_units, (max_inter + kGateUpPairs - 1) / kGateUpPairs);
+  if (g.wfmt == MOE_WFMT_NVFP4)
+    hipLaunchKernelGGL((moe_gemm_kernel<MOE_WFMT_NVFP4, 0>), g1, dim3(256), 0, s, g);
+  else
+    hipLaunchKernelGGL((moe_gemm_kernel<MOE_WFMT_INT4_G32_F16, 0>), g1, dim3(256), 0, s, g);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (tr && (e = tr->mark("gemm_gateup")) != hipSuccess) return e;
+  dim3 g2(max_units, (g.H + kDownRows - 1) / kDownRows);
+  if (g.wfmt == MOE_WFMT_NVFP4)
+    hipLaunchKernelGGL((moe_gemm_kernel<MOE_WFMT_NVFP4, 1>), g2, dim3(256), 0, s, g);
+  else
+    hipLaunchKernelGGL((moe_gemm_kernel<MOE_WFMT_INT4_G32_F16, 1>), g2, dim3(256), 0, s, g);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (tr && (e = tr->mark("gemm_down")) != hipSuccess) return e;
+  return hipSuccess;
+}
+
+}  // namespace qmoe

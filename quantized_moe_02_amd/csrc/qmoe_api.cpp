@@ -84,6 +84,41 @@ ExpertSet expert_set(const moe_qexperts& w, int inter) {
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// Expert FFNs on the grouped MFMA GEMM: work units from the permutation (or
+// the shared / dense expert alone), fp16 activations, gate/up, down.
+hipError_t run_gemm_ffn(const moe_config& c, int T, const uint16_t* x, const Workspace& w,
+                        bool has_routed, const ExpertSet& routed, const int32_t* offsets,
+                        const int32_t* active, const int32_t* n_active,
+                        const int32_t* sorted_token, bool has_shared, const ExpertSet& shared,
+                        int P, int ldh, uint16_t* h, float* o, hipStream_t stream, Tracer* tr) {
+  hipError_t e;
+  if ((e = launch_build_units(offsets, has_routed ? active : nullptr,
+                              has_routed ? n_active : nullptr, w.tiles, w.n_tiles, T, P,
+                              has_shared, stream)) != hipSuccess)
+    return e;
+  if ((e = launch_x_to_f16(x, w.x16, (size_t)T * c.hidden, stream)) != hipSuccess) return e;
+  if (tr && (e = tr->mark("gemm_prep")) != hipSuccess) return e;
+  GemmArgs g{};
+  g.tiles = w.tiles;
+  g.n_tiles = w.n_tiles;
+  g.x16 = w.x16;
+  g.sorted_token = sorted_token;
+  g.hin = h;
+  g.ldh = ldh;
+  g.routed = routed;
+  g.has_shared = has_shared;
+  g.shared = shared;
+  g.h_out = h;
+  g.o_out = o;
+  g.T = T;
+  g.H = c.hidden;
+  g.P = P;
+  g.wfmt = c.wfmt;
+  const int units = gemm_max_units(T, has_routed ? c.top_k : 0,
+                                   has_routed ? c.n_routed_experts : 0, has_shared);
+  return launch_gemm(g, units, stream, tr);
+}
+
 }  // namespace
 
 Workspace carve_workspace(const moe_config& c, int T, void* base) {
@@ -109,6 +144,10 @@ Workspace carve_workspace(const moe_config& c, int T, void* base) {
   const size_t o_sw = take(P * sizeof(float));
   const size_t o_h = take((P + T) * imax * sizeof(uint16_t));
   const size_t o_O = take((P + T) * H * sizeof(float));
+  const size_t o_x16 = take((size_t)T * H * sizeof(uint16_t));
+  const size_t o_tiles =
+      take((size_t)gemm_max_units(T, (int)K, (int)E, c.n_shared_experts == 1) * 4 * sizeof(int32_t));
+  const size_t o_ntiles = take(4 * sizeof(int32_t));
   w.total = off;
   if (base) {
     char* b = static_cast<char*>(base);
@@ -123,6 +162,9 @@ Workspace carve_workspace(const moe_config& c, int T, void* base) {
     w.sorted_w = reinterpret_cast<float*>(b + o_sw);
     w.h = reinterpret_cast<uint16_t*>(b + o_h);
     w.O = reinterpret_cast<float*>(b + o_O);
+    w.x16 = reinterpret_cast<uint16_t*>(b + o_x16);
+    w.tiles = reinterpret_cast<int4*>(b + o_tiles);
+    w.n_tiles = reinterpret_cast<int32_t*>(b + o_ntiles);
   }
   return w;
 }
@@ -214,6 +256,13 @@ moe_status moe_expert_ffn_q4(const moe_config* cfg, int32_t T, const uint16_t* x
   a.K = cfg->top_k;
   a.wfmt = cfg->wfmt;
   a.ldh = ldh;
+  if (T > kDecodeMaxTokens) {
+    const ExpertSet es = expert_set(*w, routed ? cfg->moe_inter : cfg->shared_inter);
+    const int P = routed ? T * cfg->top_k : 0;
+    return hip_status(run_gemm_ffn(*cfg, T, x, ws_, routed, es, expert_offsets, active_experts,
+                                   n_active, sorted_token, !routed, es, P, ldh, ws_.h, out,
+                                   stream, nullptr));
+  }
   if (routed) {
     a.has_routed = true;
     a.routed = expert_set(*w, cfg->moe_inter);
@@ -330,29 +379,12 @@ moe_status layer_impl(const moe_config* cfg, int32_t T, const uint16_t* x, const
                  T, cfg->top_k, cfg->n_routed_experts};
   if ((e = launch_permute(pa, stream, tr)) != hipSuccess) return MOE_ERR_HIP;
 
-  FfnArgs fa{};
-  fa.x = x;
-  fa.T = T;
-  fa.H = cfg->hidden;
-  fa.K = cfg->top_k;
-  fa.wfmt = cfg->wfmt;
-  fa.ldh = ldh;
-  fa.has_routed = true;
-  fa.routed = expert_set(*routed, cfg->moe_inter);
-  fa.max_slots = (int)std::min<int64_t>(cfg->n_routed_experts, (int64_t)P);
-  fa.offsets = w.offsets;
-  fa.sorted_token = w.sorted_token;
-  fa.active = w.active;
-  fa.n_active = w.n_active;
-  fa.h_routed = w.h;
-  fa.o_routed = w.O;
-  if (has_shared) {
-    fa.has_dense = true;
-    fa.dense = expert_set(*shared, cfg->shared_inter);
-    fa.h_dense = w.h + P * fa.ldh;
-    fa.o_dense = w.O + P * cfg->hidden;
-  }
-  if ((e = launch_ffn(fa, stream, tr)) != hipSuccess) return MOE_ERR_HIP;
+  const ExpertSet rset = expert_set(*routed, cfg->moe_inter);
+  const ExpertSet sset = has_shared ? expert_set(*shared, cfg->shared_inter) : ExpertSet{};
+  if ((e = run_gemm_ffn(*cfg, T, x, w, true, rset, w.offsets, w.active, w.n_active,
+                        w.sorted_token, has_shared, sset, (int)P, ldh, w.h, w.O, stream, tr)) !=
+      hipSuccess)
+    return MOE_ERR_HIP;
   CombineArgs ca{w.O, w.inv_perm, tw, has_shared ? w.O + P * cfg->hidden : nullptr, y,
                  out_dtype == MOE_OUT_BF16, T, cfg->hidden, cfg->top_k};
   return hip_status(launch_combine(ca, stream, tr));

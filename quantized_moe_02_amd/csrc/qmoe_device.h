@@ -127,6 +127,13 @@ __device__ __forceinline__ uint32_t bload_u16(rsrc_t r, uint32_t voff, uint32_t 
   return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
 }
 
+// Hides a loaded value from the optimiser, so that a later select on it is
+// not turned back into a predicated (branching) load.
+__device__ __forceinline__ void opaque(uint4& v) {
+  asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+}
+__device__ __forceinline__ void opaque(uint32_t& v) { asm volatile("" : "+v"(v)); }
+
 __device__ __forceinline__ float half_bits_to_f32(uint32_t bits16) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
 }

@@ -35,6 +35,9 @@ struct Workspace {
   float* sorted_w;        // [P]     routing weight of the pick at each sorted slot
   uint16_t* h;            // [P+T][Imax] fp16 SwiGLU outputs
   float* O;               // [P+T][H]   per-pick expert outputs (fp32)
+  uint16_t* x16;          // [T][H]     fp16 activations (GEMM path)
+  int4* tiles;            // [max units] GEMM work units
+  int32_t* n_tiles;       // [4]
   size_t total;
 };
 
@@ -150,5 +153,28 @@ struct DecodeArgs {
   int wfmt;
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, Tracer* tr = nullptr);
+
+// Grouped MFMA GEMM path (prefill-shaped calls).
+struct GemmArgs {
+  const int4* tiles;          // work units (see build_units)
+  const int32_t* n_tiles;
+  const uint16_t* x16;        // fp16 activations [T][H]
+  const int32_t* sorted_token;
+  const uint16_t* hin;        // fp16 h [P+T][ldh] (down input)
+  int ldh;
+  ExpertSet routed;
+  bool has_shared;
+  ExpertSet shared;
+  uint16_t* h_out;            // fp16 h [P+T][ldh] (gate/up output)
+  float* o_out;               // fp32 [P+T][H] (down output)
+  int T, H, P, wfmt;
+};
+int gemm_max_units(int T, int K, int E, bool has_shared);
+int gemm_unit_tokens();
+hipError_t launch_build_units(const int32_t* offsets, const int32_t* active,
+                              const int32_t* n_active, int4* tiles, int32_t* n_tiles, int T, int P,
+                              bool has_shared, hipStream_t s);
+hipError_t launch_x_to_f16(const uint16_t* x, uint16_t* y, size_t n, hipStream_t s);
+hipError_t launch_gemm(const GemmArgs& g, int max_units, hipStream_t s, Tracer* tr = nullptr);
 
 }  // namespace qmoe
