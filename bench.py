@@ -63,8 +63,10 @@ def expert_bytes(H, I, wfmt):
 
 
 def algorithmic(geom, wfmt, T, n_active):
-    """Bytes the method must move and flops it must do for one layer call,
-    and per kernel of the current launch sequence."""
+    """Bytes the method must move and flops it must do for one layer call, and
+    per kernel of the launch sequence (keys are the kernel names the library's
+    trace reports).  Bytes count each operand once: the weights of every
+    selected expert, activations in, results out."""
     H, I, E, k = geom["hidden"], geom["moe_inter"], geom["n_routed_experts"], geom["top_k"]
     Is = geom["shared_inter"] if geom["n_shared_experts"] else 0
     P = T * k
@@ -74,20 +76,74 @@ def algorithmic(geom, wfmt, T, n_active):
     router_b = E * H * 4 + E * 4
     layer_bytes = n_active * sum(eb.values()) + sum(sb.values()) + router_b + x_b + y_b
     layer_flops = P * 2 * H * I * 3 + T * 2 * H * Is * 3 + T * 2 * H * E
-    ldh_rows = P + (T if Is else 0)
+    rows = P + (T if Is else 0)                   # routed pairs + shared rows
+    w_gu = n_active * (eb["gate"] + eb["up"]) + sb["gate"] + sb["up"]
+    w_dn = n_active * eb["down"] + sb["down"]
+    f_gu = P * 2 * H * I * 2 + T * 2 * H * Is * 2
+    f_dn = P * 2 * H * I + T * 2 * H * Is
+    sel_b = T * E * 8 + E * 4 + P * 8 + P * 4 * 3 + (E + 1) * 4
     kern = {
+        # small-batch path
+        "dec_router_shared": dict(bytes=router_b + sb["gate"] + sb["up"] + x_b + T * E * 8 + T * Is * 2,
+                                  flops=T * 2 * H * E + T * 2 * H * Is * 2),
+        "dec_select_permute": dict(bytes=sel_b, flops=0),
+        "dec_gateup": dict(bytes=n_active * (eb["gate"] + eb["up"]) + x_b + P * I * 2,
+                           flops=P * 2 * H * I * 2),
+        "dec_down_combine": dict(bytes=w_dn + rows * I * 2 + y_b, flops=f_dn + 2 * P * H),
+        # large-batch path
         "route_logits": dict(bytes=router_b + x_b + T * E * 8, flops=T * 2 * H * E),
         "route_select": dict(bytes=T * E * 8 + E * 4 + P * 8, flops=0),
         "permute": dict(bytes=P * 4 * 3 + (E + 1) * 4, flops=0),
-        "gateup_gemv": dict(bytes=n_active * (eb["gate"] + eb["up"]) + sb["gate"] + sb["up"]
-                            + x_b + ldh_rows * I * 2,
-                            flops=P * 2 * H * I * 2 + T * 2 * H * Is * 2),
-        "down_gemv": dict(bytes=n_active * eb["down"] + sb["down"] + ldh_rows * I * 2
-                          + ldh_rows * H * 4,
-                          flops=P * 2 * H * I + T * 2 * H * Is),
-        "combine": dict(bytes=ldh_rows * H * 4 + P * 8 + y_b, flops=2 * P * H),
+        "gemm_prep": dict(bytes=x_b * 2, flops=0),
+        "gemm_gateup": dict(bytes=w_gu + x_b + rows * I * 2, flops=f_gu),
+        "gemm_down": dict(bytes=w_dn + rows * I * 2 + rows * H * 4, flops=f_dn),
+        "combine": dict(bytes=rows * H * 4 + P * 8 + y_b, flops=2 * P * H),
+        # moe_expert_ffn_q4 on few tokens
+        "gateup_gemv": dict(bytes=w_gu + x_b + rows * I * 2, flops=f_gu),
+        "down_gemv": dict(bytes=w_dn + rows * I * 2 + rows * H * 4, flops=f_dn),
     }
     return layer_bytes, layer_flops, kern
+
+
+KERNEL_SOURCES = {
+    "dec_": ["decode.hip", "select_token.h", "qmoe_device.h", "qmoe_internal.h"],
+    "gemm_": ["gemm.hip", "qmoe_device.h", "qmoe_internal.h"],
+    "route_": ["route.hip", "select_token.h", "qmoe_device.h", "qmoe_internal.h"],
+}
+
+
+def kernel_source_hash(kernel):
+    """sha256 over the sources a kernel is compiled from (None if unknown)."""
+    import hashlib
+    files = next((v for p, v in KERNEL_SOURCES.items() if kernel.startswith(p)), None)
+    if files is None:
+        return None
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "quantized_moe_02_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_for(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 PMC
+    readings (FETCH_SIZE + WRITE_SIZE, each scaled by the same counter's
+    reading for a copy kernel of known size); None when no reading exists or
+    the kernel's sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(f"{kernel}@{workload}")
+    if not rec or rec.get("sha256") != kernel_source_hash(kernel):
+        return None
+    return rec["fetch_kib"] * 1024 * rec["fetch_scale"] + rec["write_kib"] * 1024 * rec["write_scale"]
+
+
+def roofline_bound(kb):
+    """A kernel is MFMA-bound when its arithmetic intensity exceeds the
+    machine balance (dense fp16 flops per HBM byte), else HBM-bound."""
+    return "mfma" if kb["flops"] > kb["bytes"] * (PEAK_F16_TFLOPS * 1e12) / (PEAK_HBM_GBS * 1e9) else "hbm"
 
 
 # ---------------------------------------------------------------------------
@@ -224,17 +280,19 @@ def run_workload(name, args):
         kt = trace_kernels(B, ksteps)
         res["kernels_us"] = kt
         dom = max(kt, key=kt.get)
-        kb = kern.get(dom, dict(bytes=0, flops=0))
+        kb = kern[dom]
         dur = kt[dom] * 1e-6
-        if "gemm" in dom:
+        if roofline_bound(kb) == "mfma":
             ach = kb["flops"] / dur / 1e12
             res["roofline"] = dict(kernel=dom, bound="mfma", achieved=ach, peak=PEAK_F16_TFLOPS,
-                                   unit="TFLOP/s", frac=ach / PEAK_F16_TFLOPS, traffic=None,
+                                   unit="TFLOP/s", frac=ach / PEAK_F16_TFLOPS,
+                                   traffic=traffic_for(dom, name),
                                    algorithmic=kb["flops"], avg_us=kt[dom])
         else:
             ach = kb["bytes"] / dur / 1e9
             res["roofline"] = dict(kernel=dom, bound="hbm", achieved=ach, peak=PEAK_HBM_GBS,
-                                   unit="GB/s", frac=ach / PEAK_HBM_GBS, traffic=None,
+                                   unit="GB/s", frac=ach / PEAK_HBM_GBS,
+                                   traffic=traffic_for(dom, name),
                                    algorithmic=kb["bytes"], avg_us=kt[dom])
     del B
     torch.cuda.empty_cache()

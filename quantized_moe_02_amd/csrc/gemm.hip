@@ -20,6 +20,8 @@
 // and B is valid: within a 128-input block a lane loads one 16-byte chunk of
 // its row (a whole 32-input group, one scale) and feeds its four 32-bit words
 // to four consecutive MFMA K steps; the B reads from LDS use the same order.
+#include <type_traits>
+
 #include "qmoe_device.h"
 
 namespace qmoe {
@@ -78,22 +80,30 @@ struct Unit {
   bool routed;
 };
 
+// The unit is the same for the whole workgroup; readfirstlane puts it in
+// SGPRs, so that the buffer descriptors built from it are uniform (a
+// descriptor in VGPRs turns every buffer load into a waterfall loop).
 __device__ __forceinline__ Unit load_unit(const GemmArgs& g, int idx) {
   const int4 t = g.tiles[idx];
   Unit u;
-  u.routed = t.x >= 0;
-  u.e = u.routed ? t.x : 0;
-  u.p0 = t.y;
-  u.M = t.z;
-  u.tok0 = t.w;
+  const int x = __builtin_amdgcn_readfirstlane(t.x);
+  u.routed = x >= 0;
+  u.e = u.routed ? x : 0;
+  u.p0 = __builtin_amdgcn_readfirstlane(t.y);
+  u.M = __builtin_amdgcn_readfirstlane(t.z);
+  u.tok0 = __builtin_amdgcn_readfirstlane(t.w);
   return u;
 }
 
-// Activation rows of the unit -> registers -> LDS (fp16), zero rows past M.
-// Each thread moves 8 x 16 bytes: token m = tid / 2, half of the 128-input
-// block = tid % 2.  Loads are unconditional (rows and inputs clamped into
-// range) and masked afterwards, so that they all stay in flight together.
-template <int PROJ>
+// A buffer offset past every descriptor's range: loads from it return zero.
+// Buffers here are limited to kOutOfRange bytes, which the host checks.
+constexpr uint32_t kOutOfRange = 0xFFFFF000u;
+
+// Activation rows of the unit -> registers -> LDS (fp16).  Each thread moves
+// 8 x 16 bytes: token m = tid / 2, half of the 128-input block = tid % 2.
+// Rows past M and inputs past K are read from an out-of-range offset, which
+// yields zeros without a select on the loaded data, so that all eight loads
+// stay in flight together.
 __device__ __forceinline__ void load_act(const rsrc_t& ar, uint32_t rowoff, int kb, int K, bool mok,
                                          uint4 (&reg)[8]) {
   const int half = threadIdx.x & 1;
@@ -101,17 +111,14 @@ __device__ __forceinline__ void load_act(const rsrc_t& ar, uint32_t rowoff, int 
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int k = k0 + 8 * i;
-    const bool ok = mok && k < K;
+    const uint32_t off = (mok && k < K) ? rowoff + (uint32_t)k * 2u : kOutOfRange;
     uint32_t t4[4];
-    bload16(t4, ar, rowoff + (uint32_t)(k < K ? k : 0) * 2u, 0);
-    uint4 v = make_uint4(t4[0], t4[1], t4[2], t4[3]);
-    opaque(v);
-    reg[i] = ok ? v : make_uint4(0, 0, 0, 0);
+    bload16(t4, ar, off, 0);
+    reg[i] = make_uint4(t4[0], t4[1], t4[2], t4[3]);
   }
 }
 
-// Byte offset, within the activation tensor, of the row this thread stages
-// (clamped into range), and the tensor's buffer descriptor.
+// Byte offset, within the activation tensor, of the row this thread stages.
 template <int PROJ>
 __device__ __forceinline__ uint32_t act_rowoff(const GemmArgs& g, const Unit& u, int K) {
   const int m = min((int)(threadIdx.x >> 1), u.M - 1);
@@ -131,6 +138,9 @@ __device__ __forceinline__ void store_act(uint16_t* xs, const uint4 (&reg)[8]) {
   for (int i = 0; i < 8; ++i) dst[i] = reg[i];
 }
 
+template <int N>
+using ic = std::integral_constant<int, N>;
+
 // PROJ 0: gate/up (+SwiGLU), PROJ 1: down.
 template <int FMT, int PROJ>
 __global__ void __launch_bounds__(256, 2) moe_gemm_kernel(GemmArgs g) {
@@ -139,7 +149,7 @@ __global__ void __launch_bounds__(256, 2) moe_gemm_kernel(GemmArgs g) {
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int uidx = blockIdx.x;
-  if (uidx >= *g.n_tiles) return;
+  if (uidx >= __builtin_amdgcn_readfirstlane(*g.n_tiles)) return;
   const Unit u = load_unit(g, uidx);
   const ExpertSet& X = u.routed ? g.routed : g.shared;
   const int inter = X.inter;
@@ -154,23 +164,27 @@ __global__ void __launch_bounds__(256, 2) moe_gemm_kernel(GemmArgs g) {
   const int sgpr = FMT == MOE_WFMT_INT4_G32_F16 ? 32 : 16;   // inputs per scale
   const uint32_t scaleRowBytes = (uint32_t)(K / sgpr) * (FMT == MOE_WFMT_INT4_G32_F16 ? 2 : 1);
 
-  // weight buffers of this wave's row tiles: rt 0,1 gate (or down) rows,
-  // rt 2,3 the matching up rows (gate/up) or further down rows
-  rsrc_t qb[RT], sb[RT];
-  int rbase[RT];
-  float gsc[RT];
+  // One buffer per projection over this expert's whole matrix (codes and
+  // scales); rows past the end read as zero through the range check.
+  constexpr int NPJ = PROJ == 0 ? 2 : 1;
+  rsrc_t qb[NPJ], sb[NPJ];
+  float gsc[NPJ];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const ProjPtr& P = PROJ == 0 ? (rt < 2 ? X.gate : X.up) : X.down;
-    const int r = PROJ == 0 ? wrow + 16 * (rt & 1) : wrow + 16 * rt;
-    rbase[rt] = r;
-    const int rows_valid = max(0, min(16, nrow_out - r));
-    const size_t row0 = (size_t)u.e * nrow_out + r;
-    qb[rt] = make_rsrc(P.q + row0 * rowBytes, (uint32_t)rows_valid * rowBytes);
-    sb[rt] = make_rsrc(reinterpret_cast<const uint8_t*>(P.s) + row0 * scaleRowBytes,
-                       (uint32_t)rows_valid * scaleRowBytes);
-    gsc[rt] = FMT == MOE_WFMT_NVFP4 ? P.g[u.e] : 1.0f;
+  for (int j = 0; j < NPJ; ++j) {
+    const ProjPtr& P = PROJ == 0 ? (j == 0 ? X.gate : X.up) : X.down;
+    const size_t row0 = (size_t)u.e * nrow_out;
+    qb[j] = make_rsrc(P.q + row0 * rowBytes, (uint32_t)nrow_out * rowBytes);
+    sb[j] = make_rsrc(reinterpret_cast<const uint8_t*>(P.s) + row0 * scaleRowBytes,
+                      (uint32_t)nrow_out * scaleRowBytes);
+    gsc[j] = FMT == MOE_WFMT_NVFP4 ? __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                         __builtin_bit_cast(int, P.g[u.e])))
+                                   : 1.0f;
   }
+  // row tiles of this wave: gate/up rt 0,1 gate rows, rt 2,3 the matching up
+  // rows; down rt 0..3 consecutive rows
+  int rbase[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) rbase[rt] = PROJ == 0 ? wrow + 16 * (rt & 1) : wrow + 16 * rt;
   const int lrow = lane & 15, lq = lane >> 4;
   const int nkb = (K + kBK - 1) / kBK;
   const int nct = (u.M + 15) >> 4;
@@ -181,18 +195,24 @@ __global__ void __launch_bounds__(256, 2) moe_gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int c = 0; c < kCT; ++c) acc[rt][c] = float4v{0.f, 0.f, 0.f, 0.f};
 
-  // weights of one K block: lane (lrow, lq) loads group 4*kb + lq of its row
+  // weights of one K block: lane (lrow, lq) loads group 4*kb + lq of its row;
+  // groups past the row read as zero codes and zero scales
+  uint32_t qoff[RT], soff[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    qoff[rt] = (uint32_t)(rbase[rt] + lrow) * rowBytes;
+    soff[rt] = (uint32_t)(rbase[rt] + lrow) * scaleRowBytes;
+  }
   uint32_t wcode[2][RT][4], wsc[2][RT];
-  auto load_w = [&](int buf, int kb) {
+  auto load_w = [&](auto BUF, int kb) {
+    constexpr int buf = decltype(BUF)::value;
     const int grp = kb * 4 + lq;
     const bool ok = grp < nG;
-    const uint32_t gc = ok ? (uint32_t)grp : 0u;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      bload16(wcode[buf][rt], qb[rt], gc * 16u, (uint32_t)lrow * rowBytes);
-      uint32_t sc = bload_u16(sb[rt], gc * 2u, (uint32_t)lrow * scaleRowBytes);
-      opaque(sc);
-      wsc[buf][rt] = ok ? sc : 0u;  // a zero scale zeroes the group
+      const int j = PROJ == 0 ? rt >> 1 : 0;
+      bload16(wcode[buf][rt], qb[j], ok ? qoff[rt] + (uint32_t)grp * 16u : kOutOfRange, 0);
+      wsc[buf][rt] = bload_u16(sb[j], ok ? soff[rt] + (uint32_t)grp * 2u : kOutOfRange, 0);
     }
   };
 
@@ -201,17 +221,14 @@ __global__ void __launch_bounds__(256, 2) moe_gemm_kernel(GemmArgs g) {
                               : make_rsrc(g.hin, (uint32_t)(g.P + g.T) * (uint32_t)g.ldh * 2u);
   const uint32_t arowoff = act_rowoff<PROJ>(g, u, K);
   const bool amok = (int)(threadIdx.x >> 1) < u.M;
-  load_act<PROJ>(ar, arowoff, 0, K, amok, areg);
-  load_w(0, 0);
-  store_act(xs[0], areg);
-  __syncthreads();
 
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int cur = kb & 1;
+  // one K block on buffer CUR, prefetching block kb + 1 into the other one
+  auto kblock = [&](auto CUR, int kb) {
+    constexpr int cur = decltype(CUR)::value;
     const bool more = kb + 1 < nkb;
     if (more) {
-      load_act<PROJ>(ar, arowoff, kb + 1, K, amok, areg);
-      load_w(cur ^ 1, kb + 1);
+      load_act(ar, arowoff, kb + 1, K, amok, areg);
+      load_w(ic<cur ^ 1>{}, kb + 1);
     }
     const uint16_t* xb = xs[cur];
 #pragma unroll
@@ -248,11 +265,20 @@ __global__ void __launch_bounds__(256, 2) moe_gemm_kernel(GemmArgs g) {
       }
     }
     if (more) {
-      // xs[cur ^ 1] was last read in block kb-1, which every wave finished
+      // xs[cur ^ 1] was last read in block kb - 1, which every wave finished
       // before the barrier that ended it
       store_act(xs[cur ^ 1], areg);
       __syncthreads();
     }
+  };
+
+  load_act(ar, arowoff, 0, K, amok, areg);
+  load_w(ic<0>{}, 0);
+  store_act(xs[0], areg);
+  __syncthreads();
+  for (int kb = 0; kb < nkb; kb += 2) {
+    kblock(ic<0>{}, kb);
+    if (kb + 1 < nkb) kblock(ic<1>{}, kb + 1);
   }
 
   // epilogue
@@ -268,8 +294,8 @@ __global__ void __launch_bounds__(256, 2) moe_gemm_kernel(GemmArgs g) {
         uint32_t packed[2];
 #pragma unroll
         for (int i = 0; i < 4; i += 2) {
-          const float h0 = silu_mul(acc[rt][c][i] * gsc[rt], acc[rt + 2][c][i] * gsc[rt + 2]);
-          const float h1 = silu_mul(acc[rt][c][i + 1] * gsc[rt], acc[rt + 2][c][i + 1] * gsc[rt + 2]);
+          const float h0 = silu_mul(acc[rt][c][i] * gsc[0], acc[rt + 2][c][i] * gsc[1]);
+          const float h1 = silu_mul(acc[rt][c][i + 1] * gsc[0], acc[rt + 2][c][i + 1] * gsc[1]);
           const _Float16 a0 = (_Float16)h0, a1 = (_Float16)h1;
           packed[i / 2] = (uint32_t)__builtin_bit_cast(uint16_t, a0) |
                           ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
@@ -284,10 +310,10 @@ __global__ void __launch_bounds__(256, 2) moe_gemm_kernel(GemmArgs g) {
         const int col = rbase[rt] + 4 * lq;
         if (col < g.H) {
           float4 o;
-          o.x = acc[rt][c][0] * gsc[rt];
-          o.y = acc[rt][c][1] * gsc[rt];
-          o.z = acc[rt][c][2] * gsc[rt];
-          o.w = acc[rt][c][3] * gsc[rt];
+          o.x = acc[rt][c][0] * gsc[0];
+          o.y = acc[rt][c][1] * gsc[0];
+          o.z = acc[rt][c][2] * gsc[0];
+          o.w = acc[rt][c][3] * gsc[0];
           *reinterpret_cast<float4*>(g.o_out + (size_t)orow * g.H + col) = o;
         }
       }
