@@ -33,7 +33,8 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 
 constexpr int kBM = 128;          // tokens per unit
 constexpr int kBK = 128;          // inputs per K block
-constexpr int kXS = kBK + 8;      // LDS row stride in fp16 (16-byte pad against bank conflicts)
+constexpr int kChunks = kBK / 8;  // 16-byte chunks per activation row of a K block
+constexpr int kStage = kBM * kBK; // fp16 elements per activation stage in LDS
 constexpr int kCT = kBM / 16;     // 16-token column tiles
 constexpr int kGateUpPairs = 128; // row pairs per gate/up unit
 constexpr int kDownRows = 256;    // output rows per down unit
@@ -99,63 +100,95 @@ __device__ __forceinline__ Unit load_unit(const GemmArgs& g, int idx) {
 // Buffers here are limited to kOutOfRange bytes, which the host checks.
 constexpr uint32_t kOutOfRange = 0xFFFFF000u;
 
-// Activation rows of the unit -> registers -> LDS (fp16).  Each thread moves
-// 8 x 16 bytes: token m = tid / 2, half of the 128-input block = tid % 2.
-// Rows past M and inputs past K are read from an out-of-range offset, which
-// yields zeros without a select on the loaded data, so that all eight loads
-// stay in flight together.
-__device__ __forceinline__ void load_act(const rsrc_t& ar, uint32_t rowoff, int kb, int K, bool mok,
-                                         uint4 (&reg)[8]) {
-  const int half = threadIdx.x & 1;
-  const int k0 = kb * kBK + half * 64;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int k = k0 + 8 * i;
-    const uint32_t off = (mok && k < K) ? rowoff + (uint32_t)k * 2u : kOutOfRange;
-    uint32_t t4[4];
-    bload16(t4, ar, off, 0);
-    reg[i] = make_uint4(t4[0], t4[1], t4[2], t4[3]);
-  }
-}
+// Activations go from HBM straight into LDS (buffer_load ... lds: lane l of a
+// load writes 16 bytes at base + 16 l).  Stage layout: 128 token rows of 16
+// chunks of 16 bytes, chunk c of row r at slot r * 16 + (c ^ (r & 15)); the
+// XOR spreads the 16 rows that one B-operand read touches over all banks.
+// Load i of wave w covers slots (8 w + i) * 64 .. +63, i.e. rows 4 (8 w + i)
+// + lane / 16, slot lane % 16.  Rows past M and inputs past K are read from an
+// out-of-range offset, which writes zeros.
+constexpr int kActLoads = kBM * kChunks / 256;   // loads per thread per K block
 
-// Byte offset, within the activation tensor, of the row this thread stages.
 template <int PROJ>
-__device__ __forceinline__ uint32_t act_rowoff(const GemmArgs& g, const Unit& u, int K) {
-  const int m = min((int)(threadIdx.x >> 1), u.M - 1);
-  if constexpr (PROJ == 0) {
-    const int t = u.routed ? g.sorted_token[u.tok0 + m] : u.tok0 + m;
-    return (uint32_t)t * (uint32_t)K * 2u;
-  } else {
-    return (uint32_t)(u.p0 + m) * (uint32_t)g.ldh * 2u;
+__device__ __forceinline__ void act_rows(const GemmArgs& g, const Unit& u, int K, int wv, int lane,
+                                         uint32_t (&rowoff)[kActLoads]) {
+#pragma unroll
+  for (int i = 0; i < kActLoads; ++i) {
+    const int m = (wv * kActLoads + i) * 4 + (lane >> 4);
+    uint32_t off = kOutOfRange;
+    if (m < u.M) {
+      if constexpr (PROJ == 0) {
+        const int t = u.routed ? g.sorted_token[u.tok0 + m] : u.tok0 + m;
+        off = (uint32_t)t * (uint32_t)K * 2u;
+      } else {
+        off = (uint32_t)(u.p0 + m) * (uint32_t)g.ldh * 2u;
+      }
+    }
+    rowoff[i] = off;
   }
 }
 
-__device__ __forceinline__ void store_act(uint16_t* xs, const uint4 (&reg)[8]) {
-  const int tid = threadIdx.x;
-  const int m = tid >> 1, half = tid & 1;
-  uint4* dst = reinterpret_cast<uint4*>(xs + m * kXS + half * 64);
+__device__ __forceinline__ void issue_act(const rsrc_t& ar, const uint32_t (&rowoff)[kActLoads], int kb,
+                                          int K, int wv, int lane, uint16_t* stage) {
+  const int row_lo = lane >> 4;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) dst[i] = reg[i];
+  for (int i = 0; i < kActLoads; ++i) {
+    const int row = (wv * kActLoads + i) * 4 + row_lo;
+    const int chunk = (lane & 15) ^ (row & 15);
+    const int k = kb * kBK + chunk * 8;
+    const uint32_t off =
+        (rowoff[i] != kOutOfRange && k < K) ? rowoff[i] + (uint32_t)k * 2u : kOutOfRange;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        ar, (__attribute__((address_space(3))) void*)(stage + (wv * kActLoads + i) * 64 * 8), 16, off,
+        0, 0, 0);
+  }
 }
 
 template <int N>
 using ic = std::integral_constant<int, N>;
 
+constexpr int kNS = 4;            // K blocks in flight (LDS stages, weight register ring)
+constexpr int kRT = 4;            // 16-row weight tiles per wave
+constexpr int kLoadsPerKB = kActLoads + 2 * kRT;   // vector memory ops per thread per K block
+
+// Work item -> (unit, n tile).  Workgroups are dispatched round-robin over
+// the 8 XCDs; this maps the items that one XCD receives onto a contiguous
+// range, n tile fastest, so that the n tiles of one token tile run on the same
+// XCD at about the same time and share its L2 copy of the activations.
+__device__ __forceinline__ int xcd_item(int L, int total) {
+  const int x = L & 7, q = total >> 3, r = total & 7;
+  return x * q + min(x, r) + (L >> 3);
+}
+
 // PROJ 0: gate/up (+SwiGLU), PROJ 1: down.
+//
+// One workgroup of 4 waves per CU (one wave per SIMD, all 512 registers per
+// lane).  K loop: kNS-stage pipeline.  K block kb + 3 is requested (weights
+// into the register ring, activations straight into an LDS stage) while
+// block kb is multiplied; within a block, the next K step's B operands
+// (LDS) and A operands (dequantised weights) are produced while the current
+// step's MFMAs run.  Every K block issues exactly kLoadsPerKB vector memory
+// ops per thread (blocks past K read zeros), so "block kb + 1 has landed" is
+// vmcnt <= 2 * kLoadsPerKB.  One barrier per K block, before its last K step.
 template <int FMT, int PROJ>
-__global__ void __launch_bounds__(256, 2) moe_gemm_kernel(GemmArgs g) {
-  constexpr int RT = 4;  // 16-row tiles per wave
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][kBM * kXS];
+__global__ void __launch_bounds__(256, 1) moe_gemm_kernel(GemmArgs g) {
+  constexpr int RT = kRT;
+  __shared__ __attribute__((aligned(16))) uint16_t xs[kNS][kStage];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int uidx = blockIdx.x;
-  if (uidx >= __builtin_amdgcn_readfirstlane(*g.n_tiles)) return;
+  const int max_inter = max(g.routed.inter, g.has_shared ? g.shared.inter : 0);
+  const int NT = PROJ == 0 ? (max_inter + kGateUpPairs - 1) / kGateUpPairs
+                           : (g.H + kDownRows - 1) / kDownRows;
+  const int total = __builtin_amdgcn_readfirstlane(*g.n_tiles) * NT;
+  if ((int)blockIdx.x >= total) return;
+  const int w = xcd_item(blockIdx.x, total);
+  const int uidx = w / NT;
+  const int nt = w - uidx * NT;
   const Unit u = load_unit(g, uidx);
   const ExpertSet& X = u.routed ? g.routed : g.shared;
   const int inter = X.inter;
   const int K = PROJ == 0 ? g.H : inter;
   const int nrow_out = PROJ == 0 ? inter : g.H;
-  const int nt = blockIdx.y;
   // first output row of this wave (gate/up: row pairs)
   const int wrow = PROJ == 0 ? nt * kGateUpPairs + wv * 32 : nt * kDownRows + wv * 64;
   if (nt * (PROJ == 0 ? kGateUpPairs : kDownRows) >= nrow_out) return;
@@ -189,13 +222,7 @@ __global__ void __launch_bounds__(256, 2) moe_gemm_kernel(GemmArgs g) {
   const int nkb = (K + kBK - 1) / kBK;
   const int nct = (u.M + 15) >> 4;
 
-  float4v acc[RT][kCT];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-    for (int c = 0; c < kCT; ++c) acc[rt][c] = float4v{0.f, 0.f, 0.f, 0.f};
-
-  // weights of one K block: lane (lrow, lq) loads group 4*kb + lq of its row;
+  // weights of one K block: lane (lrow, lq) loads group 4 kb + lq of its row;
   // groups past the row read as zero codes and zero scales
   uint32_t qoff[RT], soff[RT];
 #pragma unroll
@@ -203,122 +230,160 @@ __global__ void __launch_bounds__(256, 2) moe_gemm_kernel(GemmArgs g) {
     qoff[rt] = (uint32_t)(rbase[rt] + lrow) * rowBytes;
     soff[rt] = (uint32_t)(rbase[rt] + lrow) * scaleRowBytes;
   }
-  uint32_t wcode[2][RT][4], wsc[2][RT];
-  auto load_w = [&](auto BUF, int kb) {
-    constexpr int buf = decltype(BUF)::value;
+  uint32_t wcode[kNS][RT][4], wsc[kNS][RT];
+  const rsrc_t ar = PROJ == 0 ? make_rsrc(g.x16, (uint32_t)g.T * (uint32_t)g.H * 2u)
+                              : make_rsrc(g.hin, (uint32_t)(g.P + g.T) * (uint32_t)g.ldh * 2u);
+  uint32_t arow[kActLoads];
+  act_rows<PROJ>(g, u, K, wv, lane, arow);
+
+  // request K block kb into stage S (LDS) and ring slot S (registers)
+  auto issue = [&](auto S, int kb) {
+    constexpr int st = decltype(S)::value;
+    issue_act(ar, arow, kb, K, wv, lane, xs[st]);
     const int grp = kb * 4 + lq;
     const bool ok = grp < nG;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       const int j = PROJ == 0 ? rt >> 1 : 0;
-      bload16(wcode[buf][rt], qb[j], ok ? qoff[rt] + (uint32_t)grp * 16u : kOutOfRange, 0);
-      wsc[buf][rt] = bload_u16(sb[j], ok ? soff[rt] + (uint32_t)grp * 2u : kOutOfRange, 0);
+      bload16(wcode[st][rt], qb[j], ok ? qoff[rt] + (uint32_t)grp * 16u : kOutOfRange, 0);
+      wsc[st][rt] = bload_u16(sb[j], ok ? soff[rt] + (uint32_t)grp * 2u : kOutOfRange, 0);
+    }
+  };
+  // A operands (dequantised weights) of K step ks from ring slot S
+  auto dequant_ks = [&](auto S, int ks, half8 (&A)[RT]) {
+    constexpr int st = decltype(S)::value;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      uint32_t s2;
+      if constexpr (FMT == MOE_WFMT_INT4_G32_F16) {
+        s2 = (wsc[st][rt] & 0xffffu) * 0x00010001u;
+      } else {
+        // inputs 0-15 of the group use scale byte 0, 16-31 byte 1
+        const _Float16 sh = (_Float16)e4m3_to_f32(wsc[st][rt], ks >> 1);
+        const uint32_t b = __builtin_bit_cast(uint16_t, sh);
+        s2 = b * 0x00010001u;
+      }
+      A[rt] = dequant_word<FMT>(wcode[st][rt][ks], s2);
     }
   };
 
-  uint4 areg[8];
-  const rsrc_t ar = PROJ == 0 ? make_rsrc(g.x16, (uint32_t)g.T * (uint32_t)g.H * 2u)
-                              : make_rsrc(g.hin, (uint32_t)(g.P + g.T) * (uint32_t)g.ldh * 2u);
-  const uint32_t arowoff = act_rowoff<PROJ>(g, u, K);
-  const bool amok = (int)(threadIdx.x >> 1) < u.M;
-
-  // one K block on buffer CUR, prefetching block kb + 1 into the other one
-  auto kblock = [&](auto CUR, int kb) {
-    constexpr int cur = decltype(CUR)::value;
-    const bool more = kb + 1 < nkb;
-    if (more) {
-      load_act(ar, arowoff, kb + 1, K, amok, areg);
-      load_w(ic<cur ^ 1>{}, kb + 1);
-    }
-    const uint16_t* xb = xs[cur];
+  auto run = [&](auto CTC) {
+    constexpr int CT = decltype(CTC)::value;   // column tiles computed (>= nct)
+    float4v acc[RT][CT];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      half8 A[RT];
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        uint32_t s2;
-        if constexpr (FMT == MOE_WFMT_INT4_G32_F16) {
-          s2 = (wsc[cur][rt] & 0xffffu) * 0x00010001u;
-        } else {
-          // inputs 0-15 of the group use scale byte 0, 16-31 byte 1
-          const _Float16 sh = (_Float16)e4m3_to_f32(wsc[cur][rt], ks >> 1);
-          const uint32_t b = __builtin_bit_cast(uint16_t, sh);
-          s2 = b * 0x00010001u;
-        }
-        A[rt] = dequant_word<FMT>(wcode[cur][rt][ks], s2);
+      for (int c = 0; c < CT; ++c) acc[rt][c] = float4v{0.f, 0.f, 0.f, 0.f};
+    half8 A[2][RT], B[2][CT];
+    auto read_b = [&](const uint16_t* xb, int ks, half8 (&Bv)[CT]) {
+#pragma unroll
+      for (int c = 0; c < CT; ++c)
+        Bv[c] = *reinterpret_cast<const half8*>(xb + (16 * c + lrow) * kBK +
+                                                 (((lq * 4 + ks) ^ lrow) * 8));
+    };
+    auto mfmas = [&](const half8 (&Av)[RT], const half8 (&Bv)[CT]) {
+#pragma unroll
+      for (int c = 0; c < CT; ++c)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+          acc[rt][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Av[rt], Bv[c], acc[rt][c], 0, 0, 0);
+    };
+    // interleave: each MFMA followed by its share of the next step's VALU and
+    // LDS reads
+    auto interleave = [&]() {
+      constexpr int NM = RT * CT;
+      constexpr int VPM = (16 * RT + NM - 1) / NM;   // dequant VALU per MFMA
+#pragma unroll
+      for (int i = 0; i < NM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+        if (i % RT == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
+    };
+
+    issue(ic<0>{}, 0);
+    issue(ic<1>{}, 1);
+    issue(ic<2>{}, 2);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kLoadsPerKB) : "memory");
+    __syncthreads();
+    read_b(xs[0], 0, B[0]);
+    dequant_ks(ic<0>{}, 0, A[0]);
+
+    auto kblock = [&](auto S, int kb) {
+      constexpr int st = decltype(S)::value;
+      constexpr int sn = (st + 1) % kNS;
+      constexpr int s3 = (st + kNS - 1) % kNS;
+      // stage s3 held block kb - 1, whose last reads every wave finished
+      // before the barrier of block kb - 1
+      issue(ic<s3>{}, kb + kNS - 1);
 #pragma unroll
-      for (int c0 = 0; c0 < kCT; c0 += 4) {
-        half8 B[4];
+      for (int ks = 0; ks < 3; ++ks) {
+        read_b(xs[st], ks + 1, B[(ks + 1) & 1]);
+        dequant_ks(ic<st>{}, ks + 1, A[(ks + 1) & 1]);
+        mfmas(A[ks & 1], B[ks & 1]);
+        interleave();
+      }
+      // block kb + 1 landed in every wave (two younger blocks may be in flight)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kLoadsPerKB) : "memory");
+      __syncthreads();
+      read_b(xs[sn], 0, B[0]);
+      dequant_ks(ic<sn>{}, 0, A[0]);
+      mfmas(A[1], B[1]);
+      interleave();
+    };
+    for (int kb = 0; kb < nkb; kb += kNS) {
+      kblock(ic<0>{}, kb);
+      if (kb + 1 < nkb) kblock(ic<1>{}, kb + 1);
+      if (kb + 2 < nkb) kblock(ic<2>{}, kb + 2);
+      if (kb + 3 < nkb) kblock(ic<3>{}, kb + 3);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+    // epilogue
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-          B[c] = *reinterpret_cast<const half8*>(xb + (16 * (c0 + c) + lrow) * kXS + lq * 32 + ks * 8);
+    for (int c = 0; c < CT; ++c) {
+      const int m = 16 * c + lrow;
+      if (m >= u.M) continue;
+      const int orow = u.p0 + m;
+      if constexpr (PROJ == 0) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          if (c0 + c < nct) {
+        for (int rt = 0; rt < 2; ++rt) {
+          uint32_t packed[2];
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-              acc[rt][c0 + c] =
-                  __builtin_amdgcn_mfma_f32_16x16x32_f16(A[rt], B[c], acc[rt][c0 + c], 0, 0, 0);
+          for (int i = 0; i < 4; i += 2) {
+            const float h0 = silu_mul(acc[rt][c][i] * gsc[0], acc[rt + 2][c][i] * gsc[1]);
+            const float h1 = silu_mul(acc[rt][c][i + 1] * gsc[0], acc[rt + 2][c][i + 1] * gsc[1]);
+            const _Float16 a0 = (_Float16)h0, a1 = (_Float16)h1;
+            packed[i / 2] = (uint32_t)__builtin_bit_cast(uint16_t, a0) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
+          }
+          const int col = rbase[rt] + 4 * lq;
+          if (col < inter)
+            *reinterpret_cast<uint2*>(g.h_out + (size_t)orow * g.ldh + col) =
+                make_uint2(packed[0], packed[1]);
+        }
+      } else {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const int col = rbase[rt] + 4 * lq;
+          if (col < g.H) {
+            float4 o;
+            o.x = acc[rt][c][0] * gsc[0];
+            o.y = acc[rt][c][1] * gsc[0];
+            o.z = acc[rt][c][2] * gsc[0];
+            o.w = acc[rt][c][3] * gsc[0];
+            *reinterpret_cast<float4*>(g.o_out + (size_t)orow * g.H + col) = o;
           }
         }
       }
     }
-    if (more) {
-      // xs[cur ^ 1] was last read in block kb - 1, which every wave finished
-      // before the barrier that ended it
-      store_act(xs[cur ^ 1], areg);
-      __syncthreads();
-    }
   };
-
-  load_act(ar, arowoff, 0, K, amok, areg);
-  load_w(ic<0>{}, 0);
-  store_act(xs[0], areg);
-  __syncthreads();
-  for (int kb = 0; kb < nkb; kb += 2) {
-    kblock(ic<0>{}, kb);
-    if (kb + 1 < nkb) kblock(ic<1>{}, kb + 1);
-  }
-
-  // epilogue
-#pragma unroll
-  for (int c = 0; c < kCT; ++c) {
-    if (c >= nct) break;
-    const int m = 16 * c + lrow;
-    if (m >= u.M) continue;
-    const int orow = u.p0 + m;
-    if constexpr (PROJ == 0) {
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        uint32_t packed[2];
-#pragma unroll
-        for (int i = 0; i < 4; i += 2) {
-          const float h0 = silu_mul(acc[rt][c][i] * gsc[0], acc[rt + 2][c][i] * gsc[1]);
-          const float h1 = silu_mul(acc[rt][c][i + 1] * gsc[0], acc[rt + 2][c][i + 1] * gsc[1]);
-          const _Float16 a0 = (_Float16)h0, a1 = (_Float16)h1;
-          packed[i / 2] = (uint32_t)__builtin_bit_cast(uint16_t, a0) |
-                          ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
-        }
-        const int col = rbase[rt] + 4 * lq;
-        if (col < inter)
-          *reinterpret_cast<uint2*>(g.h_out + (size_t)orow * g.ldh + col) = make_uint2(packed[0], packed[1]);
-      }
-    } else {
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const int col = rbase[rt] + 4 * lq;
-        if (col < g.H) {
-          float4 o;
-          o.x = acc[rt][c][0] * gsc[0];
-          o.y = acc[rt][c][1] * gsc[0];
-          o.z = acc[rt][c][2] * gsc[0];
-          o.w = acc[rt][c][3] * gsc[0];
-          *reinterpret_cast<float4*>(g.o_out + (size_t)orow * g.H + col) = o;
-        }
-      }
-    }
-  }
+  if (nct > 4)
+    run(ic<8>{});
+  else if (nct > 2)
+    run(ic<4>{});
+  else
+    run(ic<2>{});
 }
 
 // bf16 -> fp16 copy of the activations (exact for |x| in the fp16 normal range)
@@ -400,6 +465,9 @@ int gemm_max_units(int T, int K, int E, bool has_shared) {
   return (int)(routed + shared);
 }
 int gemm_unit_tokens() { return kBM; }
+bool gemm_fits(int64_t T, int64_t rows, int64_t H, int64_t ldh) {
+  return T * H * 2 <= (int64_t)kOutOfRange && rows * ldh * 2 <= (int64_t)kOutOfRange;
+}
 
 hipError_t launch_x_to_f16(const uint16_t* x, uint16_t* y, size_t n, hipStream_t s) {
   const size_t n8 = n / 8;
@@ -412,14 +480,16 @@ hipError_t launch_gemm(const GemmArgs& g, int max_units, hipStream_t s, Tracer* 
   hipError_t e;
   int max_inter = g.routed.inter;
   if (g.has_shared && g.shared.inter > max_inter) max_inter = g.shared.inter;
-  dim3 g1(max_units, (max_inter + kGateUpPairs - 1) / kGateUpPairs);
+  // one workgroup per work item (unit, n tile); items past the actual number
+  // of units exit at once
+  dim3 g1(max_units * ((max_inter + kGateUpPairs - 1) / kGateUpPairs));
   if (g.wfmt == MOE_WFMT_NVFP4)
     hipLaunchKernelGGL((moe_gemm_kernel<MOE_WFMT_NVFP4, 0>), g1, dim3(256), 0, s, g);
   else
     hipLaunchKernelGGL((moe_gemm_kernel<MOE_WFMT_INT4_G32_F16, 0>), g1, dim3(256), 0, s, g);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (tr && (e = tr->mark("gemm_gateup")) != hipSuccess) return e;
-  dim3 g2(max_units, (g.H + kDownRows - 1) / kDownRows);
+  dim3 g2(max_units * ((g.H + kDownRows - 1) / kDownRows));
   if (g.wfmt == MOE_WFMT_NVFP4)
     hipLaunchKernelGGL((moe_gemm_kernel<MOE_WFMT_NVFP4, 1>), g2, dim3(256), 0, s, g);
   else

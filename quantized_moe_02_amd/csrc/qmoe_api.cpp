@@ -257,6 +257,8 @@ moe_status moe_expert_ffn_q4(const moe_config* cfg, int32_t T, const uint16_t* x
   a.wfmt = cfg->wfmt;
   a.ldh = ldh;
   if (T > kDecodeMaxTokens) {
+    const int64_t rows = routed ? (int64_t)T * cfg->top_k : T;
+    if (!gemm_fits(T, rows, cfg->hidden, ldh)) return MOE_ERR_UNSUPPORTED;
     const ExpertSet es = expert_set(*w, routed ? cfg->moe_inter : cfg->shared_inter);
     const int P = routed ? T * cfg->top_k : 0;
     return hip_status(run_gemm_ffn(*cfg, T, x, ws_, routed, es, expert_offsets, active_experts,
@@ -328,8 +330,14 @@ moe_status layer_impl(const moe_config* cfg, int32_t T, const uint16_t* x, const
     return MOE_OK;
   }
 
-  const Workspace w = carve_workspace(*cfg, T, ws);
+  const bool has_shared = cfg->n_shared_experts == 1;
+  const int ldh = std::max(cfg->moe_inter, has_shared ? cfg->shared_inter : 0);
   const size_t P = (size_t)T * cfg->top_k;
+  const bool small = T <= kDecodeMaxTokens && decode_supported(cfg->hidden);
+  if (!small && !gemm_fits(T, (int64_t)P + (has_shared ? T : 0), cfg->hidden, ldh))
+    return MOE_ERR_UNSUPPORTED;
+
+  const Workspace w = carve_workspace(*cfg, T, ws);
   Tracer tracer;
   tracer.t = trace;
   tracer.s = stream;
@@ -338,9 +346,7 @@ moe_status layer_impl(const moe_config* cfg, int32_t T, const uint16_t* x, const
   int32_t* ids = topk_ids_out ? topk_ids_out : w.ids;
   float* tw = topk_w_out ? topk_w_out : w.tw;
   hipError_t e;
-  const bool has_shared = cfg->n_shared_experts == 1;
-  const int ldh = std::max(cfg->moe_inter, has_shared ? cfg->shared_inter : 0);
-  if (T <= kDecodeMaxTokens && decode_supported(cfg->hidden)) {
+  if (small) {
     DecodeArgs d{};
     d.x = x;
     d.T = T;

@@ -170,6 +170,9 @@ struct GemmArgs {
   int T, H, P, wfmt;
 };
 int gemm_max_units(int T, int K, int E, bool has_shared);
+// Whether the GEMM path's activation buffers (T x H fp16 activations, rows x
+// ldh fp16 intermediates) fit its 32-bit buffer descriptors.
+bool gemm_fits(int64_t T, int64_t rows, int64_t H, int64_t ldh);
 int gemm_unit_tokens();
 hipError_t launch_build_units(const int32_t* offsets, const int32_t* active,
                               const int32_t* n_active, int4* tiles, int32_t* n_tiles, int T, int P,

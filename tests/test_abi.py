@@ -142,3 +142,10 @@ def test_entry_point_validation_paths():
     assert L.moe_combine(ctypes.byref(c), 8, FAKE, FAKE, FAKE, None, FAKE, 3, None) == q.MOE_ERR_INVALID_ARG
     assert L.moe_combine(ctypes.byref(c), 8, None, FAKE, FAKE, None, FAKE, 0, None) == q.MOE_ERR_INVALID_ARG
     assert L.moe_combine(ctypes.byref(c), 0, FAKE, FAKE, FAKE, None, FAKE, 0, None) == q.MOE_OK
+
+
+def test_layer_rejects_buffers_beyond_descriptor_range():
+    # 262144 tokens x hidden 16384 x 2 bytes exceeds the 32-bit buffer range of
+    # the large-batch kernels: rejected before any device call
+    c = _cfg(hidden=16384)
+    assert _layer(c, T=262144) == q.MOE_ERR_UNSUPPORTED
