@@ -44,25 +44,39 @@ __device__ __forceinline__ uint32_t pk_fma_f16(uint32_t a, uint32_t b, uint32_t 
                    __builtin_bit_cast(half2v, c);
   return __builtin_bit_cast(uint32_t, r);
 }
+__device__ __forceinline__ uint32_t pk_add_f16(uint32_t a, uint32_t b) {
+  const half2v r = __builtin_bit_cast(half2v, a) + __builtin_bit_cast(half2v, b);
+  return __builtin_bit_cast(uint32_t, r);
+}
 __device__ __forceinline__ uint32_t pk_mul_f16(uint32_t a, uint32_t b) {
   const half2v r = __builtin_bit_cast(half2v, a) * __builtin_bit_cast(half2v, b);
   return __builtin_bit_cast(uint32_t, r);
 }
 
 // One 32-bit word (8 consecutive inputs of one row) -> fp16 A operand.
-//   int4:  (u - 8) * scale, exact integer first, then one rounding.
+//   int4:  (u - 8) * scale, exact integer first, then one rounding.  The word
+//          holds pair k = (u_2k, u_2k+1) in bits 4k..4k+3 of its two halves;
+//          or-ing a nibble into the mantissa of fp16 1024 gives 1024 + u (bits
+//          0-3) or 1024 + 16 u (bits 4-7), so pairs 0 and 1 take one
+//          v_and_or each and pairs 2 and 3 share one shift by 8.
 //   nvfp4: e2m1 * e4m3 (exact in fp16); the per-tensor fp32 scale is applied
 //          to the accumulator in the epilogue.
 template <int FMT>
 __device__ __forceinline__ half8 dequant_word(uint32_t w, uint32_t scale2) {
   uint32_t p[4];
   if constexpr (FMT == MOE_WFMT_INT4_G32_F16) {
+    const uint32_t w8 = w >> 8;
+    const uint32_t v0 = and_or(w, 0x000F000Fu, 0x64006400u);    // 1024 + u
+    const uint32_t v1 = and_or(w, 0x00F000F0u, 0x64006400u);    // 1024 + 16 u
+    const uint32_t v2 = and_or(w8, 0x000F000Fu, 0x64006400u);
+    const uint32_t v3 = and_or(w8, 0x00F000F0u, 0x64006400u);
+    // u - 8, exactly: v - 1032, or v / 16 - 72
+    p[0] = pk_add_f16(v0, 0xE408E408u);
+    p[1] = pk_fma_f16(v1, 0x2C002C00u, 0xD480D480u);
+    p[2] = pk_add_f16(v2, 0xE408E408u);
+    p[3] = pk_fma_f16(v3, 0x2C002C00u, 0xD480D480u);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t v = int4_pair_f16(w, k);                   // 1 + u/16
-      const uint32_t q = pk_fma_f16(v, 0x4C004C00u, 0xCE00CE00u);  // *16 - 24 = u - 8
-      p[k] = pk_mul_f16(q, scale2);
-    }
+    for (int k = 0; k < 4; ++k) p[k] = pk_mul_f16(p[k], scale2);
   } else {
     // natural nibble order: byte k holds inputs 2k, 2k+1
 #pragma unroll
@@ -96,52 +110,49 @@ __device__ __forceinline__ Unit load_unit(const GemmArgs& g, int idx) {
   return u;
 }
 
-// A buffer offset past every descriptor's range: loads from it return zero.
-// Buffers here are limited to kOutOfRange bytes, which the host checks.
-constexpr uint32_t kOutOfRange = 0xFFFFF000u;
+// Activation rows past M start at this offset, past the range of every
+// activation descriptor (the host keeps those buffers below 2 GiB), so their
+// loads return zeros at every K block.
+constexpr uint32_t kOOBRow = 0x80000000u;
 
 // Activations go from HBM straight into LDS (buffer_load ... lds: lane l of a
 // load writes 16 bytes at base + 16 l).  Stage layout: 128 token rows of 16
 // chunks of 16 bytes, chunk c of row r at slot r * 16 + (c ^ (r & 15)); the
 // XOR spreads the 16 rows that one B-operand read touches over all banks.
 // Load i of wave w covers slots (8 w + i) * 64 .. +63, i.e. rows 4 (8 w + i)
-// + lane / 16, slot lane % 16.  Rows past M and inputs past K are read from an
-// out-of-range offset, which writes zeros.
+// + lane / 16, slot lane % 16.  Rows are padded with zeros to a multiple of
+// the K block, so a partial last K block reads zeros past K.
 constexpr int kActLoads = kBM * kChunks / 256;   // loads per thread per K block
 
+// Byte offset of each of this thread's loads at K block 0 (K block kb adds
+// kb * 256).
 template <int PROJ>
-__device__ __forceinline__ void act_rows(const GemmArgs& g, const Unit& u, int K, int wv, int lane,
-                                         uint32_t (&rowoff)[kActLoads]) {
+__device__ __forceinline__ void act_rows(const GemmArgs& g, const Unit& u, int wv, int lane,
+                                         uint32_t (&abase)[kActLoads]) {
 #pragma unroll
   for (int i = 0; i < kActLoads; ++i) {
     const int m = (wv * kActLoads + i) * 4 + (lane >> 4);
-    uint32_t off = kOutOfRange;
+    const uint32_t chunk = (uint32_t)((lane & 15) ^ (m & 15));
+    uint32_t off = kOOBRow;
     if (m < u.M) {
       if constexpr (PROJ == 0) {
         const int t = u.routed ? g.sorted_token[u.tok0 + m] : u.tok0 + m;
-        off = (uint32_t)t * (uint32_t)K * 2u;
+        off = (uint32_t)t * (uint32_t)g.ldx * 2u;
       } else {
         off = (uint32_t)(u.p0 + m) * (uint32_t)g.ldh * 2u;
       }
     }
-    rowoff[i] = off;
+    abase[i] = off + chunk * 16u;
   }
 }
 
-__device__ __forceinline__ void issue_act(const rsrc_t& ar, const uint32_t (&rowoff)[kActLoads], int kb,
-                                          int K, int wv, int lane, uint16_t* stage) {
-  const int row_lo = lane >> 4;
+__device__ __forceinline__ void issue_act(const rsrc_t& ar, const uint32_t (&abase)[kActLoads], int kb,
+                                          int wv, uint16_t* stage) {
 #pragma unroll
-  for (int i = 0; i < kActLoads; ++i) {
-    const int row = (wv * kActLoads + i) * 4 + row_lo;
-    const int chunk = (lane & 15) ^ (row & 15);
-    const int k = kb * kBK + chunk * 8;
-    const uint32_t off =
-        (rowoff[i] != kOutOfRange && k < K) ? rowoff[i] + (uint32_t)k * 2u : kOutOfRange;
+  for (int i = 0; i < kActLoads; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        ar, (__attribute__((address_space(3))) void*)(stage + (wv * kActLoads + i) * 64 * 8), 16, off,
-        0, 0, 0);
-  }
+        ar, (__attribute__((address_space(3))) void*)(stage + (wv * kActLoads + i) * 64 * 8), 16,
+        abase[i] + (uint32_t)kb * (kBK * 2), 0, 0, 0);
 }
 
 template <int N>
@@ -222,31 +233,30 @@ __global__ void __launch_bounds__(256, 1) moe_gemm_kernel(GemmArgs g) {
   const int nkb = (K + kBK - 1) / kBK;
   const int nct = (u.M + 15) >> 4;
 
-  // weights of one K block: lane (lrow, lq) loads group 4 kb + lq of its row;
-  // groups past the row read as zero codes and zero scales
+  // weights of one K block: lane (lrow, lq) loads group 4 kb + lq of its row.
+  // Groups past the row (a partial last K block) meet zero activations; rows
+  // past the matrix read zeros through the range check.
   uint32_t qoff[RT], soff[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    qoff[rt] = (uint32_t)(rbase[rt] + lrow) * rowBytes;
-    soff[rt] = (uint32_t)(rbase[rt] + lrow) * scaleRowBytes;
+    qoff[rt] = (uint32_t)(rbase[rt] + lrow) * rowBytes + (uint32_t)lq * 16u;
+    soff[rt] = (uint32_t)(rbase[rt] + lrow) * scaleRowBytes + (uint32_t)lq * 2u;
   }
   uint32_t wcode[kNS][RT][4], wsc[kNS][RT];
-  const rsrc_t ar = PROJ == 0 ? make_rsrc(g.x16, (uint32_t)g.T * (uint32_t)g.H * 2u)
+  const rsrc_t ar = PROJ == 0 ? make_rsrc(g.x16, (uint32_t)g.T * (uint32_t)g.ldx * 2u)
                               : make_rsrc(g.hin, (uint32_t)(g.P + g.T) * (uint32_t)g.ldh * 2u);
   uint32_t arow[kActLoads];
-  act_rows<PROJ>(g, u, K, wv, lane, arow);
+  act_rows<PROJ>(g, u, wv, lane, arow);
 
   // request K block kb into stage S (LDS) and ring slot S (registers)
   auto issue = [&](auto S, int kb) {
     constexpr int st = decltype(S)::value;
-    issue_act(ar, arow, kb, K, wv, lane, xs[st]);
-    const int grp = kb * 4 + lq;
-    const bool ok = grp < nG;
+    issue_act(ar, arow, kb, wv, xs[st]);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       const int j = PROJ == 0 ? rt >> 1 : 0;
-      bload16(wcode[st][rt], qb[j], ok ? qoff[rt] + (uint32_t)grp * 16u : kOutOfRange, 0);
-      wsc[st][rt] = bload_u16(sb[j], ok ? soff[rt] + (uint32_t)grp * 2u : kOutOfRange, 0);
+      bload16(wcode[st][rt], qb[j], qoff[rt] + (uint32_t)kb * 64u, 0);
+      wsc[st][rt] = bload_u16(sb[j], soff[rt] + (uint32_t)kb * 8u, 0);
     }
   };
   // A operands (dequantised weights) of K step ks from ring slot S
@@ -357,10 +367,14 @@ __global__ void __launch_bounds__(256, 1) moe_gemm_kernel(GemmArgs g) {
             packed[i / 2] = (uint32_t)__builtin_bit_cast(uint16_t, a0) |
                             ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
           }
+          // columns from inter up to the padded stride hold zeros (the
+          // down projection's last K block reads them)
           const int col = rbase[rt] + 4 * lq;
           if (col < inter)
             *reinterpret_cast<uint2*>(g.h_out + (size_t)orow * g.ldh + col) =
                 make_uint2(packed[0], packed[1]);
+          else if (col < pad_k(inter))
+            *reinterpret_cast<uint2*>(g.h_out + (size_t)orow * g.ldh + col) = make_uint2(0u, 0u);
         }
       } else {
 #pragma unroll
@@ -386,19 +400,28 @@ __global__ void __launch_bounds__(256, 1) moe_gemm_kernel(GemmArgs g) {
     run(ic<2>{});
 }
 
-// bf16 -> fp16 copy of the activations (exact for |x| in the fp16 normal range)
+// bf16 -> fp16 copy of the activations (exact for |x| in the fp16 normal
+// range) into rows of ldx elements, zero past H.  One thread per 8 elements.
 __global__ void __launch_bounds__(256) x_to_f16_kernel(const uint16_t* __restrict__ x,
-                                                       uint16_t* __restrict__ y, size_t n8) {
+                                                       uint16_t* __restrict__ y, int T, int H,
+                                                       int ldx) {
+  const int c8 = ldx / 8;
+  const size_t n8 = (size_t)T * c8;
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (size_t)gridDim.x * 256) {
-    const uint4 v = reinterpret_cast<const uint4*>(x)[i];
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t o[4];
+    const int t = (int)(i / c8), c = (int)(i % c8);
+    uint4 o = make_uint4(0, 0, 0, 0);
+    if (c * 8 < H) {
+      const uint4 v = *reinterpret_cast<const uint4*>(x + (size_t)t * H + c * 8);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      uint32_t r[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const _Float16 lo = (_Float16)bf16_lo(w[j]), hi = (_Float16)bf16_hi(w[j]);
-      o[j] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+      for (int j = 0; j < 4; ++j) {
+        const _Float16 lo = (_Float16)bf16_lo(w[j]), hi = (_Float16)bf16_hi(w[j]);
+        r[j] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+      }
+      o = make_uint4(r[0], r[1], r[2], r[3]);
     }
-    reinterpret_cast<uint4*>(y)[i] = make_uint4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<uint4*>(y + (size_t)t * ldx + c * 8) = o;
   }
 }
 
@@ -465,14 +488,14 @@ int gemm_max_units(int T, int K, int E, bool has_shared) {
   return (int)(routed + shared);
 }
 int gemm_unit_tokens() { return kBM; }
-bool gemm_fits(int64_t T, int64_t rows, int64_t H, int64_t ldh) {
-  return T * H * 2 <= (int64_t)kOutOfRange && rows * ldh * 2 <= (int64_t)kOutOfRange;
+bool gemm_fits(int64_t T, int64_t rows, int64_t ldx, int64_t ldh) {
+  return T * ldx * 2 <= (int64_t)kOOBRow && rows * ldh * 2 <= (int64_t)kOOBRow;
 }
 
-hipError_t launch_x_to_f16(const uint16_t* x, uint16_t* y, size_t n, hipStream_t s) {
-  const size_t n8 = n / 8;
+hipError_t launch_x_to_f16(const uint16_t* x, uint16_t* y, int T, int H, int ldx, hipStream_t s) {
+  const size_t n8 = (size_t)T * (ldx / 8);
   const int blocks = (int)std::min<size_t>((n8 + 255) / 256, 4096);
-  hipLaunchKernelGGL(x_to_f16_kernel, dim3(blocks), dim3(256), 0, s, x, y, n8);
+  hipLaunchKernelGGL(x_to_f16_kernel, dim3(blocks), dim3(256), 0, s, x, y, T, H, ldx);
   return hipGetLastError();
 }
 

@@ -96,12 +96,13 @@ hipError_t run_gemm_ffn(const moe_config& c, int T, const uint16_t* x, const Wor
                               has_routed ? n_active : nullptr, w.tiles, w.n_tiles, T, P,
                               has_shared, stream)) != hipSuccess)
     return e;
-  if ((e = launch_x_to_f16(x, w.x16, (size_t)T * c.hidden, stream)) != hipSuccess) return e;
+  if ((e = launch_x_to_f16(x, w.x16, T, c.hidden, pad_k(c.hidden), stream)) != hipSuccess) return e;
   if (tr && (e = tr->mark("gemm_prep")) != hipSuccess) return e;
   GemmArgs g{};
   g.tiles = w.tiles;
   g.n_tiles = w.n_tiles;
   g.x16 = w.x16;
+  g.ldx = pad_k(c.hidden);
   g.sorted_token = sorted_token;
   g.hin = h;
   g.ldh = ldh;
@@ -126,7 +127,7 @@ Workspace carve_workspace(const moe_config& c, int T, void* base) {
   if (T == 0) return w;
   const size_t E = c.n_routed_experts, K = c.top_k, H = c.hidden;
   const size_t P = (size_t)T * K;
-  const size_t imax = (size_t)std::max(c.moe_inter, c.n_shared_experts ? c.shared_inter : 0);
+  const size_t imax = (size_t)pad_k(std::max(c.moe_inter, c.n_shared_experts ? c.shared_inter : 0));
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -144,7 +145,7 @@ Workspace carve_workspace(const moe_config& c, int T, void* base) {
   const size_t o_sw = take(P * sizeof(float));
   const size_t o_h = take((P + T) * imax * sizeof(uint16_t));
   const size_t o_O = take((P + T) * H * sizeof(float));
-  const size_t o_x16 = take((size_t)T * H * sizeof(uint16_t));
+  const size_t o_x16 = take((size_t)T * pad_k((int)H) * sizeof(uint16_t));
   const size_t o_tiles =
       take((size_t)gemm_max_units(T, (int)K, (int)E, c.n_shared_experts == 1) * 4 * sizeof(int32_t));
   const size_t o_ntiles = take(4 * sizeof(int32_t));
@@ -248,7 +249,7 @@ moe_status moe_expert_ffn_q4(const moe_config* cfg, int32_t T, const uint16_t* x
   if ((s = check_ws(*cfg, T, ws, ws_bytes)) != MOE_OK) return s;
   if (T == 0) return MOE_OK;
   const Workspace ws_ = carve_workspace(*cfg, T, ws);
-  const int ldh = std::max(cfg->moe_inter, cfg->n_shared_experts ? cfg->shared_inter : 0);
+  const int ldh = pad_k(std::max(cfg->moe_inter, cfg->n_shared_experts ? cfg->shared_inter : 0));
   FfnArgs a{};
   a.x = x;
   a.T = T;
@@ -258,7 +259,7 @@ moe_status moe_expert_ffn_q4(const moe_config* cfg, int32_t T, const uint16_t* x
   a.ldh = ldh;
   if (T > kDecodeMaxTokens) {
     const int64_t rows = routed ? (int64_t)T * cfg->top_k : T;
-    if (!gemm_fits(T, rows, cfg->hidden, ldh)) return MOE_ERR_UNSUPPORTED;
+    if (!gemm_fits(T, rows, pad_k(cfg->hidden), ldh)) return MOE_ERR_UNSUPPORTED;
     const ExpertSet es = expert_set(*w, routed ? cfg->moe_inter : cfg->shared_inter);
     const int P = routed ? T * cfg->top_k : 0;
     return hip_status(run_gemm_ffn(*cfg, T, x, ws_, routed, es, expert_offsets, active_experts,
@@ -331,10 +332,10 @@ moe_status layer_impl(const moe_config* cfg, int32_t T, const uint16_t* x, const
   }
 
   const bool has_shared = cfg->n_shared_experts == 1;
-  const int ldh = std::max(cfg->moe_inter, has_shared ? cfg->shared_inter : 0);
+  const int ldh = pad_k(std::max(cfg->moe_inter, has_shared ? cfg->shared_inter : 0));
   const size_t P = (size_t)T * cfg->top_k;
   const bool small = T <= kDecodeMaxTokens && decode_supported(cfg->hidden);
-  if (!small && !gemm_fits(T, (int64_t)P + (has_shared ? T : 0), cfg->hidden, ldh))
+  if (!small && !gemm_fits(T, (int64_t)P + (has_shared ? T : 0), pad_k(cfg->hidden), ldh))
     return MOE_ERR_UNSUPPORTED;
 
   const Workspace w = carve_workspace(*cfg, T, ws);

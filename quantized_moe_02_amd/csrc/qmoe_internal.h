@@ -158,9 +158,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, Tracer* tr = nullpt
 struct GemmArgs {
   const int4* tiles;          // work units (see build_units)
   const int32_t* n_tiles;
-  const uint16_t* x16;        // fp16 activations [T][H]
+  const uint16_t* x16;        // fp16 activations [T][ldx], zero past H
+  int ldx;
   const int32_t* sorted_token;
-  const uint16_t* hin;        // fp16 h [P+T][ldh] (down input)
+  const uint16_t* hin;        // fp16 h [P+T][ldh] (down input), zero past inter
   int ldh;
   ExpertSet routed;
   bool has_shared;
@@ -170,14 +171,17 @@ struct GemmArgs {
   int T, H, P, wfmt;
 };
 int gemm_max_units(int T, int K, int E, bool has_shared);
-// Whether the GEMM path's activation buffers (T x H fp16 activations, rows x
-// ldh fp16 intermediates) fit its 32-bit buffer descriptors.
-bool gemm_fits(int64_t T, int64_t rows, int64_t H, int64_t ldh);
+// Row strides (elements) of the fp16 activation and intermediate buffers: a
+// multiple of the GEMM's K block, the padding held at zero.
+__host__ __device__ inline int pad_k(int n) { return (n + 127) & ~127; }
+// Whether the GEMM path's activation buffers (T x ldx fp16 activations, rows x
+// ldh fp16 intermediates) fit its buffer descriptors (2 GiB each).
+bool gemm_fits(int64_t T, int64_t rows, int64_t ldx, int64_t ldh);
 int gemm_unit_tokens();
 hipError_t launch_build_units(const int32_t* offsets, const int32_t* active,
                               const int32_t* n_active, int4* tiles, int32_t* n_tiles, int T, int P,
                               bool has_shared, hipStream_t s);
-hipError_t launch_x_to_f16(const uint16_t* x, uint16_t* y, size_t n, hipStream_t s);
+hipError_t launch_x_to_f16(const uint16_t* x, uint16_t* y, int T, int H, int ldx, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs& g, int max_units, hipStream_t s, Tracer* tr = nullptr);
 
 }  // namespace qmoe
