@@ -134,7 +134,8 @@ Workspace carve_workspace(const moe_config& c, int T, void* base) {
     off = round_up(off + bytes, kAlign);
     return o;
   };
-  const size_t o_logits = take((size_t)T * E * sizeof(double));
+  const size_t o_logits =
+      take((size_t)route_splits(T, c.hidden, (int)E) * T * E * sizeof(double));
   const size_t o_ids = take(P * sizeof(int32_t));
   const size_t o_tw = take(P * sizeof(float));
   const size_t o_off = take((E + 1) * sizeof(int32_t));

@@ -75,6 +75,9 @@ struct RouteArgs {
   float rsf;
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t s, Tracer* tr = nullptr);
+// Number of hidden-dimension slices route_logits uses (its logits buffer
+// holds that many T x E partial sums).
+int route_splits(int T, int H, int E);
 
 struct PermuteArgs {
   const int32_t* ids;

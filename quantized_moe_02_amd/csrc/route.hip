@@ -3,58 +3,115 @@
 // (page "Show HN: Menjalankan GLM 5.2 di komputer lambat", section "Fitur utama").
 //
 // Two kernels:
-//   route_logits  l[t][e] = sum_h x[t][h] * Wr[e][h] in float64.  A bf16 times
-//                 an fp32 is exact in float64, so the only rounding is the
-//                 float64 sum.  One wave per (expert, block of TT tokens); the
-//                 lanes stride the hidden dimension with 16-byte loads of Wr.
+//   route_logits  l[t][e] = sum_h x[t][h] * Wr[e][h] in float64 on the matrix
+//                 cores (v_mfma_f64_16x16x4_f64).  A bf16 times an fp32 is
+//                 exact in float64, so the only rounding is the float64 sum.
+//                 One wave per 32 tokens x 64 experts x slice of the hidden
+//                 dimension; with several slices (few tokens) each writes its
+//                 partial sums and route_select adds them in slice order.
 //   route_select  one wave per token (select_token.h).
+#include <algorithm>
+
 #include "select_token.h"
 
 namespace qmoe {
 namespace {
 
-constexpr int kLogitTokens = 8;  // tokens per wave in route_logits
+typedef double double4v __attribute__((ext_vector_type(4)));
 
+constexpr int kLogitTok = 32;   // tokens per wave (two 16-row tiles)
+constexpr int kLogitExp = 64;   // experts per wave (four 16-column tiles)
+
+// v_mfma_f64_16x16x4_f64: A lane l holds row l%16, k = l/16; B lane l holds
+// column l%16, k = l/16; D lane l holds rows l/16 + 4i (i = 0..3) of column
+// l%16.  Rows are tokens and columns experts, so that the 16 lanes of a row
+// group store 16 consecutive logits.  Within a 32-input block, lane group q
+// supplies inputs 8q..8q+7 over the block's 8 MFMA steps (K order is free).
 __global__ void __launch_bounds__(256) route_logits_kernel(const uint16_t* __restrict__ x,
                                                            const float* __restrict__ Wr,
                                                            double* __restrict__ logits, int T,
-                                                           int H, int E) {
+                                                           int H, int E, int kb_per_split) {
   const int lane = threadIdx.x & 63;
-  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int t0 = blockIdx.y * kLogitTokens;
-  if (e >= E) return;
-  const int nt = min(kLogitTokens, T - t0);
-  double acc[kLogitTokens];
+  const int tg = blockIdx.x * 4 + (threadIdx.x >> 6);
+  logits += (size_t)blockIdx.z * T * E;
+  const int kb0 = blockIdx.z * kb_per_split;
+  const int kb1 = min(H / 32, kb0 + kb_per_split);
+  if (tg * kLogitTok >= T) return;
+  const int t0 = tg * kLogitTok, e0 = blockIdx.y * kLogitExp;
+  const int r = lane & 15, q = lane >> 4;
+  // rows and columns past the end are clamped (their results are not stored)
+  const uint16_t* xp[2];
+  const float* wp[4];
 #pragma unroll
-  for (int i = 0; i < kLogitTokens; ++i) acc[i] = 0.0;
-  const float* wrow = Wr + (size_t)e * H;
-  for (int h = lane * 4; h < H; h += 256) {
-    const float4 w4 = *reinterpret_cast<const float4*>(wrow + h);
+  for (int rt = 0; rt < 2; ++rt) xp[rt] = x + (size_t)min(t0 + 16 * rt + r, T - 1) * H + q * 8;
 #pragma unroll
-    for (int i = 0; i < kLogitTokens; ++i) {
-      if (i < nt) {
-        const uint2 xv = *reinterpret_cast<const uint2*>(x + (size_t)(t0 + i) * H + h);
-        double a = acc[i];
-        a = fma((double)bf16_lo(xv.x), (double)w4.x, a);
-        a = fma((double)bf16_hi(xv.x), (double)w4.y, a);
-        a = fma((double)bf16_lo(xv.y), (double)w4.z, a);
-        a = fma((double)bf16_hi(xv.y), (double)w4.w, a);
-        acc[i] = a;
+  for (int ct = 0; ct < 4; ++ct) wp[ct] = Wr + (size_t)min(e0 + 16 * ct + r, E - 1) * H + q * 8;
+
+  double4v acc[2][4];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) acc[rt][ct] = double4v{0.0, 0.0, 0.0, 0.0};
+
+  uint4 xa[2], xn[2];
+  float4 wa[4][2], wn[4][2];
+  auto load = [&](int kb, uint4 (&xv)[2], float4 (&wv)[4][2]) {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) xv[rt] = *reinterpret_cast<const uint4*>(xp[rt] + kb * 32);
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      wv[ct][0] = *reinterpret_cast<const float4*>(wp[ct] + kb * 32);
+      wv[ct][1] = *reinterpret_cast<const float4*>(wp[ct] + kb * 32 + 4);
+    }
+  };
+  load(kb0, xa, wa);
+  for (int kb = kb0; kb < kb1; ++kb) {
+    if (kb + 1 < kb1) load(kb + 1, xn, wn);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      double xd[2], wd[4];
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const uint32_t w = (&xa[rt].x)[j >> 1];
+        xd[rt] = (double)((j & 1) ? bf16_hi(w) : bf16_lo(w));
+      }
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) wd[ct] = (double)(&wa[ct][j >> 2].x)[j & 3];
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+          acc[rt][ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(xd[rt], wd[ct], acc[rt][ct], 0, 0, 0);
+    }
+    if (kb + 1 < kb1) {
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) xa[rt] = xn[rt];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        wa[ct][0] = wn[ct][0];
+        wa[ct][1] = wn[ct][1];
       }
     }
   }
 #pragma unroll
-  for (int i = 0; i < kLogitTokens; ++i) {
-    const double v = wave_sum(acc[i]);
-    if (lane == 0 && i < nt) logits[(size_t)(t0 + i) * E + e] = v;
-  }
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const int e = e0 + 16 * ct + r;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + 16 * rt + q + 4 * i;
+        if (t < T && e < E) logits[(size_t)t * E + e] = acc[rt][ct][i];
+      }
+    }
 }
 
 __global__ void __launch_bounds__(256) route_select_kernel(const double* __restrict__ logits,
                                                            const float* __restrict__ bias,
                                                            int32_t* __restrict__ ids,
                                                            float* __restrict__ tw, int T, int E,
-                                                           int G, int TG, int K, float rsf) {
+                                                           int G, int TG, int K, float rsf,
+                                                           int nsplit) {
   __shared__ SelectScratch sc[4];
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
@@ -62,7 +119,8 @@ __global__ void __launch_bounds__(256) route_select_kernel(const double* __restr
   if (t >= T) return;
   int id, rank;
   float w;
-  select_token(logits + (size_t)t * E, bias, E, G, TG, K, rsf, sc[wv], id, w, rank);
+  select_token(logits + (size_t)t * E, bias, E, G, TG, K, rsf, sc[wv], id, w, rank, nsplit,
+               (size_t)T * E);
   if (lane < K) {
     ids[(size_t)t * K + rank] = id;
     tw[(size_t)t * K + rank] = w;
@@ -71,16 +129,29 @@ __global__ void __launch_bounds__(256) route_select_kernel(const double* __restr
 
 }  // namespace
 
+int route_splits(int T, int H, int E) {
+  // enough waves to fill the chip, at least 8 K blocks of 32 inputs per wave
+  const int waves = ((T + kLogitTok - 1) / kLogitTok) * ((E + kLogitExp - 1) / kLogitExp);
+  const int by_waves = (2048 + waves - 1) / waves;
+  const int by_k = H / 32 / 8;
+  return std::max(1, std::min(by_waves, by_k));
+}
+
 hipError_t launch_route(const RouteArgs& a, hipStream_t s, Tracer* tr) {
   if (a.T == 0) return hipSuccess;
   hipError_t e;
-  dim3 g1((a.E + 3) / 4, (a.T + kLogitTokens - 1) / kLogitTokens);
+  const int groups = (a.T + kLogitTok - 1) / kLogitTok;
+  const int S = route_splits(a.T, a.H, a.E);
+  const int nkb = a.H / 32;
+  const int per = (nkb + S - 1) / S;
+  const int S_used = (nkb + per - 1) / per;
+  dim3 g1((groups + 3) / 4, (a.E + kLogitExp - 1) / kLogitExp, S_used);
   hipLaunchKernelGGL(route_logits_kernel, g1, dim3(256), 0, s, a.x, a.router_w, a.logits, a.T,
-                     a.H, a.E);
+                     a.H, a.E, per);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (tr && (e = tr->mark("route_logits")) != hipSuccess) return e;
   hipLaunchKernelGGL(route_select_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, a.logits, a.bias,
-                     a.ids, a.tw, a.T, a.E, a.G, a.TG, a.K, a.rsf);
+                     a.ids, a.tw, a.T, a.E, a.G, a.TG, a.K, a.rsf, S_used);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (tr && (e = tr->mark("route_select")) != hipSuccess) return e;
   return hipSuccess;

@@ -87,11 +87,12 @@ __device__ __forceinline__ double wave_max(double v) {
 
 // Lanes < K return their chosen expert in `id`, its weight in `w` and its
 // position in ascending id order in `rank`.  `logits` points at the token's E
-// float64 logits.  Must be called by all 64 lanes of the wave.
+// float64 logits, given as `nsplit` partial sums `split_stride` apart (added
+// in order).  Must be called by all 64 lanes of the wave.
 __device__ __forceinline__ void select_token(const double* __restrict__ logits,
                                              const float* __restrict__ bias, int E, int G, int TG,
                                              int K, float rsf, SelectScratch& sc, int& id, float& w,
-                                             int& rank) {
+                                             int& rank, int nsplit = 1, size_t split_stride = 0) {
   const int lane = threadIdx.x & 63;
   const int per = E / G;
   const int e0 = 4 * lane;
@@ -100,7 +101,8 @@ __device__ __forceinline__ void select_token(const double* __restrict__ logits,
   for (int j = 0; j < 4; ++j) {
     const int e = e0 + j;
     const bool in = e < E;
-    const double l = logits[in ? e : 0];
+    double l = logits[in ? e : 0];
+    for (int sp = 1; sp < nsplit; ++sp) l += logits[sp * split_stride + (in ? e : 0)];
     s[j] = 1.0 / (1.0 + exp(-l));
     sb[j] = in ? s[j] + (bias ? (double)bias[e] : 0.0) : -INFINITY;
   }
