@@ -109,6 +109,10 @@ KERNEL_SOURCES = {
     "dec_": ["decode.hip", "select_token.h", "qmoe_device.h", "qmoe_internal.h"],
     "gemm_": ["gemm.hip", "qmoe_device.h", "qmoe_internal.h"],
     "route_": ["route.hip", "select_token.h", "qmoe_device.h", "qmoe_internal.h"],
+    "permute": ["permute.hip", "qmoe_device.h", "qmoe_internal.h"],
+    "combine": ["gemv.hip", "qmoe_device.h", "qmoe_internal.h"],
+    "gateup_gemv": ["gemv.hip", "qmoe_device.h", "qmoe_internal.h"],
+    "down_gemv": ["gemv.hip", "qmoe_device.h", "qmoe_internal.h"],
 }
 
 
@@ -135,7 +139,8 @@ def traffic_for(kernel, workload):
         return None
     with open(path) as f:
         rec = json.load(f).get(f"{kernel}@{workload}")
-    if not rec or rec.get("sha256") != kernel_source_hash(kernel):
+    h = kernel_source_hash(kernel)
+    if not rec or h is None or rec.get("sha256") != h:
         return None
     return rec["fetch_kib"] * 1024 * rec["fetch_scale"] + rec["write_kib"] * 1024 * rec["write_scale"]
 
