@@ -292,7 +292,7 @@ __global__ void __launch_bounds__(256) dec_router_shared_kernel(DecodeArgs a, in
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) dec_select_permute_kernel(DecodeArgs a) {
   __shared__ SelectScratch sc[4];
-  __shared__ int pid[64];
+  __shared__ __attribute__((aligned(16))) int pid[64];
   __shared__ float pw[64];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -313,42 +313,46 @@ __global__ void __launch_bounds__(256) dec_select_permute_kernel(DecodeArgs a) {
   if (wv != 0) return;
   // Stable sort of the P <= 64 picks by expert, one pick per lane: a pick's
   // slot = #picks with a smaller id, or the same id and a smaller pick index.
+  // Every lane reads all picks from LDS (broadcast reads, four at a time;
+  // entries past P are masked).
   const bool have = lane < P;
   const int e = have ? pid[lane] : 0x7fffffff;
-  const float pwv = have ? pw[lane] : 0.0f;
-  int pos = 0;
-  for (int q = 0; q < P; ++q) {
-    const int o = __builtin_amdgcn_readlane(e, q);
-    pos += (o < e || (o == e && q < lane)) ? 1 : 0;
+  int pos = 0, dup = 0;
+  for (int q = 0; q < P; q += 4) {
+    const int4 o4 = *reinterpret_cast<const int4*>(&pid[q]);
+    const int o[4] = {o4.x, o4.y, o4.z, o4.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool in = q + i < P;
+      pos += (in && (o[i] < e || (o[i] == e && q + i < lane))) ? 1 : 0;
+      dup |= (in && o[i] == e && q + i < lane) ? 1 : 0;
+    }
   }
   if (have) {
     a.sorted_token[pos] = lane / K;
     a.inv_perm[lane] = pos;
-    a.sorted_w[pos] = pwv;
+    a.sorted_w[pos] = pw[lane];
   }
-  // distinct experts in ascending order: a pick is the first of its expert
-  // if no pick has the same id and a smaller slot
-  int dup = 0;
-  for (int q = 0; q < P; ++q) {
-    const int o = __builtin_amdgcn_readlane(e, q);
-    dup |= (o == e && q < lane) ? 1 : 0;
-  }
+  // distinct experts in ascending order: a pick is the first of its expert if
+  // no earlier pick has the same id; its rank among the firsts orders them.
+  // offsets[x] = #picks with id < x, for x = 0..E.
   const bool first = have && !dup;
-  int arank = 0;  // #distinct experts with a smaller id
   const uint64_t firsts = __ballot(first);
-  for (int q = 0; q < P; ++q) {
-    const int o = __builtin_amdgcn_readlane(e, q);
-    arank += (((firsts >> q) & 1ull) && o < e) ? 1 : 0;
+  int arank = 0;
+  int cnt[5] = {0, 0, 0, 0, 0};
+  for (int q = 0; q < P; q += 4) {
+    const int4 o4 = *reinterpret_cast<const int4*>(&pid[q]);
+    const int o[4] = {o4.x, o4.y, o4.z, o4.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool in = q + i < P;
+      arank += (in && ((firsts >> (q + i)) & 1ull) && o[i] < e) ? 1 : 0;
+#pragma unroll
+      for (int j = 0; j < 5; ++j) cnt[j] += (in && o[i] < lane + 64 * j) ? 1 : 0;
+    }
   }
   if (first) a.active[arank] = e;
   if (lane == 0) a.n_active[0] = __popcll(firsts);
-  // offsets[x] = #picks with id < x, for x = 0..E
-  int cnt[5] = {0, 0, 0, 0, 0};
-  for (int q = 0; q < P; ++q) {
-    const int o = __builtin_amdgcn_readlane(e, q);
-#pragma unroll
-    for (int j = 0; j < 5; ++j) cnt[j] += (o < lane + 64 * j) ? 1 : 0;
-  }
 #pragma unroll
   for (int j = 0; j < 5; ++j)
     if (lane + 64 * j <= a.E) a.offsets[lane + 64 * j] = cnt[j];

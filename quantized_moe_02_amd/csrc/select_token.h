@@ -25,10 +25,13 @@ namespace qmoe {
 constexpr int kSelMaxE = 256;
 constexpr int kSelMaxG = 64;
 
-// Per-wave LDS scratch of select_token (used only for irregular group shapes).
-struct SelectScratch {
-  double sb[kSelMaxE];
-  double gs[kSelMaxG];
+constexpr int kSelMaxK = 16;
+
+// Per-wave LDS scratch of select_token.
+struct alignas(16) SelectScratch {
+  double sb[kSelMaxE];   // irregular group shapes only
+  double gs[kSelMaxG];   // group scores
+  int ids[kSelMaxK];     // chosen experts, for their ascending ranks
 };
 
 // Orders LDS traffic between lanes of one wave.
@@ -45,10 +48,15 @@ __device__ __forceinline__ double readlane_d(double v, int l) {
   return __longlong_as_double(((uint64_t)hi << 32) | lo);
 }
 
+// max / min by compare and select: the scores are never NaN, so the IEEE
+// maxNum quieting that fmax compiles to is not needed
+__device__ __forceinline__ double dmax(double a, double b) { return a > b ? a : b; }
+__device__ __forceinline__ double dmin(double a, double b) { return a < b ? a : b; }
+
 // top-2 pair (a1 >= a2) merged with (b1 >= b2)
 __device__ __forceinline__ void merge_top2(double& a1, double& a2, double b1, double b2) {
-  const double hi = fmax(a1, b1);
-  const double lo = fmax(fmin(a1, b1), fmax(a2, b2));
+  const double hi = dmax(a1, b1);
+  const double lo = dmax(dmin(a1, b1), dmax(a2, b2));
   a1 = hi;
   a2 = lo;
 }
@@ -68,13 +76,13 @@ __device__ __forceinline__ void top2_swap(double& m1, double& m2) {
 
 template <int CTRL>
 __device__ __forceinline__ double max_dpp(double v) {
-  return fmax(v, dppd<CTRL>(v));
+  return dmax(v, dppd<CTRL>(v));
 }
 template <int M>
 __device__ __forceinline__ double max_swap(double v) {
   double a, b;
   swap_pair<M>(v, a, b);
-  return fmax(a, b);
+  return dmax(a, b);
 }
 __device__ __forceinline__ double wave_max(double v) {
   v = max_dpp<kDppXor1>(v);
@@ -83,6 +91,31 @@ __device__ __forceinline__ double wave_max(double v) {
   v = max_dpp<kDppMirror>(v);
   v = max_swap<16>(v);
   return max_swap<32>(v);
+}
+
+// Order-preserving map of a (non-NaN) float64 to an unsigned 64-bit key.
+__device__ __forceinline__ uint64_t okey(double d) {
+  const uint64_t u = (uint64_t)__double_as_longlong(d);
+  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t umax_dpp(uint32_t v) {
+  const uint32_t o = dpp<CTRL>(v);
+  return v > o ? v : o;
+}
+template <int M>
+__device__ __forceinline__ uint32_t umax_swap(uint32_t v) {
+  int a, b;
+  swap_pair<M>((int)v, a, b);
+  return (uint32_t)a > (uint32_t)b ? (uint32_t)a : (uint32_t)b;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = umax_dpp<kDppXor1>(v);
+  v = umax_dpp<kDppXor2>(v);
+  v = umax_dpp<kDppHalfMirror>(v);
+  v = umax_dpp<kDppMirror>(v);
+  v = umax_swap<16>(v);
+  return umax_swap<32>(v);
 }
 
 // Lanes < K return their chosen expert in `id`, its weight in `w` and its
@@ -112,8 +145,8 @@ __device__ __forceinline__ void select_token(const double* __restrict__ logits,
   bool keep_j[4];
   if (lane_groups) {
     // local top-2 of four, then merge across the group's lanes
-    double m1 = fmax(sb[0], sb[1]), m2 = fmin(sb[0], sb[1]);
-    merge_top2(m1, m2, fmax(sb[2], sb[3]), fmin(sb[2], sb[3]));
+    double m1 = dmax(sb[0], sb[1]), m2 = dmin(sb[0], sb[1]);
+    merge_top2(m1, m2, dmax(sb[2], sb[3]), dmin(sb[2], sb[3]));
     if (L >= 2) top2_dpp<kDppXor1>(m1, m2);
     if (L >= 4) top2_dpp<kDppXor2>(m1, m2);
     if (L >= 8) top2_dpp<kDppHalfMirror>(m1, m2);
@@ -122,10 +155,15 @@ __device__ __forceinline__ void select_token(const double* __restrict__ logits,
     if (L >= 64) top2_swap<32>(m1, m2);
     const double gmine = m1 + m2;
     const int gidx = lane / L;
+    // every lane reads the G group scores from LDS and ranks its own group
+    wave_lds_sync();  // a previous call's reads of `sc` come first
+    if (lane % L == 0) sc.gs[gidx] = gmine;
+    wave_lds_sync();
     int r = 0;
-    for (int g = 0; g < G; ++g) {
-      const double o = readlane_d(gmine, g * L);
-      r += (o > gmine || (o == gmine && g < gidx)) ? 1 : 0;
+    for (int g = 0; g < G; g += 2) {
+      const double2 o2 = *reinterpret_cast<const double2*>(&sc.gs[g]);
+      r += (o2.x > gmine || (o2.x == gmine && g < gidx)) ? 1 : 0;
+      r += (g + 1 < G && (o2.y > gmine || (o2.y == gmine && g + 1 < gidx))) ? 1 : 0;
     }
     const bool keep = r < TG;
 #pragma unroll
@@ -166,21 +204,29 @@ __device__ __forceinline__ void select_token(const double* __restrict__ logits,
     for (int j = 0; j < 4; ++j) keep_j[j] = r[j] < TG;
   }
   // ---- candidates sorted within the lane: value desc, id asc -------------
-  double cv[4];
+  // Keys are the order-preserving integer images of s'; experts outside the
+  // kept groups get key 0, below every score.
+  uint64_t ck[4];
+  double cs[4];
   int cj[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    cv[j] = keep_j[j] ? sb[j] : -INFINITY;
-    cj[j] = j;
+    ck[j] = (keep_j[j] && e0 + j < E) ? okey(sb[j]) : 0ull;
+    cs[j] = s[j];
+    cj[j] = e0 + j;
   }
   auto cswap = [&](int a, int b) {
-    // keep (cv[a], cj[a]) ahead of (cv[b], cj[b])
-    const bool sw = cv[b] > cv[a] || (cv[b] == cv[a] && cj[b] < cj[a]);
-    const double tv = sw ? cv[b] : cv[a];
+    // keep (ck[a], cj[a]) ahead of (ck[b], cj[b]): key descending, id
+    // ascending (a sorting network is not stable, so the id decides ties)
+    const bool sw = ck[b] > ck[a] || (ck[b] == ck[a] && cj[b] < cj[a]);
+    const uint64_t tk = sw ? ck[b] : ck[a];
+    const double ts = sw ? cs[b] : cs[a];
     const int tj = sw ? cj[b] : cj[a];
-    cv[b] = sw ? cv[a] : cv[b];
+    ck[b] = sw ? ck[a] : ck[b];
+    cs[b] = sw ? cs[a] : cs[b];
     cj[b] = sw ? cj[a] : cj[b];
-    cv[a] = tv;
+    ck[a] = tk;
+    cs[a] = ts;
     cj[a] = tj;
   };
   cswap(0, 1);
@@ -189,30 +235,46 @@ __device__ __forceinline__ void select_token(const double* __restrict__ logits,
   cswap(1, 3);
   cswap(1, 2);
   // ---- top_k rounds -------------------------------------------------------
-  int head = 0;
+  // Each round takes the wave maximum of the lanes' head keys, first on their
+  // high 32 bits; lanes tied there are settled on the low 32 bits (rare).  The
+  // lowest lane holding the maximum wins, which is also the lowest expert id.
+  // The winning lane shifts its list.  No lane branches: every step is a
+  // select.
   int my_id = 0;
   double my_s = 0.0;
   for (int rr = 0; rr < K; ++rr) {
-    const double hv = head == 0 ? cv[0] : head == 1 ? cv[1] : head == 2 ? cv[2] : head == 3 ? cv[3] : -INFINITY;
-    const int hj = head == 0 ? cj[0] : head == 1 ? cj[1] : head == 2 ? cj[2] : cj[3];
-    const double mx = wave_max(hv);
-    const uint64_t hit = __ballot(hv == mx && head < 4);
-    // hit is never empty for finite scores; an empty mask (NaN scores) picks lane 0
-    const int wl = hit ? (int)__builtin_ctzll(hit) : 0;
-    const int wid = __builtin_amdgcn_readlane(e0 + hj, wl);
-    const double hs = (hj == 0 ? s[0] : hj == 1 ? s[1] : hj == 2 ? s[2] : s[3]);
-    const double ws = readlane_d(hs, wl);
-    if (lane == rr) {
-      my_id = wid < E ? wid : 0;
-      my_s = ws;
+    const uint32_t hi = (uint32_t)(ck[0] >> 32), lo = (uint32_t)ck[0];
+    const uint32_t mhi = wave_max_u32(hi);
+    uint64_t hit = __ballot(hi == mhi);
+    if (__popcll(hit) > 1) {
+      const uint32_t mlo = wave_max_u32(hi == mhi ? lo : 0u);
+      hit = __ballot(hi == mhi && lo == mlo);
     }
-    if (lane == wl) ++head;
+    const int wl = hit ? (int)__builtin_ctzll(hit) : 0;
+    const int wid = __builtin_amdgcn_readlane(cj[0], wl);
+    const double ws = readlane_d(cs[0], wl);
+    my_id = lane == rr ? wid : my_id;
+    my_s = lane == rr ? ws : my_s;
+    const bool take = lane == wl;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      ck[j] = take ? ck[j + 1] : ck[j];
+      cs[j] = take ? cs[j + 1] : cs[j];
+      cj[j] = take ? cj[j + 1] : cj[j];
+    }
+    ck[3] = take ? 0ull : ck[3];
   }
+  my_id = my_id < E ? my_id : 0;
   // ---- ascending order and weights ---------------------------------------
+  if (lane < K) sc.ids[lane] = my_id;
+  wave_lds_sync();
   rank = 0;
-  for (int j = 0; j < K; ++j) {
-    const int o = __builtin_amdgcn_readlane(my_id, j);
-    rank += (o < my_id || (o == my_id && j < lane)) ? 1 : 0;
+  for (int j = 0; j < K; j += 4) {
+    const int4 o4 = *reinterpret_cast<const int4*>(&sc.ids[j]);
+    const int o[4] = {o4.x, o4.y, o4.z, o4.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      rank += (j + i < K && (o[i] < my_id || (o[i] == my_id && j + i < lane))) ? 1 : 0;
   }
   const double total = wave_sum(lane < K ? my_s : 0.0);
   id = my_id;
