@@ -20,6 +20,9 @@
 // "Fitur utama" -- DeepSeek-V3 router, batch-union MoE, int4
 // dequant-on-use); "NVIDIA stellt neues GLM-5.2 NVFP4 Modell vor" (section
 // "Technische Details": NVFP4 expert weights).
+#include <algorithm>
+#include <type_traits>
+
 #include "select_token.h"
 
 namespace qmoe {
@@ -290,7 +293,56 @@ __global__ void __launch_bounds__(256) dec_router_shared_kernel(DecodeArgs a, in
 // ---------------------------------------------------------------------------
 // K2: selection of every token, then the permutation of the P <= 64 picks
 // ---------------------------------------------------------------------------
+// Shared expert's down projection for one token, in K2's launch (it needs
+// only K1's output, so it streams while the selection runs): wave rows
+// r, r + stride, ...; lane c takes group c (inter <= 2048), the next row's
+// loads are in flight while the current one is reduced.
+template <int FMT>
+__device__ __forceinline__ void shared_down_rows(const DecodeArgs& a, int blk, int nblk) {
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const ExpertSet& S = a.shared;
+  const int H = a.H, nG = S.inter / 32;
+  const uint32_t rowBytes = (uint32_t)S.inter / 2, srow = (uint32_t)nG * 2u;
+  const bool ok = lane < nG;
+  const uint32_t c = ok ? (uint32_t)lane : 0u;
+  const rsrc_t q = make_rsrc(S.down.q, (uint32_t)H * rowBytes);
+  const rsrc_t sr = make_rsrc(S.down.s, (uint32_t)H * srow);
+  uint32_t hm[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 v = *reinterpret_cast<const uint4*>(a.h_shared + c * 32 + 8 * i);
+    hm[4 * i] = v.x; hm[4 * i + 1] = v.y; hm[4 * i + 2] = v.z; hm[4 * i + 3] = v.w;
+  }
+  const float hs = FMT == MOE_WFMT_INT4_G32_F16 ? act_sum<true>(hm) : 0.0f;
+  const float g = FMT == MOE_WFMT_NVFP4 ? S.down.g[0] : 1.0f;
+  const int gw = blk * 4 + wv, nw = nblk * 4;
+  uint32_t w[2][4], sc[2];
+  auto ld = [&](auto B, int r) {
+    constexpr int b = decltype(B)::value;
+    bload16(w[b], q, c * 16u, (uint32_t)r * rowBytes);
+    sc[b] = bload_u16(sr, c * 2u, (uint32_t)r * srow);
+  };
+  auto step = [&](auto B, int r) {
+    constexpr int b = decltype(B)::value;
+    if (r + nw < H) ld(std::integral_constant<int, b ^ 1>{}, r + nw);
+    const float d = group_dot<FMT, true>(w[b], sc[b], hm, hs, g);
+    const float v = wave_sum(ok ? d : 0.0f);
+    if (lane == 0) a.o_shared[r] = v;
+  };
+  if (gw < H) ld(std::integral_constant<int, 0>{}, gw);
+  for (int r = gw; r < H; r += 2 * nw) {
+    step(std::integral_constant<int, 0>{}, r);
+    if (r + nw < H) step(std::integral_constant<int, 1>{}, r + nw);
+  }
+}
+
+template <int FMT>
 __global__ void __launch_bounds__(256) dec_select_permute_kernel(DecodeArgs a) {
+  if (blockIdx.x > 0) {
+    shared_down_rows<FMT>(a, blockIdx.x - 1, gridDim.x - 1);
+    return;
+  }
   __shared__ SelectScratch sc[4];
   __shared__ __attribute__((aligned(16))) int pid[64];
   __shared__ float pw[64];
@@ -351,7 +403,34 @@ __global__ void __launch_bounds__(256) dec_select_permute_kernel(DecodeArgs a) {
       for (int j = 0; j < 5; ++j) cnt[j] += (in && o[i] < lane + 64 * j) ? 1 : 0;
     }
   }
-  if (first) a.active[arank] = e;
+  if (first) {
+    a.active[arank] = e;
+    // the expert's record: its picks in pick order (at most one per token)
+    DecSlot sl;
+    sl.e = e;
+    sl.p0 = pos;
+    sl.pad = 0;
+    int M = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sl.t[i] = 0;
+      sl.w[i] = 0.0f;
+    }
+    for (int tt = 0; tt < a.T; ++tt) {
+      int found = -1;
+      for (int j = 0; j < K; ++j) found = pid[tt * K + j] == e ? tt * K + j : found;
+      if (found >= 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sl.t[i] = i == M ? tt : sl.t[i];
+          sl.w[i] = i == M ? pw[found] : sl.w[i];
+        }
+        ++M;
+      }
+    }
+    sl.M = M;
+    a.slots[arank] = sl;
+  }
   if (lane == 0) a.n_active[0] = __popcll(firsts);
 #pragma unroll
   for (int j = 0; j < 5; ++j)
@@ -366,17 +445,23 @@ __global__ void __launch_bounds__(256) dec_select_permute_kernel(DecodeArgs a) {
 template <int FMT, int GPL>
 __global__ void __launch_bounds__(256) dec_gateup_kernel(DecodeArgs a) {
   const int slot = blockIdx.y;
-  if (slot >= *a.n_active) return;
+  // the count and the slot's record are fetched together (one round trip)
+  const int na = __builtin_amdgcn_readfirstlane(*a.n_active);
+  const DecSlot sl = a.slots[slot];
+  if (slot >= na) return;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const ExpertSet& R = a.routed;
   const int pair0 = blockIdx.x * kPairsPerBlock + wv * kPairsPerWave;
   if (pair0 >= R.inter) return;
-  const int e = a.active[slot];
-  const int p0 = a.offsets[e], M = a.offsets[e + 1] - p0;
+  const int e = __builtin_amdgcn_readfirstlane(sl.e);
+  const int p0 = __builtin_amdgcn_readfirstlane(sl.p0);
+  const int M = __builtin_amdgcn_readfirstlane(sl.M);
   const float gg = (FMT == MOE_WFMT_NVFP4) ? R.gate.g[e] : 1.0f;
   const float gu = (FMT == MOE_WFMT_NVFP4) ? R.up.g[e] : 1.0f;
-  for (int m = 0; m < M; ++m) {
-    const int t = a.sorted_token[p0 + m];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    if (m >= M) break;
+    const int t = __builtin_amdgcn_readfirstlane(sl.t[m]);
     gateup_wave<FMT, GPL>(a.x + (size_t)t * a.H, a.H, R.gate, R.up, (size_t)e * R.inter, R.inter,
                           pair0, gg, gu, a.h_routed + (size_t)(p0 + m) * a.ldh);
   }
@@ -398,18 +483,31 @@ struct DownItem {
 struct SlotInfo {
   rsrc_t q, s, h;
   int p0, M, nG;
+  uint32_t tpk;   // token of pick i in byte i
+  float w[4];
   float g;
   bool routed;
 };
 
+// Slot s of the down projection: routed slot s < n_routed from its record
+// `ent`, else the shared expert (all T tokens, weight 1).
 template <int FMT>
-__device__ __forceinline__ SlotInfo slot_info(const DecodeArgs& a, int s, int n_routed, int row0) {
+__device__ __forceinline__ SlotInfo slot_info(const DecodeArgs& a, int s, int n_routed, int row0,
+                                              const DecSlot& ent) {
   SlotInfo d;
   d.routed = s < n_routed;
   const ExpertSet& X = d.routed ? a.routed : a.shared;
-  const int e = d.routed ? a.active[s] : 0;
-  d.p0 = d.routed ? a.offsets[e] : 0;
-  d.M = d.routed ? a.offsets[e + 1] - d.p0 : a.T;
+  const int e = d.routed ? __builtin_amdgcn_readfirstlane(ent.e) : 0;
+  d.p0 = d.routed ? __builtin_amdgcn_readfirstlane(ent.p0) : 0;
+  d.M = d.routed ? __builtin_amdgcn_readfirstlane(ent.M) : a.T;
+  d.tpk = d.routed ? (uint32_t)__builtin_amdgcn_readfirstlane(ent.t[0] | (ent.t[1] << 8) |
+                                                               (ent.t[2] << 16) | (ent.t[3] << 24))
+                   : 0x03020100u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    d.w[i] = d.routed ? __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                            __builtin_bit_cast(int, ent.w[i])))
+                      : 1.0f;
   d.nG = X.inter / 32;
   const uint32_t rowBytes = (uint32_t)X.inter / 2;
   const size_t rb = (size_t)e * a.H + row0;
@@ -460,8 +558,9 @@ __device__ __forceinline__ void down_compute(const DownItem& it, const SlotInfo&
       }
     }
     const float hs = (FMT == MOE_WFMT_INT4_G32_F16) ? act_sum<true>(hm) : 0.0f;
-    const int t = d.routed ? a.sorted_token[d.p0 + m] : m;
-    const float wpick = ok ? (d.routed ? a.sorted_w[d.p0 + m] : 1.0f) : 0.0f;
+    const int t = (int)((d.tpk >> (8 * m)) & 0xffu);
+    const float wm = m == 0 ? d.w[0] : m == 1 ? d.w[1] : m == 2 ? d.w[2] : d.w[3];
+    const float wpick = ok ? wm : 0.0f;
 #pragma unroll
     for (int r = 0; r < kDownRows; ++r) {
       const float v = wpick * group_dot<FMT, true>(it.w[r], it.sc[r], hm, hs, d.g);
@@ -479,7 +578,9 @@ __global__ void __launch_bounds__(256) dec_down_combine_kernel(DecodeArgs a) {
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int H = a.H, T = a.T;
   const int row0 = blockIdx.x * kDownRows;
-  const int n_routed = *a.n_active;
+  // the count and this wave's first record are fetched together
+  const int n_routed = __builtin_amdgcn_readfirstlane(*a.n_active);
+  const DecSlot ent0 = a.slots[wv];
   const int nslots = n_routed + (a.has_shared ? 1 : 0);
   const int nG_max = max(a.routed.inter, a.has_shared ? a.shared.inter : 0) / 32;
   float acc[MT][kDownRows];
@@ -496,8 +597,8 @@ __global__ void __launch_bounds__(256) dec_down_combine_kernel(DecodeArgs a) {
       // prefetch past the last slot reads the last slot again (in bounds) and
       // is never computed.
       int sa = wv, sb = wv + 4;
-      SlotInfo da = slot_info<FMT>(a, sa, n_routed, row0);
-      SlotInfo db = slot_info<FMT>(a, min(sb, last), n_routed, row0);
+      SlotInfo da = slot_info<FMT>(a, sa, n_routed, row0, ent0);
+      SlotInfo db = slot_info<FMT>(a, min(sb, last), n_routed, row0, a.slots[min(sb, last)]);
       DownItem A, B;
       down_load(A, da, c);
       down_load(B, db, c);
@@ -507,14 +608,14 @@ __global__ void __launch_bounds__(256) dec_down_combine_kernel(DecodeArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         if (sb > last) break;
         sa = sb + 4;
-        da = slot_info<FMT>(a, min(sa, last), n_routed, row0);
+        da = slot_info<FMT>(a, min(sa, last), n_routed, row0, a.slots[min(sa, last)]);
         down_load(A, da, c);
         __builtin_amdgcn_sched_barrier(0);
         down_compute<FMT, MT>(B, db, c, true, a, acc);  // sb <= last here
         __builtin_amdgcn_sched_barrier(0);
         if (sa > last) break;
         sb = sa + 4;
-        db = slot_info<FMT>(a, min(sb, last), n_routed, row0);
+        db = slot_info<FMT>(a, min(sb, last), n_routed, row0, a.slots[min(sb, last)]);
         down_load(B, db, c);
       }
     }
@@ -546,6 +647,173 @@ __global__ void __launch_bounds__(256) dec_down_combine_kernel(DecodeArgs a) {
       reinterpret_cast<float*>(a.y)[(size_t)t * H + row0 + r] = v;
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// K4 for a single token (the decode shape): down projection of the k <= 8
+// selected experts and the shared expert, combined into y.
+//
+// One resident round of workgroups; each wave streams whole output rows.
+// For row r it issues, for every slot, the 16-byte code chunk and the scale of
+// group `lane` (inter <= 2048, so one pass of 64 lanes covers a row) -- all
+// slots of row r + stride are in flight while row r is reduced.  The SwiGLU
+// outputs h of all slots sit in LDS, staged once per workgroup in the order
+// the lanes read them: quarter q of group c of slot s at 16-byte slot
+// (s * 4 + q) * nG + c, so each read of 64 lanes is 1 KB contiguous.  The sum
+// over slots runs in slot order within each lane, then across the lanes.
+// ---------------------------------------------------------------------------
+constexpr int kD1MaxRouted = 8;  // top_k <= 8 routed experts, plus the shared expert
+
+__device__ __forceinline__ void store_y(const DecodeArgs& a, int t, int row, float v) {
+  if (a.out_bf16) {
+    uint32_t u = __float_as_uint(v);
+    if ((u & 0x7fffffffu) > 0x7f800000u) {
+      u = (u >> 16) | 0x40u;
+    } else {
+      u += 0x7fffu + ((u >> 16) & 1u);
+      u >>= 16;
+    }
+    reinterpret_cast<uint16_t*>(a.y)[(size_t)t * a.H + row] = (uint16_t)u;
+  } else {
+    reinterpret_cast<float*>(a.y)[(size_t)t * a.H + row] = v;
+  }
+}
+
+template <int FMT>
+__global__ void __launch_bounds__(256, 2) dec_down_t1_kernel(DecodeArgs a) {
+  extern __shared__ uint4 hl[];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int H = a.H;
+  const int nr = a.K;                       // one token: k distinct experts
+  const bool shared = a.has_shared && !a.shared_in_k2;   // else K2 wrote its output
+  const int ns = nr + (shared ? 1 : 0);
+  const int inter = a.routed.inter;         // routed and shared inter are equal here
+  const int nG = inter / 32;
+  const uint32_t rowBytes = (uint32_t)inter / 2;
+
+  // slot records: expert, weight (uniform)
+  int es[kD1MaxRouted];
+  float wsl[kD1MaxRouted], gsl[kD1MaxRouted];
+#pragma unroll
+  for (int s = 0; s < kD1MaxRouted; ++s) {
+    const DecSlot& rec = a.slots[s < nr ? s : 0];
+    es[s] = s < nr ? __builtin_amdgcn_readfirstlane(rec.e) : 0;
+    wsl[s] = s < nr ? __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                          __builtin_bit_cast(int, rec.w[0])))
+                    : 0.0f;
+  }
+#pragma unroll
+  for (int s = 0; s < kD1MaxRouted; ++s)
+    gsl[s] = (FMT == MOE_WFMT_NVFP4 && s < nr) ? a.routed.down.g[es[s]] : 1.0f;
+  const float gsh = (FMT == MOE_WFMT_NVFP4 && shared) ? a.shared.down.g[0] : 1.0f;
+  const rsrc_t rq = make_rsrc(a.routed.down.q, 0xFFFFFFFFu);
+  const rsrc_t rs = make_rsrc(a.routed.down.s, 0xFFFFFFFFu);
+  const rsrc_t sq = make_rsrc(a.shared.down.q, shared ? 0xFFFFFFFFu : 0u);
+  const rsrc_t ss = make_rsrc(a.shared.down.s, shared ? 0xFFFFFFFFu : 0u);
+  // h of all slots (rows 0..k-1 routed in slot order, row k shared): every
+  // load is issued here, the LDS writes wait until the weights of the first
+  // row are requested as well
+  constexpr int kHPerThread = (kD1MaxRouted + 1) * 256 / 256;   // 16-byte chunks per thread
+  const int hper = nG * 4;                  // 16-byte chunks per row
+  uint4 hv[kHPerThread];
+#pragma unroll
+  for (int j = 0; j < kHPerThread; ++j) {
+    const int i = threadIdx.x + 256 * j;
+    const int sl = i / hper, rem = i - sl * hper;
+    hv[j] = i < ns * hper ? *reinterpret_cast<const uint4*>(a.h_routed + (size_t)sl * a.ldh + rem * 8)
+                          : make_uint4(0, 0, 0, 0);
+  }
+  const bool ok = lane < nG;
+  const uint32_t c = ok ? (uint32_t)lane : 0u;
+  const uint32_t srow = (uint32_t)nG * 2u;
+
+  // B: buffer; routed slots 0..7 and the shared slot
+  uint32_t wq[2][kD1MaxRouted][4], wsc[2][kD1MaxRouted], wqs[2][4], wscs[2];
+  auto load_row = [&](auto B, int r) {
+    constexpr int b = decltype(B)::value;
+#pragma unroll
+    for (int s = 0; s < kD1MaxRouted; ++s) {
+      if (s < nr) {
+        const uint32_t row = (uint32_t)(es[s] * H + r);
+        bload16(wq[b][s], rq, c * 16u, row * rowBytes);
+        wsc[b][s] = bload_u16(rs, c * 2u, row * srow);
+      }
+    }
+    if (shared) {
+      bload16(wqs[b], sq, c * 16u, (uint32_t)r * rowBytes);
+      wscs[b] = bload_u16(ss, c * 2u, (uint32_t)r * srow);
+    }
+  };
+  const int gw = blockIdx.x * 4 + wv, nw = gridDim.x * 4;
+  if (gw < H) load_row(std::integral_constant<int, 0>{}, gw);
+#pragma unroll
+  for (int j = 0; j < kHPerThread; ++j) {
+    const int i = threadIdx.x + 256 * j;
+    const int sl = i / hper, rem = i - sl * hper;
+    if (i < ns * hper) hl[(sl * 4 + (rem & 3)) * nG + (rem >> 2)] = hv[j];
+  }
+  __syncthreads();
+  auto h_of = [&](int s, uint32_t (&hm)[16]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 v = hl[(s * 4 + q) * nG + c];
+      hm[4 * q] = v.x; hm[4 * q + 1] = v.y; hm[4 * q + 2] = v.z; hm[4 * q + 3] = v.w;
+    }
+  };
+  // per-slot activation sums (int4 offset correction), the same for every row
+  float hsum[kD1MaxRouted], hsums = 0.0f;
+#pragma unroll
+  for (int s = 0; s < kD1MaxRouted; ++s) {
+    hsum[s] = 0.0f;
+    if (FMT == MOE_WFMT_INT4_G32_F16 && s < nr) {
+      uint32_t hm[16];
+      h_of(s, hm);
+      hsum[s] = act_sum<true>(hm);
+    }
+  }
+  if (FMT == MOE_WFMT_INT4_G32_F16 && shared) {
+    uint32_t hm[16];
+    h_of(nr, hm);
+    hsums = act_sum<true>(hm);
+  }
+  // row r from buffer B, with row r + nw requested into the other buffer
+  auto row_step = [&](auto B, int r) {
+    constexpr int b = decltype(B)::value;
+    if (r + nw < H) load_row(std::integral_constant<int, b ^ 1>{}, r + nw);
+    float acc = 0.0f;
+#pragma unroll
+    for (int s = 0; s < kD1MaxRouted; ++s) {
+      if (s < nr) {
+        uint32_t hm[16];
+        h_of(s, hm);
+        const float d = group_dot<FMT, true>(wq[b][s], wsc[b][s], hm, hsum[s], gsl[s]);
+        acc += ok ? wsl[s] * d : 0.0f;
+      }
+    }
+    if (shared) {
+      uint32_t hm[16];
+      h_of(nr, hm);
+      const float d = group_dot<FMT, true>(wqs[b], wscs[b], hm, hsums, gsh);
+      acc += ok ? d : 0.0f;
+    }
+    const float v = wave_sum(acc);
+    if (lane == 0) store_y(a, 0, r, a.shared_in_k2 ? v + a.o_shared[r] : v);
+  };
+  for (int r = gw; r < H; r += 2 * nw) {
+    row_step(std::integral_constant<int, 0>{}, r);
+    if (r + nw < H) row_step(std::integral_constant<int, 1>{}, r + nw);
+  }
+}
+
+// Whether the single-token down kernel covers this shape; its LDS bytes.
+__host__ __device__ inline bool down_t1_fits(const DecodeArgs& a) {
+  const long long nG = a.routed.inter / 32;
+  return a.T == 1 && a.K <= kD1MaxRouted && nG <= 64 &&
+         (!a.has_shared || a.shared.inter == a.routed.inter) &&
+         (long long)(a.K + 1) * a.routed.inter * 2 <= 65536 &&
+         (long long)a.E * a.H * (a.routed.inter / 2) < 0xFFFFFFFFll &&
+         (long long)a.E * a.H * nG * 2 < 0xFFFFFFFFll;
 }
 
 template <int GPL>
@@ -589,7 +857,14 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
   if (e != hipSuccess) return e;
   if (tr && (e = tr->mark("dec_router_shared")) != hipSuccess) return e;
 
-  hipLaunchKernelGGL(dec_select_permute_kernel, dim3(1), dim3(256), 0, s, a);
+  DecodeArgs a2 = a;
+  a2.shared_in_k2 = down_t1_fits(a) && a.has_shared ? 1 : 0;
+  const int k2_blocks = 1 + (a2.shared_in_k2 ? 128 : 0);
+  if (f4)
+    hipLaunchKernelGGL((dec_select_permute_kernel<MOE_WFMT_NVFP4>), dim3(k2_blocks), dim3(256), 0, s, a2);
+  else
+    hipLaunchKernelGGL((dec_select_permute_kernel<MOE_WFMT_INT4_G32_F16>), dim3(k2_blocks), dim3(256), 0,
+                       s, a2);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (tr && (e = tr->mark("dec_select_permute")) != hipSuccess) return e;
 
@@ -605,7 +880,16 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
   if (tr && (e = tr->mark("dec_gateup")) != hipSuccess) return e;
 
   dim3 g4(a.H / kDownRows);
-  if (a.T == 1) {
+  if (down_t1_fits(a)) {
+    const size_t lds =
+        (size_t)(a.K + (a.has_shared && !a2.shared_in_k2 ? 1 : 0)) * a.routed.inter * 2;
+    const int blocks = std::min((a.H + 3) / 4, 512);
+    if (f4)
+      hipLaunchKernelGGL((dec_down_t1_kernel<MOE_WFMT_NVFP4>), dim3(blocks), dim3(256), lds, s, a2);
+    else
+      hipLaunchKernelGGL((dec_down_t1_kernel<MOE_WFMT_INT4_G32_F16>), dim3(blocks), dim3(256), lds, s,
+                         a2);
+  } else if (a.T == 1) {
     if (f4)
       hipLaunchKernelGGL((dec_down_combine_kernel<MOE_WFMT_NVFP4, 1>), g4, dim3(256), 0, s, a);
     else

@@ -150,6 +150,7 @@ Workspace carve_workspace(const moe_config& c, int T, void* base) {
   const size_t o_tiles =
       take((size_t)gemm_max_units(T, (int)K, (int)E, c.n_shared_experts == 1) * 4 * sizeof(int32_t));
   const size_t o_ntiles = take(4 * sizeof(int32_t));
+  const size_t o_dslots = take(kDecMaxSlots * sizeof(DecSlot));
   w.total = off;
   if (base) {
     char* b = static_cast<char*>(base);
@@ -167,6 +168,7 @@ Workspace carve_workspace(const moe_config& c, int T, void* base) {
     w.x16 = reinterpret_cast<uint16_t*>(b + o_x16);
     w.tiles = reinterpret_cast<int4*>(b + o_tiles);
     w.n_tiles = reinterpret_cast<int32_t*>(b + o_ntiles);
+    w.dslots = reinterpret_cast<DecSlot*>(b + o_dslots);
   }
   return w;
 }
@@ -369,11 +371,13 @@ moe_status layer_impl(const moe_config* cfg, int32_t T, const uint16_t* x, const
     d.active = w.active;
     d.n_active = w.n_active;
     d.sorted_w = w.sorted_w;
+    d.slots = w.dslots;
     d.routed = expert_set(*routed, cfg->moe_inter);
     d.has_shared = has_shared;
     if (has_shared) d.shared = expert_set(*shared, cfg->shared_inter);
     d.h_routed = w.h;
     d.h_shared = w.h + P * ldh;
+    d.o_shared = w.O + P * cfg->hidden;
     d.ldh = ldh;
     d.y = y;
     d.out_bf16 = out_dtype == MOE_OUT_BF16;

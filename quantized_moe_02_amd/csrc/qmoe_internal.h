@@ -23,6 +23,18 @@ struct ExpertSet {
 };
 
 // Pieces of the caller's workspace.  Every piece starts on a 256-byte boundary.
+// One selected expert of a small batch (decode path), written by the
+// selection kernel and read by the FFN kernels in three 16-byte loads:
+// expert e, its first sorted slot p0, its M <= 4 tokens and their weights in
+// pick order.
+struct alignas(16) DecSlot {
+  int32_t e, p0, M, pad;
+  int32_t t[4];
+  float w[4];
+};
+static_assert(sizeof(DecSlot) == 48, "three 16-byte loads");
+constexpr int kDecMaxSlots = 64;
+
 struct Workspace {
   double* logits;         // [T][E]   router logits (fp64)
   int32_t* ids;           // [T][k]   routing when the caller keeps none
@@ -37,6 +49,7 @@ struct Workspace {
   float* O;               // [P+T][H]   per-pick expert outputs (fp32)
   uint16_t* x16;          // [T][H]     fp16 activations (GEMM path)
   int4* tiles;            // [max units] GEMM work units
+  DecSlot* dslots;        // [kDecMaxSlots] decode path: selected experts
   int32_t* n_tiles;       // [4]
   size_t total;
 };
@@ -145,11 +158,14 @@ struct DecodeArgs {
   int32_t* active;
   int32_t* n_active;
   float* sorted_w;
+  DecSlot* slots;
   ExpertSet routed;
   bool has_shared;
   ExpertSet shared;
   uint16_t* h_routed;  // [P][ldh]
   uint16_t* h_shared;  // [T][ldh]
+  float* o_shared;     // [T][H] shared-expert output when K2 computes it
+  int shared_in_k2;    // K2 runs the shared expert's down projection (T = 1)
   int ldh;
   void* y;
   int out_bf16;

@@ -143,6 +143,9 @@ EDGE = {
     "ragged_groups": (dict(hidden=2080, moe_inter=96, shared_inter=160), 5, "int4", "normal0.1"),
     "nvfp4":     (dict(), 8, "nvfp4", "normal0.1"),
     "nvfp4_ragged": (dict(hidden=96, moe_inter=160, shared_inter=64), 13, "nvfp4", "zipf"),
+    "nvfp4_T1":  (dict(), 1, "nvfp4", "normal0.1"),
+    "nvfp4_T3":  (dict(hidden=96, moe_inter=160, shared_inter=64), 3, "nvfp4", "zipf"),
+    "T1_uneven_shared": (dict(moe_inter=64, shared_inter=96), 1, "int4", "normal0.1"),
 }
 
 
