@@ -2,89 +2,182 @@
 // lambat", section "Fitur utama": the unique experts of a batch are read once
 // and applied to every position routed to them).
 //
-// Stable counting sort of the P = T*k picks by expert id.  One workgroup of
-// 1024 threads: an LDS histogram, an exclusive scan over the E <= 256 buckets,
-// then the picks in chunks of 1024 in pick order.  Inside a chunk a pick's
-// rank among equal keys is (equal keys in earlier waves of the chunk) + (equal
-// keys in lower lanes of its own wave); the latter comes from eight ballots
-// over the bits of the key.
+// Stable counting sort of the P = T*k picks by expert id, order within an
+// expert by pick index p = t*k + i.  The tokens are cut into B <= 128 chunks:
+//   perm_hist     one workgroup per chunk: the chunk's count of each expert
+//   perm_scan     one workgroup: per expert, the exclusive prefix of the chunk
+//                 counts (the chunk's first slot in that expert's run), the
+//                 expert offsets, and the active experts in ascending order
+//   perm_scatter  one wave per chunk walks its picks in order, 64 at a time; a
+//                 pick's slot is its expert's cursor plus its rank among the
+//                 equal picks of the step, after which the cursor advances
+// Counts are integers, so the LDS atomics leave nothing order-dependent.
 #include "qmoe_device.h"
 
 namespace qmoe {
 namespace {
 
-constexpr int kPermThreads = 1024;
-constexpr int kPermWaves = kPermThreads / 64;
 constexpr int kMaxE = 256;
+constexpr int kMaxChunks = 128;
 
-__global__ void __launch_bounds__(kPermThreads) permute_kernel(
-    const int32_t* __restrict__ ids, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ sorted_token, int32_t* __restrict__ inv_perm,
-    int32_t* __restrict__ active, int32_t* __restrict__ n_active, int P, int K, int E) {
-  __shared__ int count[kMaxE];
-  __shared__ int cursor[kMaxE];
-  __shared__ int wcount[kPermWaves][kMaxE];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wv = tid >> 6;
+__global__ void __launch_bounds__(256) perm_hist_kernel(const int32_t* __restrict__ ids,
+                                                        int32_t* __restrict__ hist, int T, int K,
+                                                        int E, int chunk) {
+  __shared__ int h[kMaxE];
+  const int b = blockIdx.x;
+  for (int e = threadIdx.x; e < kMaxE; e += 256) h[e] = 0;
+  __syncthreads();
+  const int p0 = b * chunk * K, p1 = min(T, (b + 1) * chunk) * K;
+  for (int p = p0 + threadIdx.x; p < p1; p += 256) atomicAdd(&h[ids[p]], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) hist[(size_t)b * E + e] = h[e];
+}
 
-  for (int e = tid; e < kMaxE; e += kPermThreads) count[e] = 0;
-  __syncthreads();
-  for (int p = tid; p < P; p += kPermThreads) atomicAdd(&count[ids[p]], 1);
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0, na = 0;
-    for (int e = 0; e < E; ++e) {
-      offsets[e] = run;
-      cursor[e] = run;
-      if (count[e] > 0) active[na++] = e;
-      run += count[e];
+constexpr int kScanGroups = 4;                         // chunk ranges scanned side by side
+constexpr int kScanPer = kMaxChunks / kScanGroups;     // chunks per range
+
+// 1024 threads: thread (g, e) holds the counts of expert e in chunk range g
+// in registers (all loads in flight at once), so hist is read and written
+// once each.
+__global__ void __launch_bounds__(1024) perm_scan_kernel(int32_t* __restrict__ hist,
+                                                         int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ active,
+                                                         int32_t* __restrict__ n_active, int E,
+                                                         int nb) {
+  __shared__ int gtot[kScanGroups][kMaxE];
+  __shared__ int cnt[kMaxE], act[kMaxE];
+  const int e = threadIdx.x % kMaxE;
+  const int g = __builtin_amdgcn_readfirstlane(threadIdx.x / kMaxE);   // one range per wave
+  const int per = (nb + kScanGroups - 1) / kScanGroups;
+  const int b0 = g * per, nloc = max(0, min(nb, b0 + per) - b0);
+  // one VGPR offset per lane, the chunk row in the scalar offset
+  const rsrc_t rh = make_rsrc(hist, (uint32_t)(nb * E * 4));
+  const uint32_t voff = (uint32_t)min(e, E - 1) * 4;
+  int v[kScanPer];
+#pragma unroll
+  for (int j = 0; j < kScanPer; ++j)
+    if (j < per)
+      v[j] = (int)__builtin_amdgcn_raw_buffer_load_b32(rh, voff, (uint32_t)(min(b0 + j, nb - 1) * E * 4), 0);
+  int run = 0;
+#pragma unroll
+  for (int j = 0; j < kScanPer; ++j) {
+    if (j < per) {
+      const int c = (j < nloc && e < E) ? v[j] : 0;
+      v[j] = run;   // exclusive prefix within the range
+      run += c;
     }
-    offsets[E] = run;
-    n_active[0] = na;
+  }
+  gtot[g][e] = run;
+  __syncthreads();
+  int gpre = 0, tot = 0;
+#pragma unroll
+  for (int r = 0; r < kScanGroups; ++r) {
+    const int t = gtot[r][e];
+    gpre += r < g ? t : 0;
+    tot += t;
+  }
+  if (g == 0) {
+    cnt[e] = tot;
+    act[e] = tot > 0 ? 1 : 0;
   }
   __syncthreads();
-
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int base = 0; base < P; base += kPermThreads) {
-    for (int i = tid; i < kPermWaves * kMaxE; i += kPermThreads) (&wcount[0][0])[i] = 0;
+  // inclusive scans over the 256 buckets (Hillis-Steele in LDS)
+  for (int d = 1; d < kMaxE; d <<= 1) {
+    int c = 0, a = 0;
+    if (g == 0 && e >= d) {
+      c = cnt[e - d];
+      a = act[e - d];
+    }
     __syncthreads();
-    const int p = base + tid;
-    const bool has = p < P;
-    const int e = has ? ids[p] : 0;
-    // lanes of this wave holding the same key
-    uint64_t peers = __ballot(has);
+    if (g == 0) {
+      cnt[e] += c;
+      act[e] += a;
+    }
+    __syncthreads();
+  }
+  const int excl = cnt[e] - tot;
+  if (e < E) {
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const uint64_t ones = __ballot(has && ((e >> b) & 1));
-      peers &= ((e >> b) & 1) ? ones : ~ones;
+    for (int j = 0; j < kScanPer; ++j)
+      if (j < nloc)
+        __builtin_amdgcn_raw_buffer_store_b32((uint32_t)(excl + gpre + v[j]), rh, voff,
+                                              (uint32_t)((b0 + j) * E * 4), 0);
+    if (g == 0) {
+      offsets[e] = excl;
+      if (tot > 0) active[act[e] - 1] = e;
     }
-    const int rank = __popcll(peers & lt_mask);
-    if (has && rank == 0) wcount[wv][e] = __popcll(peers);
-    __syncthreads();
-    if (has) {
-      int before = 0;
-      for (int w2 = 0; w2 < wv; ++w2) before += wcount[w2][e];
-      const int pos = cursor[e] + before + rank;
-      sorted_token[pos] = p / K;
-      inv_perm[p] = pos;
+  }
+  if (threadIdx.x == kMaxE - 1) {
+    offsets[E] = cnt[kMaxE - 1];
+    n_active[0] = act[kMaxE - 1];
+  }
+}
+
+// One wave per chunk, 64 consecutive picks per step.  Lanes holding the same
+// expert find each other with one ballot per bit of the id; a pick's slot is
+// its expert's cursor plus the number of equal picks on lower lanes, and the
+// highest of them advances the cursor.
+__global__ void __launch_bounds__(64) perm_scatter_kernel(const int32_t* __restrict__ ids,
+                                                          const int32_t* __restrict__ hist,
+                                                          int32_t* __restrict__ sorted_token,
+                                                          int32_t* __restrict__ inv_perm, int T,
+                                                          int K, int E, int chunk) {
+  __shared__ int cur[kMaxE];
+  const int b = blockIdx.x, lane = threadIdx.x;
+  {
+    int v[kMaxE / 64];
+#pragma unroll
+    for (int j = 0; j < kMaxE / 64; ++j) v[j] = hist[(size_t)b * E + min(lane + 64 * j, E - 1)];
+#pragma unroll
+    for (int j = 0; j < kMaxE / 64; ++j) cur[lane + 64 * j] = v[j];
+  }
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  const uint64_t below = (1ull << lane) - 1;
+  const int p0 = b * chunk * K, p1 = min(T, (b + 1) * chunk) * K;
+  for (int q0 = p0; q0 < p1; q0 += 64 * 8) {
+    int v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = ids[min(q0 + 64 * j + lane, p1 - 1)];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (q0 + 64 * j >= p1) break;
+      const int p = q0 + 64 * j + lane, e = v[j];
+      const bool valid = p < p1;
+      uint64_t m = __builtin_amdgcn_ballot_w64(valid);
+      for (int bit = 0; bit < nbits; ++bit) {
+        const bool set = (e >> bit) & 1;
+        const uint64_t bb = __builtin_amdgcn_ballot_w64(set);
+        m &= set ? bb : ~bb;
+      }
+      const int rank = __popcll(m & below), cnt = __popcll(m);
+      const int base = cur[e];
+      if (valid) {
+        inv_perm[p] = base + rank;
+        sorted_token[base + rank] = p / K;
+        if (rank == cnt - 1) cur[e] = base + cnt;
+      }
     }
-    __syncthreads();
-    for (int e2 = tid; e2 < E; e2 += kPermThreads) {
-      int tot = 0;
-      for (int w2 = 0; w2 < kPermWaves; ++w2) tot += wcount[w2][e2];
-      cursor[e2] += tot;
-    }
-    __syncthreads();
   }
 }
 
 }  // namespace
 
+int permute_chunk(int T) { return std::max(64, (T + kMaxChunks - 1) / kMaxChunks); }
+size_t permute_hist_ints(int T, int E) {
+  const int c = permute_chunk(T);
+  return (size_t)((T + c - 1) / c) * E;
+}
+
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s, Tracer* tr) {
   if (a.T == 0) return hipSuccess;
-  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), 0, s, a.ids, a.offsets,
-                     a.sorted_token, a.inv_perm, a.active, a.n_active, a.T * a.K, a.K, a.E);
+  const int chunk = permute_chunk(a.T);
+  const int nb = (a.T + chunk - 1) / chunk;
+  hipLaunchKernelGGL(perm_hist_kernel, dim3(nb), dim3(256), 0, s, a.ids, a.hist, a.T, a.K, a.E, chunk);
+  hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(kScanGroups * kMaxE), 0, s, a.hist, a.offsets, a.active,
+                     a.n_active, a.E, nb);
+  hipLaunchKernelGGL(perm_scatter_kernel, dim3(nb), dim3(64), 0, s, a.ids, a.hist, a.sorted_token,
+                     a.inv_perm, a.T, a.K, a.E, chunk);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && tr) e = tr->mark("permute");
   return e;

@@ -151,6 +151,7 @@ Workspace carve_workspace(const moe_config& c, int T, void* base) {
       take((size_t)gemm_max_units(T, (int)K, (int)E, c.n_shared_experts == 1) * 4 * sizeof(int32_t));
   const size_t o_ntiles = take(4 * sizeof(int32_t));
   const size_t o_dslots = take(kDecMaxSlots * sizeof(DecSlot));
+  const size_t o_phist = take(permute_hist_ints(T, (int)E) * sizeof(int32_t));
   w.total = off;
   if (base) {
     char* b = static_cast<char*>(base);
@@ -169,6 +170,7 @@ Workspace carve_workspace(const moe_config& c, int T, void* base) {
     w.tiles = reinterpret_cast<int4*>(b + o_tiles);
     w.n_tiles = reinterpret_cast<int32_t*>(b + o_ntiles);
     w.dslots = reinterpret_cast<DecSlot*>(b + o_dslots);
+    w.phist = reinterpret_cast<int32_t*>(b + o_phist);
   }
   return w;
 }
@@ -227,8 +229,9 @@ moe_status moe_permute(const moe_config* cfg, int32_t T, const int32_t* topk_ids
     return MOE_ERR_INVALID_ARG;
   if ((s = check_ws(*cfg, T, ws, ws_bytes)) != MOE_OK) return s;
   if (T == 0) return MOE_OK;
+  const Workspace w = carve_workspace(*cfg, T, ws);
   PermuteArgs a{topk_ids, expert_offsets, sorted_token, inv_perm, active_experts, n_active,
-                T, cfg->top_k, cfg->n_routed_experts};
+                T, cfg->top_k, cfg->n_routed_experts, w.phist};
   return hip_status(launch_permute(a, stream));
 }
 
@@ -388,7 +391,7 @@ moe_status layer_impl(const moe_config* cfg, int32_t T, const uint16_t* x, const
                cfg->n_group, cfg->topk_group, cfg->top_k, cfg->routed_scaling_factor};
   if ((e = launch_route(ra, stream, tr)) != hipSuccess) return MOE_ERR_HIP;
   PermuteArgs pa{ids, w.offsets, w.sorted_token, w.inv_perm, w.active, w.n_active,
-                 T, cfg->top_k, cfg->n_routed_experts};
+                 T, cfg->top_k, cfg->n_routed_experts, w.phist};
   if ((e = launch_permute(pa, stream, tr)) != hipSuccess) return MOE_ERR_HIP;
 
   const ExpertSet rset = expert_set(*routed, cfg->moe_inter);

@@ -51,6 +51,7 @@ struct Workspace {
   int4* tiles;            // [max units] GEMM work units
   DecSlot* dslots;        // [kDecMaxSlots] decode path: selected experts
   int32_t* n_tiles;       // [4]
+  int32_t* phist;         // [permute_hist_ints] permutation scratch
   size_t total;
 };
 
@@ -100,8 +101,12 @@ struct PermuteArgs {
   int32_t* active;
   int32_t* n_active;
   int T, K, E;
+  int32_t* hist;   // [permute_hist_ints] per-chunk expert counts (scratch)
 };
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s, Tracer* tr = nullptr);
+// Tokens per chunk of the permutation and the size of its scratch.
+int permute_chunk(int T);
+size_t permute_hist_ints(int T, int E);
 
 struct FfnArgs {
   const uint16_t* x;
