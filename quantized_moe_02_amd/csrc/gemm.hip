@@ -20,7 +20,9 @@
 // and B is valid: within a 128-input block a lane loads one 16-byte chunk of
 // its row (a whole 32-input group, one scale) and feeds its four 32-bit words
 // to four consecutive MFMA K steps; the B reads from LDS use the same order.
+#include <algorithm>
 #include <type_traits>
+#include <utility>
 
 #include "qmoe_device.h"
 
@@ -34,8 +36,15 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 constexpr int kBM = 128;          // tokens per unit
 constexpr int kBK = 128;          // inputs per K block
 constexpr int kChunks = kBK / 8;  // 16-byte chunks per activation row of a K block
-constexpr int kStage = kBM * kBK; // fp16 elements per activation stage in LDS
-constexpr int kCT = kBM / 16;     // 16-token column tiles
+// Thin units: an expert with at most kBMThin tokens gets one unit of the thin
+// kernel, whose LDS stages hold kBMThin rows.  With few token columns a K
+// block carries little MFMA work, so the thin kernel keeps more K blocks in
+// flight to cover the memory latency.
+#ifndef QMOE_THIN_NS
+#define QMOE_THIN_NS 4
+#endif
+constexpr int kBMThin = 32;
+constexpr int kNSThin = QMOE_THIN_NS;
 constexpr int kGateUpPairs = 128; // row pairs per gate/up unit
 constexpr int kDownRows = 256;    // output rows per down unit
 
@@ -90,7 +99,7 @@ __device__ __forceinline__ half8 dequant_word(uint32_t w, uint32_t scale2) {
 struct Unit {
   int e;        // expert index in its weight set (0 for the shared expert)
   int p0;       // first row of the unit in the h / O buffers
-  int M;        // tokens in the unit (<= kBM)
+  int M;        // tokens in the unit (<= the kernel's unit rows)
   int tok0;     // routed: first sorted slot (index into sorted_token); shared: first token
   bool routed;
 };
@@ -98,8 +107,8 @@ struct Unit {
 // The unit is the same for the whole workgroup; readfirstlane puts it in
 // SGPRs, so that the buffer descriptors built from it are uniform (a
 // descriptor in VGPRs turns every buffer load into a waterfall loop).
-__device__ __forceinline__ Unit load_unit(const GemmArgs& g, int idx) {
-  const int4 t = g.tiles[idx];
+__device__ __forceinline__ Unit load_unit(const int4* tiles, int idx) {
+  const int4 t = tiles[idx];
   Unit u;
   const int x = __builtin_amdgcn_readfirstlane(t.x);
   u.routed = x >= 0;
@@ -122,16 +131,17 @@ constexpr uint32_t kOOBRow = 0x80000000u;
 // Load i of wave w covers slots (8 w + i) * 64 .. +63, i.e. rows 4 (8 w + i)
 // + lane / 16, slot lane % 16.  Rows are padded with zeros to a multiple of
 // the K block, so a partial last K block reads zeros past K.
-constexpr int kActLoads = kBM * kChunks / 256;   // loads per thread per K block
+template <int BM>
+__host__ __device__ constexpr int act_loads() { return BM * kChunks / 256; }   // loads per thread per K block
 
 // Byte offset of each of this thread's loads at K block 0 (K block kb adds
 // kb * 256).
-template <int PROJ>
+template <int PROJ, int NA>
 __device__ __forceinline__ void act_rows(const GemmArgs& g, const Unit& u, int wv, int lane,
-                                         uint32_t (&abase)[kActLoads]) {
+                                         uint32_t (&abase)[NA]) {
 #pragma unroll
-  for (int i = 0; i < kActLoads; ++i) {
-    const int m = (wv * kActLoads + i) * 4 + (lane >> 4);
+  for (int i = 0; i < NA; ++i) {
+    const int m = (wv * NA + i) * 4 + (lane >> 4);
     const uint32_t chunk = (uint32_t)((lane & 15) ^ (m & 15));
     uint32_t off = kOOBRow;
     if (m < u.M) {
@@ -146,13 +156,20 @@ __device__ __forceinline__ void act_rows(const GemmArgs& g, const Unit& u, int w
   }
 }
 
-__device__ __forceinline__ void issue_act(const rsrc_t& ar, const uint32_t (&abase)[kActLoads], int kb,
+template <int NA>
+__device__ __forceinline__ void issue_act(const rsrc_t& ar, const uint32_t* abase, int kb,
                                           int wv, uint16_t* stage) {
 #pragma unroll
-  for (int i = 0; i < kActLoads; ++i)
+  for (int i = 0; i < NA; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        ar, (__attribute__((address_space(3))) void*)(stage + (wv * kActLoads + i) * 64 * 8), 16,
+        ar, (__attribute__((address_space(3))) void*)(stage + (wv * NA + i) * 64 * 8), 16,
         abase[i] + (uint32_t)kb * (kBK * 2), 0, 0, 0);
+}
+
+// 16 bytes per lane from buffer offset voff into LDS at dst + 16 * lane.
+__device__ __forceinline__ void lds_copy16(const rsrc_t& r, uint8_t* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff,
+                                           0, 0, 0);
 }
 
 template <int N>
@@ -160,7 +177,16 @@ using ic = std::integral_constant<int, N>;
 
 constexpr int kNS = 4;            // K blocks in flight (LDS stages, weight register ring)
 constexpr int kRT = 4;            // 16-row weight tiles per wave
-constexpr int kLoadsPerKB = kActLoads + 2 * kRT;   // vector memory ops per thread per K block
+
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+// f(integral_constant<int, j>) for j = 0 .. N-1
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // Work item -> (unit, n tile).  Workgroups are dispatched round-robin over
 // the 8 XCDs; this maps the items that one XCD receives onto a contiguous
@@ -174,28 +200,51 @@ __device__ __forceinline__ int xcd_item(int L, int total) {
 // PROJ 0: gate/up (+SwiGLU), PROJ 1: down.
 //
 // One workgroup of 4 waves per CU (one wave per SIMD, all 512 registers per
-// lane).  K loop: kNS-stage pipeline.  K block kb + 3 is requested (weights
-// into the register ring, activations straight into an LDS stage) while
-// block kb is multiplied; within a block, the next K step's B operands
-// (LDS) and A operands (dequantised weights) are produced while the current
-// step's MFMAs run.  Every K block issues exactly kLoadsPerKB vector memory
-// ops per thread (blocks past K read zeros), so "block kb + 1 has landed" is
-// vmcnt <= 2 * kLoadsPerKB.  One barrier per K block, before its last K step.
-template <int FMT, int PROJ>
-__global__ void __launch_bounds__(256, 1) moe_gemm_kernel(GemmArgs g) {
+// lane).  BM: token rows of a unit; NS: K blocks in flight.  K loop: NS-stage
+// pipeline.  K block kb + NS - 1 is requested (weights into the register
+// ring, activations straight into an LDS stage) while block kb is
+// multiplied; within a block, the next K step's B operands (LDS) and A
+// operands (dequantised weights) are produced while the current step's MFMAs
+// run.  The vector memory ops issued per thread for any two consecutive K
+// blocks are the same in number, WAITN (blocks past K read zeros), so "block
+// kb + 1 has landed" is vmcnt <= WAITN once block kb + 3 is requested.  One
+// barrier per K block, before its last K step.
+#ifndef QMOE_THIN_WGS
+#define QMOE_THIN_WGS 2
+#endif
+//
+// Scales.  Each lane needs one 2-byte scale per K block, scattered over 16
+// rows per load; loaded per block, these requests cost as much as the codes.
+// SL (thin units, K % 512 == 0): each wave instead copies the scales of its 64 rows for
+// four K blocks at a time (a "super-block", 32 bytes per row) straight into
+// LDS with two 16-byte-per-lane loads, three super-blocks deep, and reads its
+// 2 bytes from there.  The copy for super-block S + 1 rides on the even K
+// blocks of super-block S, so every two K blocks carry one extra load.
+// Otherwise (ragged K) each lane loads its own 2 bytes per block.
+constexpr int kSclBytesPerWave = 3 * 2 * 1024;   // three super-blocks x two 1 KB copies
+
+template <int FMT, int PROJ, int BM, int NS, bool SL>
+__global__ void __launch_bounds__(256, BM == kBMThin ? QMOE_THIN_WGS : 1) moe_gemm_kernel(GemmArgs g) {
   constexpr int RT = kRT;
-  __shared__ __attribute__((aligned(16))) uint16_t xs[kNS][kStage];
+  constexpr int NA = act_loads<BM>();
+  static_assert(NS == 4, "the scale copies ride on K blocks 0 and 2 of each group of four");
+  // vector memory ops per thread issued for K blocks kb + 2 and kb + 3: all
+  // that may still be in flight once block kb + 1 has landed
+  constexpr int WAITN = 2 * (NA + RT) + (SL ? 1 : 2 * RT);
+  __shared__ __attribute__((aligned(16))) uint16_t xs[NS][BM * kBK];
+  __shared__ __attribute__((aligned(16))) uint8_t scl[SL ? 4 * kSclBytesPerWave : 16];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int max_inter = max(g.routed.inter, g.has_shared ? g.shared.inter : 0);
   const int NT = PROJ == 0 ? (max_inter + kGateUpPairs - 1) / kGateUpPairs
                            : (g.H + kDownRows - 1) / kDownRows;
-  const int total = __builtin_amdgcn_readfirstlane(*g.n_tiles) * NT;
+  constexpr bool thin = BM == kBMThin;
+  const int total = __builtin_amdgcn_readfirstlane(g.n_tiles[thin ? 1 : 0]) * NT;
   if ((int)blockIdx.x >= total) return;
   const int w = xcd_item(blockIdx.x, total);
   const int uidx = w / NT;
   const int nt = w - uidx * NT;
-  const Unit u = load_unit(g, uidx);
+  const Unit u = load_unit(thin ? g.tiles + g.thin_off : g.tiles, uidx);
   const ExpertSet& X = u.routed ? g.routed : g.shared;
   const int inter = X.inter;
   const int K = PROJ == 0 ? g.H : inter;
@@ -240,23 +289,53 @@ __global__ void __launch_bounds__(256, 1) moe_gemm_kernel(GemmArgs g) {
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     qoff[rt] = (uint32_t)(rbase[rt] + lrow) * rowBytes + (uint32_t)lq * 16u;
-    soff[rt] = (uint32_t)(rbase[rt] + lrow) * scaleRowBytes + (uint32_t)lq * 2u;
+    soff[rt] = (uint32_t)(rbase[rt] + lrow) * scaleRowBytes + (uint32_t)lq * 2u;   // !SL
   }
-  uint32_t wcode[kNS][RT][4], wsc[kNS][RT];
+  // SL: copy q (0, 1) of a super-block holds 32 rows x 32 bytes; lane l
+  // copies half l & 1 of row l >> 1 (gate/up: copy 0 the gate rows, copy 1
+  // the up rows; down: copy q rows 32 q ..).  Lane (lrow, lq) reads row
+  // 16 (rt & 1) + lrow of copy rt >> 1, byte 8 (kb & 3) + 2 lq.
+  uint8_t* const sclw = scl + (SL ? wv * kSclBytesPerWave : 0);
+  uint32_t scopy[2], sread[RT];
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+    scopy[q] = (uint32_t)(wrow + (PROJ == 0 ? 0 : 32 * q) + (lane >> 1)) * scaleRowBytes +
+               16u * (uint32_t)(lane & 1);
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+    sread[rt] = (uint32_t)((rt >> 1) * 1024 + 32 * (16 * (rt & 1) + lrow) + 2 * lq);
+  // copy q of super-block sbk into its LDS slot (sbk % 3)
+  auto copy_scales = [&](int q, int sbk) {
+    const int j = PROJ == 0 ? q : 0;
+    lds_copy16(sb[j], sclw + (sbk % 3) * 2048 + q * 1024, scopy[q] + (uint32_t)sbk * 32u);
+  };
+  uint32_t wcode[NS][RT][4], wsc[NS][RT];
   const rsrc_t ar = PROJ == 0 ? make_rsrc(g.x16, (uint32_t)g.T * (uint32_t)g.ldx * 2u)
                               : make_rsrc(g.hin, (uint32_t)(g.P + g.T) * (uint32_t)g.ldh * 2u);
-  uint32_t arow[kActLoads];
-  act_rows<PROJ>(g, u, wv, lane, arow);
+  uint32_t arow[NA];
+  act_rows<PROJ, NA>(g, u, wv, lane, arow);
 
-  // request K block kb into stage S (LDS) and ring slot S (registers)
+  // request K block kb into stage S (LDS) and ring slot S (registers); kb is
+  // congruent to S modulo NS, so (kb & 3) is known here
   auto issue = [&](auto S, int kb) {
     constexpr int st = decltype(S)::value;
-    issue_act(ar, arow, kb, wv, xs[st]);
+    issue_act<NA>(ar, arow, kb, wv, xs[st]);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       const int j = PROJ == 0 ? rt >> 1 : 0;
       bload16(wcode[st][rt], qb[j], qoff[rt] + (uint32_t)kb * 64u, 0);
-      wsc[st][rt] = bload_u16(sb[j], soff[rt] + (uint32_t)kb * 8u, 0);
+      if constexpr (!SL) wsc[st][rt] = bload_u16(sb[j], soff[rt] + (uint32_t)kb * 8u, 0);
+    }
+    if constexpr (SL && (st & 1) == 0) copy_scales(st >> 1, (kb >> 2) + 1);
+  };
+  // SL: this lane's scales of K block kb (congruent to S) into ring slot S
+  auto read_scales = [&](auto S, int kb) {
+    constexpr int st = decltype(S)::value;
+    if constexpr (SL) {
+      const uint8_t* base = sclw + ((kb >> 2) % 3) * 2048 + 8 * st;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        wsc[st][rt] = *reinterpret_cast<const uint16_t*>(base + sread[rt]);
     }
   };
   // A operands (dequantised weights) of K step ks from ring slot S
@@ -265,11 +344,12 @@ __global__ void __launch_bounds__(256, 1) moe_gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       uint32_t s2;
+      const uint32_t sw = wsc[st][rt];
       if constexpr (FMT == MOE_WFMT_INT4_G32_F16) {
-        s2 = (wsc[st][rt] & 0xffffu) * 0x00010001u;
+        s2 = (sw & 0xffffu) * 0x00010001u;
       } else {
         // inputs 0-15 of the group use scale byte 0, 16-31 byte 1
-        const _Float16 sh = (_Float16)e4m3_to_f32(wsc[st][rt], ks >> 1);
+        const _Float16 sh = (_Float16)e4m3_to_f32(sw, ks >> 1);
         const uint32_t b = __builtin_bit_cast(uint16_t, sh);
         s2 = b * 0x00010001u;
       }
@@ -311,21 +391,27 @@ __global__ void __launch_bounds__(256, 1) moe_gemm_kernel(GemmArgs g) {
       }
     };
 
-    issue(ic<0>{}, 0);
-    issue(ic<1>{}, 1);
-    issue(ic<2>{}, 2);
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kLoadsPerKB) : "memory");
+    if constexpr (SL) {   // super-block 0's scales, ahead of every K block
+      copy_scales(0, 0);
+      copy_scales(1, 0);
+    }
+    static_for<NS - 1>([&](auto J) { issue(J, J); });
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(WAITN) : "memory");
     __syncthreads();
+    read_scales(ic<0>{}, 0);
     read_b(xs[0], 0, B[0]);
     dequant_ks(ic<0>{}, 0, A[0]);
 
     auto kblock = [&](auto S, int kb) {
       constexpr int st = decltype(S)::value;
-      constexpr int sn = (st + 1) % kNS;
-      constexpr int s3 = (st + kNS - 1) % kNS;
+      constexpr int sn = (st + 1) % NS;
+      constexpr int s3 = (st + NS - 1) % NS;
       // stage s3 held block kb - 1, whose last reads every wave finished
       // before the barrier of block kb - 1
-      issue(ic<s3>{}, kb + kNS - 1);
+      issue(ic<s3>{}, kb + NS - 1);
+      // block kb + 1's scales: their copy rode on block kb - 1 or earlier,
+      // which has landed
+      read_scales(ic<sn>{}, kb + 1);
 #pragma unroll
       for (int ks = 0; ks < 3; ++ks) {
         read_b(xs[st], ks + 1, B[(ks + 1) & 1]);
@@ -333,20 +419,18 @@ __global__ void __launch_bounds__(256, 1) moe_gemm_kernel(GemmArgs g) {
         mfmas(A[ks & 1], B[ks & 1]);
         interleave();
       }
-      // block kb + 1 landed in every wave (two younger blocks may be in flight)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kLoadsPerKB) : "memory");
+      // block kb + 1 landed in every wave (blocks kb + 2, kb + 3 may be in flight)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(WAITN) : "memory");
       __syncthreads();
       read_b(xs[sn], 0, B[0]);
       dequant_ks(ic<sn>{}, 0, A[0]);
       mfmas(A[1], B[1]);
       interleave();
     };
-    for (int kb = 0; kb < nkb; kb += kNS) {
-      kblock(ic<0>{}, kb);
-      if (kb + 1 < nkb) kblock(ic<1>{}, kb + 1);
-      if (kb + 2 < nkb) kblock(ic<2>{}, kb + 2);
-      if (kb + 3 < nkb) kblock(ic<3>{}, kb + 3);
-    }
+    for (int kb = 0; kb < nkb; kb += NS)
+      static_for<NS>([&](auto J) {
+        if (kb + J < nkb) kblock(J, kb + J);
+      });
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // epilogue
@@ -392,12 +476,16 @@ __global__ void __launch_bounds__(256, 1) moe_gemm_kernel(GemmArgs g) {
       }
     }
   };
-  if (nct > 4)
-    run(ic<8>{});
-  else if (nct > 2)
-    run(ic<4>{});
-  else
-    run(ic<2>{});
+  if constexpr (thin) {
+    run(ic<kBMThin / 16>{});
+  } else {
+    if (nct > 4)
+      run(ic<8>{});
+    else if (nct > 2)
+      run(ic<4>{});
+    else
+      run(ic<2>{});
+  }
 }
 
 // bf16 -> fp16 copy of the activations (exact for |x| in the fp16 normal
@@ -433,61 +521,94 @@ __global__ void __launch_bounds__(64) build_units_kernel(const int32_t* __restri
                                                          const int32_t* __restrict__ n_active,
                                                          int4* __restrict__ tiles,
                                                          int32_t* __restrict__ n_tiles, int T, int P,
-                                                         int has_shared) {
+                                                         int has_shared, int thin_off) {
   const int lane = threadIdx.x;
   const int na = n_active ? *n_active : 0;
-  int base = 0;
+  int4* thin = tiles + thin_off;
+  int base = 0, tbase = 0;   // fat units, thin units so far
   for (int a0 = 0; a0 < na; a0 += 64) {
     const int a = a0 + lane;
-    int e = 0, o = 0, M = 0, nm = 0;
+    int e = 0, o = 0, M = 0, nm = 0, nt = 0;
     if (a < na) {
       e = active[a];
       o = offsets[e];
       M = offsets[e + 1] - o;
-      nm = (M + kBM - 1) / kBM;
+      nt = M <= kBMThin ? 1 : 0;
+      nm = nt ? 0 : (M + kBM - 1) / kBM;
     }
-    // exclusive prefix of nm across the wave
-    int pre = nm;
+    // exclusive prefixes of the fat and thin unit counts across the wave
+    int pre = nm, tpre = nt;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
-      const int v = __shfl_up(pre, d, 64);
-      if (lane >= d) pre += v;
+      const int v = __shfl_up(pre, d, 64), tv = __shfl_up(tpre, d, 64);
+      if (lane >= d) {
+        pre += v;
+        tpre += tv;
+      }
     }
     const int excl = base + pre - nm;
     for (int i = 0; i < nm; ++i) {
       const int m0 = i * kBM;
       tiles[excl + i] = make_int4(e, o + m0, min(kBM, M - m0), o + m0);
     }
+    if (nt) thin[tbase + tpre - 1] = make_int4(e, o, M, o);
     base += __shfl(pre, 63, 64);
+    tbase += __shfl(tpre, 63, 64);
   }
   if (has_shared) {
-    const int ns = (T + kBM - 1) / kBM;
-    for (int i = lane; i < ns; i += 64) {
-      const int t0 = i * kBM;
-      tiles[base + i] = make_int4(-1, P + t0, min(kBM, T - t0), t0);
+    if (T <= kBMThin) {
+      if (lane == 0) thin[tbase] = make_int4(-1, P, T, 0);
+      ++tbase;
+    } else {
+      const int ns = (T + kBM - 1) / kBM;
+      for (int i = lane; i < ns; i += 64) {
+        const int t0 = i * kBM;
+        tiles[base + i] = make_int4(-1, P + t0, min(kBM, T - t0), t0);
+      }
+      base += ns;
     }
-    base += ns;
   }
-  if (lane == 0) *n_tiles = base;
+  if (lane == 0) {
+    n_tiles[0] = base;
+    n_tiles[1] = tbase;
+  }
+}
+
+// Most work units of each kind: fat units hold up to kBM tokens of an expert
+// with more than kBMThin of them, thin units an expert's (or the shared
+// expert's) tokens when there are at most kBMThin.
+long fat_units_max(int T, int K, int E, bool has_shared) {
+  const long P = (long)T * K;
+  const long fat_experts = std::min<long>(E, P / (kBMThin + 1));
+  const long routed = (P + kBM - 1) / kBM + fat_experts;
+  const long shared = has_shared && T > kBMThin ? (T + kBM - 1) / kBM : 0;
+  return routed + shared;
+}
+long thin_units_max(int T, int K, int E, bool has_shared) {
+  const long P = (long)T * K;
+  return std::min<long>(E, P) + (has_shared && T <= kBMThin ? 1 : 0);
 }
 
 }  // namespace
 
 hipError_t launch_build_units(const int32_t* offsets, const int32_t* active,
                               const int32_t* n_active, int4* tiles, int32_t* n_tiles, int T, int P,
-                              bool has_shared, hipStream_t s) {
+                              int K, int E, bool has_shared, hipStream_t s) {
   hipLaunchKernelGGL(build_units_kernel, dim3(1), dim3(64), 0, s, offsets, active, n_active, tiles,
-                     n_tiles, T, P, has_shared ? 1 : 0);
+                     n_tiles, T, P, has_shared ? 1 : 0, (int)fat_units_max(T, K, E, has_shared));
   return hipGetLastError();
 }
 
+// Work units: for each active expert (ascending) its sorted slots, in one thin
+// unit or slices of kBM; then the shared expert's tokens likewise.
+// tiles[i] = {expert or -1, first h/O row, tokens, first sorted slot or
+// token}; the thin units start at tiles[thin_off].
 int gemm_max_units(int T, int K, int E, bool has_shared) {
-  const long P = (long)T * K;
-  const long routed = (P + kBM - 1) / kBM + (P < E ? P : E);
-  const long shared = has_shared ? (T + kBM - 1) / kBM : 0;
-  return (int)(routed + shared);
+  return (int)(fat_units_max(T, K, E, has_shared) + thin_units_max(T, K, E, has_shared));
 }
-int gemm_unit_tokens() { return kBM; }
+int gemm_thin_offset(int T, int K, int E, bool has_shared) {
+  return (int)fat_units_max(T, K, E, has_shared);
+}
 bool gemm_fits(int64_t T, int64_t rows, int64_t ldx, int64_t ldh) {
   return T * ldx * 2 <= (int64_t)kOOBRow && rows * ldh * 2 <= (int64_t)kOOBRow;
 }
@@ -499,25 +620,50 @@ hipError_t launch_x_to_f16(const uint16_t* x, uint16_t* y, int T, int H, int ldx
   return hipGetLastError();
 }
 
-hipError_t launch_gemm(const GemmArgs& g, int max_units, hipStream_t s, Tracer* tr) {
+template <int PROJ, int BM, int NS>
+hipError_t launch_gemm_kernel(const GemmArgs& g, long units, int nt, hipStream_t s) {
+  if (units <= 0) return hipSuccess;
+  const dim3 grid((unsigned)(units * nt));
+  // scales through LDS: thin units (for the MFMA-bound fat units the copies
+  // cost more than they save), every K of this projection (hidden; routed
+  // and shared inter) a multiple of 512
+  bool sdw;
+  if (PROJ == 0)
+    sdw = g.H % 512 == 0;
+  else
+    sdw = g.routed.inter % 512 == 0 && (!g.has_shared || g.shared.inter % 512 == 0);
+  sdw = sdw && BM == kBMThin;
+  if (g.wfmt == MOE_WFMT_NVFP4) {
+    if (sdw)
+      hipLaunchKernelGGL((moe_gemm_kernel<MOE_WFMT_NVFP4, PROJ, BM, NS, true>), grid, dim3(256), 0, s, g);
+    else
+      hipLaunchKernelGGL((moe_gemm_kernel<MOE_WFMT_NVFP4, PROJ, BM, NS, false>), grid, dim3(256), 0, s, g);
+  } else {
+    if (sdw)
+      hipLaunchKernelGGL((moe_gemm_kernel<MOE_WFMT_INT4_G32_F16, PROJ, BM, NS, true>), grid, dim3(256),
+                         0, s, g);
+    else
+      hipLaunchKernelGGL((moe_gemm_kernel<MOE_WFMT_INT4_G32_F16, PROJ, BM, NS, false>), grid,
+                         dim3(256), 0, s, g);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm(const GemmArgs& g, int K, int E, hipStream_t s, Tracer* tr) {
   hipError_t e;
   int max_inter = g.routed.inter;
   if (g.has_shared && g.shared.inter > max_inter) max_inter = g.shared.inter;
+  const long fat = fat_units_max(g.T, K, E, g.has_shared);
+  const long thin = thin_units_max(g.T, K, E, g.has_shared);
   // one workgroup per work item (unit, n tile); items past the actual number
   // of units exit at once
-  dim3 g1(max_units * ((max_inter + kGateUpPairs - 1) / kGateUpPairs));
-  if (g.wfmt == MOE_WFMT_NVFP4)
-    hipLaunchKernelGGL((moe_gemm_kernel<MOE_WFMT_NVFP4, 0>), g1, dim3(256), 0, s, g);
-  else
-    hipLaunchKernelGGL((moe_gemm_kernel<MOE_WFMT_INT4_G32_F16, 0>), g1, dim3(256), 0, s, g);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int ntg = (max_inter + kGateUpPairs - 1) / kGateUpPairs;
+  const int ntd = (g.H + kDownRows - 1) / kDownRows;
+  if ((e = launch_gemm_kernel<0, kBM, kNS>(g, fat, ntg, s)) != hipSuccess) return e;
+  if ((e = launch_gemm_kernel<0, kBMThin, kNSThin>(g, thin, ntg, s)) != hipSuccess) return e;
   if (tr && (e = tr->mark("gemm_gateup")) != hipSuccess) return e;
-  dim3 g2(max_units * ((g.H + kDownRows - 1) / kDownRows));
-  if (g.wfmt == MOE_WFMT_NVFP4)
-    hipLaunchKernelGGL((moe_gemm_kernel<MOE_WFMT_NVFP4, 1>), g2, dim3(256), 0, s, g);
-  else
-    hipLaunchKernelGGL((moe_gemm_kernel<MOE_WFMT_INT4_G32_F16, 1>), g2, dim3(256), 0, s, g);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_gemm_kernel<1, kBM, kNS>(g, fat, ntd, s)) != hipSuccess) return e;
+  if ((e = launch_gemm_kernel<1, kBMThin, kNSThin>(g, thin, ntd, s)) != hipSuccess) return e;
   if (tr && (e = tr->mark("gemm_down")) != hipSuccess) return e;
   return hipSuccess;
 }

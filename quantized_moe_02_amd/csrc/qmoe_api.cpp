@@ -92,8 +92,9 @@ hipError_t run_gemm_ffn(const moe_config& c, int T, const uint16_t* x, const Wor
                         const int32_t* sorted_token, bool has_shared, const ExpertSet& shared,
                         int P, int ldh, uint16_t* h, float* o, hipStream_t stream, Tracer* tr) {
   hipError_t e;
+  const int K = has_routed ? c.top_k : 0, E = has_routed ? c.n_routed_experts : 0;
   if ((e = launch_build_units(offsets, has_routed ? active : nullptr,
-                              has_routed ? n_active : nullptr, w.tiles, w.n_tiles, T, P,
+                              has_routed ? n_active : nullptr, w.tiles, w.n_tiles, T, P, K, E,
                               has_shared, stream)) != hipSuccess)
     return e;
   if ((e = launch_x_to_f16(x, w.x16, T, c.hidden, pad_k(c.hidden), stream)) != hipSuccess) return e;
@@ -101,6 +102,7 @@ hipError_t run_gemm_ffn(const moe_config& c, int T, const uint16_t* x, const Wor
   GemmArgs g{};
   g.tiles = w.tiles;
   g.n_tiles = w.n_tiles;
+  g.thin_off = gemm_thin_offset(T, K, E, has_shared);
   g.x16 = w.x16;
   g.ldx = pad_k(c.hidden);
   g.sorted_token = sorted_token;
@@ -115,9 +117,7 @@ hipError_t run_gemm_ffn(const moe_config& c, int T, const uint16_t* x, const Wor
   g.H = c.hidden;
   g.P = P;
   g.wfmt = c.wfmt;
-  const int units = gemm_max_units(T, has_routed ? c.top_k : 0,
-                                   has_routed ? c.n_routed_experts : 0, has_shared);
-  return launch_gemm(g, units, stream, tr);
+  return launch_gemm(g, K, E, stream, tr);
 }
 
 }  // namespace

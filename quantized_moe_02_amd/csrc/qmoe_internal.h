@@ -180,8 +180,9 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, Tracer* tr = nullpt
 
 // Grouped MFMA GEMM path (prefill-shaped calls).
 struct GemmArgs {
-  const int4* tiles;          // work units (see build_units)
-  const int32_t* n_tiles;
+  const int4* tiles;          // work units (see build_units): fat units, then thin ones
+  const int32_t* n_tiles;     // [0]: fat units, [1]: thin units
+  int thin_off;               // index of the first thin unit in tiles
   const uint16_t* x16;        // fp16 activations [T][ldx], zero past H
   int ldx;
   const int32_t* sorted_token;
@@ -201,11 +202,11 @@ __host__ __device__ inline int pad_k(int n) { return (n + 127) & ~127; }
 // Whether the GEMM path's activation buffers (T x ldx fp16 activations, rows x
 // ldh fp16 intermediates) fit its buffer descriptors (2 GiB each).
 bool gemm_fits(int64_t T, int64_t rows, int64_t ldx, int64_t ldh);
-int gemm_unit_tokens();
+int gemm_thin_offset(int T, int K, int E, bool has_shared);
 hipError_t launch_build_units(const int32_t* offsets, const int32_t* active,
                               const int32_t* n_active, int4* tiles, int32_t* n_tiles, int T, int P,
-                              bool has_shared, hipStream_t s);
+                              int K, int E, bool has_shared, hipStream_t s);
 hipError_t launch_x_to_f16(const uint16_t* x, uint16_t* y, int T, int H, int ldx, hipStream_t s);
-hipError_t launch_gemm(const GemmArgs& g, int max_units, hipStream_t s, Tracer* tr = nullptr);
+hipError_t launch_gemm(const GemmArgs& g, int K, int E, hipStream_t s, Tracer* tr = nullptr);
 
 }  // namespace qmoe

@@ -177,6 +177,34 @@ def test_full_decode():
     _full("decode", 1)
 
 
+def test_decode_poisoned_workspace_reused():
+    """Two different single tokens through one workspace whose bytes are all
+    0xFF before the first call: every workspace value a call reads is written
+    by that call first -- in particular the experts' SwiGLU outputs, which
+    are published between workgroups inside one launch before the down
+    projection reads them (a read before the write would see the NaN fill or
+    the previous token's values)."""
+    from helpers import np_u16
+    L = layer("decode")
+    g = L.geom
+    H, k = g["hidden"], g["top_k"]
+    cfg = q.make_config(g, L.wfmt)
+    ws = q.workspace(cfg, 1)
+    ws.fill_(0xFF)
+    for seed in (11, 12):
+        x = synth.make_tokens("decode", 1, "cuda", seed=seed)
+        y = torch.empty(1, H, device="cuda", dtype=torch.float32)
+        ids = torch.empty(1, k, dtype=torch.int32, device="cuda")
+        tw = torch.empty(1, k, dtype=torch.float32, device="cuda")
+        q.moe_layer(cfg, 1, x, L.router_w, L.bias, qexp(L.routed), qexp(L.shared), y,
+                    q.MOE_OUT_F32, ids, tw, ws)
+        torch.cuda.synchronize()
+        assert torch.isfinite(y).all()
+        xn = np_u16(x)
+        ids_g, _ = check_routing(L, ids, tw, x_np=xn)
+        check_outputs(L, y, ids_g, x_np=xn)
+
+
 def test_full_verify4():
     _full("verify4", 4)
 
