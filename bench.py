@@ -82,14 +82,20 @@ def algorithmic(geom, wfmt, T, n_active):
     f_gu = P * 2 * H * I * 2 + T * 2 * H * Is * 2
     f_dn = P * 2 * H * I + T * 2 * H * Is
     sel_b = T * E * 8 + E * 4 + P * 8 + P * 4 * 3 + (E + 1) * 4
+    # a single token with equal routed and shared inter runs the shared
+    # expert's down projection in the selection launch (dec_select_permute)
+    sh_k2 = T == 1 and Is == I and Is > 0
+    sh_dn_b = sb["down"] + T * Is * 2 + T * H * 4 if sh_k2 else 0
+    sh_dn_f = T * 2 * H * Is if sh_k2 else 0
     kern = {
         # small-batch path
         "dec_router_shared": dict(bytes=router_b + sb["gate"] + sb["up"] + x_b + T * E * 8 + T * Is * 2,
                                   flops=T * 2 * H * E + T * 2 * H * Is * 2),
-        "dec_select_permute": dict(bytes=sel_b, flops=0),
+        "dec_select_permute": dict(bytes=sel_b + sh_dn_b, flops=sh_dn_f),
         "dec_gateup": dict(bytes=n_active * (eb["gate"] + eb["up"]) + x_b + P * I * 2,
                            flops=P * 2 * H * I * 2),
-        "dec_down_combine": dict(bytes=w_dn + rows * I * 2 + y_b, flops=f_dn + 2 * P * H),
+        "dec_down_combine": dict(bytes=w_dn + rows * I * 2 + y_b - sh_dn_b + (T * H * 4 if sh_k2 else 0),
+                                 flops=f_dn + 2 * P * H - sh_dn_f),
         # large-batch path
         "route_logits": dict(bytes=router_b + x_b + T * E * 8, flops=T * 2 * H * E),
         "route_select": dict(bytes=T * E * 8 + E * 4 + P * 8, flops=0),
