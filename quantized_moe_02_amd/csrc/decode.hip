@@ -349,6 +349,46 @@ __global__ void __launch_bounds__(256) dec_select_permute_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int K = a.K, P = a.T * a.K;
+  if (a.T == 1) {
+    // One token: its k picks are distinct experts, so the sorted order is the
+    // ascending-id order select_token ranks them in, and every record, slot
+    // and offset follows from (id, weight, rank) in the picking lanes.
+    if (wv != 0) return;
+    int id, rank;
+    float w;
+    select_token(a.logits, a.bias, a.E, a.G, a.TG, K, a.rsf, sc[0], id, w, rank);
+    if (lane < K) {
+      a.ids[rank] = id;
+      a.tw[rank] = w;
+      a.sorted_token[rank] = 0;
+      a.inv_perm[rank] = rank;
+      a.sorted_w[rank] = w;
+      a.active[rank] = id;
+      DecSlot sl;
+      sl.e = id;
+      sl.p0 = rank;
+      sl.M = 1;
+      sl.pad = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sl.t[i] = 0;
+        sl.w[i] = i == 0 ? w : 0.0f;
+      }
+      a.slots[rank] = sl;
+    }
+    if (lane == 0) a.n_active[0] = K;
+    // offsets[x] = number of picks with id < x
+    int cnt[5] = {0, 0, 0, 0, 0};
+    for (int j = 0; j < K; ++j) {
+      const int o = __builtin_amdgcn_readlane(id, j);
+#pragma unroll
+      for (int c = 0; c < 5; ++c) cnt[c] += o < lane + 64 * c ? 1 : 0;
+    }
+#pragma unroll
+    for (int c = 0; c < 5; ++c)
+      if (lane + 64 * c <= a.E) a.offsets[lane + 64 * c] = cnt[c];
+    return;
+  }
   if (wv < a.T) {
     int id, rank;
     float w;
