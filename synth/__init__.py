@@ -243,6 +243,11 @@ def make_bias(recipe: str, n_experts: int, seed: int, device="cpu") -> torch.Ten
         b = torch.zeros(n_experts, dtype=torch.float32)
         b[hot] = HOT_DELTA
         return b.to(device)
+    if recipe == "hot1":
+        # expert 0 far ahead of every other: every token picks it
+        b = torch.zeros(n_experts, dtype=torch.float32)
+        b[0] = 10.0
+        return b.to(device)
     if recipe == "zipf":
         rank = torch.randperm(n_experts, generator=gcpu).to(torch.float64) + 1.0
         return (ZIPF_BETA * rank.pow(-ZIPF_S)).to(torch.float32).to(device)

@@ -146,6 +146,15 @@ EDGE = {
     "nvfp4_T1":  (dict(), 1, "nvfp4", "normal0.1"),
     "nvfp4_T3":  (dict(hidden=96, moe_inter=160, shared_inter=64), 3, "nvfp4", "zipf"),
     "T1_uneven_shared": (dict(moe_inter=64, shared_inter=96), 1, "int4", "normal0.1"),
+    # the GEMM's unit kinds: one expert takes every token, so it gets one full
+    # thin unit (32 tokens), one partial fat unit (33), or a full and a short
+    # fat unit (160)
+    "hot_thin32": (dict(top_k=2), 32, "int4", "hot1"),
+    "hot_fat33": (dict(top_k=2), 33, "int4", "hot1"),
+    "hot_fat160": (dict(top_k=2), 160, "int4", "hot1"),
+    # K a multiple of 512: thin units read their scales through LDS
+    "lds_scales": (dict(hidden=512, moe_inter=512, shared_inter=512), 9, "int4", "normal0.1"),
+    "lds_scales_nvfp4": (dict(hidden=1024, moe_inter=512, shared_inter=512), 11, "nvfp4", "zipf"),
 }
 
 
