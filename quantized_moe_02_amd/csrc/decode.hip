@@ -279,15 +279,18 @@ __global__ void __launch_bounds__(256) dec_router_shared_kernel(DecodeArgs a, in
           rpart[3][threadIdx.x];
     return;
   }
-  // shared expert: all T tokens
+  // shared expert: block (token t, row block j) for t < T; the T blocks of
+  // one row block are nsb apart, so they land on one XCD and share its L2
   const ExpertSet& S = a.shared;
-  const int pair0 = ((int)blockIdx.x - nrb) * kSharedPairsPerBlock + wv * (2 * kSharedRP);
+  const int nsb = (S.inter + kSharedPairsPerBlock - 1) / kSharedPairsPerBlock;
+  const int sb = (int)blockIdx.x - nrb;
+  const int t = sb / nsb;
+  const int pair0 = (sb - t * nsb) * kSharedPairsPerBlock + wv * (2 * kSharedRP);
   if (pair0 >= S.inter) return;
   const float gg = (FMT == MOE_WFMT_NVFP4) ? S.gate.g[0] : 1.0f;
   const float gu = (FMT == MOE_WFMT_NVFP4) ? S.up.g[0] : 1.0f;
-  for (int t = 0; t < a.T; ++t)
-    gateup_wave<FMT, GPL, 2, kSharedRP>(a.x + (size_t)t * a.H, a.H, S.gate, S.up, 0, S.inter,
-                                        pair0, gg, gu, a.h_shared + (size_t)t * a.ldh);
+  gateup_wave<FMT, GPL, 2, kSharedRP>(a.x + (size_t)t * a.H, a.H, S.gate, S.up, 0, S.inter, pair0,
+                                      gg, gu, a.h_shared + (size_t)t * a.ldh);
 }
 
 // ---------------------------------------------------------------------------
@@ -337,6 +340,11 @@ __device__ __forceinline__ void shared_down_rows(const DecodeArgs& a, int blk, i
   }
 }
 
+// Selection and grouping.  What the later kernels read: the per-token ids
+// and weights (outputs of the layer), the selected experts' records (slots,
+// in ascending expert order, each with its picks in pick order), their count,
+// and for each sorted pick p (grouped by expert) its expert and token; the h
+// rows follow the sorted pick order.
 template <int FMT>
 __global__ void __launch_bounds__(256) dec_select_permute_kernel(DecodeArgs a) {
   if (blockIdx.x > 0) {
@@ -344,15 +352,15 @@ __global__ void __launch_bounds__(256) dec_select_permute_kernel(DecodeArgs a) {
     return;
   }
   __shared__ SelectScratch sc[4];
-  __shared__ __attribute__((aligned(16))) int pid[64];
+  __shared__ int pid[64];
   __shared__ float pw[64];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int K = a.K, P = a.T * a.K;
   if (a.T == 1) {
     // One token: its k picks are distinct experts, so the sorted order is the
-    // ascending-id order select_token ranks them in, and every record, slot
-    // and offset follows from (id, weight, rank) in the picking lanes.
+    // ascending-id order select_token ranks them in, and every record follows
+    // from (id, weight, rank) in the picking lanes.
     if (wv != 0) return;
     int id, rank;
     float w;
@@ -360,10 +368,7 @@ __global__ void __launch_bounds__(256) dec_select_permute_kernel(DecodeArgs a) {
     if (lane < K) {
       a.ids[rank] = id;
       a.tw[rank] = w;
-      a.sorted_token[rank] = 0;
-      a.inv_perm[rank] = rank;
-      a.sorted_w[rank] = w;
-      a.active[rank] = id;
+      a.sorted_et[rank] = id;
       DecSlot sl;
       sl.e = id;
       sl.p0 = rank;
@@ -377,16 +382,6 @@ __global__ void __launch_bounds__(256) dec_select_permute_kernel(DecodeArgs a) {
       a.slots[rank] = sl;
     }
     if (lane == 0) a.n_active[0] = K;
-    // offsets[x] = number of picks with id < x
-    int cnt[5] = {0, 0, 0, 0, 0};
-    for (int j = 0; j < K; ++j) {
-      const int o = __builtin_amdgcn_readlane(id, j);
-#pragma unroll
-      for (int c = 0; c < 5; ++c) cnt[c] += o < lane + 64 * c ? 1 : 0;
-    }
-#pragma unroll
-    for (int c = 0; c < 5; ++c)
-      if (lane + 64 * c <= a.E) a.offsets[lane + 64 * c] = cnt[c];
     return;
   }
   if (wv < a.T) {
@@ -403,108 +398,68 @@ __global__ void __launch_bounds__(256) dec_select_permute_kernel(DecodeArgs a) {
   }
   __syncthreads();
   if (wv != 0) return;
-  // Stable sort of the P <= 64 picks by expert, one pick per lane: a pick's
-  // slot = #picks with a smaller id, or the same id and a smaller pick index.
-  // Every lane reads all picks from LDS (broadcast reads, four at a time;
-  // entries past P are masked).
+  // One pick per lane (P <= 64), p = t*k + i.  Sorted order: expert id, then
+  // pick index.  Lanes holding the same expert, and those holding a smaller
+  // one, are found with one ballot per id bit, from the top bit down: `eq`
+  // keeps the lanes that agree with this one on the bits so far, and a lane
+  // that agrees so far but has 0 where this one has 1 is smaller.
   const bool have = lane < P;
-  const int e = have ? pid[lane] : 0x7fffffff;
-  int pos = 0, dup = 0;
-  for (int q = 0; q < P; q += 4) {
-    const int4 o4 = *reinterpret_cast<const int4*>(&pid[q]);
-    const int o[4] = {o4.x, o4.y, o4.z, o4.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool in = q + i < P;
-      pos += (in && (o[i] < e || (o[i] == e && q + i < lane))) ? 1 : 0;
-      dup |= (in && o[i] == e && q + i < lane) ? 1 : 0;
-    }
+  const int e = have ? pid[lane] : 0;
+  int nbits = 0;
+  while ((1 << nbits) < a.E) ++nbits;
+  uint64_t eq = __ballot(have), lt = 0;
+  for (int bit = nbits - 1; bit >= 0; --bit) {
+    const bool set = (e >> bit) & 1;
+    const uint64_t b = __ballot(have && set);
+    lt |= set ? (eq & ~b) : 0ull;
+    eq &= set ? b : ~b;
   }
-  if (have) {
-    a.sorted_token[pos] = lane / K;
-    a.inv_perm[lane] = pos;
-    a.sorted_w[pos] = pw[lane];
-  }
-  // distinct experts in ascending order: a pick is the first of its expert if
-  // no earlier pick has the same id; its rank among the firsts orders them.
-  // offsets[x] = #picks with id < x, for x = 0..E.
-  const bool first = have && !dup;
+  const uint64_t below = (1ull << lane) - 1ull;
+  const int pos = __popcll(lt) + __popcll(eq & below);
+  const bool first = have && (eq & below) == 0;
   const uint64_t firsts = __ballot(first);
-  int arank = 0;
-  int cnt[5] = {0, 0, 0, 0, 0};
-  for (int q = 0; q < P; q += 4) {
-    const int4 o4 = *reinterpret_cast<const int4*>(&pid[q]);
-    const int o[4] = {o4.x, o4.y, o4.z, o4.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool in = q + i < P;
-      arank += (in && ((firsts >> (q + i)) & 1ull) && o[i] < e) ? 1 : 0;
-#pragma unroll
-      for (int j = 0; j < 5; ++j) cnt[j] += (in && o[i] < lane + 64 * j) ? 1 : 0;
-    }
-  }
+  if (have) a.sorted_et[pos] = e | ((lane / K) << 16);
   if (first) {
-    a.active[arank] = e;
-    // the expert's record: its picks in pick order (at most one per token)
+    // the expert's record: its picks (the lanes in eq) in pick order, at most
+    // one per token, so at most four
     DecSlot sl;
     sl.e = e;
     sl.p0 = pos;
+    sl.M = __popcll(eq);
     sl.pad = 0;
-    int M = 0;
+    uint64_t rem = eq;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sl.t[i] = 0;
-      sl.w[i] = 0.0f;
+    for (int m = 0; m < 4; ++m) {
+      const int l = rem ? (int)__builtin_ctzll(rem) : lane;
+      rem &= rem - 1ull;
+      sl.t[m] = m < sl.M ? l / K : 0;
+      sl.w[m] = m < sl.M ? pw[l] : 0.0f;
     }
-    for (int tt = 0; tt < a.T; ++tt) {
-      int found = -1;
-      for (int j = 0; j < K; ++j) found = pid[tt * K + j] == e ? tt * K + j : found;
-      if (found >= 0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sl.t[i] = i == M ? tt : sl.t[i];
-          sl.w[i] = i == M ? pw[found] : sl.w[i];
-        }
-        ++M;
-      }
-    }
-    sl.M = M;
-    a.slots[arank] = sl;
+    a.slots[__popcll(lt & firsts)] = sl;
   }
   if (lane == 0) a.n_active[0] = __popcll(firsts);
-#pragma unroll
-  for (int j = 0; j < 5; ++j)
-    if (lane + 64 * j <= a.E) a.offsets[lane + 64 * j] = cnt[j];
 }
 
 // ---------------------------------------------------------------------------
-// K3: gate/up of the selected experts.  Block = (row block, slot); each wave
-// runs the double-buffered GEMV over its row pairs, once per token routed to
-// the expert (a second token re-reads the rows, mostly from cache).
+// K3: gate/up of the selected experts.  Block = (row block, sorted pick p):
+// the double-buffered GEMV of the pick's expert over the block's row pairs
+// for the pick's token, written to h row p.  Picks of one expert sit next to
+// each other, so the blocks that share its weights run together on one XCD
+// and the later ones read them from L2.
 // ---------------------------------------------------------------------------
 template <int FMT, int GPL>
 __global__ void __launch_bounds__(256) dec_gateup_kernel(DecodeArgs a) {
-  const int slot = blockIdx.y;
-  // the count and the slot's record are fetched together (one round trip)
-  const int na = __builtin_amdgcn_readfirstlane(*a.n_active);
-  const DecSlot sl = a.slots[slot];
-  if (slot >= na) return;
+  const int p = blockIdx.y;
+  const int et = __builtin_amdgcn_readfirstlane(a.sorted_et[p]);
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const ExpertSet& R = a.routed;
   const int pair0 = blockIdx.x * kPairsPerBlock + wv * kPairsPerWave;
   if (pair0 >= R.inter) return;
-  const int e = __builtin_amdgcn_readfirstlane(sl.e);
-  const int p0 = __builtin_amdgcn_readfirstlane(sl.p0);
-  const int M = __builtin_amdgcn_readfirstlane(sl.M);
+  const int e = et & 0xffff, t = et >> 16;
   const float gg = (FMT == MOE_WFMT_NVFP4) ? R.gate.g[e] : 1.0f;
   const float gu = (FMT == MOE_WFMT_NVFP4) ? R.up.g[e] : 1.0f;
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    if (m >= M) break;
-    const int t = __builtin_amdgcn_readfirstlane(sl.t[m]);
-    gateup_wave<FMT, GPL>(a.x + (size_t)t * a.H, a.H, R.gate, R.up, (size_t)e * R.inter, R.inter,
-                          pair0, gg, gu, a.h_routed + (size_t)(p0 + m) * a.ldh);
-  }
+  gateup_wave<FMT, GPL>(a.x + (size_t)t * a.H, a.H, R.gate, R.up, (size_t)e * R.inter, R.inter,
+                        pair0, gg, gu, a.h_routed + (size_t)p * a.ldh);
 }
 
 // ---------------------------------------------------------------------------
@@ -856,6 +811,274 @@ __host__ __device__ inline bool down_t1_fits(const DecodeArgs& a) {
          (long long)a.E * a.H * nG * 2 < 0xFFFFFFFFll;
 }
 
+// ---------------------------------------------------------------------------
+// K4 for 2..4 tokens (short verify batches): down projection of the selected
+// experts and the shared expert, combined into y.
+//
+// One workgroup per CU.  The SwiGLU outputs of all P = T*k picks (rows
+// 0..P-1, sorted pick order) and of the shared expert (rows P..P+T-1) are
+// staged in LDS once: quarter q of group c of row j at 16-byte slot
+// (j * 4 + q) * 64 + c, groups past the row's last one zero, so 64 lanes read
+// 1 KB contiguous at offsets that are compile-time constants.  Next to them,
+// the int4 code-offset term of every (row, group).  Each wave then streams whole
+// output rows: for row r and slot s, lane c loads group c of expert s's row r
+// (inter <= 2048) and applies it to every token routed to s.  The (row, slot)
+// items of a wave form one sequence with kDMDepth items in flight; the sum
+// runs in slot order within a lane, then across the lanes, independent of
+// timing.  The work is bound by the dequantisation and dot products, so each
+// item's codes are dequantised once for all its tokens.
+// ---------------------------------------------------------------------------
+#ifndef QMOE_DM_DEPTH
+#define QMOE_DM_DEPTH 12
+#endif
+#ifndef QMOE_DM_WAVES
+#define QMOE_DM_WAVES 8
+#endif
+constexpr int kDMDepth = QMOE_DM_DEPTH;   // (row, slot) items in flight per wave
+constexpr int kDMWaves = QMOE_DM_WAVES;   // waves per workgroup
+constexpr int kDMRows = 36;               // h rows held in LDS (P + T)
+constexpr int kDMChunks = kDMRows * 256;  // 16-byte chunks: 4 quarters x 64 groups per row
+static_assert(kDMChunks % (64 * kDMWaves) == 0, "h chunks split evenly over the threads");
+
+template <int FMT>
+__global__ void __launch_bounds__(64 * kDMWaves) dec_down_multi_kernel(DecodeArgs a) {
+  __shared__ uint4 hl[kDMChunks];
+  __shared__ float hsl[kDMRows * 64];
+  constexpr int NT = 64 * kDMWaves;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int H = a.H, T = a.T, P = a.T * a.K;
+  // the count and the records are fetched together; lanes at or past the
+  // count hold stale records that are never read
+  const DecSlot rec = a.slots[lane];
+  const int nr = __builtin_amdgcn_readfirstlane(*a.n_active);
+  const bool shared = a.has_shared;
+  const int ns = nr + (shared ? 1 : 0);
+  const int nG = a.routed.inter / 32;
+  const int nrows = P + (shared ? T : 0);
+  const uint32_t rowBytes = (uint32_t)nG * 16u, srow = (uint32_t)nG * 2u;
+
+  // slot `lane`'s record: weight row base, tokens, weights, first h row
+  const bool sh_lane = shared && lane == nr;
+  const bool rt_lane = lane < nr;
+  const uint32_t m_row = rt_lane ? (uint32_t)rec.e * (uint32_t)H : 0u;
+  // tokens as a bit mask, weights by token (zero where absent); the slot's
+  // h rows are p0 + (rank of the token in the mask)
+  const int m_p0 = sh_lane ? P : rec.p0;
+  int m_mask = sh_lane ? (1 << T) - 1 : 0;
+  float m_wt[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) m_wt[t] = sh_lane && t < T ? 1.0f : 0.0f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const bool has = !sh_lane && m < rec.M;
+    m_mask |= has ? 1 << (rec.t[m] & 3) : 0;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) m_wt[t] = has && rec.t[m] == t ? rec.w[m] : m_wt[t];
+  }
+  float m_g = 1.0f;
+  if (FMT == MOE_WFMT_NVFP4) {
+    if (rt_lane) m_g = a.routed.down.g[rec.e];
+    if (sh_lane) m_g = a.shared.down.g[0];
+  }
+  const rsrc_t rq = make_rsrc(a.routed.down.q, 0xFFFFFFFFu);
+  const rsrc_t rs = make_rsrc(a.routed.down.s, 0xFFFFFFFFu);
+  const rsrc_t sq = make_rsrc(a.shared.down.q, shared ? 0xFFFFFFFFu : 0u);
+  const rsrc_t ss = make_rsrc(a.shared.down.s, shared ? 0xFFFFFFFFu : 0u);
+  // lanes past the row's last group load group 0 and meet zero h
+  const uint32_t c = lane < nG ? (uint32_t)lane : 0u;
+
+  // this wave's items: rows gw, gw + nw, ...; slots 0 .. ns-1 within a row
+  const int gw = blockIdx.x * kDMWaves + wv, nw = gridDim.x * kDMWaves;
+  const int nrw = gw < H ? (H - gw + nw - 1) / nw : 0;
+  const int N = nrw * ns;
+
+  // h of every row, in LDS order: all of this thread's loads are issued
+  // before the first weight items', so they do not queue behind them
+  constexpr int kStPer = kDMChunks / NT;   // 16-byte chunks per thread
+  uint32_t hv[kStPer][4];
+  static_for<kStPer>([&](auto U) {   // fully unrolled, so hv stays in registers
+    constexpr int u = decltype(U)::value;
+    const int L = (int)threadIdx.x + u * NT;          // LDS chunk
+    const int g = L & 63, jq = L >> 6, j = jq >> 2, q = jq & 3;
+    // chunks outside the staged rows or past the last group reload a valid
+    // one and are stored as zero
+    const bool in = j < nrows && g < nG;
+    const int jj = in ? j : 0, gg = in ? g : 0;
+    const uint16_t* src = jj < P ? a.h_routed + (size_t)jj * a.ldh : a.h_shared + (size_t)(jj - P) * a.ldh;
+    load16(hv[u], src + gg * 32 + q * 8);
+  });
+  __builtin_amdgcn_sched_barrier(0);   // keep the h loads ahead of the weight loads
+
+  uint32_t wq[kDMDepth][4], wsc[kDMDepth];
+  int is = 0, ir = gw < H ? gw : 0, iss = 0;   // next item to issue: slot, row, index
+  // Items past the last one reload the last one (in bounds) and are never
+  // computed, so every step issues the same loads; a wave without rows loads
+  // row 0 of slot 0.  (Issuing the first items under a condition would leave
+  // the compiler unsure of the load order and make every wait a full one.)
+  auto issue = [&](auto B) {
+    constexpr int b = decltype(B)::value;
+    const int sl = __builtin_amdgcn_readfirstlane(is);
+    const bool sh = shared && sl == nr;
+    const uint32_t row = (uint32_t)__builtin_amdgcn_readlane((int)m_row, sl) + (uint32_t)ir;
+    bload16(wq[b], sh ? sq : rq, c * 16u, row * rowBytes);
+    wsc[b] = bload_u16(sh ? ss : rs, c * 2u, row * srow);
+    if (iss < N - 1) {
+      ++iss;
+      if (++is == ns) {
+        is = 0;
+        ir += nw;
+      }
+    }
+  };
+  static_for<kDMDepth>([&](auto B) { issue(B); });
+  __builtin_amdgcn_sched_barrier(0);
+
+  static_for<kStPer>([&](auto U) {
+    constexpr int u = decltype(U)::value;
+    const int L = (int)threadIdx.x + u * NT;
+    const int g = L & 63, j = L >> 8;
+    const bool in = j < nrows && g < nG;
+    hl[L] = in ? make_uint4(hv[u][0], hv[u][1], hv[u][2], hv[u][3]) : make_uint4(0, 0, 0, 0);
+  });
+  __syncthreads();
+  if (FMT == MOE_WFMT_INT4_G32_F16) {
+    for (int i = threadIdx.x; i < kDMRows * 64; i += NT) {
+      const int j = i >> 6, g = i & 63;
+      uint32_t hm[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4 v = hl[(j * 4 + q) * 64 + g];
+        hm[4 * q] = v.x; hm[4 * q + 1] = v.y; hm[4 * q + 2] = v.z; hm[4 * q + 3] = v.w;
+      }
+      // the code offsets of the dequantisation below: 1032 per even-pair
+      // input, 72 per odd-pair input
+      float se = 0.0f, so = 0.0f;
+#pragma unroll
+      for (int m = 0; m < 16; m += 2) {
+        se = dot2_f16(hm[m], 0x3C003C00u, se);
+        so = dot2_f16(hm[m + 1], 0x3C003C00u, so);
+      }
+      hsl[i] = fmaf(1032.0f, se, 72.0f * so);
+    }
+    __syncthreads();
+  }
+  if (N == 0) return;
+
+  int cs = 0, cr = 0;    // next item to compute: slot, row index within the wave
+  float y0 = 0.0f, y1 = 0.0f, y2 = 0.0f, y3 = 0.0f;
+  // one accumulator per token
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  const uint4* hlane = hl + lane;
+  const float* hslane = hsl + lane;
+  auto compute = [&](auto B) {
+    constexpr int b = decltype(B)::value;
+    const int sl = __builtin_amdgcn_readfirstlane(cs);
+    const uint32_t mask = (uint32_t)__builtin_amdgcn_readlane(m_mask, sl);
+    const int p0 = __builtin_amdgcn_readlane(m_p0, sl);
+    // the codes as 16-bit float pairs, once for all tokens of the slot
+    uint32_t wf[16];
+    float sc0, sc1 = 0.0f;
+    if constexpr (FMT == MOE_WFMT_INT4_G32_F16) {
+      // or-ing a code u into the mantissa of fp16 1024 gives 1024 + u (nibble
+      // at bits 0-3 of a half) or 1024 + 16 u (bits 4-7): even pairs the
+      // first, odd pairs the second, one shift by 8 per word for pairs 2, 3
+      const uint32_t one = 0x64006400u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w = wq[b][j], w8 = w >> 8;
+        wf[4 * j + 0] = and_or(w, 0x000F000Fu, one);
+        wf[4 * j + 1] = and_or(w, 0x00F000F0u, one);
+        wf[4 * j + 2] = and_or(w8, 0x000F000Fu, one);
+        wf[4 * j + 3] = and_or(w8, 0x00F000F0u, one);
+      }
+      sc0 = half_bits_to_f32(wsc[b] & 0xffffu);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) wf[4 * j + k] = fp4_pair_f16(wq[b][j], k);
+      const float g = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m_g), sl));
+      sc0 = e4m3_to_f32(wsc[b], 0) * g;
+      sc1 = e4m3_to_f32(wsc[b], 1) * g;
+    }
+    // token t (a compile-time index, so its accumulator is a fixed register)
+    // under a uniform branch on the slot's mask
+    static_for<4>([&](auto TT) {
+      constexpr int t = decltype(TT)::value;
+      if (mask & (1u << t)) {
+        const int j = p0 + __builtin_popcount(mask & ((1u << t) - 1u));
+        uint32_t hm[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint4 v = hlane[(j * 4 + q) * 64];
+          hm[4 * q] = v.x; hm[4 * q + 1] = v.y; hm[4 * q + 2] = v.z; hm[4 * q + 3] = v.w;
+        }
+        float v;
+        if constexpr (FMT == MOE_WFMT_INT4_G32_F16) {
+          // sum (u - 8) h = d_even + d_odd / 16 - (1032 A_even + 72 A_odd),
+          // the last term staged with h
+          float de = 0.0f, dd = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 16; i += 2) {
+            de = dot2_f16(wf[i], hm[i], de);
+            dd = dot2_f16(wf[i + 1], hm[i + 1], dd);
+          }
+          v = sc0 * (fmaf(0.0625f, dd, de) - hslane[j * 64]);
+        } else {
+          float d0 = 0.0f, d1 = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) d0 = dot2_f16(wf[i], hm[i], d0);
+#pragma unroll
+          for (int i = 8; i < 16; ++i) d1 = dot2_f16(wf[i], hm[i], d1);
+          v = fmaf(sc0, d0, sc1 * d1);
+        }
+        const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m_wt[t]), sl));
+        acc[t] = fmaf(w, v, acc[t]);
+      }
+    });
+    if (++cs == ns) {
+      // row k's sums go to lane k; y is written after the loop, so no store
+      // sits between the loads and their use
+      const float v0 = wave_sum(acc[0]), v1 = wave_sum(acc[1]);
+      const float v2 = wave_sum(acc[2]), v3 = wave_sum(acc[3]);
+      const bool mine = lane == cr;
+      y0 = mine ? v0 : y0;
+      y1 = mine ? v1 : y1;
+      y2 = mine ? v2 : y2;
+      y3 = mine ? v3 : y3;
+      acc[0] = acc[1] = acc[2] = acc[3] = 0.0f;
+      cs = 0;
+      ++cr;
+    }
+  };
+  for (int i0 = 0; i0 < N; i0 += kDMDepth) {
+    static_for<kDMDepth>([&](auto B) {
+      if (i0 + decltype(B)::value < N) compute(B);
+      issue(B);
+    });
+  }
+  if (lane < nrw) {
+    const int r = gw + lane * nw;
+    store_y(a, 0, r, y0);
+    store_y(a, 1, r, y1);
+    if (T > 2) store_y(a, 2, r, y2);
+    if (T > 3) store_y(a, 3, r, y3);
+  }
+}
+
+// Whether the 2..4-token down kernel covers this shape.
+__host__ __device__ inline bool down_multi_fits(const DecodeArgs& a) {
+  const long long nG = a.routed.inter / 32;
+  const long long P = (long long)a.T * a.K;
+  return a.T >= 2 && a.T <= kMaxT && nG <= 64 && P + (a.has_shared ? 1 : 0) <= 64 &&
+         (!a.has_shared || a.shared.inter == a.routed.inter) &&
+         P + (a.has_shared ? a.T : 0) <= kDMRows &&
+         (a.H + 256 * kDMWaves - 1) / (256 * kDMWaves) <= 64 &&
+         (long long)a.E * a.H * (a.routed.inter / 2) < 0xFFFFFFFFll &&
+         (long long)a.E * a.H * nG * 2 < 0xFFFFFFFFll;
+}
+
 template <int GPL>
 hipError_t launch_k1(const DecodeArgs& a, hipStream_t s, int nrb, int nsb) {
   if (a.wfmt == MOE_WFMT_NVFP4)
@@ -886,7 +1109,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
   const int gpl = (a.H / 32 + 63) / 64;
   const int nrb = a.E;
   const int nsb =
-      a.has_shared ? (a.shared.inter + kSharedPairsPerBlock - 1) / kSharedPairsPerBlock : 0;
+      a.has_shared ? a.T * ((a.shared.inter + kSharedPairsPerBlock - 1) / kSharedPairsPerBlock) : 0;
   const bool f4 = a.wfmt == MOE_WFMT_NVFP4;
   switch (gpl) {
     case 1: e = launch_k1<1>(a, s, nrb, nsb); break;
@@ -908,8 +1131,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (tr && (e = tr->mark("dec_select_permute")) != hipSuccess) return e;
 
-  const int slots = a.E < a.T * a.K ? a.E : a.T * a.K;
-  dim3 g3((a.routed.inter + kPairsPerBlock - 1) / kPairsPerBlock, slots);
+  dim3 g3((a.routed.inter + kPairsPerBlock - 1) / kPairsPerBlock, a.T * a.K);
   switch (gpl) {
     case 1: e = launch_k3<1>(a, s, g3); break;
     case 2: e = launch_k3<2>(a, s, g3); break;
@@ -929,6 +1151,13 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
     else
       hipLaunchKernelGGL((dec_down_t1_kernel<MOE_WFMT_INT4_G32_F16>), dim3(blocks), dim3(256), lds, s,
                          a2);
+  } else if (down_multi_fits(a)) {
+    const int blocks = std::min((a.H + kDMWaves - 1) / kDMWaves, 256);
+    if (f4)
+      hipLaunchKernelGGL((dec_down_multi_kernel<MOE_WFMT_NVFP4>), dim3(blocks), dim3(64 * kDMWaves), 0, s, a);
+    else
+      hipLaunchKernelGGL((dec_down_multi_kernel<MOE_WFMT_INT4_G32_F16>), dim3(blocks), dim3(64 * kDMWaves), 0,
+                         s, a);
   } else if (a.T == 1) {
     if (f4)
       hipLaunchKernelGGL((dec_down_combine_kernel<MOE_WFMT_NVFP4, 1>), g4, dim3(256), 0, s, a);

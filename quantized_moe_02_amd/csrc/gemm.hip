@@ -178,16 +178,6 @@ using ic = std::integral_constant<int, N>;
 constexpr int kNS = 4;            // K blocks in flight (LDS stages, weight register ring)
 constexpr int kRT = 4;            // 16-row weight tiles per wave
 
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-// f(integral_constant<int, j>) for j = 0 .. N-1
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
 // Work item -> (unit, n tile).  Workgroups are dispatched round-robin over
 // the 8 XCDs; this maps the items that one XCD receives onto a contiguous
 // range, n tile fastest, so that the n tiles of one token tile run on the same

@@ -151,6 +151,7 @@ Workspace carve_workspace(const moe_config& c, int T, void* base) {
       take((size_t)gemm_max_units(T, (int)K, (int)E, c.n_shared_experts == 1) * 4 * sizeof(int32_t));
   const size_t o_ntiles = take(4 * sizeof(int32_t));
   const size_t o_dslots = take(kDecMaxSlots * sizeof(DecSlot));
+  const size_t o_dpick = take(kDecMaxSlots * sizeof(int32_t));
   const size_t o_phist = take(permute_hist_ints(T, (int)E) * sizeof(int32_t));
   w.total = off;
   if (base) {
@@ -170,6 +171,7 @@ Workspace carve_workspace(const moe_config& c, int T, void* base) {
     w.tiles = reinterpret_cast<int4*>(b + o_tiles);
     w.n_tiles = reinterpret_cast<int32_t*>(b + o_ntiles);
     w.dslots = reinterpret_cast<DecSlot*>(b + o_dslots);
+    w.dpick = reinterpret_cast<int32_t*>(b + o_dpick);
     w.phist = reinterpret_cast<int32_t*>(b + o_phist);
   }
   return w;
@@ -375,6 +377,7 @@ moe_status layer_impl(const moe_config* cfg, int32_t T, const uint16_t* x, const
     d.n_active = w.n_active;
     d.sorted_w = w.sorted_w;
     d.slots = w.dslots;
+    d.sorted_et = w.dpick;
     d.routed = expert_set(*routed, cfg->moe_inter);
     d.has_shared = has_shared;
     if (has_shared) d.shared = expert_set(*shared, cfg->shared_inter);

@@ -4,12 +4,16 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 #include "qmoe_internal.h"
 
 namespace qmoe {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
@@ -254,6 +258,16 @@ __device__ __forceinline__ void wave_argmax(double& v, int& i) {
   argmax_dpp<kDppMirror>(v, i);
   argmax_swap<16>(v, i);
   argmax_swap<32>(v, i);
+}
+
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+// f(integral_constant<int, j>) for j = 0 .. N-1
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) {

@@ -50,6 +50,7 @@ struct Workspace {
   uint16_t* x16;          // [T][H]     fp16 activations (GEMM path)
   int4* tiles;            // [max units] GEMM work units
   DecSlot* dslots;        // [kDecMaxSlots] decode path: selected experts
+  int32_t* dpick;         // [kDecMaxSlots] decode path: expert | token << 16 of each sorted pick
   int32_t* n_tiles;       // [4]
   int32_t* phist;         // [permute_hist_ints] permutation scratch
   size_t total;
@@ -164,6 +165,7 @@ struct DecodeArgs {
   int32_t* n_active;
   float* sorted_w;
   DecSlot* slots;
+  int32_t* sorted_et;     // [P] expert (low 16 bits) and token (high 16 bits) of sorted pick p
   ExpertSet routed;
   bool has_shared;
   ExpertSet shared;

@@ -152,6 +152,19 @@ EDGE = {
     "hot_thin32": (dict(top_k=2), 32, "int4", "hot1"),
     "hot_fat33": (dict(top_k=2), 33, "int4", "hot1"),
     "hot_fat160": (dict(top_k=2), 160, "int4", "hot1"),
+    # 2..4 tokens: the small-batch down kernel that stages h in LDS (several
+    # tokens per expert, no shared expert, one group per row, full 64-group
+    # rows), and shapes that fall back to the per-block kernel (65 slots,
+    # shared inter != routed inter)
+    "T2": (dict(), 2, "int4", "normal0.1"),
+    "T4": (dict(), 4, "int4", "normal0.1"),
+    "T4_hot": (dict(top_k=2), 4, "int4", "hot1"),
+    "T4_no_shared": (dict(n_shared_experts=0), 4, "int4", "normal0.1"),
+    "T4_min_dims": (dict(hidden=32, moe_inter=32, shared_inter=32), 4, "int4", "normal0.1"),
+    "T4_inter2048": (dict(hidden=512, moe_inter=2048, shared_inter=2048), 4, "int4", "zipf"),
+    "T4_k16": (dict(n_routed_experts=64, n_group=4, topk_group=4, top_k=16), 4, "int4", "normal0.1"),
+    "T3_uneven_shared": (dict(moe_inter=64, shared_inter=96), 3, "int4", "normal0.1"),
+    "nvfp4_T4": (dict(), 4, "nvfp4", "zipf"),
     # K a multiple of 512: thin units read their scales through LDS
     "lds_scales": (dict(hidden=512, moe_inter=512, shared_inter=512), 9, "int4", "normal0.1"),
     "lds_scales_nvfp4": (dict(hidden=1024, moe_inter=512, shared_inter=512), 11, "nvfp4", "zipf"),
