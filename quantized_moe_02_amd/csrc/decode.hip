@@ -5,15 +5,19 @@
 // loads in flight and doing as little else as possible.
 //
 //   K1 dec_router_shared   router logits (float64, one wave per expert) and,
-//                          in the same launch, the shared expert's gate/up
-//                          GEMV, which does not depend on the routing
+//                          for one token, in the same launch, the shared
+//                          expert's gate/up GEMV, which does not depend on
+//                          the routing (for more tokens it runs in K3)
 //   K2 dec_select_permute  one workgroup: per-token selection (one wave per
-//                          token) and the batch-union permutation of the
-//                          <= 64 picks
-//   K3 dec_gateup          gate/up GEMV of the selected experts with SwiGLU
-//   K4 dec_down_combine    down GEMV of every selected expert and the shared
-//                          expert for a block of output rows, with the
-//                          weighted combine done in registers
+//                          token) and the grouping of the <= 64 picks by
+//                          expert (batch union); for one token, the shared
+//                          expert's down GEMV in the other workgroups
+//   K3 dec_gateup          gate/up GEMV of every pick's expert with SwiGLU
+//   K4                     down GEMV of every selected expert (and the shared
+//                          expert) with the weighted combine in registers:
+//                          dec_down_t1 (one token), dec_down_multi (2..4
+//                          tokens, SwiGLU outputs staged in LDS) or
+//                          dec_down_combine (other shapes)
 //
 // Pages: "Show HN: Menjalankan GLM 5.2 di komputer lambat" (sections "Cara
 // kerja eksekusi MoE" -- routed experts vs resident shared expert -- and
@@ -29,7 +33,7 @@ namespace qmoe {
 namespace {
 
 #ifndef QMOE_DEC_RPW
-#define QMOE_DEC_RPW 2
+#define QMOE_DEC_RPW 1
 #endif
 #ifndef QMOE_DEC_ITEMS
 #define QMOE_DEC_ITEMS 4
@@ -100,6 +104,61 @@ __device__ __forceinline__ float act_sum(const uint32_t (&act)[16]) {
   for (int i = 0; i < 16; ++i)
     s = F16ACT ? dot2_f16(act[i], 0x3C003C00u, s) : dot2_bf16(act[i], 0x3F803F80u, s);
   return s;
+}
+
+// int4 codes against fp16 activations (the SwiGLU outputs h): or-ing a code u
+// into the mantissa of fp16 1024 gives 1024 + u (nibble at bits 0-3 of a
+// half) or 1024 + 16 u (bits 4-7), so pairs 0 and 1 of a word take one
+// v_and_or_b32 each and pairs 2 and 3 share one shift by 8.  Over a group,
+//   sum (u - 8) a = d_even + d_odd / 16 - (1032 A_even + 72 A_odd)
+// with d_even / d_odd the dot products over the even / odd pairs and A_even /
+// A_odd the activation sums over them; the last term depends on the
+// activations only (int4_offset) and is computed once per group of h.
+__device__ __forceinline__ void int4_f16_1024(const uint32_t (&wq)[4], uint32_t (&wf)[16]) {
+  const uint32_t one = 0x64006400u;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t w = wq[j], w8 = w >> 8;
+    wf[4 * j + 0] = and_or(w, 0x000F000Fu, one);
+    wf[4 * j + 1] = and_or(w, 0x00F000F0u, one);
+    wf[4 * j + 2] = and_or(w8, 0x000F000Fu, one);
+    wf[4 * j + 3] = and_or(w8, 0x00F000F0u, one);
+  }
+}
+__device__ __forceinline__ float int4_dot_1024(const uint32_t (&wf)[16], const uint32_t (&act)[16]) {
+  float de = 0.0f, dd = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) {
+    de = dot2_f16(wf[i], act[i], de);
+    dd = dot2_f16(wf[i + 1], act[i + 1], dd);
+  }
+  return fmaf(0.0625f, dd, de);
+}
+__device__ __forceinline__ float int4_offset(const uint32_t (&act)[16]) {
+  float se = 0.0f, so = 0.0f;
+#pragma unroll
+  for (int m = 0; m < 16; m += 2) {
+    se = dot2_f16(act[m], 0x3C003C00u, se);
+    so = dot2_f16(act[m + 1], 0x3C003C00u, so);
+  }
+  return fmaf(1032.0f, se, 72.0f * so);
+}
+// One group against fp16 activations.  int4: `off` = int4_offset(act);
+// nvfp4: `off` unused, gs the per-tensor scale.
+template <int FMT>
+__device__ __forceinline__ float group_dot_h(const uint32_t (&wq)[4], uint32_t sc,
+                                             const uint32_t (&act)[16], float off, float gs) {
+  if constexpr (FMT == MOE_WFMT_INT4_G32_F16) {
+    uint32_t wf[16];
+    int4_f16_1024(wq, wf);
+    return half_bits_to_f32(sc & 0xffffu) * (int4_dot_1024(wf, act) - off);
+  } else {
+    return group_dot<FMT, true>(wq, sc, act, 0.0f, gs);
+  }
+}
+template <int FMT>
+__device__ __forceinline__ float offset_h(const uint32_t (&act)[16]) {
+  return FMT == MOE_WFMT_INT4_G32_F16 ? int4_offset(act) : 0.0f;
 }
 
 // ---------------------------------------------------------------------------
@@ -222,7 +281,8 @@ __device__ __forceinline__ void gateup_wave(const uint16_t* __restrict__ x, int 
 }
 
 // ---------------------------------------------------------------------------
-// K1: router logits (blocks [0, nrb)) and shared-expert gate/up (the rest)
+// K1: router logits (blocks [0, nrb)) and, for one token, the shared
+// expert's gate/up (the rest)
 // ---------------------------------------------------------------------------
 template <int FMT, int GPL>
 __global__ void __launch_bounds__(256) dec_router_shared_kernel(DecodeArgs a, int nrb) {
@@ -279,18 +339,14 @@ __global__ void __launch_bounds__(256) dec_router_shared_kernel(DecodeArgs a, in
           rpart[3][threadIdx.x];
     return;
   }
-  // shared expert: block (token t, row block j) for t < T; the T blocks of
-  // one row block are nsb apart, so they land on one XCD and share its L2
+  // shared expert (one token): row block blockIdx.x - nrb
   const ExpertSet& S = a.shared;
-  const int nsb = (S.inter + kSharedPairsPerBlock - 1) / kSharedPairsPerBlock;
-  const int sb = (int)blockIdx.x - nrb;
-  const int t = sb / nsb;
-  const int pair0 = (sb - t * nsb) * kSharedPairsPerBlock + wv * (2 * kSharedRP);
+  const int pair0 = ((int)blockIdx.x - nrb) * kSharedPairsPerBlock + wv * (2 * kSharedRP);
   if (pair0 >= S.inter) return;
   const float gg = (FMT == MOE_WFMT_NVFP4) ? S.gate.g[0] : 1.0f;
   const float gu = (FMT == MOE_WFMT_NVFP4) ? S.up.g[0] : 1.0f;
-  gateup_wave<FMT, GPL, 2, kSharedRP>(a.x + (size_t)t * a.H, a.H, S.gate, S.up, 0, S.inter, pair0,
-                                      gg, gu, a.h_shared + (size_t)t * a.ldh);
+  gateup_wave<FMT, GPL, 2, kSharedRP>(a.x, a.H, S.gate, S.up, 0, S.inter, pair0, gg, gu,
+                                      a.h_shared);
 }
 
 // ---------------------------------------------------------------------------
@@ -317,7 +373,7 @@ __device__ __forceinline__ void shared_down_rows(const DecodeArgs& a, int blk, i
     const uint4 v = *reinterpret_cast<const uint4*>(a.h_shared + c * 32 + 8 * i);
     hm[4 * i] = v.x; hm[4 * i + 1] = v.y; hm[4 * i + 2] = v.z; hm[4 * i + 3] = v.w;
   }
-  const float hs = FMT == MOE_WFMT_INT4_G32_F16 ? act_sum<true>(hm) : 0.0f;
+  const float hs = offset_h<FMT>(hm);
   const float g = FMT == MOE_WFMT_NVFP4 ? S.down.g[0] : 1.0f;
   const int gw = blk * 4 + wv, nw = nblk * 4;
   uint32_t w[2][4], sc[2];
@@ -329,7 +385,7 @@ __device__ __forceinline__ void shared_down_rows(const DecodeArgs& a, int blk, i
   auto step = [&](auto B, int r) {
     constexpr int b = decltype(B)::value;
     if (r + nw < H) ld(std::integral_constant<int, b ^ 1>{}, r + nw);
-    const float d = group_dot<FMT, true>(w[b], sc[b], hm, hs, g);
+    const float d = group_dot_h<FMT>(w[b], sc[b], hm, hs, g);
     const float v = wave_sum(ok ? d : 0.0f);
     if (lane == 0) a.o_shared[r] = v;
   };
@@ -449,17 +505,23 @@ __global__ void __launch_bounds__(256) dec_select_permute_kernel(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 template <int FMT, int GPL>
 __global__ void __launch_bounds__(256) dec_gateup_kernel(DecodeArgs a) {
-  const int p = blockIdx.y;
-  const int et = __builtin_amdgcn_readfirstlane(a.sorted_et[p]);
+  // with more than one token, y < T: the shared expert for token y (first,
+  // so that the blocks sharing its weights start together), then pick y - T;
+  // one token's shared gate/up runs in K1
+  const int nsh = a.has_shared && a.T > 1 ? a.T : 0;
+  const bool sh = (int)blockIdx.y < nsh;
+  const int p = (int)blockIdx.y - nsh;
+  const int et = sh ? (int)blockIdx.y << 16 : __builtin_amdgcn_readfirstlane(a.sorted_et[p]);
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const ExpertSet& R = a.routed;
+  const ExpertSet& R = sh ? a.shared : a.routed;
   const int pair0 = blockIdx.x * kPairsPerBlock + wv * kPairsPerWave;
   if (pair0 >= R.inter) return;
   const int e = et & 0xffff, t = et >> 16;
   const float gg = (FMT == MOE_WFMT_NVFP4) ? R.gate.g[e] : 1.0f;
   const float gu = (FMT == MOE_WFMT_NVFP4) ? R.up.g[e] : 1.0f;
+  uint16_t* h = sh ? a.h_shared + (size_t)t * a.ldh : a.h_routed + (size_t)p * a.ldh;
   gateup_wave<FMT, GPL>(a.x + (size_t)t * a.H, a.H, R.gate, R.up, (size_t)e * R.inter, R.inter,
-                        pair0, gg, gu, a.h_routed + (size_t)p * a.ldh);
+                        pair0, gg, gu, h);
 }
 
 // ---------------------------------------------------------------------------
@@ -552,13 +614,13 @@ __device__ __forceinline__ void down_compute(const DownItem& it, const SlotInfo&
         for (int i = 0; i < 4; ++i) hm[4 * q + i] = t4[i];
       }
     }
-    const float hs = (FMT == MOE_WFMT_INT4_G32_F16) ? act_sum<true>(hm) : 0.0f;
+    const float hs = offset_h<FMT>(hm);
     const int t = (int)((d.tpk >> (8 * m)) & 0xffu);
     const float wm = m == 0 ? d.w[0] : m == 1 ? d.w[1] : m == 2 ? d.w[2] : d.w[3];
     const float wpick = ok ? wm : 0.0f;
 #pragma unroll
     for (int r = 0; r < kDownRows; ++r) {
-      const float v = wpick * group_dot<FMT, true>(it.w[r], it.sc[r], hm, hs, d.g);
+      const float v = wpick * group_dot_h<FMT>(it.w[r], it.sc[r], hm, hs, d.g);
 #pragma unroll
       for (int tt = 0; tt < MT; ++tt)
         if (tt == t) acc[tt][r] += v;
@@ -764,13 +826,13 @@ __global__ void __launch_bounds__(256, 2) dec_down_t1_kernel(DecodeArgs a) {
     if (FMT == MOE_WFMT_INT4_G32_F16 && s < nr) {
       uint32_t hm[16];
       h_of(s, hm);
-      hsum[s] = act_sum<true>(hm);
+      hsum[s] = int4_offset(hm);
     }
   }
   if (FMT == MOE_WFMT_INT4_G32_F16 && shared) {
     uint32_t hm[16];
     h_of(nr, hm);
-    hsums = act_sum<true>(hm);
+    hsums = int4_offset(hm);
   }
   // row r from buffer B, with row r + nw requested into the other buffer
   auto row_step = [&](auto B, int r) {
@@ -782,14 +844,14 @@ __global__ void __launch_bounds__(256, 2) dec_down_t1_kernel(DecodeArgs a) {
       if (s < nr) {
         uint32_t hm[16];
         h_of(s, hm);
-        const float d = group_dot<FMT, true>(wq[b][s], wsc[b][s], hm, hsum[s], gsl[s]);
+        const float d = group_dot_h<FMT>(wq[b][s], wsc[b][s], hm, hsum[s], gsl[s]);
         acc += ok ? wsl[s] * d : 0.0f;
       }
     }
     if (shared) {
       uint32_t hm[16];
       h_of(nr, hm);
-      const float d = group_dot<FMT, true>(wqs[b], wscs[b], hm, hsums, gsh);
+      const float d = group_dot_h<FMT>(wqs[b], wscs[b], hm, hsums, gsh);
       acc += ok ? d : 0.0f;
     }
     const float v = wave_sum(acc);
@@ -951,15 +1013,7 @@ __global__ void __launch_bounds__(64 * kDMWaves) dec_down_multi_kernel(DecodeArg
         const uint4 v = hl[(j * 4 + q) * 64 + g];
         hm[4 * q] = v.x; hm[4 * q + 1] = v.y; hm[4 * q + 2] = v.z; hm[4 * q + 3] = v.w;
       }
-      // the code offsets of the dequantisation below: 1032 per even-pair
-      // input, 72 per odd-pair input
-      float se = 0.0f, so = 0.0f;
-#pragma unroll
-      for (int m = 0; m < 16; m += 2) {
-        se = dot2_f16(hm[m], 0x3C003C00u, se);
-        so = dot2_f16(hm[m + 1], 0x3C003C00u, so);
-      }
-      hsl[i] = fmaf(1032.0f, se, 72.0f * so);
+      hsl[i] = int4_offset(hm);
     }
     __syncthreads();
   }
@@ -980,18 +1034,7 @@ __global__ void __launch_bounds__(64 * kDMWaves) dec_down_multi_kernel(DecodeArg
     uint32_t wf[16];
     float sc0, sc1 = 0.0f;
     if constexpr (FMT == MOE_WFMT_INT4_G32_F16) {
-      // or-ing a code u into the mantissa of fp16 1024 gives 1024 + u (nibble
-      // at bits 0-3 of a half) or 1024 + 16 u (bits 4-7): even pairs the
-      // first, odd pairs the second, one shift by 8 per word for pairs 2, 3
-      const uint32_t one = 0x64006400u;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t w = wq[b][j], w8 = w >> 8;
-        wf[4 * j + 0] = and_or(w, 0x000F000Fu, one);
-        wf[4 * j + 1] = and_or(w, 0x00F000F0u, one);
-        wf[4 * j + 2] = and_or(w8, 0x000F000Fu, one);
-        wf[4 * j + 3] = and_or(w8, 0x00F000F0u, one);
-      }
+      int4_f16_1024(wq[b], wf);
       sc0 = half_bits_to_f32(wsc[b] & 0xffffu);
     } else {
 #pragma unroll
@@ -1016,15 +1059,7 @@ __global__ void __launch_bounds__(64 * kDMWaves) dec_down_multi_kernel(DecodeArg
         }
         float v;
         if constexpr (FMT == MOE_WFMT_INT4_G32_F16) {
-          // sum (u - 8) h = d_even + d_odd / 16 - (1032 A_even + 72 A_odd),
-          // the last term staged with h
-          float de = 0.0f, dd = 0.0f;
-#pragma unroll
-          for (int i = 0; i < 16; i += 2) {
-            de = dot2_f16(wf[i], hm[i], de);
-            dd = dot2_f16(wf[i + 1], hm[i + 1], dd);
-          }
-          v = sc0 * (fmaf(0.0625f, dd, de) - hslane[j * 64]);
+          v = sc0 * (int4_dot_1024(wf, hm) - hslane[j * 64]);   // offset staged with h
         } else {
           float d0 = 0.0f, d1 = 0.0f;
 #pragma unroll
@@ -1108,8 +1143,12 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
   hipError_t e;
   const int gpl = (a.H / 32 + 63) / 64;
   const int nrb = a.E;
-  const int nsb =
-      a.has_shared ? a.T * ((a.shared.inter + kSharedPairsPerBlock - 1) / kSharedPairsPerBlock) : 0;
+  // one token: the shared expert's gate/up runs beside the router; more
+  // tokens: as extra blocks of K3
+  const bool sh_k3 = a.has_shared && a.T > 1;
+  const int nsb = a.has_shared && !sh_k3
+                      ? (a.shared.inter + kSharedPairsPerBlock - 1) / kSharedPairsPerBlock
+                      : 0;
   const bool f4 = a.wfmt == MOE_WFMT_NVFP4;
   switch (gpl) {
     case 1: e = launch_k1<1>(a, s, nrb, nsb); break;
@@ -1131,7 +1170,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (tr && (e = tr->mark("dec_select_permute")) != hipSuccess) return e;
 
-  dim3 g3((a.routed.inter + kPairsPerBlock - 1) / kPairsPerBlock, a.T * a.K);
+  const int inter3 = std::max(a.routed.inter, sh_k3 ? a.shared.inter : 0);
+  dim3 g3((inter3 + kPairsPerBlock - 1) / kPairsPerBlock, a.T * a.K + (sh_k3 ? a.T : 0));
   switch (gpl) {
     case 1: e = launch_k3<1>(a, s, g3); break;
     case 2: e = launch_k3<2>(a, s, g3); break;
