@@ -890,22 +890,26 @@ __host__ __device__ inline bool down_t1_fits(const DecodeArgs& a) {
 // timing.  The work is bound by the dequantisation and dot products, so each
 // item's codes are dequantised once for all its tokens.
 // ---------------------------------------------------------------------------
-#ifndef QMOE_DM_DEPTH
-#define QMOE_DM_DEPTH 12
-#endif
 #ifndef QMOE_DM_WAVES
 #define QMOE_DM_WAVES 8
 #endif
-constexpr int kDMDepth = QMOE_DM_DEPTH;   // (row, slot) items in flight per wave
+#ifndef QMOE_DM_DEPTH
+#define QMOE_DM_DEPTH 12
+#endif
 constexpr int kDMWaves = QMOE_DM_WAVES;   // waves per workgroup
-constexpr int kDMRows = 36;               // h rows held in LDS (P + T)
-constexpr int kDMChunks = kDMRows * 256;  // 16-byte chunks: 4 quarters x 64 groups per row
-static_assert(kDMChunks % (64 * kDMWaves) == 0, "h chunks split evenly over the threads");
+// up to 36 h rows (4 tokens x 8 picks and the shared expert's 4 rows); one
+// workgroup per CU.  (Used for one token as well -- 16 rows, every item of a
+// wave in flight -- it measured slower than dec_down_t1.)
+constexpr int kDMRows = 36, kDMDepth = QMOE_DM_DEPTH, kDMBlocks = 256;
 
-template <int FMT>
+// ROWS: h rows the LDS holds; D: (row, slot) items in flight per wave
+template <int FMT, int ROWS, int D>
 __global__ void __launch_bounds__(64 * kDMWaves) dec_down_multi_kernel(DecodeArgs a) {
+  constexpr int kDMChunks = ROWS * 256;   // 16-byte chunks: 4 quarters x 64 groups per row
+  constexpr int kDMDepth = D;
+  static_assert(kDMChunks % (64 * kDMWaves) == 0, "h chunks split evenly over the threads");
   __shared__ uint4 hl[kDMChunks];
-  __shared__ float hsl[kDMRows * 64];
+  __shared__ float hsl[ROWS * 64];
   constexpr int NT = 64 * kDMWaves;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -914,7 +918,7 @@ __global__ void __launch_bounds__(64 * kDMWaves) dec_down_multi_kernel(DecodeArg
   // count hold stale records that are never read
   const DecSlot rec = a.slots[lane];
   const int nr = __builtin_amdgcn_readfirstlane(*a.n_active);
-  const bool shared = a.has_shared;
+  const bool shared = a.has_shared && !a.shared_in_k2;   // else K2 wrote its output
   const int ns = nr + (shared ? 1 : 0);
   const int nG = a.routed.inter / 32;
   const int nrows = P + (shared ? T : 0);
@@ -1005,7 +1009,7 @@ __global__ void __launch_bounds__(64 * kDMWaves) dec_down_multi_kernel(DecodeArg
   });
   __syncthreads();
   if (FMT == MOE_WFMT_INT4_G32_F16) {
-    for (int i = threadIdx.x; i < kDMRows * 64; i += NT) {
+    for (int i = threadIdx.x; i < ROWS * 64; i += NT) {
       const int j = i >> 6, g = i & 63;
       uint32_t hm[16];
 #pragma unroll
@@ -1095,23 +1099,26 @@ __global__ void __launch_bounds__(64 * kDMWaves) dec_down_multi_kernel(DecodeArg
   }
   if (lane < nrw) {
     const int r = gw + lane * nw;
+    if (a.shared_in_k2) y0 += a.o_shared[r];
     store_y(a, 0, r, y0);
-    store_y(a, 1, r, y1);
+    if (T > 1) store_y(a, 1, r, y1);
     if (T > 2) store_y(a, 2, r, y2);
     if (T > 3) store_y(a, 3, r, y3);
   }
 }
 
-// Whether the 2..4-token down kernel covers this shape.
-__host__ __device__ inline bool down_multi_fits(const DecodeArgs& a) {
-  const long long nG = a.routed.inter / 32;
-  const long long P = (long long)a.T * a.K;
-  return a.T >= 2 && a.T <= kMaxT && nG <= 64 && P + (a.has_shared ? 1 : 0) <= 64 &&
-         (!a.has_shared || a.shared.inter == a.routed.inter) &&
-         P + (a.has_shared ? a.T : 0) <= kDMRows &&
-         (a.H + 256 * kDMWaves - 1) / (256 * kDMWaves) <= 64 &&
-         (long long)a.E * a.H * (a.routed.inter / 2) < 0xFFFFFFFFll &&
-         (long long)a.E * a.H * nG * 2 < 0xFFFFFFFFll;
+// Whether dec_down_multi with ROWS h rows in LDS covers this shape (a2 with
+// shared_in_k2 decided).
+template <int ROWS>
+__host__ __device__ inline bool down_multi_fits(const DecodeArgs& a2) {
+  const long long nG = a2.routed.inter / 32;
+  const long long P = (long long)a2.T * a2.K;
+  const bool sh4 = a2.has_shared && !a2.shared_in_k2;
+  return a2.T >= 1 && a2.T <= kMaxT && nG <= 64 && P + (sh4 ? 1 : 0) <= 64 &&
+         (!sh4 || a2.shared.inter == a2.routed.inter) && P + (sh4 ? a2.T : 0) <= ROWS &&
+         (a2.H + 256 * kDMWaves - 1) / (256 * kDMWaves) <= 64 &&
+         (long long)a2.E * a2.H * (a2.routed.inter / 2) < 0xFFFFFFFFll &&
+         (long long)a2.E * a2.H * nG * 2 < 0xFFFFFFFFll;
 }
 
 template <int GPL>
@@ -1191,13 +1198,14 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
     else
       hipLaunchKernelGGL((dec_down_t1_kernel<MOE_WFMT_INT4_G32_F16>), dim3(blocks), dim3(256), lds, s,
                          a2);
-  } else if (down_multi_fits(a)) {
-    const int blocks = std::min((a.H + kDMWaves - 1) / kDMWaves, 256);
+  } else if (a.T > 1 && down_multi_fits<kDMRows>(a2)) {
+    const int blocks = std::min((a.H + kDMWaves - 1) / kDMWaves, kDMBlocks);
     if (f4)
-      hipLaunchKernelGGL((dec_down_multi_kernel<MOE_WFMT_NVFP4>), dim3(blocks), dim3(64 * kDMWaves), 0, s, a);
+      hipLaunchKernelGGL((dec_down_multi_kernel<MOE_WFMT_NVFP4, kDMRows, kDMDepth>), dim3(blocks),
+                         dim3(64 * kDMWaves), 0, s, a2);
     else
-      hipLaunchKernelGGL((dec_down_multi_kernel<MOE_WFMT_INT4_G32_F16>), dim3(blocks), dim3(64 * kDMWaves), 0,
-                         s, a);
+      hipLaunchKernelGGL((dec_down_multi_kernel<MOE_WFMT_INT4_G32_F16, kDMRows, kDMDepth>),
+                         dim3(blocks), dim3(64 * kDMWaves), 0, s, a2);
   } else if (a.T == 1) {
     if (f4)
       hipLaunchKernelGGL((dec_down_combine_kernel<MOE_WFMT_NVFP4, 1>), g4, dim3(256), 0, s, a);
