@@ -249,35 +249,39 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return u >> 16;
 }
 
+// One block per (token, 1024 columns): each thread's k + 1 row loads are all
+// in flight together (a block per token leaves most of the chip idle at small
+// T and serialises the rows).  Per element the sum runs in pick order, then
+// the shared expert, as before.
 __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
   const int t = blockIdx.x;
-  const int H = a.H;
-  for (int n = threadIdx.x * 4; n < H; n += 1024) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int i = 0; i < a.K; ++i) {
-      const int p = a.inv_perm[(size_t)t * a.K + i];
-      const float w = a.tw[(size_t)t * a.K + i];
-      const float4 o = *reinterpret_cast<const float4*>(a.expert_out + (size_t)p * H + n);
-      acc.x = fmaf(w, o.x, acc.x);
-      acc.y = fmaf(w, o.y, acc.y);
-      acc.z = fmaf(w, o.z, acc.z);
-      acc.w = fmaf(w, o.w, acc.w);
-    }
-    if (a.shared_out) {
-      const float4 o = *reinterpret_cast<const float4*>(a.shared_out + (size_t)t * H + n);
-      acc.x += o.x;
-      acc.y += o.y;
-      acc.z += o.z;
-      acc.w += o.w;
-    }
-    if (a.out_bf16) {
-      uint2 v;
-      v.x = f32_to_bf16_rne(acc.x) | (f32_to_bf16_rne(acc.y) << 16);
-      v.y = f32_to_bf16_rne(acc.z) | (f32_to_bf16_rne(acc.w) << 16);
-      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.y) + (size_t)t * H + n) = v;
-    } else {
-      *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.y) + (size_t)t * H + n) = acc;
-    }
+  const int H = a.H, K = a.K;
+  const int n = (blockIdx.y * 256 + threadIdx.x) * 4;
+  if (n >= H) return;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i = 0; i < K; ++i) {
+    const int p = a.inv_perm[(size_t)t * K + i];
+    const float w = a.tw[(size_t)t * K + i];
+    const float4 o = *reinterpret_cast<const float4*>(a.expert_out + (size_t)p * H + n);
+    acc.x = fmaf(w, o.x, acc.x);
+    acc.y = fmaf(w, o.y, acc.y);
+    acc.z = fmaf(w, o.z, acc.z);
+    acc.w = fmaf(w, o.w, acc.w);
+  }
+  if (a.shared_out) {
+    const float4 o = *reinterpret_cast<const float4*>(a.shared_out + (size_t)t * H + n);
+    acc.x += o.x;
+    acc.y += o.y;
+    acc.z += o.z;
+    acc.w += o.w;
+  }
+  if (a.out_bf16) {
+    uint2 v;
+    v.x = f32_to_bf16_rne(acc.x) | (f32_to_bf16_rne(acc.y) << 16);
+    v.y = f32_to_bf16_rne(acc.z) | (f32_to_bf16_rne(acc.w) << 16);
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.y) + (size_t)t * H + n) = v;
+  } else {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.y) + (size_t)t * H + n) = acc;
   }
 }
 
@@ -310,7 +314,7 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, Tracer* tr) {
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s, Tracer* tr) {
   if (a.T == 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_kernel, dim3(a.T), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(combine_kernel, dim3(a.T, (a.H + 1023) / 1024), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && tr) e = tr->mark("combine");
   return e;

@@ -129,14 +129,29 @@ __device__ __forceinline__ void select_token(const double* __restrict__ logits,
   const int lane = threadIdx.x & 63;
   const int per = E / G;
   const int e0 = 4 * lane;
-  double s[4], sb[4];
+  double s[4], sb[4], l[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) l[j] = logits[e0 + j < E ? e0 + j : 0];
+  // partial sums added in split order; each batch's loads are issued together
+  constexpr int kBatch = 4;
+  for (int sp = 1; sp < nsplit; sp += kBatch) {
+    double v[kBatch][4];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        v[u][j] = logits[(size_t)min(sp + u, nsplit - 1) * split_stride + (e0 + j < E ? e0 + j : 0)];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (sp + u < nsplit) l[j] += v[u][j];
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = e0 + j;
     const bool in = e < E;
-    double l = logits[in ? e : 0];
-    for (int sp = 1; sp < nsplit; ++sp) l += logits[sp * split_stride + (in ? e : 0)];
-    s[j] = 1.0 / (1.0 + exp(-l));
+    s[j] = 1.0 / (1.0 + exp(-l[j]));
     sb[j] = in ? s[j] + (bias ? (double)bias[e] : 0.0) : -INFINITY;
   }
   // ---- group scores and kept groups ------------------------------------
