@@ -36,14 +36,19 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 constexpr int kBM = 128;          // tokens per unit
 constexpr int kBK = 128;          // inputs per K block
 constexpr int kChunks = kBK / 8;  // 16-byte chunks per activation row of a K block
-// Thin units: an expert with at most kBMThin tokens gets one unit of the thin
-// kernel, whose LDS stages hold kBMThin rows.  With few token columns a K
+// Thin units: up to kBMThin tokens of an expert with few tokens, run by the
+// thin kernel, whose LDS stages hold kBMThin rows.  With few token columns a K
 // block carries little MFMA work, so the thin kernel keeps more K blocks in
 // flight to cover the memory latency.
 #ifndef QMOE_THIN_NS
 #define QMOE_THIN_NS 4
 #endif
 constexpr int kBMThin = 32;
+// With fewer fat units than this (gate/up: 16 work items each) the fat
+// launches would leave most of the chip idle, so the experts they would hold
+// are cut into thin units, which run in the thin launch with the bulk of the
+// work (their weights are then read once per 32 tokens).
+constexpr int kFewFat = 16;
 constexpr int kNSThin = QMOE_THIN_NS;
 constexpr int kGateUpPairs = 128; // row pairs per gate/up unit
 constexpr int kDownRows = 256;    // output rows per down unit
@@ -515,6 +520,19 @@ __global__ void __launch_bounds__(64) build_units_kernel(const int32_t* __restri
   const int lane = threadIdx.x;
   const int na = n_active ? *n_active : 0;
   int4* thin = tiles + thin_off;
+  // fat units if every expert with more than kBMThin tokens took them; when
+  // there are fewer than kFewFat, their launch would leave most of the chip
+  // idle, so every expert is cut into thin units instead
+  int nfat = 0;
+  for (int a = lane; a < na; a += 64) {
+    const int e = active[a];
+    const int M = offsets[e + 1] - offsets[e];
+    nfat += M > kBMThin ? (M + kBM - 1) / kBM : 0;
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) nfat += __shfl_xor(nfat, d, 64);
+  if (has_shared && T > kBMThin) nfat += (T + kBM - 1) / kBM;
+  const int thin_max = nfat < kFewFat ? 0x7fffffff : kBMThin;   // most tokens of a thin-cut expert
   int base = 0, tbase = 0;   // fat units, thin units so far
   for (int a0 = 0; a0 < na; a0 += 64) {
     const int a = a0 + lane;
@@ -523,7 +541,7 @@ __global__ void __launch_bounds__(64) build_units_kernel(const int32_t* __restri
       e = active[a];
       o = offsets[e];
       M = offsets[e + 1] - o;
-      nt = M <= kBMThin ? 1 : 0;
+      nt = M <= thin_max ? (M + kBMThin - 1) / kBMThin : 0;
       nm = nt ? 0 : (M + kBM - 1) / kBM;
     }
     // exclusive prefixes of the fat and thin unit counts across the wave
@@ -541,14 +559,19 @@ __global__ void __launch_bounds__(64) build_units_kernel(const int32_t* __restri
       const int m0 = i * kBM;
       tiles[excl + i] = make_int4(e, o + m0, min(kBM, M - m0), o + m0);
     }
-    if (nt) thin[tbase + tpre - 1] = make_int4(e, o, M, o);
+    for (int i = 0; i < nt; ++i) {
+      const int m0 = i * kBMThin;
+      thin[tbase + tpre - nt + i] = make_int4(e, o + m0, min(kBMThin, M - m0), o + m0);
+    }
     base += __shfl(pre, 63, 64);
     tbase += __shfl(tpre, 63, 64);
   }
   if (has_shared) {
-    if (T <= kBMThin) {
-      if (lane == 0) thin[tbase] = make_int4(-1, P, T, 0);
-      ++tbase;
+    if (T <= thin_max) {
+      const int ns = (T + kBMThin - 1) / kBMThin;
+      for (int i = lane; i < ns; i += 64)
+        thin[tbase + i] = make_int4(-1, P + i * kBMThin, min(kBMThin, T - i * kBMThin), i * kBMThin);
+      tbase += ns;
     } else {
       const int ns = (T + kBM - 1) / kBM;
       for (int i = lane; i < ns; i += 64) {
@@ -565,8 +588,9 @@ __global__ void __launch_bounds__(64) build_units_kernel(const int32_t* __restri
 }
 
 // Most work units of each kind: fat units hold up to kBM tokens of an expert
-// with more than kBMThin of them, thin units an expert's (or the shared
-// expert's) tokens when there are at most kBMThin.
+// with more than kBMThin of them, thin units up to kBMThin tokens of an
+// expert (or the shared expert) with at most kBMThin, or of any expert when
+// there would be fewer than kFewFat fat units.
 long fat_units_max(int T, int K, int E, bool has_shared) {
   const long P = (long)T * K;
   const long fat_experts = std::min<long>(E, P / (kBMThin + 1));
@@ -576,7 +600,10 @@ long fat_units_max(int T, int K, int E, bool has_shared) {
 }
 long thin_units_max(int T, int K, int E, bool has_shared) {
   const long P = (long)T * K;
-  return std::min<long>(E, P) + (has_shared && T <= kBMThin ? 1 : 0);
+  // one per expert with at most kBMThin tokens (and the shared expert's one);
+  // when fewer than kFewFat fat units are cut up, each gives at most
+  // kBM / kBMThin thin units
+  return std::min<long>(E, P) + (has_shared ? 1 : 0) + (long)(kFewFat - 1) * (kBM / kBMThin);
 }
 
 }  // namespace
@@ -589,8 +616,9 @@ hipError_t launch_build_units(const int32_t* offsets, const int32_t* active,
   return hipGetLastError();
 }
 
-// Work units: for each active expert (ascending) its sorted slots, in one thin
-// unit or slices of kBM; then the shared expert's tokens likewise.
+// Work units: for each active expert (ascending) its sorted slots, in thin
+// units of kBMThin or fat units of kBM; then the shared expert's tokens
+// likewise.
 // tiles[i] = {expert or -1, first h/O row, tokens, first sorted slot or
 // token}; the thin units start at tiles[thin_off].
 int gemm_max_units(int T, int K, int E, bool has_shared) {

@@ -146,12 +146,16 @@ EDGE = {
     "nvfp4_T1":  (dict(), 1, "nvfp4", "normal0.1"),
     "nvfp4_T3":  (dict(hidden=96, moe_inter=160, shared_inter=64), 3, "nvfp4", "zipf"),
     "T1_uneven_shared": (dict(moe_inter=64, shared_inter=96), 1, "int4", "normal0.1"),
-    # the GEMM's unit kinds: one expert takes every token, so it gets one full
-    # thin unit (32 tokens), one partial fat unit (33), or a full and a short
-    # fat unit (160)
+    # the GEMM's work units: one expert takes every token, so it gets one full
+    # thin unit (32 tokens); with few would-be fat units every expert is cut
+    # into thin units: a full and a one-token unit (33), two full (64), five
+    # (160; the shared expert likewise); with many (about 160 tokens for each
+    # of 16 experts) a full and a short fat unit each
     "hot_thin32": (dict(top_k=2), 32, "int4", "hot1"),
-    "hot_fat33": (dict(top_k=2), 33, "int4", "hot1"),
-    "hot_fat160": (dict(top_k=2), 160, "int4", "hot1"),
+    "hot_cut33": (dict(top_k=2), 33, "int4", "hot1"),
+    "hot_cut64": (dict(top_k=2), 64, "int4", "hot1"),
+    "hot_cut160": (dict(top_k=2), 160, "int4", "hot1"),
+    "fat_units": (dict(), 640, "int4", "normal0.1"),
     # 2..4 tokens: the small-batch down kernel that stages h in LDS (several
     # tokens per expert, no shared expert, one group per row, full 64-group
     # rows), and shapes that fall back to the per-block kernel (65 slots,
