@@ -136,6 +136,9 @@ EDGE = {
     "group_of_one": (dict(n_group=16, topk_group=4), 11, "int4", "normal0.1"),
     "k1":        (dict(top_k=1), 9, "int4", "normal0.1"),
     "k16":       (dict(n_routed_experts=64, n_group=4, topk_group=4, top_k=16), 21, "int4", "normal0.1"),
+    # one token with more picks than the single-token down kernel holds
+    "T1_k16":    (dict(n_routed_experts=64, n_group=4, topk_group=4, top_k=16), 1, "int4", "normal0.1"),
+    "T1_k16_nvfp4": (dict(n_routed_experts=64, n_group=4, topk_group=4, top_k=16), 1, "nvfp4", "zipf"),
     "no_shared": (dict(n_shared_experts=0), 12, "int4", "normal0.1"),
     "min_dims":  (dict(hidden=32, moe_inter=32, shared_inter=32), 7, "int4", "normal0.1"),
     "E256":      (dict(n_routed_experts=256, n_group=8, topk_group=4, top_k=8, hidden=256,
