@@ -49,10 +49,14 @@ def test_tiny_layer():
     check_outputs(L, y, ids_g)
 
 
-def test_tiny_bf16_output_is_rne_of_fp32():
+@pytest.mark.parametrize("T", [8, 1, 3])
+def test_tiny_bf16_output_is_rne_of_fp32(T):
+    """bf16 output is the round-to-nearest-even of the fp32 output, on the
+    large-batch path (8 tokens) and the small-batch down kernels (1 and 3)."""
     L = layer("tiny")
-    y32, _, _ = run_layer(L, q.MOE_OUT_F32)
-    y16, _, _ = run_layer(L, q.MOE_OUT_BF16)
+    x = L.x[:T].contiguous()
+    y32, _, _ = run_layer(L, q.MOE_OUT_F32, x=x)
+    y16, _, _ = run_layer(L, q.MOE_OUT_BF16, x=x)
     assert torch.equal(y32.to(torch.bfloat16), y16)
 
 
