@@ -472,7 +472,12 @@ __global__ void __launch_bounds__(256, BM == kBMThin ? QMOE_THIN_WGS : 1) moe_ge
     }
   };
   if constexpr (thin) {
-    run(ic<kBMThin / 16>{});
+    // units of at most 16 tokens (most of them at small batch) need one
+    // column tile: half the B reads and MFMAs
+    if (nct > 1)
+      run(ic<kBMThin / 16>{});
+    else
+      run(ic<1>{});
   } else {
     if (nct > 4)
       run(ic<8>{});
