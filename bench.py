@@ -84,26 +84,20 @@ def algorithmic(geom, wfmt, T, n_active):
     # selection: logits and bias in; ids, weights, expert records (48 bytes),
     # per-pick expert/token words and the count out
     sel_b = T * E * 8 + E * 4 + P * 8 + n_active * 48 + P * 4 + 4
-    # a single token runs the shared expert's gate/up beside the router
-    # (dec_router_shared) and, with equal routed and shared inter, its down
-    # projection in the selection launch (dec_select_permute); more tokens
-    # run its gate/up as extra blocks of dec_gateup
-    sh_k1 = T == 1 and Is > 0
+    # the shared expert's gate/up runs beside the selection for a single token
+    # (dec_select_permute) and as extra blocks of dec_gateup for more tokens;
+    # its down projection runs with the routed ones
+    sh_k2 = T == 1 and Is > 0
     sh_gu_b = sb["gate"] + sb["up"] + T * Is * 2
     sh_gu_f = T * 2 * H * Is * 2
-    sh_k2 = T == 1 and Is == I and Is > 0
-    sh_dn_b = sb["down"] + T * Is * 2 + T * H * 4 if sh_k2 else 0
-    sh_dn_f = T * 2 * H * Is if sh_k2 else 0
     kern = {
         # small-batch path
-        "dec_router_shared": dict(bytes=router_b + x_b + T * E * 8 + (sh_gu_b if sh_k1 else 0),
-                                  flops=T * 2 * H * E + (sh_gu_f if sh_k1 else 0)),
-        "dec_select_permute": dict(bytes=sel_b + sh_dn_b, flops=sh_dn_f),
+        "dec_router": dict(bytes=router_b + x_b + T * E * 8, flops=T * 2 * H * E),
+        "dec_select_permute": dict(bytes=sel_b + (sh_gu_b if sh_k2 else 0), flops=sh_gu_f if sh_k2 else 0),
         "dec_gateup": dict(bytes=n_active * (eb["gate"] + eb["up"]) + x_b + P * I * 2
-                           + (sh_gu_b if Is and not sh_k1 else 0),
-                           flops=P * 2 * H * I * 2 + (sh_gu_f if Is and not sh_k1 else 0)),
-        "dec_down_combine": dict(bytes=w_dn + rows * I * 2 + y_b - sh_dn_b + (T * H * 4 if sh_k2 else 0),
-                                 flops=f_dn + 2 * P * H - sh_dn_f),
+                           + (sh_gu_b if Is and not sh_k2 else 0),
+                           flops=P * 2 * H * I * 2 + (sh_gu_f if Is and not sh_k2 else 0)),
+        "dec_down_combine": dict(bytes=w_dn + rows * I * 2 + y_b, flops=f_dn + 2 * P * H),
         # large-batch path
         "route_logits": dict(bytes=router_b + x_b + T * E * 8, flops=T * 2 * H * E),
         "route_select": dict(bytes=T * E * 8 + E * 4 + P * 8, flops=0),

@@ -4,17 +4,15 @@
 // bound, so the kernels are built around keeping many independent 128-bit
 // loads in flight and doing as little else as possible.
 //
-//   K1 dec_router_shared   router logits (float64, one wave per expert) and,
-//                          for one token, in the same launch, the shared
-//                          expert's gate/up GEMV, which does not depend on
-//                          the routing (for more tokens it runs in K3)
+//   K1 dec_router          router logits (float64, one block per expert)
 //   K2 dec_select_permute  one workgroup: per-token selection (one wave per
 //                          token) and the grouping of the <= 64 picks by
 //                          expert (batch union); for one token, the shared
-//                          expert's down GEMV in the other workgroups
+//                          expert's gate/up GEMV in the other workgroups
 //   K3 dec_gateup          gate/up GEMV of every pick's expert with SwiGLU
-//   K4                     down GEMV of every selected expert (and the shared
-//                          expert) with the weighted combine in registers:
+//                          (and of the shared expert for 2..4 tokens)
+//   K4                     down GEMV of every selected expert and the shared
+//                          expert with the weighted combine in registers:
 //                          dec_down_t1 (one token), dec_down_multi (2..4
 //                          tokens, SwiGLU outputs staged in LDS) or
 //                          dec_down_combine (other shapes)
@@ -281,15 +279,13 @@ __device__ __forceinline__ void gateup_wave(const uint16_t* __restrict__ x, int 
 }
 
 // ---------------------------------------------------------------------------
-// K1: router logits (blocks [0, nrb)) and, for one token, the shared
-// expert's gate/up (the rest)
+// K1: router logits, one block per expert
 // ---------------------------------------------------------------------------
-template <int FMT, int GPL>
-__global__ void __launch_bounds__(256) dec_router_shared_kernel(DecodeArgs a, int nrb) {
+__global__ void __launch_bounds__(256) dec_router_kernel(DecodeArgs a) {
   __shared__ double rpart[4][kMaxT];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if ((int)blockIdx.x < nrb) {
+  {
     // expert e's logits: the four waves take quarters of the hidden dimension
     const int e = blockIdx.x;
     const int H = a.H, T = a.T;
@@ -337,74 +333,31 @@ __global__ void __launch_bounds__(256) dec_router_shared_kernel(DecodeArgs a, in
       a.logits[(size_t)threadIdx.x * a.E + e] =
           ((rpart[0][threadIdx.x] + rpart[1][threadIdx.x]) + rpart[2][threadIdx.x]) +
           rpart[3][threadIdx.x];
-    return;
   }
-  // shared expert (one token): row block blockIdx.x - nrb
-  const ExpertSet& S = a.shared;
-  const int pair0 = ((int)blockIdx.x - nrb) * kSharedPairsPerBlock + wv * (2 * kSharedRP);
-  if (pair0 >= S.inter) return;
-  const float gg = (FMT == MOE_WFMT_NVFP4) ? S.gate.g[0] : 1.0f;
-  const float gu = (FMT == MOE_WFMT_NVFP4) ? S.up.g[0] : 1.0f;
-  gateup_wave<FMT, GPL, 2, kSharedRP>(a.x, a.H, S.gate, S.up, 0, S.inter, pair0, gg, gu,
-                                      a.h_shared);
 }
 
 // ---------------------------------------------------------------------------
 // K2: selection of every token, then the permutation of the P <= 64 picks
 // ---------------------------------------------------------------------------
-// Shared expert's down projection for one token, in K2's launch (it needs
-// only K1's output, so it streams while the selection runs): wave rows
-// r, r + stride, ...; lane c takes group c (inter <= 2048), the next row's
-// loads are in flight while the current one is reduced.
-template <int FMT>
-__device__ __forceinline__ void shared_down_rows(const DecodeArgs& a, int blk, int nblk) {
-  const int lane = threadIdx.x & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const ExpertSet& S = a.shared;
-  const int H = a.H, nG = S.inter / 32;
-  const uint32_t rowBytes = (uint32_t)S.inter / 2, srow = (uint32_t)nG * 2u;
-  const bool ok = lane < nG;
-  const uint32_t c = ok ? (uint32_t)lane : 0u;
-  const rsrc_t q = make_rsrc(S.down.q, (uint32_t)H * rowBytes);
-  const rsrc_t sr = make_rsrc(S.down.s, (uint32_t)H * srow);
-  uint32_t hm[16];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint4 v = *reinterpret_cast<const uint4*>(a.h_shared + c * 32 + 8 * i);
-    hm[4 * i] = v.x; hm[4 * i + 1] = v.y; hm[4 * i + 2] = v.z; hm[4 * i + 3] = v.w;
-  }
-  const float hs = offset_h<FMT>(hm);
-  const float g = FMT == MOE_WFMT_NVFP4 ? S.down.g[0] : 1.0f;
-  const int gw = blk * 4 + wv, nw = nblk * 4;
-  uint32_t w[2][4], sc[2];
-  auto ld = [&](auto B, int r) {
-    constexpr int b = decltype(B)::value;
-    bload16(w[b], q, c * 16u, (uint32_t)r * rowBytes);
-    sc[b] = bload_u16(sr, c * 2u, (uint32_t)r * srow);
-  };
-  auto step = [&](auto B, int r) {
-    constexpr int b = decltype(B)::value;
-    if (r + nw < H) ld(std::integral_constant<int, b ^ 1>{}, r + nw);
-    const float d = group_dot_h<FMT>(w[b], sc[b], hm, hs, g);
-    const float v = wave_sum(ok ? d : 0.0f);
-    if (lane == 0) a.o_shared[r] = v;
-  };
-  if (gw < H) ld(std::integral_constant<int, 0>{}, gw);
-  for (int r = gw; r < H; r += 2 * nw) {
-    step(std::integral_constant<int, 0>{}, r);
-    if (r + nw < H) step(std::integral_constant<int, 1>{}, r + nw);
-  }
-}
-
 // Selection and grouping.  What the later kernels read: the per-token ids
 // and weights (outputs of the layer), the selected experts' records (slots,
 // in ascending expert order, each with its picks in pick order), their count,
 // and for each sorted pick p (grouped by expert) its expert and token; the h
 // rows follow the sorted pick order.
-template <int FMT>
+// For one token, the other workgroups run the shared expert's gate/up GEMV
+// (one per row block): it does not depend on the routing, so it streams while
+// block 0 selects.
+template <int FMT, int GPL>
 __global__ void __launch_bounds__(256) dec_select_permute_kernel(DecodeArgs a) {
   if (blockIdx.x > 0) {
-    shared_down_rows<FMT>(a, blockIdx.x - 1, gridDim.x - 1);
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const ExpertSet& S = a.shared;
+    const int pair0 = ((int)blockIdx.x - 1) * kSharedPairsPerBlock + wv * (2 * kSharedRP);
+    if (pair0 >= S.inter) return;
+    const float gg = (FMT == MOE_WFMT_NVFP4) ? S.gate.g[0] : 1.0f;
+    const float gu = (FMT == MOE_WFMT_NVFP4) ? S.up.g[0] : 1.0f;
+    gateup_wave<FMT, GPL, 2, kSharedRP>(a.x, a.H, S.gate, S.up, 0, S.inter, pair0, gg, gu,
+                                        a.h_shared);
     return;
   }
   __shared__ SelectScratch sc[4];
@@ -507,7 +460,7 @@ template <int FMT, int GPL>
 __global__ void __launch_bounds__(256) dec_gateup_kernel(DecodeArgs a) {
   // with more than one token, y < T: the shared expert for token y (first,
   // so that the blocks sharing its weights start together), then pick y - T;
-  // one token's shared gate/up runs in K1
+  // one token's shared gate/up runs in K2
   const int nsh = a.has_shared && a.T > 1 ? a.T : 0;
   const bool sh = (int)blockIdx.y < nsh;
   const int p = (int)blockIdx.y - nsh;
@@ -743,7 +696,7 @@ __global__ void __launch_bounds__(256, 2) dec_down_t1_kernel(DecodeArgs a) {
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int H = a.H;
   const int nr = a.K;                       // one token: k distinct experts
-  const bool shared = a.has_shared && !a.shared_in_k2;   // else K2 wrote its output
+  const bool shared = a.has_shared;
   const int ns = nr + (shared ? 1 : 0);
   const int inter = a.routed.inter;         // routed and shared inter are equal here
   const int nG = inter / 32;
@@ -855,7 +808,7 @@ __global__ void __launch_bounds__(256, 2) dec_down_t1_kernel(DecodeArgs a) {
       acc += ok ? d : 0.0f;
     }
     const float v = wave_sum(acc);
-    if (lane == 0) store_y(a, 0, r, a.shared_in_k2 ? v + a.o_shared[r] : v);
+    if (lane == 0) store_y(a, 0, r, v);
   };
   for (int r = gw; r < H; r += 2 * nw) {
     row_step(std::integral_constant<int, 0>{}, r);
@@ -918,7 +871,7 @@ __global__ void __launch_bounds__(64 * kDMWaves) dec_down_multi_kernel(DecodeArg
   // count hold stale records that are never read
   const DecSlot rec = a.slots[lane];
   const int nr = __builtin_amdgcn_readfirstlane(*a.n_active);
-  const bool shared = a.has_shared && !a.shared_in_k2;   // else K2 wrote its output
+  const bool shared = a.has_shared;
   const int ns = nr + (shared ? 1 : 0);
   const int nG = a.routed.inter / 32;
   const int nrows = P + (shared ? T : 0);
@@ -1099,7 +1052,6 @@ __global__ void __launch_bounds__(64 * kDMWaves) dec_down_multi_kernel(DecodeArg
   }
   if (lane < nrw) {
     const int r = gw + lane * nw;
-    if (a.shared_in_k2) y0 += a.o_shared[r];
     store_y(a, 0, r, y0);
     if (T > 1) store_y(a, 1, r, y1);
     if (T > 2) store_y(a, 2, r, y2);
@@ -1107,28 +1059,27 @@ __global__ void __launch_bounds__(64 * kDMWaves) dec_down_multi_kernel(DecodeArg
   }
 }
 
-// Whether dec_down_multi with ROWS h rows in LDS covers this shape (a2 with
-// shared_in_k2 decided).
+// Whether dec_down_multi with ROWS h rows in LDS covers this shape.
 template <int ROWS>
-__host__ __device__ inline bool down_multi_fits(const DecodeArgs& a2) {
-  const long long nG = a2.routed.inter / 32;
-  const long long P = (long long)a2.T * a2.K;
-  const bool sh4 = a2.has_shared && !a2.shared_in_k2;
-  return a2.T >= 1 && a2.T <= kMaxT && nG <= 64 && P + (sh4 ? 1 : 0) <= 64 &&
-         (!sh4 || a2.shared.inter == a2.routed.inter) && P + (sh4 ? a2.T : 0) <= ROWS &&
-         (a2.H + 256 * kDMWaves - 1) / (256 * kDMWaves) <= 64 &&
-         (long long)a2.E * a2.H * (a2.routed.inter / 2) < 0xFFFFFFFFll &&
-         (long long)a2.E * a2.H * nG * 2 < 0xFFFFFFFFll;
+__host__ __device__ inline bool down_multi_fits(const DecodeArgs& a) {
+  const long long nG = a.routed.inter / 32;
+  const long long P = (long long)a.T * a.K;
+  const bool sh4 = a.has_shared;
+  return a.T >= 1 && a.T <= kMaxT && nG <= 64 && P + (sh4 ? 1 : 0) <= 64 &&
+         (!sh4 || a.shared.inter == a.routed.inter) && P + (sh4 ? a.T : 0) <= ROWS &&
+         (a.H + 256 * kDMWaves - 1) / (256 * kDMWaves) <= 64 &&
+         (long long)a.E * a.H * (a.routed.inter / 2) < 0xFFFFFFFFll &&
+         (long long)a.E * a.H * nG * 2 < 0xFFFFFFFFll;
 }
 
 template <int GPL>
-hipError_t launch_k1(const DecodeArgs& a, hipStream_t s, int nrb, int nsb) {
+hipError_t launch_k2(const DecodeArgs& a, hipStream_t s, int blocks) {
   if (a.wfmt == MOE_WFMT_NVFP4)
-    hipLaunchKernelGGL((dec_router_shared_kernel<MOE_WFMT_NVFP4, GPL>), dim3(nrb + nsb), dim3(256),
-                       0, s, a, nrb);
+    hipLaunchKernelGGL((dec_select_permute_kernel<MOE_WFMT_NVFP4, GPL>), dim3(blocks), dim3(256), 0, s,
+                       a);
   else
-    hipLaunchKernelGGL((dec_router_shared_kernel<MOE_WFMT_INT4_G32_F16, GPL>), dim3(nrb + nsb),
-                       dim3(256), 0, s, a, nrb);
+    hipLaunchKernelGGL((dec_select_permute_kernel<MOE_WFMT_INT4_G32_F16, GPL>), dim3(blocks), dim3(256),
+                       0, s, a);
   return hipGetLastError();
 }
 
@@ -1149,32 +1100,23 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
   if (a.T == 0) return hipSuccess;
   hipError_t e;
   const int gpl = (a.H / 32 + 63) / 64;
-  const int nrb = a.E;
-  // one token: the shared expert's gate/up runs beside the router; more
+  const bool f4 = a.wfmt == MOE_WFMT_NVFP4;
+  hipLaunchKernelGGL(dec_router_kernel, dim3(a.E), dim3(256), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (tr && (e = tr->mark("dec_router")) != hipSuccess) return e;
+
+  // one token: the shared expert's gate/up in K2, beside the selection; more
   // tokens: as extra blocks of K3
   const bool sh_k3 = a.has_shared && a.T > 1;
-  const int nsb = a.has_shared && !sh_k3
-                      ? (a.shared.inter + kSharedPairsPerBlock - 1) / kSharedPairsPerBlock
-                      : 0;
-  const bool f4 = a.wfmt == MOE_WFMT_NVFP4;
+  const int k2_blocks =
+      1 + (a.has_shared && !sh_k3 ? (a.shared.inter + kSharedPairsPerBlock - 1) / kSharedPairsPerBlock : 0);
   switch (gpl) {
-    case 1: e = launch_k1<1>(a, s, nrb, nsb); break;
-    case 2: e = launch_k1<2>(a, s, nrb, nsb); break;
-    case 3: e = launch_k1<3>(a, s, nrb, nsb); break;
-    default: e = launch_k1<4>(a, s, nrb, nsb); break;
+    case 1: e = launch_k2<1>(a, s, k2_blocks); break;
+    case 2: e = launch_k2<2>(a, s, k2_blocks); break;
+    case 3: e = launch_k2<3>(a, s, k2_blocks); break;
+    default: e = launch_k2<4>(a, s, k2_blocks); break;
   }
   if (e != hipSuccess) return e;
-  if (tr && (e = tr->mark("dec_router_shared")) != hipSuccess) return e;
-
-  DecodeArgs a2 = a;
-  a2.shared_in_k2 = down_t1_fits(a) && a.has_shared ? 1 : 0;
-  const int k2_blocks = 1 + (a2.shared_in_k2 ? 128 : 0);
-  if (f4)
-    hipLaunchKernelGGL((dec_select_permute_kernel<MOE_WFMT_NVFP4>), dim3(k2_blocks), dim3(256), 0, s, a2);
-  else
-    hipLaunchKernelGGL((dec_select_permute_kernel<MOE_WFMT_INT4_G32_F16>), dim3(k2_blocks), dim3(256), 0,
-                       s, a2);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   if (tr && (e = tr->mark("dec_select_permute")) != hipSuccess) return e;
 
   const int inter3 = std::max(a.routed.inter, sh_k3 ? a.shared.inter : 0);
@@ -1190,22 +1132,21 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
 
   dim3 g4(a.H / kDownRows);
   if (down_t1_fits(a)) {
-    const size_t lds =
-        (size_t)(a.K + (a.has_shared && !a2.shared_in_k2 ? 1 : 0)) * a.routed.inter * 2;
+    const size_t lds = (size_t)(a.K + (a.has_shared ? 1 : 0)) * a.routed.inter * 2;
     const int blocks = std::min((a.H + 3) / 4, 512);
     if (f4)
-      hipLaunchKernelGGL((dec_down_t1_kernel<MOE_WFMT_NVFP4>), dim3(blocks), dim3(256), lds, s, a2);
+      hipLaunchKernelGGL((dec_down_t1_kernel<MOE_WFMT_NVFP4>), dim3(blocks), dim3(256), lds, s, a);
     else
       hipLaunchKernelGGL((dec_down_t1_kernel<MOE_WFMT_INT4_G32_F16>), dim3(blocks), dim3(256), lds, s,
-                         a2);
-  } else if (a.T > 1 && down_multi_fits<kDMRows>(a2)) {
+                         a);
+  } else if (a.T > 1 && down_multi_fits<kDMRows>(a)) {
     const int blocks = std::min((a.H + kDMWaves - 1) / kDMWaves, kDMBlocks);
     if (f4)
       hipLaunchKernelGGL((dec_down_multi_kernel<MOE_WFMT_NVFP4, kDMRows, kDMDepth>), dim3(blocks),
-                         dim3(64 * kDMWaves), 0, s, a2);
+                         dim3(64 * kDMWaves), 0, s, a);
     else
       hipLaunchKernelGGL((dec_down_multi_kernel<MOE_WFMT_INT4_G32_F16, kDMRows, kDMDepth>),
-                         dim3(blocks), dim3(64 * kDMWaves), 0, s, a2);
+                         dim3(blocks), dim3(64 * kDMWaves), 0, s, a);
   } else if (a.T == 1) {
     if (f4)
       hipLaunchKernelGGL((dec_down_combine_kernel<MOE_WFMT_NVFP4, 1>), g4, dim3(256), 0, s, a);

@@ -383,7 +383,6 @@ moe_status layer_impl(const moe_config* cfg, int32_t T, const uint16_t* x, const
     if (has_shared) d.shared = expert_set(*shared, cfg->shared_inter);
     d.h_routed = w.h;
     d.h_shared = w.h + P * ldh;
-    d.o_shared = w.O + P * cfg->hidden;
     d.ldh = ldh;
     d.y = y;
     d.out_bf16 = out_dtype == MOE_OUT_BF16;

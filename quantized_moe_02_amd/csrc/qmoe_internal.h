@@ -143,8 +143,8 @@ struct CombineArgs {
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s, Tracer* tr = nullptr);
 
 // Small-batch path of moe_layer (T <= kDecodeMaxTokens): four kernels --
-// router logits with the shared expert's gate/up, selection + permutation,
-// routed gate/up, down with the weighted combine.
+// router logits, selection + grouping of the picks, gate/up, down with the
+// weighted combine.
 constexpr int kDecodeMaxTokens = 4;
 constexpr int kDecodeMaxGPL = 4;   // hidden <= 64 lanes * 4 groups * 32 = 8192
 bool decode_supported(int hidden);
@@ -171,8 +171,6 @@ struct DecodeArgs {
   ExpertSet shared;
   uint16_t* h_routed;  // [P][ldh]
   uint16_t* h_shared;  // [T][ldh]
-  float* o_shared;     // [T][H] shared-expert output when K2 computes it
-  int shared_in_k2;    // K2 runs the shared expert's down projection (T = 1)
   int ldh;
   void* y;
   int out_bf16;
