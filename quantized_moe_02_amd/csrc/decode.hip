@@ -39,8 +39,6 @@ namespace {
 #ifndef QMOE_DEC_DOWN_ROWS
 #define QMOE_DEC_DOWN_ROWS 4
 #endif
-constexpr int kGPL = 3;                      // 32-input groups per lane per pass
-constexpr int kChunk = 64 * kGPL;            // groups covered by one pass of a wave
 constexpr int kRPW = QMOE_DEC_RPW;           // gate/up row pairs per pipeline item
 constexpr int kItems = QMOE_DEC_ITEMS;       // pipeline items per wave (even)
 constexpr int kPairsPerWave = kRPW * kItems;

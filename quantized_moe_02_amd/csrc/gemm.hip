@@ -247,7 +247,6 @@ __global__ void __launch_bounds__(256, BM == kBMThin ? QMOE_THIN_WGS : 1) moe_ge
   // first output row of this wave (gate/up: row pairs)
   const int wrow = PROJ == 0 ? nt * kGateUpPairs + wv * 32 : nt * kDownRows + wv * 64;
   if (nt * (PROJ == 0 ? kGateUpPairs : kDownRows) >= nrow_out) return;
-  const int nG = K / 32;
   const uint32_t rowBytes = (uint32_t)K / 2;
   const int sgpr = FMT == MOE_WFMT_INT4_G32_F16 ? 32 : 16;   // inputs per scale
   const uint32_t scaleRowBytes = (uint32_t)(K / sgpr) * (FMT == MOE_WFMT_INT4_G32_F16 ? 2 : 1);
