@@ -25,13 +25,10 @@ namespace qmoe {
 constexpr int kSelMaxE = 256;
 constexpr int kSelMaxG = 64;
 
-constexpr int kSelMaxK = 16;
-
 // Per-wave LDS scratch of select_token.
 struct alignas(16) SelectScratch {
   double sb[kSelMaxE];   // irregular group shapes only
-  double gs[kSelMaxG];   // group scores
-  int ids[kSelMaxK];     // chosen experts, for their ascending ranks
+  double gs[kSelMaxG];   // group scores (more than 16 groups)
 };
 
 // Orders LDS traffic between lanes of one wave.
@@ -170,15 +167,23 @@ __device__ __forceinline__ void select_token(const double* __restrict__ logits,
     if (L >= 64) top2_swap<32>(m1, m2);
     const double gmine = m1 + m2;
     const int gidx = lane / L;
-    // every lane reads the G group scores from LDS and ranks its own group
-    wave_lds_sync();  // a previous call's reads of `sc` come first
-    if (lane % L == 0) sc.gs[gidx] = gmine;
-    wave_lds_sync();
+    // every lane ranks its own group against the G group scores: up to 16
+    // read straight from the groups' first lanes, more through LDS
     int r = 0;
-    for (int g = 0; g < G; g += 2) {
-      const double2 o2 = *reinterpret_cast<const double2*>(&sc.gs[g]);
-      r += (o2.x > gmine || (o2.x == gmine && g < gidx)) ? 1 : 0;
-      r += (g + 1 < G && (o2.y > gmine || (o2.y == gmine && g + 1 < gidx))) ? 1 : 0;
+    if (G <= 16) {
+      for (int g = 0; g < G; ++g) {
+        const double o = readlane_d(gmine, g * L);
+        r += (o > gmine || (o == gmine && g < gidx)) ? 1 : 0;
+      }
+    } else {
+      wave_lds_sync();  // a previous call's reads of `sc` come first
+      if (lane % L == 0) sc.gs[gidx] = gmine;
+      wave_lds_sync();
+      for (int g = 0; g < G; g += 2) {
+        const double2 o2 = *reinterpret_cast<const double2*>(&sc.gs[g]);
+        r += (o2.x > gmine || (o2.x == gmine && g < gidx)) ? 1 : 0;
+        r += (g + 1 < G && (o2.y > gmine || (o2.y == gmine && g + 1 < gidx))) ? 1 : 0;
+      }
     }
     const bool keep = r < TG;
 #pragma unroll
@@ -281,15 +286,11 @@ __device__ __forceinline__ void select_token(const double* __restrict__ logits,
   }
   my_id = my_id < E ? my_id : 0;
   // ---- ascending order and weights ---------------------------------------
-  if (lane < K) sc.ids[lane] = my_id;
-  wave_lds_sync();
+  // pick j's id sits in lane j (K <= 16)
   rank = 0;
-  for (int j = 0; j < K; j += 4) {
-    const int4 o4 = *reinterpret_cast<const int4*>(&sc.ids[j]);
-    const int o[4] = {o4.x, o4.y, o4.z, o4.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      rank += (j + i < K && (o[i] < my_id || (o[i] == my_id && j + i < lane))) ? 1 : 0;
+  for (int j = 0; j < K; ++j) {
+    const int o = __builtin_amdgcn_readlane(my_id, j);
+    rank += (o < my_id || (o == my_id && j < lane)) ? 1 : 0;
   }
   const double total = wave_sum(lane < K ? my_s : 0.0);
   id = my_id;
