@@ -130,10 +130,10 @@ __global__ void __launch_bounds__(256) route_select_kernel(const double* __restr
 }  // namespace
 
 int route_splits(int T, int H, int E) {
-  // enough waves to fill the chip, at least 8 K blocks of 32 inputs per wave
+  // enough waves to fill the chip, at least 4 K blocks of 32 inputs per wave
   const int waves = ((T + kLogitTok - 1) / kLogitTok) * ((E + kLogitExp - 1) / kLogitExp);
   const int by_waves = (2048 + waves - 1) / waves;
-  const int by_k = H / 32 / 8;
+  const int by_k = H / 32 / 4;
   return std::max(1, std::min(by_waves, by_k));
 }
 

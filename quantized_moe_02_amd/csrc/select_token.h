@@ -130,7 +130,7 @@ __device__ __forceinline__ void select_token(const double* __restrict__ logits,
 #pragma unroll
   for (int j = 0; j < 4; ++j) l[j] = logits[e0 + j < E ? e0 + j : 0];
   // partial sums added in split order; each batch's loads are issued together
-  constexpr int kBatch = 4;
+  constexpr int kBatch = 8;
   for (int sp = 1; sp < nsplit; sp += kBatch) {
     double v[kBatch][4];
 #pragma unroll
