@@ -12,6 +12,7 @@
 //                 pick's slot is its expert's cursor plus its rank among the
 //                 equal picks of the step, after which the cursor advances
 // Counts are integers, so the LDS atomics leave nothing order-dependent.
+// Up to 8192 picks, perm_small does all three steps in one workgroup.
 #include "qmoe_device.h"
 
 namespace qmoe {
@@ -161,6 +162,96 @@ __global__ void __launch_bounds__(64) perm_scatter_kernel(const int32_t* __restr
   }
 }
 
+// Small batches (P <= kSmallP picks): the same stable counting sort in one
+// workgroup of 16 waves, wave w taking the w-th chunk of picks, so that the
+// three launches above become one.  Counts per (chunk, expert) in LDS; each
+// chunk's first slot per expert is the expert's offset plus the counts of
+// the earlier chunks; the scatter is perm_scatter's, one wave per chunk.
+constexpr int kSmallWaves = 16;
+constexpr int kSmallP = 8192;
+
+__global__ void __launch_bounds__(64 * kSmallWaves) perm_small_kernel(
+    const int32_t* __restrict__ ids, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_token,
+    int32_t* __restrict__ inv_perm, int32_t* __restrict__ active, int32_t* __restrict__ n_active, int P,
+    int K, int E) {
+  __shared__ int cnt[kSmallWaves][kMaxE];
+  __shared__ int tot[kMaxE], act[kMaxE];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int chunk = (P + kSmallWaves - 1) / kSmallWaves;
+  const int p0 = min(P, w * chunk), p1 = min(P, p0 + chunk);
+  for (int i = threadIdx.x; i < kSmallWaves * kMaxE; i += 64 * kSmallWaves) (&cnt[0][0])[i] = 0;
+  __syncthreads();
+  for (int p = p0 + lane; p < p1; p += 64) atomicAdd(&cnt[w][ids[p]], 1);
+  __syncthreads();
+  // per expert: exclusive prefix over the chunks, and the total
+  if (threadIdx.x < kMaxE) {
+    const int e = threadIdx.x;
+    int run = 0;
+#pragma unroll
+    for (int c = 0; c < kSmallWaves; ++c) {
+      const int v = cnt[c][e];
+      cnt[c][e] = run;
+      run += v;
+    }
+    tot[e] = e < E ? run : 0;
+    act[e] = e < E && run > 0 ? 1 : 0;
+  }
+  __syncthreads();
+  // inclusive scans of the totals and of the active flags over the experts
+  for (int d = 1; d < kMaxE; d <<= 1) {
+    int c = 0, a = 0;
+    if (threadIdx.x < kMaxE && (int)threadIdx.x >= d) {
+      c = tot[threadIdx.x - d];
+      a = act[threadIdx.x - d];
+    }
+    __syncthreads();
+    if (threadIdx.x < kMaxE) {
+      tot[threadIdx.x] += c;
+      act[threadIdx.x] += a;
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x < kMaxE) {
+    const int e = threadIdx.x;
+    const int incl = tot[e];
+    const int excl = e > 0 ? tot[e - 1] : 0;
+#pragma unroll
+    for (int c = 0; c < kSmallWaves; ++c) cnt[c][e] += excl;
+    if (e < E) {
+      offsets[e] = excl;
+      if (incl > excl) active[act[e] - 1] = e;
+    }
+    if (e == kMaxE - 1) {
+      offsets[E] = incl;
+      n_active[0] = act[e];
+    }
+  }
+  __syncthreads();
+  // scatter: chunk w in pick order, 64 picks at a time
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  const uint64_t below = (1ull << lane) - 1;
+  for (int q = p0; q < p1; q += 64) {
+    const int p = q + lane;
+    const bool valid = p < p1;
+    const int e = valid ? ids[p] : 0;
+    uint64_t m = __builtin_amdgcn_ballot_w64(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool set = (e >> bit) & 1;
+      const uint64_t bb = __builtin_amdgcn_ballot_w64(set);
+      m &= set ? bb : ~bb;
+    }
+    const int rank = __popcll(m & below), n = __popcll(m);
+    const int base = cnt[w][e];
+    if (valid) {
+      inv_perm[p] = base + rank;
+      sorted_token[base + rank] = p / K;
+      if (rank == n - 1) cnt[w][e] = base + n;
+    }
+  }
+}
+
 }  // namespace
 
 int permute_chunk(int T) { return std::max(64, (T + kMaxChunks - 1) / kMaxChunks); }
@@ -171,6 +262,13 @@ size_t permute_hist_ints(int T, int E) {
 
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s, Tracer* tr) {
   if (a.T == 0) return hipSuccess;
+  if ((long)a.T * a.K <= kSmallP) {
+    hipLaunchKernelGGL(perm_small_kernel, dim3(1), dim3(64 * kSmallWaves), 0, s, a.ids, a.offsets,
+                       a.sorted_token, a.inv_perm, a.active, a.n_active, a.T * a.K, a.K, a.E);
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess && tr) e = tr->mark("permute");
+    return e;
+  }
   const int chunk = permute_chunk(a.T);
   const int nb = (a.T + chunk - 1) / chunk;
   hipLaunchKernelGGL(perm_hist_kernel, dim3(nb), dim3(256), 0, s, a.ids, a.hist, a.T, a.K, a.E, chunk);

@@ -116,6 +116,45 @@ def test_tiny_entry_points():
     assert row_rel_err(y.cpu().numpy(), yref).max() <= 1e-6
 
 
+@pytest.mark.parametrize("T,k,E,dist", [
+    (1, 1, 16, "uniform"),
+    (3, 4, 16, "uniform"),
+    (64, 8, 256, "hot"),
+    (1024, 8, 256, "uniform"),     # 8192 picks: the one-workgroup permutation
+    (1025, 8, 256, "uniform"),     # 8200 picks: the three-launch permutation
+    (2048, 4, 16, "one"),
+])
+def test_permute_paths(T, k, E, dist):
+    """moe_permute equals the oracle's stable argsort on seeded ids, on both
+    sides of the one-workgroup bound, with a hot expert and with every pick on
+    one expert."""
+    g = synth.small_geom(n_routed_experts=E, top_k=k, n_group=4, topk_group=4)
+    cfg = q.make_config(g, "int4")
+    rng = np.random.default_rng(7000 + T)
+    if dist == "uniform":
+        ids_np = rng.integers(0, E, size=(T, k))
+    elif dist == "hot":
+        ids_np = np.where(rng.random((T, k)) < 0.7, 5, rng.integers(0, E, size=(T, k)))
+    else:
+        ids_np = np.zeros((T, k), dtype=np.int64)
+    dev = dict(device="cuda")
+    ids = torch.from_numpy(ids_np.astype(np.int32)).to("cuda")
+    P = T * k
+    offs = torch.empty(E + 1, dtype=torch.int32, **dev)
+    st = torch.empty(P, dtype=torch.int32, **dev)
+    inv = torch.empty(P, dtype=torch.int32, **dev)
+    act = torch.empty(E, dtype=torch.int32, **dev)
+    na = torch.empty(1, dtype=torch.int32, **dev)
+    q.moe_permute(cfg, T, ids, offs, st, inv, act, na, q.workspace(cfg, T))
+    torch.cuda.synchronize()
+    r_off, r_st, r_inv, r_act = oracle.permute(ids_np, E)
+    assert np.array_equal(offs.cpu().numpy(), r_off)
+    assert np.array_equal(st.cpu().numpy(), r_st)
+    assert np.array_equal(inv.cpu().numpy(), r_inv)
+    assert int(na.item()) == len(r_act)
+    assert np.array_equal(act.cpu().numpy()[: len(r_act)], r_act)
+
+
 def test_empty_input_is_noop():
     L = layer("tiny")
     cfg = q.make_config(L.geom, L.wfmt)
