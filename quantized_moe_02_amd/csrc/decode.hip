@@ -4,11 +4,14 @@
 // bound, so the kernels are built around keeping many independent 128-bit
 // loads in flight and doing as little else as possible.
 //
-//   K1 dec_router          router logits (float64, one block per expert)
+//   K1 dec_router          router logits (float64, one block per expert);
+//                          for one token, the shared expert's gate/up GEMV
+//                          in the other workgroups
 //   K2 dec_select_permute  one workgroup: per-token selection (one wave per
 //                          token) and the grouping of the <= 64 picks by
-//                          expert (batch union); for one token, the shared
-//                          expert's gate/up GEMV in the other workgroups
+//                          expert (batch union)
+//   one token (dec_fused_t1, when the device's resident grid is known):
+//                          K3 and K4 in one launch with a grid barrier
 //   K3 dec_gateup          gate/up GEMV of every pick's expert with SwiGLU
 //                          (and of the shared expert for 2..4 tokens)
 //   K4                     down GEMV of every selected expert and the shared
@@ -23,6 +26,8 @@
 // dequant-on-use); "NVIDIA stellt neues GLM-5.2 NVFP4 Modell vor" (section
 // "Technische Details": NVFP4 expert weights).
 #include <algorithm>
+#include <atomic>
+#include <cstdlib>
 #include <type_traits>
 
 #include "select_token.h"
@@ -212,8 +217,10 @@ __device__ __forceinline__ void gu_compute(const GateUpItem<GPL, RP>& it,
     g = wave_sum(g);
     u = wave_sum(u);
     if (lane == r) {
+      // a device-scope store: dec_fused_t1 reads h in the same launch
       const _Float16 hv = (_Float16)silu_mul(g, u);
-      hrow[pair0 + r] = __builtin_bit_cast(uint16_t, hv);
+      __hip_atomic_store(hrow + pair0 + r, __builtin_bit_cast(uint16_t, hv), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -279,10 +286,13 @@ __device__ __forceinline__ void gateup_wave(const uint16_t* __restrict__ x, int 
 // ---------------------------------------------------------------------------
 // K1: router logits, one block per expert
 // ---------------------------------------------------------------------------
+// The first workgroups also zero dec_fused_t1's barrier count and flags.
 __global__ void __launch_bounds__(256) dec_router_kernel(DecodeArgs a) {
   __shared__ double rpart[4][kMaxT];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  for (int i = (int)blockIdx.x * 256 + (int)threadIdx.x; i <= kDecFusedMaxGrid; i += (int)gridDim.x * 256)
+    a.bar[kDecFlagStride * i] = 0u;
   {
     // expert e's logits: the four waves take quarters of the hidden dimension
     const int e = blockIdx.x;
@@ -687,11 +697,18 @@ __device__ __forceinline__ void store_y(const DecodeArgs& a, int t, int row, flo
   }
 }
 
-template <int FMT>
-__global__ void __launch_bounds__(256, 2) dec_down_t1_kernel(DecodeArgs a) {
-  extern __shared__ uint4 hl[];
+// Rows gw, gw + nw, ... of y for one token; hl: (k + 1) * inter * 2 bytes of
+// LDS.  FUSED (dec_fused_t1): the weights of the first row are requested
+// before `before_h` (the grid barrier) is called, those of the second and h
+// after it (more rows requested early measured slower: they compete with the
+// last gate/up waves, which the barrier waits for); a false return writes NaN
+// to the rows.  Otherwise h is requested first, and each row's weights while
+// the row before it is reduced.
+template <int FMT, bool FUSED, class BeforeH>
+__device__ __forceinline__ void down_t1_rows(const DecodeArgs& a, uint4* hl, int gw, int nw,
+                                             BeforeH before_h, const int* sel_e = nullptr,
+                                             const float* sel_w = nullptr) {
   const int lane = threadIdx.x & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int H = a.H;
   const int nr = a.K;                       // one token: k distinct experts
   const bool shared = a.has_shared;
@@ -700,20 +717,26 @@ __global__ void __launch_bounds__(256, 2) dec_down_t1_kernel(DecodeArgs a) {
   const int nG = inter / 32;
   const uint32_t rowBytes = (uint32_t)inter / 2;
 
-  // slot records: expert, weight (uniform)
+  // slots in ascending expert order (expert, weight; nvfp4: the expert's
+  // tensor scale), FUSED: from the workgroup's own selection (sel_e, sel_w in
+  // LDS), else from K2's records: lane s reads slot s, then every lane takes
+  // them from there -- one round trip
   int es[kD1MaxRouted];
   float wsl[kD1MaxRouted], gsl[kD1MaxRouted];
+  {
+    const int sl = lane < nr ? lane : 0;
+    const int e_l = FUSED ? sel_e[sl] : a.slots[sl].e;
+    const float w_l = FUSED ? sel_w[sl] : a.slots[sl].w[0];
+    const float g_l = FMT == MOE_WFMT_NVFP4 ? a.routed.down.g[e_l] : 1.0f;
 #pragma unroll
-  for (int s = 0; s < kD1MaxRouted; ++s) {
-    const DecSlot& rec = a.slots[s < nr ? s : 0];
-    es[s] = s < nr ? __builtin_amdgcn_readfirstlane(rec.e) : 0;
-    wsl[s] = s < nr ? __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
-                          __builtin_bit_cast(int, rec.w[0])))
-                    : 0.0f;
+    for (int s = 0; s < kD1MaxRouted; ++s) {
+      es[s] = s < nr ? __builtin_amdgcn_readlane(e_l, s) : 0;
+      wsl[s] = s < nr ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w_l), s))
+                      : 0.0f;
+      gsl[s] = s < nr ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g_l), s))
+                      : 1.0f;
+    }
   }
-#pragma unroll
-  for (int s = 0; s < kD1MaxRouted; ++s)
-    gsl[s] = (FMT == MOE_WFMT_NVFP4 && s < nr) ? a.routed.down.g[es[s]] : 1.0f;
   const float gsh = (FMT == MOE_WFMT_NVFP4 && shared) ? a.shared.down.g[0] : 1.0f;
   const rsrc_t rq = make_rsrc(a.routed.down.q, 0xFFFFFFFFu);
   const rsrc_t rs = make_rsrc(a.routed.down.s, 0xFFFFFFFFu);
@@ -724,20 +747,31 @@ __global__ void __launch_bounds__(256, 2) dec_down_t1_kernel(DecodeArgs a) {
   // row are requested as well
   constexpr int kHPerThread = (kD1MaxRouted + 1) * 256 / 256;   // 16-byte chunks per thread
   const int hper = nG * 4;                  // 16-byte chunks per row
+  // h rows 0..k (the shared expert's row follows the k routed ones); FUSED:
+  // device-scope loads, as the rows were written in this launch
   uint4 hv[kHPerThread];
+  const rsrc_t hr = make_rsrc(a.h_routed, (uint32_t)(ns * a.ldh * 2));
+  auto load_h = [&] {
 #pragma unroll
-  for (int j = 0; j < kHPerThread; ++j) {
-    const int i = threadIdx.x + 256 * j;
-    const int sl = i / hper, rem = i - sl * hper;
-    hv[j] = i < ns * hper ? *reinterpret_cast<const uint4*>(a.h_routed + (size_t)sl * a.ldh + rem * 8)
-                          : make_uint4(0, 0, 0, 0);
-  }
+    for (int j = 0; j < kHPerThread; ++j) {
+      const int i = threadIdx.x + 256 * j;
+      const int sl = i / hper, rem = i - sl * hper;
+      const uint32_t off = (uint32_t)(sl * a.ldh + rem * 8) * 2u;
+      if constexpr (FUSED)
+        hv[j] = i < ns * hper ? bload16_device(hr, off, 0) : make_uint4(0, 0, 0, 0);
+      else
+        hv[j] = i < ns * hper ? *reinterpret_cast<const uint4*>(a.h_routed + (size_t)sl * a.ldh + rem * 8)
+                              : make_uint4(0, 0, 0, 0);
+    }
+  };
+  if constexpr (!FUSED) load_h();
   const bool ok = lane < nG;
   const uint32_t c = ok ? (uint32_t)lane : 0u;
   const uint32_t srow = (uint32_t)nG * 2u;
 
   // B: buffer; routed slots 0..7 and the shared slot
-  uint32_t wq[2][kD1MaxRouted][4], wsc[2][kD1MaxRouted], wqs[2][4], wscs[2];
+  constexpr int NB = 2;                     // row buffers
+  uint32_t wq[NB][kD1MaxRouted][4], wsc[NB][kD1MaxRouted], wqs[NB][4], wscs[NB];
   auto load_row = [&](auto B, int r) {
     constexpr int b = decltype(B)::value;
 #pragma unroll
@@ -753,8 +787,10 @@ __global__ void __launch_bounds__(256, 2) dec_down_t1_kernel(DecodeArgs a) {
       wscs[b] = bload_u16(ss, c * 2u, (uint32_t)r * srow);
     }
   };
-  const int gw = blockIdx.x * 4 + wv, nw = gridDim.x * 4;
   if (gw < H) load_row(std::integral_constant<int, 0>{}, gw);
+  const bool fine = before_h();
+  if (FUSED && gw + nw < H) load_row(std::integral_constant<int, 1>{}, gw + nw);
+  if constexpr (FUSED) load_h();
 #pragma unroll
   for (int j = 0; j < kHPerThread; ++j) {
     const int i = threadIdx.x + 256 * j;
@@ -785,10 +821,12 @@ __global__ void __launch_bounds__(256, 2) dec_down_t1_kernel(DecodeArgs a) {
     h_of(nr, hm);
     hsums = int4_offset(hm);
   }
-  // row r from buffer B, with row r + nw requested into the other buffer
+  // row r from buffer B; row r + nw requested into the other buffer first, or
+  // (FUSED, both buffers filled before the first row) row r + 2 nw into this
+  // one after
   auto row_step = [&](auto B, int r) {
     constexpr int b = decltype(B)::value;
-    if (r + nw < H) load_row(std::integral_constant<int, b ^ 1>{}, r + nw);
+    if (!FUSED && r + nw < H) load_row(std::integral_constant<int, (b + 1) % NB>{}, r + nw);
     float acc = 0.0f;
 #pragma unroll
     for (int s = 0; s < kD1MaxRouted; ++s) {
@@ -805,13 +843,23 @@ __global__ void __launch_bounds__(256, 2) dec_down_t1_kernel(DecodeArgs a) {
       const float d = group_dot_h<FMT>(wqs[b], wscs[b], hm, hsums, gsh);
       acc += ok ? d : 0.0f;
     }
+    if (FUSED && r + NB * nw < H) load_row(B, r + NB * nw);
     const float v = wave_sum(acc);
-    if (lane == 0) store_y(a, 0, r, v);
+    if (lane == 0) store_y(a, 0, r, fine ? v : __builtin_nanf(""));
   };
-  for (int r = gw; r < H; r += 2 * nw) {
-    row_step(std::integral_constant<int, 0>{}, r);
-    if (r + nw < H) row_step(std::integral_constant<int, 1>{}, r + nw);
+  for (int r = gw; r < H; r += NB * nw) {
+    static_for<NB>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      if (r + i * nw < H) row_step(I, r + i * nw);
+    });
   }
+}
+
+template <int FMT>
+__global__ void __launch_bounds__(256, 2) dec_down_t1_kernel(DecodeArgs a) {
+  extern __shared__ uint4 hl[];
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  down_t1_rows<FMT, false>(a, hl, blockIdx.x * 4 + wv, gridDim.x * 4, [] { return true; });
 }
 
 // Whether the single-token down kernel covers this shape; its LDS bytes.
@@ -822,6 +870,114 @@ __host__ __device__ inline bool down_t1_fits(const DecodeArgs& a) {
          (long long)(a.K + 1) * a.routed.inter * 2 <= 65536 &&
          (long long)a.E * a.H * (a.routed.inter / 2) < 0xFFFFFFFFll &&
          (long long)a.E * a.H * nG * 2 < 0xFFFFFFFFll;
+}
+
+// ---------------------------------------------------------------------------
+// K3 and K4 for a single token in one launch (dec_fused_t1): the gate/up
+// GEMVs of the k picks, a barrier across the grid, then the rows of
+// dec_down_t1.  The down weights do not depend on h, so every wave requests
+// its first two rows as soon as its workgroup has arrived at the barrier:
+// the down stream starts while the last gate/up waves finish instead of
+// after a second launch has ramped up.
+//
+// The barrier needs every workgroup resident at once, so the grid is at most
+// what the device holds (hipOccupancyMaxActiveBlocksPerMultiprocessor x CUs,
+// and kDecFusedMaxGrid), and the kernel is launched after K2 on the same stream,
+// with the whole GPU free to it.  h is written and read with device-scope
+// (sc1) accesses, so no cache-wide write-back or invalidate is needed: a
+// workgroup arrives once its waves' stores have completed, by adding one to
+// bar[0]; the last to arrive sets every workgroup's flag (bar[kDecFlagStride *
+// (1 + b)], one per 256 bytes, so that the waiting workgroups do not all poll
+// one address).  K2 zeroes the count and the flags.  The wait is bounded
+// (kBarrierSpins polls); a workgroup that gives up writes NaN to its rows of y
+// rather than a sum over an incomplete h.
+// ---------------------------------------------------------------------------
+constexpr int kFusedPairs = 8;            // gate/up row pairs per wave item
+constexpr int kFusedBlocksPerCU = 2;
+constexpr uint32_t kBarrierSpins = 1u << 16;
+static_assert(32 % kFusedPairs == 0, "an item never straddles an expert (inter is a multiple of 32)");
+
+__device__ __forceinline__ void grid_arrive(uint32_t* bar, uint32_t n) {
+  __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0): this wave's h stores are done
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    uint32_t old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__builtin_amdgcn_readfirstlane(old) == n - 1)
+      for (uint32_t b = lane; b < n; b += 64)
+        __hip_atomic_store(bar + kDecFlagStride * (1 + b), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Whether this workgroup's flag was set within the bound.
+__device__ __forceinline__ bool grid_wait(const uint32_t* bar) {
+  __shared__ int arrived;
+  if (threadIdx.x == 0) {
+    const uint32_t* flag = bar + kDecFlagStride * (1 + blockIdx.x);
+    int ok = 0;
+    for (uint32_t spin = 0; spin < kBarrierSpins; ++spin) {
+      if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+        ok = 1;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    arrived = ok;
+  }
+  __syncthreads();
+  return arrived != 0;
+}
+
+template <int FMT, int GPL>
+__global__ void __launch_bounds__(256, kFusedBlocksPerCU) dec_fused_t1_kernel(DecodeArgs a) {
+  extern __shared__ uint4 hl[];
+  __shared__ SelectScratch sc;
+  __shared__ int sel_e[kD1MaxRouted];
+  __shared__ float sel_w[kD1MaxRouted];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int gw = blockIdx.x * 4 + wv, nw = gridDim.x * 4;
+  if (wv == 0) {
+    // every workgroup selects the token's experts itself (the same result
+    // everywhere), so no workgroup waits for another to publish them;
+    // workgroup 0 writes the layer's ids and weights
+    int id, rank;
+    float w;
+    select_token(a.logits, a.bias, a.E, a.G, a.TG, a.K, a.rsf, sc, id, w, rank);
+    if (lane < a.K) {
+      sel_e[rank] = id;
+      sel_w[rank] = w;
+      if (blockIdx.x == 0) {
+        a.ids[rank] = id;
+        a.tw[rank] = w;
+      }
+    }
+  } else if (a.has_shared) {
+    // meanwhile waves 1..3 run the shared expert's gate/up, two row pairs at
+    // a time
+    const ExpertSet& S = a.shared;
+    const float gg = (FMT == MOE_WFMT_NVFP4) ? S.gate.g[0] : 1.0f;
+    const float gu = (FMT == MOE_WFMT_NVFP4) ? S.up.g[0] : 1.0f;
+    for (int pair0 = 2 * ((int)blockIdx.x * 3 + wv - 1); pair0 < S.inter; pair0 += 2 * 3 * (int)gridDim.x)
+      gateup_wave<FMT, GPL, 2, 1>(a.x, a.H, S.gate, S.up, 0, S.inter, pair0, gg, gu, a.h_shared);
+  }
+  __syncthreads();
+  const ExpertSet& R = a.routed;
+  // wave item it: pick p = it / per_pick (rank p of the k distinct experts),
+  // row pairs [8 m, 8 m + 8) with m = it % per_pick
+  const int per_pick = R.inter / kFusedPairs;
+  for (int it = gw; it < a.K * per_pick; it += nw) {
+    const int p = it / per_pick;
+    const int e = sel_e[p];
+    const float gg = (FMT == MOE_WFMT_NVFP4) ? R.gate.g[e] : 1.0f;
+    const float gu = (FMT == MOE_WFMT_NVFP4) ? R.up.g[e] : 1.0f;
+    gateup_wave<FMT, GPL, kFusedPairs, 1>(a.x, a.H, R.gate, R.up, (size_t)e * R.inter, R.inter,
+                                          (it - p * per_pick) * kFusedPairs, gg, gu,
+                                          a.h_routed + (size_t)p * a.ldh);
+  }
+  grid_arrive(a.bar, gridDim.x);
+  down_t1_rows<FMT, true>(a, hl, gw, nw, [&] { return grid_wait(a.bar); }, sel_e, sel_w);
 }
 
 // ---------------------------------------------------------------------------
@@ -1090,6 +1246,49 @@ hipError_t launch_k3(const DecodeArgs& a, hipStream_t s, dim3 grid) {
   return hipGetLastError();
 }
 
+// Grid of dec_fused_t1<FMT, GPL> on the current device: the workgroups it
+// holds at once (at most kFusedBlocksPerCU per CU) for the largest LDS size
+// down_t1_fits allows; 0 if that cannot be determined.  Cached per device.
+template <int FMT, int GPL>
+int fused_grid_of() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];   // 0: not known yet, -1: none
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v != 0) return v < 0 ? 0 : v;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, dec_fused_t1_kernel<FMT, GPL>, 256,
+                                                   65536) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    per_cu = cus = 0;
+  v = std::min(std::min(per_cu, kFusedBlocksPerCU) * cus, kDecFusedMaxGrid);
+  (void)hipGetLastError();
+  cache[dev].store(v > 0 ? v : -1, std::memory_order_relaxed);
+  return v > 0 ? v : 0;
+}
+template <int GPL>
+int fused_grid(bool f4) {
+  return f4 ? fused_grid_of<MOE_WFMT_NVFP4, GPL>() : fused_grid_of<MOE_WFMT_INT4_G32_F16, GPL>();
+}
+
+template <int GPL>
+hipError_t launch_fused(const DecodeArgs& a, hipStream_t s, size_t lds, int grid) {
+  if (a.wfmt == MOE_WFMT_NVFP4)
+    hipLaunchKernelGGL((dec_fused_t1_kernel<MOE_WFMT_NVFP4, GPL>), dim3(grid), dim3(256), lds, s, a);
+  else
+    hipLaunchKernelGGL((dec_fused_t1_kernel<MOE_WFMT_INT4_G32_F16, GPL>), dim3(grid), dim3(256), lds,
+                       s, a);
+  return hipGetLastError();
+}
+
+// QMOE_DECODE_FUSED=0 in the environment turns dec_fused_t1 off (one token
+// then takes K3 and dec_down_t1).
+bool fused_enabled() {
+  const char* v = std::getenv("QMOE_DECODE_FUSED");
+  return !(v && v[0] == '0' && v[1] == '\0');
+}
+
 }  // namespace
 
 bool decode_supported(int H) { return H / 32 <= 64 * kDecodeMaxGPL; }
@@ -1099,9 +1298,31 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
   hipError_t e;
   const int gpl = (a.H / 32 + 63) / 64;
   const bool f4 = a.wfmt == MOE_WFMT_NVFP4;
+  // one token: selection, the shared expert's gate/up and K3/K4 in
+  // dec_fused_t1 when the device's resident grid is known
+  int fgrid = 0;
+  if (down_t1_fits(a) && fused_enabled()) {
+    switch (gpl) {
+      case 1: fgrid = fused_grid<1>(f4); break;
+      case 2: fgrid = fused_grid<2>(f4); break;
+      case 3: fgrid = fused_grid<3>(f4); break;
+      default: fgrid = fused_grid<4>(f4); break;
+    }
+  }
   hipLaunchKernelGGL(dec_router_kernel, dim3(a.E), dim3(256), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (tr && (e = tr->mark("dec_router")) != hipSuccess) return e;
+  const size_t lds1 = (size_t)(a.K + (a.has_shared ? 1 : 0)) * a.routed.inter * 2;
+  if (fgrid > 0) {
+    switch (gpl) {
+      case 1: e = launch_fused<1>(a, s, lds1, fgrid); break;
+      case 2: e = launch_fused<2>(a, s, lds1, fgrid); break;
+      case 3: e = launch_fused<3>(a, s, lds1, fgrid); break;
+      default: e = launch_fused<4>(a, s, lds1, fgrid); break;
+    }
+    if (e != hipSuccess) return e;
+    return tr ? tr->mark("dec_fused_t1") : hipSuccess;
+  }
 
   // one token: the shared expert's gate/up in K2, beside the selection; more
   // tokens: as extra blocks of K3
@@ -1130,12 +1351,11 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
 
   dim3 g4(a.H / kDownRows);
   if (down_t1_fits(a)) {
-    const size_t lds = (size_t)(a.K + (a.has_shared ? 1 : 0)) * a.routed.inter * 2;
     const int blocks = std::min((a.H + 3) / 4, 512);
     if (f4)
-      hipLaunchKernelGGL((dec_down_t1_kernel<MOE_WFMT_NVFP4>), dim3(blocks), dim3(256), lds, s, a);
+      hipLaunchKernelGGL((dec_down_t1_kernel<MOE_WFMT_NVFP4>), dim3(blocks), dim3(256), lds1, s, a);
     else
-      hipLaunchKernelGGL((dec_down_t1_kernel<MOE_WFMT_INT4_G32_F16>), dim3(blocks), dim3(256), lds, s,
+      hipLaunchKernelGGL((dec_down_t1_kernel<MOE_WFMT_INT4_G32_F16>), dim3(blocks), dim3(256), lds1, s,
                          a);
   } else if (a.T > 1 && down_multi_fits<kDMRows>(a)) {
     const int blocks = std::min((a.H + kDMWaves - 1) / kDMWaves, kDMBlocks);

@@ -152,6 +152,7 @@ Workspace carve_workspace(const moe_config& c, int T, void* base) {
   const size_t o_ntiles = take(4 * sizeof(int32_t));
   const size_t o_dslots = take(kDecMaxSlots * sizeof(DecSlot));
   const size_t o_dpick = take(kDecMaxSlots * sizeof(int32_t));
+  const size_t o_dbar = take(kDecBarrierWords * sizeof(uint32_t));
   const size_t o_phist = take(permute_hist_ints(T, (int)E) * sizeof(int32_t));
   w.total = off;
   if (base) {
@@ -172,6 +173,7 @@ Workspace carve_workspace(const moe_config& c, int T, void* base) {
     w.n_tiles = reinterpret_cast<int32_t*>(b + o_ntiles);
     w.dslots = reinterpret_cast<DecSlot*>(b + o_dslots);
     w.dpick = reinterpret_cast<int32_t*>(b + o_dpick);
+    w.dbar = reinterpret_cast<uint32_t*>(b + o_dbar);
     w.phist = reinterpret_cast<int32_t*>(b + o_phist);
   }
   return w;
@@ -378,6 +380,7 @@ moe_status layer_impl(const moe_config* cfg, int32_t T, const uint16_t* x, const
     d.sorted_w = w.sorted_w;
     d.slots = w.dslots;
     d.sorted_et = w.dpick;
+    d.bar = w.dbar;
     d.routed = expert_set(*routed, cfg->moe_inter);
     d.has_shared = has_shared;
     if (has_shared) d.shared = expert_set(*shared, cfg->shared_inter);

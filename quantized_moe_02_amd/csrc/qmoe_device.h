@@ -127,6 +127,13 @@ __device__ __forceinline__ void bload16(uint32_t (&d)[4], rsrc_t r, uint32_t vof
   d[2] = v[2];
   d[3] = v[3];
 }
+// The same 16-byte load at device scope (sc1): it reads what other
+// workgroups' device-scope stores wrote during this launch.
+__device__ __forceinline__ uint4 bload16_device(rsrc_t r, uint32_t voff, uint32_t soff) {
+  constexpr int kSc1 = 16;   // cache-policy bit of device (agent) scope
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kSc1);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
 __device__ __forceinline__ uint32_t bload_u16(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
 }

@@ -51,6 +51,7 @@ struct Workspace {
   int4* tiles;            // [max units] GEMM work units
   DecSlot* dslots;        // [kDecMaxSlots] decode path: selected experts
   int32_t* dpick;         // [kDecMaxSlots] decode path: expert | token << 16 of each sorted pick
+  uint32_t* dbar;         // [kDecBarrierWords] decode path: grid-barrier count and flags
   int32_t* n_tiles;       // [4]
   int32_t* phist;         // [permute_hist_ints] permutation scratch
   size_t total;
@@ -147,6 +148,11 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s, Tracer* tr = null
 // weighted combine.
 constexpr int kDecodeMaxTokens = 4;
 constexpr int kDecodeMaxGPL = 4;   // hidden <= 64 lanes * 4 groups * 32 = 8192
+// Grid barrier of the fused single-token kernel: an arrival count and one
+// flag per workgroup (at most kDecFusedMaxGrid), kDecFlagStride words apart.
+constexpr int kDecFlagStride = 64;
+constexpr int kDecFusedMaxGrid = 1024;
+constexpr size_t kDecBarrierWords = (size_t)kDecFlagStride * (kDecFusedMaxGrid + 1);
 bool decode_supported(int hidden);
 
 struct DecodeArgs {
@@ -166,6 +172,7 @@ struct DecodeArgs {
   float* sorted_w;
   DecSlot* slots;
   int32_t* sorted_et;     // [P] expert (low 16 bits) and token (high 16 bits) of sorted pick p
+  uint32_t* bar;          // grid-barrier arrival count of the fused single-token kernel
   ExpertSet routed;
   bool has_shared;
   ExpertSet shared;

@@ -277,6 +277,26 @@ def test_decode_poisoned_workspace_reused():
         check_outputs(L, y, ids_g, x_np=xn)
 
 
+@pytest.mark.parametrize("case", ["T1", "nvfp4_T1", "decode"])
+def test_single_token_fused_matches_two_launches(case, monkeypatch):
+    """One token runs gate/up and down in one launch with a grid barrier
+    between them; QMOE_DECODE_FUSED=0 selects the two-launch kernels, which
+    sum in the same order.  Both match the oracle, and each other bit for
+    bit."""
+    if case == "decode":
+        L = layer("decode")
+    else:
+        over, T, wfmt, bias = EDGE[case]
+        L = synth.make_custom(synth.small_geom(**over), T, wfmt, bias, seed=300, device="cuda")
+    fused = run_layer(L)
+    monkeypatch.setenv("QMOE_DECODE_FUSED", "0")
+    split = run_layer(L)
+    ids_g, _ = check_routing(L, split[1], split[2])
+    check_outputs(L, split[0], ids_g)
+    for u, v in zip(fused, split):
+        assert torch.equal(u, v)
+
+
 def test_full_verify4():
     _full("verify4", 4)
 
