@@ -4,14 +4,17 @@
 // bound, so the kernels are built around keeping many independent 128-bit
 // loads in flight and doing as little else as possible.
 //
-//   K1 dec_router          router logits (float64, one block per expert);
-//                          for one token, the shared expert's gate/up GEMV
-//                          in the other workgroups
+//   K1 dec_router          router scores (float64 logits through the
+//                          sigmoid, one block per expert)
+//   one token, when the device's resident grid is known: dec_fused_t1 --
+//                          every workgroup selects the experts itself, then
+//                          the shared and routed gate/up GEMVs, a grid
+//                          barrier, and the down GEMV with the combine
+//   otherwise:
 //   K2 dec_select_permute  one workgroup: per-token selection (one wave per
 //                          token) and the grouping of the <= 64 picks by
-//                          expert (batch union)
-//   one token (dec_fused_t1, when the device's resident grid is known):
-//                          K3 and K4 in one launch with a grid barrier
+//                          expert (batch union); for one token, the shared
+//                          expert's gate/up GEMV in the other workgroups
 //   K3 dec_gateup          gate/up GEMV of every pick's expert with SwiGLU
 //                          (and of the shared expert for 2..4 tokens)
 //   K4                     down GEMV of every selected expert and the shared
@@ -284,7 +287,7 @@ __device__ __forceinline__ void gateup_wave(const uint16_t* __restrict__ x, int 
 }
 
 // ---------------------------------------------------------------------------
-// K1: router logits, one block per expert
+// K1: router scores sigmoid(logit) in float64, one block per expert
 // ---------------------------------------------------------------------------
 // The first workgroups also zero dec_fused_t1's barrier count and flags.
 __global__ void __launch_bounds__(256) dec_router_kernel(DecodeArgs a) {
@@ -337,10 +340,12 @@ __global__ void __launch_bounds__(256) dec_router_kernel(DecodeArgs a) {
       if (lane == 0) rpart[wv][t] = v;
     }
     __syncthreads();
-    if (threadIdx.x < T)
-      a.logits[(size_t)threadIdx.x * a.E + e] =
-          ((rpart[0][threadIdx.x] + rpart[1][threadIdx.x]) + rpart[2][threadIdx.x]) +
-          rpart[3][threadIdx.x];
+    // the sigmoid score: the selection reads scores, not logits
+    if (threadIdx.x < T) {
+      const double l = ((rpart[0][threadIdx.x] + rpart[1][threadIdx.x]) + rpart[2][threadIdx.x]) +
+                       rpart[3][threadIdx.x];
+      a.logits[(size_t)threadIdx.x * a.E + e] = 1.0 / (1.0 + exp(-l));
+    }
   }
 }
 
@@ -381,7 +386,7 @@ __global__ void __launch_bounds__(256) dec_select_permute_kernel(DecodeArgs a) {
     if (wv != 0) return;
     int id, rank;
     float w;
-    select_token(a.logits, a.bias, a.E, a.G, a.TG, K, a.rsf, sc[0], id, w, rank);
+    select_token<true>(a.logits, a.bias, a.E, a.G, a.TG, K, a.rsf, sc[0], id, w, rank);
     if (lane < K) {
       a.ids[rank] = id;
       a.tw[rank] = w;
@@ -404,7 +409,7 @@ __global__ void __launch_bounds__(256) dec_select_permute_kernel(DecodeArgs a) {
   if (wv < a.T) {
     int id, rank;
     float w;
-    select_token(a.logits + (size_t)wv * a.E, a.bias, a.E, a.G, a.TG, K, a.rsf, sc[wv], id, w,
+    select_token<true>(a.logits + (size_t)wv * a.E, a.bias, a.E, a.G, a.TG, K, a.rsf, sc[wv], id, w,
                  rank);
     if (lane < K) {
       a.ids[wv * K + rank] = id;
@@ -704,7 +709,7 @@ __device__ __forceinline__ void store_y(const DecodeArgs& a, int t, int row, flo
 // last gate/up waves, which the barrier waits for); a false return writes NaN
 // to the rows.  Otherwise h is requested first, and each row's weights while
 // the row before it is reduced.
-template <int FMT, bool FUSED, class BeforeH>
+template <int FMT, bool FUSED, int NT, class BeforeH>
 __device__ __forceinline__ void down_t1_rows(const DecodeArgs& a, uint4* hl, int gw, int nw,
                                              BeforeH before_h, const int* sel_e = nullptr,
                                              const float* sel_w = nullptr) {
@@ -745,7 +750,7 @@ __device__ __forceinline__ void down_t1_rows(const DecodeArgs& a, uint4* hl, int
   // h of all slots (rows 0..k-1 routed in slot order, row k shared): every
   // load is issued here, the LDS writes wait until the weights of the first
   // row are requested as well
-  constexpr int kHPerThread = (kD1MaxRouted + 1) * 256 / 256;   // 16-byte chunks per thread
+  constexpr int kHPerThread = ((kD1MaxRouted + 1) * 256 + NT - 1) / NT;   // 16-byte chunks per thread
   const int hper = nG * 4;                  // 16-byte chunks per row
   // h rows 0..k (the shared expert's row follows the k routed ones); FUSED:
   // device-scope loads, as the rows were written in this launch
@@ -754,7 +759,7 @@ __device__ __forceinline__ void down_t1_rows(const DecodeArgs& a, uint4* hl, int
   auto load_h = [&] {
 #pragma unroll
     for (int j = 0; j < kHPerThread; ++j) {
-      const int i = threadIdx.x + 256 * j;
+      const int i = threadIdx.x + NT * j;
       const int sl = i / hper, rem = i - sl * hper;
       const uint32_t off = (uint32_t)(sl * a.ldh + rem * 8) * 2u;
       if constexpr (FUSED)
@@ -793,7 +798,7 @@ __device__ __forceinline__ void down_t1_rows(const DecodeArgs& a, uint4* hl, int
   if constexpr (FUSED) load_h();
 #pragma unroll
   for (int j = 0; j < kHPerThread; ++j) {
-    const int i = threadIdx.x + 256 * j;
+    const int i = threadIdx.x + NT * j;
     const int sl = i / hper, rem = i - sl * hper;
     if (i < ns * hper) hl[(sl * 4 + (rem & 3)) * nG + (rem >> 2)] = hv[j];
   }
@@ -859,7 +864,7 @@ template <int FMT>
 __global__ void __launch_bounds__(256, 2) dec_down_t1_kernel(DecodeArgs a) {
   extern __shared__ uint4 hl[];
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  down_t1_rows<FMT, false>(a, hl, blockIdx.x * 4 + wv, gridDim.x * 4, [] { return true; });
+  down_t1_rows<FMT, false, 256>(a, hl, blockIdx.x * 4 + wv, gridDim.x * 4, [] { return true; });
 }
 
 // Whether the single-token down kernel covers this shape; its LDS bytes.
@@ -873,27 +878,32 @@ __host__ __device__ inline bool down_t1_fits(const DecodeArgs& a) {
 }
 
 // ---------------------------------------------------------------------------
-// K3 and K4 for a single token in one launch (dec_fused_t1): the gate/up
-// GEMVs of the k picks, a barrier across the grid, then the rows of
-// dec_down_t1.  The down weights do not depend on h, so every wave requests
-// its first two rows as soon as its workgroup has arrived at the barrier:
-// the down stream starts while the last gate/up waves finish instead of
-// after a second launch has ramped up.
+// One token after K1 in one launch (dec_fused_t1): every workgroup selects
+// the experts itself from K1's scores (wave 0; the same result everywhere, so
+// no workgroup waits for another to publish it) while its other waves run the
+// shared expert's gate/up; then the gate/up GEMVs of the k picks, a barrier
+// across the grid, and the rows of dec_down_t1.  The down weights do not
+// depend on h, so every wave requests its first row as soon as its workgroup
+// has arrived at the barrier: the down stream starts while the last gate/up
+// waves finish, and neither K2 nor K4 ramps up a launch of its own.
 //
-// The barrier needs every workgroup resident at once, so the grid is at most
-// what the device holds (hipOccupancyMaxActiveBlocksPerMultiprocessor x CUs,
-// and kDecFusedMaxGrid), and the kernel is launched after K2 on the same stream,
+// One workgroup of kFusedWaves waves per CU: each workgroup stages all of h
+// in LDS after the barrier, so fewer, larger workgroups read less of it.  The
+// barrier needs every workgroup resident at once, so the grid is at most what
+// the device holds (hipOccupancyMaxActiveBlocksPerMultiprocessor x CUs, and
+// kDecFusedMaxGrid), and the kernel is launched after K1 on the same stream,
 // with the whole GPU free to it.  h is written and read with device-scope
 // (sc1) accesses, so no cache-wide write-back or invalidate is needed: a
 // workgroup arrives once its waves' stores have completed, by adding one to
 // bar[0]; the last to arrive sets every workgroup's flag (bar[kDecFlagStride *
 // (1 + b)], one per 256 bytes, so that the waiting workgroups do not all poll
-// one address).  K2 zeroes the count and the flags.  The wait is bounded
+// one address).  K1 zeroes the count and the flags.  The wait is bounded
 // (kBarrierSpins polls); a workgroup that gives up writes NaN to its rows of y
 // rather than a sum over an incomplete h.
 // ---------------------------------------------------------------------------
 constexpr int kFusedPairs = 8;            // gate/up row pairs per wave item
-constexpr int kFusedBlocksPerCU = 2;
+constexpr int kFusedWaves = 8;           // waves per workgroup, one workgroup per CU
+constexpr int kFusedBlocksPerCU = 1;
 constexpr uint32_t kBarrierSpins = 1u << 16;
 static_assert(32 % kFusedPairs == 0, "an item never straddles an expert (inter is a multiple of 32)");
 
@@ -930,21 +940,21 @@ __device__ __forceinline__ bool grid_wait(const uint32_t* bar) {
 }
 
 template <int FMT, int GPL>
-__global__ void __launch_bounds__(256, kFusedBlocksPerCU) dec_fused_t1_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(64 * kFusedWaves, kFusedBlocksPerCU) dec_fused_t1_kernel(DecodeArgs a) {
   extern __shared__ uint4 hl[];
   __shared__ SelectScratch sc;
   __shared__ int sel_e[kD1MaxRouted];
   __shared__ float sel_w[kD1MaxRouted];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int gw = blockIdx.x * 4 + wv, nw = gridDim.x * 4;
+  const int gw = blockIdx.x * kFusedWaves + wv, nw = gridDim.x * kFusedWaves;
   if (wv == 0) {
     // every workgroup selects the token's experts itself (the same result
     // everywhere), so no workgroup waits for another to publish them;
     // workgroup 0 writes the layer's ids and weights
     int id, rank;
     float w;
-    select_token(a.logits, a.bias, a.E, a.G, a.TG, a.K, a.rsf, sc, id, w, rank);
+    select_token<true>(a.logits, a.bias, a.E, a.G, a.TG, a.K, a.rsf, sc, id, w, rank);
     if (lane < a.K) {
       sel_e[rank] = id;
       sel_w[rank] = w;
@@ -954,12 +964,13 @@ __global__ void __launch_bounds__(256, kFusedBlocksPerCU) dec_fused_t1_kernel(De
       }
     }
   } else if (a.has_shared) {
-    // meanwhile waves 1..3 run the shared expert's gate/up, two row pairs at
-    // a time
+    // meanwhile the other waves run the shared expert's gate/up, two row
+    // pairs at a time
     const ExpertSet& S = a.shared;
     const float gg = (FMT == MOE_WFMT_NVFP4) ? S.gate.g[0] : 1.0f;
     const float gu = (FMT == MOE_WFMT_NVFP4) ? S.up.g[0] : 1.0f;
-    for (int pair0 = 2 * ((int)blockIdx.x * 3 + wv - 1); pair0 < S.inter; pair0 += 2 * 3 * (int)gridDim.x)
+    constexpr int kW = kFusedWaves - 1;
+    for (int pair0 = 2 * ((int)blockIdx.x * kW + wv - 1); pair0 < S.inter; pair0 += 2 * kW * (int)gridDim.x)
       gateup_wave<FMT, GPL, 2, 1>(a.x, a.H, S.gate, S.up, 0, S.inter, pair0, gg, gu, a.h_shared);
   }
   __syncthreads();
@@ -977,7 +988,7 @@ __global__ void __launch_bounds__(256, kFusedBlocksPerCU) dec_fused_t1_kernel(De
                                           a.h_routed + (size_t)p * a.ldh);
   }
   grid_arrive(a.bar, gridDim.x);
-  down_t1_rows<FMT, true>(a, hl, gw, nw, [&] { return grid_wait(a.bar); }, sel_e, sel_w);
+  down_t1_rows<FMT, true, 64 * kFusedWaves>(a, hl, gw, nw, [&] { return grid_wait(a.bar); }, sel_e, sel_w);
 }
 
 // ---------------------------------------------------------------------------
@@ -1258,8 +1269,8 @@ int fused_grid_of() {
   int v = cache[dev].load(std::memory_order_relaxed);
   if (v != 0) return v < 0 ? 0 : v;
   int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, dec_fused_t1_kernel<FMT, GPL>, 256,
-                                                   65536) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, dec_fused_t1_kernel<FMT, GPL>,
+                                                   64 * kFusedWaves, 65536) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     per_cu = cus = 0;
   v = std::min(std::min(per_cu, kFusedBlocksPerCU) * cus, kDecFusedMaxGrid);
@@ -1275,10 +1286,11 @@ int fused_grid(bool f4) {
 template <int GPL>
 hipError_t launch_fused(const DecodeArgs& a, hipStream_t s, size_t lds, int grid) {
   if (a.wfmt == MOE_WFMT_NVFP4)
-    hipLaunchKernelGGL((dec_fused_t1_kernel<MOE_WFMT_NVFP4, GPL>), dim3(grid), dim3(256), lds, s, a);
+    hipLaunchKernelGGL((dec_fused_t1_kernel<MOE_WFMT_NVFP4, GPL>), dim3(grid), dim3(64 * kFusedWaves),
+                       lds, s, a);
   else
-    hipLaunchKernelGGL((dec_fused_t1_kernel<MOE_WFMT_INT4_G32_F16, GPL>), dim3(grid), dim3(256), lds,
-                       s, a);
+    hipLaunchKernelGGL((dec_fused_t1_kernel<MOE_WFMT_INT4_G32_F16, GPL>), dim3(grid),
+                       dim3(64 * kFusedWaves), lds, s, a);
   return hipGetLastError();
 }
 

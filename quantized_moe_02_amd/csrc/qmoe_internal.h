@@ -161,7 +161,7 @@ struct DecodeArgs {
   float rsf;
   const float* router_w;
   const float* bias;
-  double* logits;
+  double* logits;         // [T][E] router scores (sigmoid of the float64 logits)
   int32_t* ids;
   float* tw;
   int32_t* offsets;

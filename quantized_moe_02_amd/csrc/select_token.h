@@ -118,7 +118,10 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // Lanes < K return their chosen expert in `id`, its weight in `w` and its
 // position in ascending id order in `rank`.  `logits` points at the token's E
 // float64 logits, given as `nsplit` partial sums `split_stride` apart (added
-// in order).  Must be called by all 64 lanes of the wave.
+// in order); SCORES: at the E sigmoid scores instead (nsplit 1), computed
+// where the logits were, off this wave's critical path.  Must be called by
+// all 64 lanes of the wave.
+template <bool SCORES = false>
 __device__ __forceinline__ void select_token(const double* __restrict__ logits,
                                              const float* __restrict__ bias, int E, int G, int TG,
                                              int K, float rsf, SelectScratch& sc, int& id, float& w,
@@ -127,8 +130,12 @@ __device__ __forceinline__ void select_token(const double* __restrict__ logits,
   const int per = E / G;
   const int e0 = 4 * lane;
   double s[4], sb[4], l[4];
+  float bv[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) l[j] = logits[e0 + j < E ? e0 + j : 0];
+  for (int j = 0; j < 4; ++j) {
+    l[j] = logits[e0 + j < E ? e0 + j : 0];
+    bv[j] = bias ? bias[e0 + j < E ? e0 + j : 0] : 0.0f;
+  }
   // partial sums added in split order; each batch's loads are issued together
   constexpr int kBatch = 8;
   for (int sp = 1; sp < nsplit; sp += kBatch) {
@@ -148,8 +155,8 @@ __device__ __forceinline__ void select_token(const double* __restrict__ logits,
   for (int j = 0; j < 4; ++j) {
     const int e = e0 + j;
     const bool in = e < E;
-    s[j] = 1.0 / (1.0 + exp(-l[j]));
-    sb[j] = in ? s[j] + (bias ? (double)bias[e] : 0.0) : -INFINITY;
+    s[j] = SCORES ? l[j] : 1.0 / (1.0 + exp(-l[j]));
+    sb[j] = in ? s[j] + (double)bv[j] : -INFINITY;
   }
   // ---- group scores and kept groups ------------------------------------
   const int L = per / 4;  // lanes per group when groups are whole lanes
