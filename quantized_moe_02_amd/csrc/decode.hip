@@ -704,8 +704,8 @@ __device__ __forceinline__ void store_y(const DecodeArgs& a, int t, int row, flo
 
 // Rows gw, gw + nw, ... of y for one token; hl: (k + 1) * inter * 2 bytes of
 // LDS.  FUSED (dec_fused_t1): the weights of the first row are requested
-// before `before_h` (the grid barrier) is called, those of the second and h
-// after it (more rows requested early measured slower: they compete with the
+// before `before_h` (the grid barrier) is called, h and then the second row's
+// weights after it (more rows requested early measured slower: they compete with the
 // last gate/up waves, which the barrier waits for); a false return writes NaN
 // to the rows.  Otherwise h is requested first, and each row's weights while
 // the row before it is reduced.
@@ -794,8 +794,8 @@ __device__ __forceinline__ void down_t1_rows(const DecodeArgs& a, uint4* hl, int
   };
   if (gw < H) load_row(std::integral_constant<int, 0>{}, gw);
   const bool fine = before_h();
+  if constexpr (FUSED) load_h();   // first, so that it does not queue behind the second row
   if (FUSED && gw + nw < H) load_row(std::integral_constant<int, 1>{}, gw + nw);
-  if constexpr (FUSED) load_h();
 #pragma unroll
   for (int j = 0; j < kHPerThread; ++j) {
     const int i = threadIdx.x + NT * j;
