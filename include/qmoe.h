@@ -182,7 +182,15 @@ moe_status moe_combine(const moe_config* cfg, int32_t T, const float* expert_out
  *   routed   E experts (inter = moe_inter)
  *   shared   one expert (inter = shared_inter); NULL iff n_shared_experts == 0
  *   y        [T][H] fp32 or bf16
- *   topk_ids_out, topk_w_out  optional copies of the routing ([T][k]), or NULL */
+ *   topk_ids_out, topk_w_out  optional copies of the routing ([T][k]), or NULL
+ * For one token in the usual decode shapes (top_k <= 8, moe_inter <= 2048,
+ * shared_inter equal to moe_inter if there is a shared expert), one of the
+ * kernels sizes its grid to what the device holds at once and has its
+ * workgroups wait for each other; it expects the device to itself while it
+ * runs.  If other work keeps some of its workgroups from starting, the wait
+ * gives up after a bounded time and the rows of y it could not finish are
+ * NaN.  Setting QMOE_DECODE_FUSED=0 in the environment selects kernels that
+ * do not wait for each other (same results, bit for bit). */
 moe_status moe_layer(const moe_config* cfg, int32_t T, const uint16_t* x,
                      const float* router_w, const float* bias, const moe_qexperts* routed,
                      const moe_qexperts* shared, void* y, int32_t out_dtype,
