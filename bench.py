@@ -240,13 +240,28 @@ def time_steps(B: Bench, steps, warmup, use_graph):
             g.replay()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        return n, (t1 - t0)
+        # per-step spread, from events around each replay (after the timed run)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record()
+        for j in range(reps):
+            g.replay()
+            ev[j + 1].record()
+        torch.cuda.synchronize()
+        per = [ev[j].elapsed_time(ev[j + 1]) * 1e3 / R for j in range(reps)]
+        return n, (t1 - t0), per
     t0 = time.perf_counter()
     for i in range(steps):
         B.step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    return steps, (t1 - t0)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
+        B.step(i)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(steps)]
+    return steps, (t1 - t0), per
 
 
 def trace_kernels(B: Bench, steps):
@@ -284,7 +299,7 @@ def run_workload(name, args):
     B = Bench(name, replicas)
     steps = args.steps or (400 if decode_like else (40 if T <= 4096 else 12))
     warmup = args.warmup if args.warmup is not None else (20 if decode_like else 3)
-    n, dt = time_steps(B, steps, warmup, use_graph=decode_like)
+    n, dt, per_step = time_steps(B, steps, warmup, use_graph=decode_like)
     B.step(0)
     torch.cuda.synchronize()
     n_active = B.n_active()
@@ -294,7 +309,11 @@ def run_workload(name, args):
                ms_per_step=s_per_step * 1e3, tokens_per_s=B.T / s_per_step,
                hbm_gbs=lb / s_per_step / 1e9, hbm_pct_peak=100 * lb / s_per_step / 1e9 / PEAK_HBM_GBS,
                tflops=lf / s_per_step / 1e12, active_experts=n_active,
-               algorithmic_bytes=lb, algorithmic_flops=lf, graph=decode_like)
+               algorithmic_bytes=lb, algorithmic_flops=lf, graph=decode_like,
+               # spread over a second run of the same steps, one event pair per step
+               # (per graph replay of `replicas` steps for decode-sized workloads)
+               step_us={"p10": float(np.percentile(per_step, 10)), "median": float(np.median(per_step)),
+                        "p90": float(np.percentile(per_step, 90))})
     if not args.no_trace:
         ksteps = min(steps, 64 if decode_like else 8)
         kt = trace_kernels(B, ksteps)
