@@ -920,13 +920,13 @@ __device__ __forceinline__ void grid_arrive(uint32_t* bar, uint32_t n) {
   }
 }
 
-// Whether this workgroup's flag was set within the bound.
-__device__ __forceinline__ bool grid_wait(const uint32_t* bar) {
+// Whether this workgroup's flag was set within `spins` polls.
+__device__ __forceinline__ bool grid_wait(const uint32_t* bar, uint32_t spins) {
   __shared__ int arrived;
   if (threadIdx.x == 0) {
     const uint32_t* flag = bar + kDecFlagStride * (1 + blockIdx.x);
     int ok = 0;
-    for (uint32_t spin = 0; spin < kBarrierSpins; ++spin) {
+    for (uint32_t spin = 0; spin < spins; ++spin) {
       if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
         ok = 1;
         break;
@@ -988,7 +988,8 @@ __global__ void __launch_bounds__(64 * kFusedWaves, kFusedBlocksPerCU) dec_fused
                                           a.h_routed + (size_t)p * a.ldh);
   }
   grid_arrive(a.bar, gridDim.x);
-  down_t1_rows<FMT, true, 64 * kFusedWaves>(a, hl, gw, nw, [&] { return grid_wait(a.bar); }, sel_e, sel_w);
+  down_t1_rows<FMT, true, 64 * kFusedWaves>(a, hl, gw, nw, [&] { return grid_wait(a.bar, a.barrier_spins); },
+                                            sel_e, sel_w);
 }
 
 // ---------------------------------------------------------------------------
@@ -1301,6 +1302,17 @@ bool fused_enabled() {
   return !(v && v[0] == '0' && v[1] == '\0');
 }
 
+// Polls a workgroup of dec_fused_t1 makes before it gives up on the barrier:
+// kBarrierSpins, or QMOE_BARRIER_SPINS from the environment (a test sets it to
+// 0 to exercise the give-up path without waiting).
+uint32_t barrier_spins() {
+  const char* v = std::getenv("QMOE_BARRIER_SPINS");
+  if (!v || !*v) return kBarrierSpins;
+  char* end = nullptr;
+  const unsigned long n = std::strtoul(v, &end, 10);
+  return (end && *end == '\0' && n <= kBarrierSpins) ? (uint32_t)n : kBarrierSpins;
+}
+
 }  // namespace
 
 bool decode_supported(int H) { return H / 32 <= 64 * kDecodeMaxGPL; }
@@ -1326,11 +1338,13 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
   if (tr && (e = tr->mark("dec_router")) != hipSuccess) return e;
   const size_t lds1 = (size_t)(a.K + (a.has_shared ? 1 : 0)) * a.routed.inter * 2;
   if (fgrid > 0) {
+    DecodeArgs af = a;
+    af.barrier_spins = barrier_spins();
     switch (gpl) {
-      case 1: e = launch_fused<1>(a, s, lds1, fgrid); break;
-      case 2: e = launch_fused<2>(a, s, lds1, fgrid); break;
-      case 3: e = launch_fused<3>(a, s, lds1, fgrid); break;
-      default: e = launch_fused<4>(a, s, lds1, fgrid); break;
+      case 1: e = launch_fused<1>(af, s, lds1, fgrid); break;
+      case 2: e = launch_fused<2>(af, s, lds1, fgrid); break;
+      case 3: e = launch_fused<3>(af, s, lds1, fgrid); break;
+      default: e = launch_fused<4>(af, s, lds1, fgrid); break;
     }
     if (e != hipSuccess) return e;
     return tr ? tr->mark("dec_fused_t1") : hipSuccess;

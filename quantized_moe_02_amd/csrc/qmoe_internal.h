@@ -172,7 +172,8 @@ struct DecodeArgs {
   float* sorted_w;
   DecSlot* slots;
   int32_t* sorted_et;     // [P] expert (low 16 bits) and token (high 16 bits) of sorted pick p
-  uint32_t* bar;          // grid-barrier arrival count of the fused single-token kernel
+  uint32_t* bar;          // grid-barrier count and flags of the fused single-token kernel
+  uint32_t barrier_spins; // polls before a workgroup of that kernel gives up on the barrier
   ExpertSet routed;
   bool has_shared;
   ExpertSet shared;

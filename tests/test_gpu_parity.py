@@ -297,6 +297,23 @@ def test_single_token_fused_matches_two_launches(case, monkeypatch):
         assert torch.equal(u, v)
 
 
+def test_fused_decode_gives_up_to_nan(monkeypatch):
+    """The fused single-token kernel's barrier wait is bounded.  With the bound
+    forced to zero polls from the host, no workgroup waits: every row of y is
+    NaN (never a sum over an incomplete h), the routing outputs are still
+    written, and the next call is exact again."""
+    over, T, wfmt, bias = EDGE["T1"]
+    L = synth.make_custom(synth.small_geom(**over), T, wfmt, bias, seed=301, device="cuda")
+    monkeypatch.setenv("QMOE_BARRIER_SPINS", "0")
+    y, ids, tw = run_layer(L)
+    assert torch.isnan(y).all()
+    check_routing(L, ids, tw)
+    monkeypatch.delenv("QMOE_BARRIER_SPINS")
+    y, ids, tw = run_layer(L)
+    ids_g, _ = check_routing(L, ids, tw)
+    check_outputs(L, y, ids_g)
+
+
 def test_full_verify4():
     _full("verify4", 4)
 
