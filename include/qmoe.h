@@ -190,7 +190,9 @@ moe_status moe_combine(const moe_config* cfg, int32_t T, const float* expert_out
  * runs.  If other work keeps some of its workgroups from starting, the wait
  * gives up after a bounded time and the rows of y it could not finish are
  * NaN.  Setting QMOE_DECODE_FUSED=0 in the environment selects kernels that
- * do not wait for each other (same results, bit for bit). */
+ * do not wait for each other (same results, bit for bit); QMOE_BARRIER_SPINS
+ * (at most 65536, the default) lowers the number of polls before giving up,
+ * which tests use to reach that path. */
 moe_status moe_layer(const moe_config* cfg, int32_t T, const uint16_t* x,
                      const float* router_w, const float* bias, const moe_qexperts* routed,
                      const moe_qexperts* shared, void* y, int32_t out_dtype,
