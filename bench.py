@@ -84,20 +84,18 @@ def algorithmic(geom, wfmt, T, n_active):
     # selection: logits and bias in; ids, weights, expert records (48 bytes),
     # per-pick expert/token words and the count out
     sel_b = T * E * 8 + E * 4 + P * 8 + n_active * 48 + P * 4 + 4
-    # the shared expert's gate/up runs beside the selection for a single token
-    # (dec_fused_t1, or dec_select_permute when that does not run) and as
-    # extra blocks of dec_gateup for more tokens; its down projection runs with
+    # the shared expert's gate/up runs beside the selection (dec_fused_t1 for
+    # one token, dec_select_permute otherwise); its down projection runs with
     # the routed ones
-    sh_t1 = T == 1 and Is > 0
+    sh_sel = Is > 0
     sh_gu_b = sb["gate"] + sb["up"] + T * Is * 2
     sh_gu_f = T * 2 * H * Is * 2
     kern = {
         # small-batch path
         "dec_router": dict(bytes=router_b + x_b + T * E * 8, flops=T * 2 * H * E),
-        "dec_select_permute": dict(bytes=sel_b + (sh_gu_b if sh_t1 else 0), flops=sh_gu_f if sh_t1 else 0),
-        "dec_gateup": dict(bytes=n_active * (eb["gate"] + eb["up"]) + x_b + P * I * 2
-                           + (sh_gu_b if Is and not sh_t1 else 0),
-                           flops=P * 2 * H * I * 2 + (sh_gu_f if Is and not sh_t1 else 0)),
+        "dec_select_permute": dict(bytes=sel_b + (sh_gu_b if sh_sel else 0), flops=sh_gu_f if sh_sel else 0),
+        "dec_gateup": dict(bytes=n_active * (eb["gate"] + eb["up"]) + x_b + P * I * 2,
+                           flops=P * 2 * H * I * 2),
         "dec_down_combine": dict(bytes=w_dn + rows * I * 2 + y_b, flops=f_dn + 2 * P * H),
     }
     # one token: selection, gate/up and down in one launch (the three rows

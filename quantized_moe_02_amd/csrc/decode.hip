@@ -13,10 +13,9 @@
 //   otherwise:
 //   K2 dec_select_permute  one workgroup: per-token selection (one wave per
 //                          token) and the grouping of the <= 64 picks by
-//                          expert (batch union); for one token, the shared
-//                          expert's gate/up GEMV in the other workgroups
+//                          expert (batch union); the shared expert's gate/up
+//                          GEMV of every token in the other workgroups
 //   K3 dec_gateup          gate/up GEMV of every pick's expert with SwiGLU
-//                          (and of the shared expert for 2..4 tokens)
 //   K4                     down GEMV of every selected expert and the shared
 //                          expert with the weighted combine in registers:
 //                          dec_down_t1 (one token), dec_down_multi (2..4
@@ -51,8 +50,8 @@ constexpr int kRPW = QMOE_DEC_RPW;           // gate/up row pairs per pipeline i
 constexpr int kItems = QMOE_DEC_ITEMS;       // pipeline items per wave (even)
 constexpr int kPairsPerWave = kRPW * kItems;
 constexpr int kPairsPerBlock = 4 * kPairsPerWave;
-constexpr int kSharedRP = 1;                              // K1: row pairs per item
-constexpr int kSharedPairsPerBlock = 4 * 2 * kSharedRP;   // K1: two items per wave
+constexpr int kSharedRP = 1;                              // K2 shared gate/up: row pairs per item
+constexpr int kSharedPairsPerBlock = 4 * 2 * kSharedRP;   // K2 shared gate/up: two items per wave
 static_assert(kItems % 2 == 0, "items are double-buffered in pairs");
 static_assert(32 % kPairsPerWave == 0 && 32 % (2 * kRPW) == 0, "a wave never straddles inter (a multiple of 32)");
 constexpr int kDownRows = QMOE_DEC_DOWN_ROWS; // down/combine output rows per block
@@ -357,20 +356,23 @@ __global__ void __launch_bounds__(256) dec_router_kernel(DecodeArgs a) {
 // in ascending expert order, each with its picks in pick order), their count,
 // and for each sorted pick p (grouped by expert) its expert and token; the h
 // rows follow the sorted pick order.
-// For one token, the other workgroups run the shared expert's gate/up GEMV
-// (one per row block): it does not depend on the routing, so it streams while
-// block 0 selects.
+// The other workgroups run the shared expert's gate/up GEMV, one per (token,
+// row block): it does not depend on the routing, so it streams while block 0
+// selects.  (For 2..4 tokens this measured 2 us per call faster than extra
+// blocks of K3: 141.5 against 143.7 us at four tokens.)
 template <int FMT, int GPL>
 __global__ void __launch_bounds__(256) dec_select_permute_kernel(DecodeArgs a) {
   if (blockIdx.x > 0) {
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const ExpertSet& S = a.shared;
-    const int pair0 = ((int)blockIdx.x - 1) * kSharedPairsPerBlock + wv * (2 * kSharedRP);
+    const int nsb = (S.inter + kSharedPairsPerBlock - 1) / kSharedPairsPerBlock;   // row blocks
+    const int t = ((int)blockIdx.x - 1) / nsb, rb = ((int)blockIdx.x - 1) - t * nsb;
+    const int pair0 = rb * kSharedPairsPerBlock + wv * (2 * kSharedRP);
     if (pair0 >= S.inter) return;
     const float gg = (FMT == MOE_WFMT_NVFP4) ? S.gate.g[0] : 1.0f;
     const float gu = (FMT == MOE_WFMT_NVFP4) ? S.up.g[0] : 1.0f;
-    gateup_wave<FMT, GPL, 2, kSharedRP>(a.x, a.H, S.gate, S.up, 0, S.inter, pair0, gg, gu,
-                                        a.h_shared);
+    gateup_wave<FMT, GPL, 2, kSharedRP>(a.x + (size_t)t * a.H, a.H, S.gate, S.up, 0, S.inter, pair0, gg,
+                                        gu, a.h_shared + (size_t)t * a.ldh);
     return;
   }
   __shared__ SelectScratch sc[4];
@@ -471,23 +473,17 @@ __global__ void __launch_bounds__(256) dec_select_permute_kernel(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 template <int FMT, int GPL>
 __global__ void __launch_bounds__(256) dec_gateup_kernel(DecodeArgs a) {
-  // with more than one token, y < T: the shared expert for token y (first,
-  // so that the blocks sharing its weights start together), then pick y - T;
-  // one token's shared gate/up runs in K2
-  const int nsh = a.has_shared && a.T > 1 ? a.T : 0;
-  const bool sh = (int)blockIdx.y < nsh;
-  const int p = (int)blockIdx.y - nsh;
-  const int et = sh ? (int)blockIdx.y << 16 : __builtin_amdgcn_readfirstlane(a.sorted_et[p]);
+  const int p = (int)blockIdx.y;
+  const int et = __builtin_amdgcn_readfirstlane(a.sorted_et[p]);
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const ExpertSet& R = sh ? a.shared : a.routed;
+  const ExpertSet& R = a.routed;
   const int pair0 = blockIdx.x * kPairsPerBlock + wv * kPairsPerWave;
   if (pair0 >= R.inter) return;
   const int e = et & 0xffff, t = et >> 16;
   const float gg = (FMT == MOE_WFMT_NVFP4) ? R.gate.g[e] : 1.0f;
   const float gu = (FMT == MOE_WFMT_NVFP4) ? R.up.g[e] : 1.0f;
-  uint16_t* h = sh ? a.h_shared + (size_t)t * a.ldh : a.h_routed + (size_t)p * a.ldh;
   gateup_wave<FMT, GPL>(a.x + (size_t)t * a.H, a.H, R.gate, R.up, (size_t)e * R.inter, R.inter,
-                        pair0, gg, gu, h);
+                        pair0, gg, gu, a.h_routed + (size_t)p * a.ldh);
 }
 
 // ---------------------------------------------------------------------------
@@ -1350,11 +1346,9 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
     return tr ? tr->mark("dec_fused_t1") : hipSuccess;
   }
 
-  // one token: the shared expert's gate/up in K2, beside the selection; more
-  // tokens: as extra blocks of K3
-  const bool sh_k3 = a.has_shared && a.T > 1;
+  // the shared expert's gate/up in K2, beside the selection
   const int k2_blocks =
-      1 + (a.has_shared && !sh_k3 ? (a.shared.inter + kSharedPairsPerBlock - 1) / kSharedPairsPerBlock : 0);
+      1 + (a.has_shared ? a.T * ((a.shared.inter + kSharedPairsPerBlock - 1) / kSharedPairsPerBlock) : 0);
   switch (gpl) {
     case 1: e = launch_k2<1>(a, s, k2_blocks); break;
     case 2: e = launch_k2<2>(a, s, k2_blocks); break;
@@ -1364,8 +1358,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
   if (e != hipSuccess) return e;
   if (tr && (e = tr->mark("dec_select_permute")) != hipSuccess) return e;
 
-  const int inter3 = std::max(a.routed.inter, sh_k3 ? a.shared.inter : 0);
-  dim3 g3((inter3 + kPairsPerBlock - 1) / kPairsPerBlock, a.T * a.K + (sh_k3 ? a.T : 0));
+  dim3 g3((a.routed.inter + kPairsPerBlock - 1) / kPairsPerBlock, a.T * a.K);
   switch (gpl) {
     case 1: e = launch_k3<1>(a, s, g3); break;
     case 2: e = launch_k3<2>(a, s, g3); break;
