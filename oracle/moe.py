@@ -311,7 +311,7 @@ def _expert_weights(src: ExpertSource, e: int):
 
 def layer(x_bits, Wr, b, cfg: RouterConfig, routed: ExpertSource,
           shared: Optional[ExpertSource] = None, ids: Optional[np.ndarray] = None,
-          token_idx: Optional[np.ndarray] = None):
+          token_idx: Optional[np.ndarray] = None, ffn_map=None):
     """y_t = sum_{e in S_t} w_{t,e} FFN_e(x_t) + FFN_shared(x_t).
 
     (S_t, w_t) come from `route` unless `ids` is given, in which case the
@@ -320,6 +320,9 @@ def layer(x_bits, Wr, b, cfg: RouterConfig, routed: ExpertSource,
     The shared expert enters with weight 1 (routed_scaling_factor applies to the
     routed experts only).  Each routed expert is dequantised once and applied to
     the tokens that chose it; that only reorders the sum over experts.
+    `ffn_map`, if given, evaluates the list of (source, expert, X rows) jobs and
+    returns their FFN outputs in order -- e.g. spread over worker processes,
+    each calling `expert_ffn`; it only decides where the jobs run.
     Returns (y float64 [T', H], ids, w)."""
     X = bf16_bits_to_f64(x_bits)
     if token_idx is not None:
@@ -331,14 +334,23 @@ def layer(x_bits, Wr, b, cfg: RouterConfig, routed: ExpertSource,
         ids = np.asarray(ids)
         w = route_weights(s, ids, cfg.routed_scaling_factor)
     T, H = X.shape
-    y = np.zeros((T, H))
-    for e in np.unique(ids):
-        rows, slots = np.nonzero(ids == e)
-        Wg, Wu, Wd = _expert_weights(routed, int(e))
-        y[rows] += w[rows, slots][:, None] * swiglu_ffn(X[rows], Wg, Wu, Wd)
+    experts = [int(e) for e in np.unique(ids)]
+    jobs = [(routed, e, X[np.nonzero(ids == e)[0]]) for e in experts]
     if shared is not None:
-        y += swiglu_ffn(X, *_expert_weights(shared, 0))
+        jobs.append((shared, 0, X))
+    outs = ffn_map(jobs) if ffn_map is not None else [expert_ffn(*j) for j in jobs]
+    y = np.zeros((T, H))
+    for e, F in zip(experts, outs):
+        rows, slots = np.nonzero(ids == e)
+        y[rows] += w[rows, slots][:, None] * F
+    if shared is not None:
+        y += outs[-1]
     return y, ids, w
+
+
+def expert_ffn(src: ExpertSource, e: int, X: np.ndarray) -> np.ndarray:
+    """FFN of expert e of `src` (dequantised from its packed bytes) on rows X."""
+    return swiglu_ffn(X, *_expert_weights(src, e))
 
 
 def dense_layer(x_bits, Wr, b, cfg: RouterConfig, routed: ExpertSource,

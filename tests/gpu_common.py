@@ -10,6 +10,7 @@ import quantized_moe_02_amd as q
 from helpers import np_u16, oracle_inputs, row_rel_err
 
 TOL = 2e-3          # max row-normalised relative error of outputs
+W_TOL = 1e-6        # routing weights: decided in fp64 on both sides, rounded to fp32 by the GPU
 TAU = 1e-9          # selections whose fp64 margin is below this may differ (checked for validity)
 
 
@@ -54,18 +55,96 @@ def check_routing(L, ids_gpu, tw_gpu, x_np=None):
         assert oracle.valid_under_perturbation(ids_g[t], info["sb"][t], cfg, TAU), t
     w_ref = oracle.route_weights(info["s"], ids_g, cfg.routed_scaling_factor)
     rel = np.abs(tw_gpu.cpu().numpy() - w_ref) / np.abs(w_ref)
-    assert rel.max() <= TOL, rel.max()
+    assert rel.max() <= W_TOL, rel.max()
     return ids_g, int((~exact).sum())
 
 
-def check_outputs(L, y_gpu, ids_g, token_idx=None, tol=TOL, x_np=None):
-    """y within tol (row-normalised) of the oracle evaluated on the GPU's ids."""
+def check_outputs(L, y_gpu, ids_g, token_idx=None, tol=TOL, x_np=None, ffn_map=None, srcs=None):
+    """y within tol (row-normalised) of the oracle evaluated on the GPU's ids.
+    ffn_map: where the oracle's expert FFNs run (see FFNCache); srcs: the
+    (routed, shared) expert sources that ffn_map was filled from."""
     x, Wr, b, cfg, routed, shared = oracle_inputs(L, lazy=True)
+    if srcs is not None:
+        routed, shared = srcs
     if x_np is not None:
         x = x_np
     idx = np.arange(x.shape[0]) if token_idx is None else np.asarray(token_idx)
-    y_ref, _, _ = oracle.layer(x, Wr, b, cfg, routed, shared, ids=ids_g[idx], token_idx=idx)
+    y_ref, _, _ = oracle.layer(x, Wr, b, cfg, routed, shared, ids=ids_g[idx], token_idx=idx,
+                               ffn_map=ffn_map)
     y = y_gpu.float().cpu().numpy()[idx]
     err = row_rel_err(y, y_ref)
     assert err.max() <= tol, f"max row error {err.max():.3e} at token {idx[err.argmax()]}"
     return err.max()
+
+
+class FFNCache:
+    """The oracle's expert FFN rows, computed in worker processes
+    (oracle_pool) and kept per (source, expert, activation row), so that
+    several checks over one layer dequantise each expert once.  Called with a
+    list of (source, expert, X rows) jobs, as oracle.layer's ffn_map."""
+
+    def __init__(self):
+        self.rows = {}
+
+    @staticmethod
+    def _key(src, e, xrow):
+        return (id(src), int(e), xrow.tobytes())
+
+    def fill(self, jobs):
+        import oracle_pool
+        todo = []
+        for src, e, X in jobs:
+            need = [r for r in range(X.shape[0]) if self._key(src, e, X[r]) not in self.rows]
+            if need:
+                todo.append((src, e, X[need]))
+        for (src, e, X), F in zip(todo, oracle_pool.expert_ffns(todo)):
+            for r in range(X.shape[0]):
+                self.rows[self._key(src, e, X[r])] = F[r]
+
+    def __call__(self, jobs):
+        self.fill(jobs)
+        return [np.stack([self.rows[self._key(src, e, X[r])] for r in range(X.shape[0])])
+                for src, e, X in jobs]
+
+
+def cover_tokens(ids_g, limit=64, always=()):
+    """A few tokens whose picks together touch every selected expert (greedy
+    set cover), plus `always`."""
+    chosen = [int(t) for t in always]
+    covered = set(ids_g[chosen].ravel().tolist()) if chosen else set()
+    need = set(ids_g.ravel().tolist())
+    sets = [set(r) for r in ids_g.tolist()]
+    while covered != need and len(chosen) < limit:
+        t = max(range(len(sets)), key=lambda i: len(sets[i] - covered))
+        chosen.append(t)
+        covered |= sets[t]
+    return np.array(sorted(set(chosen)))
+
+
+def expert_slots_to_check(offsets, n_full=8, seed=0):
+    """Sorted slots to compare for a routed expert-FFN output: every slot of
+    n_full experts (the most and least loaded, ones whose last work unit is
+    shortest and longest, random others) and the first, a middle and the last
+    slot of every other active expert.  Returns {expert: slot array}."""
+    offsets = np.asarray(offsets)
+    counts = np.diff(offsets)
+    active = np.nonzero(counts)[0]
+    rng = np.random.default_rng(seed)
+    full = []
+    by = lambda key: sorted(active, key=key)
+    for cand in (by(lambda e: -counts[e])[0], by(lambda e: counts[e])[0],
+                 by(lambda e: (counts[e] - 1) % 128)[0], by(lambda e: -((counts[e] - 1) % 128))[0],
+                 by(lambda e: (counts[e] - 1) % 32)[0]):
+        if cand not in full:
+            full.append(int(cand))
+    rest = [int(e) for e in active if e not in full]
+    rng.shuffle(rest)
+    full += rest[: max(0, n_full - len(full))]
+    out = {}
+    for e in active:
+        lo, hi = offsets[e], offsets[e + 1]
+        if int(e) in full:
+            out[int(e)] = np.arange(lo, hi)
+        else:
+            out[int(e)] = np.unique([lo, (lo + hi - 1) // 2, hi - 1])
+    return out

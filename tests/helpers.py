@@ -43,6 +43,20 @@ class LazyExperts:
         self.qe, self.wfmt = qe, wfmt
         self._cache = {}
 
+    def packed(self, e):
+        """Host copies of expert e's packed bytes, (q, scale, gscale) per
+        projection, each with a leading expert dimension of one."""
+        out = []
+        for proj in ("gate", "up", "down"):
+            p = getattr(self.qe, proj)
+            q = p.q[e:e + 1].detach().cpu().numpy()
+            if self.wfmt == "int4":
+                out.append((q, np_u16(p.scale[e:e + 1]), None))
+            else:
+                out.append((q, p.scale[e:e + 1].detach().cpu().numpy(),
+                            p.gscale[e:e + 1].detach().cpu().numpy()))
+        return tuple(out)
+
     def weight(self, proj, e):
         key = (proj, e)
         if key not in self._cache:

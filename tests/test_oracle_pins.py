@@ -409,3 +409,71 @@ def test_nvfp4_layer_dense_equivalence():
     x, Wr, b, cfg, routed, shared = oracle_inputs(L)
     y, _, _ = oracle.layer(x, Wr, b, cfg, routed, shared)
     assert np.allclose(y, oracle.dense_layer(x, Wr, b, cfg, routed, shared), rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# Decision margins, routing on given ids, one-expert groups
+# ---------------------------------------------------------------------------
+
+def _margin_case(TG, k, G=4):
+    """8 experts, zero router weights (every sigmoid score is 1/2), so the
+    biased scores are 1/2 + b, chosen by hand."""
+    cfg = oracle.RouterConfig(8, G, TG, k, 1.0)
+    b = np.array([0.40, 0.10, 0.30, 0.28, 0.05, 0.00, 0.20, 0.15])
+    _, _, info = oracle.route(np.ones((1, 4)), np.zeros((8, 4)), b, cfg)
+    return info["margin"][0]
+
+
+def test_route_margins_hand_computed():
+    """Biased scores .9 .6 | .8 .78 | .55 .5 | .7 .65 in groups of two: group
+    scores 1.5, 1.58, 1.05, 1.35.
+      TG=2, k=3: groups 1, 0 kept; group gap 1.5 - 1.35 = .15; allowed
+                 scores .9 .8 .78 .6, gap after the 3rd .78 - .6 = .18 -> .15
+      TG=2, k=2: expert gap .8 - .78 = .02 -> .02
+      TG=4, k=3: no group boundary; all eight allowed, .78 - .7 = .08
+      TG=1, k=2: group gap 1.58 - 1.5 = .08; both experts of the kept group
+                 are chosen, so no expert boundary -> .08
+      TG=4, k=8: no boundary at all -> inf"""
+    assert abs(_margin_case(2, 3) - 0.15) < 1e-12
+    assert abs(_margin_case(2, 2) - 0.02) < 1e-12
+    assert abs(_margin_case(4, 3) - 0.08) < 1e-12
+    assert abs(_margin_case(1, 2) - 0.08) < 1e-12
+    assert _margin_case(4, 8) == np.inf
+
+
+@pytest.mark.parametrize("wfmt,bias", [("int4", "normal0.1"), ("nvfp4", "zipf")])
+def test_layer_on_given_ids_equals_routed_layer(wfmt, bias):
+    """layer(ids=...) with the router's own ids reproduces layer() exactly:
+    the weights it recomputes for given ids are the router's weights."""
+    L = synth.make_custom(synth.small_geom(), 8, wfmt, bias, seed=31)
+    x, Wr, b, cfg, routed, shared = oracle_inputs(L)
+    y, ids, w = oracle.layer(x, Wr, b, cfg, routed, shared)
+    y2, ids2, w2 = oracle.layer(x, Wr, b, cfg, routed, shared, ids=ids)
+    assert np.array_equal(ids, ids2) and np.array_equal(w, w2) and np.array_equal(y, y2)
+    # and on a token subset, with the subset's ids (BLAS may block a smaller
+    # product differently: equal up to fp64 rounding)
+    idx = np.array([0, 3, 7])
+    y3, _, _ = oracle.layer(x, Wr, b, cfg, routed, shared, ids=ids[idx], token_idx=idx)
+    assert np.allclose(y3, y[idx], rtol=1e-13, atol=1e-15)
+
+
+@pytest.mark.parametrize("E,G,TG,k", [(16, 16, 6, 4), (12, 6, 3, 4)])
+def test_router_small_groups_brute_force(E, G, TG, k):
+    """Groups of one expert (a group's score is its single biased score) and
+    of two (the top-two sum is the whole group): brute force over every
+    TG-subset of groups and every k-subset of their experts."""
+    geom = synth.small_geom(n_routed_experts=E, n_group=G, topk_group=TG, top_k=k)
+    L = synth.make_custom(geom, 12, "int4", "normal0.1", seed=32 + G)
+    x, Wr, b, cfg, _, _ = oracle_inputs(L)
+    X = oracle.bf16_bits_to_f64(x)
+    ids, _, info = oracle.route(X, Wr, b, cfg)
+    per = E // G
+    sb = 1 / (1 + np.exp(-(X @ Wr.T))) + b
+    for t in range(X.shape[0]):
+        gscore = [sum(sb[t, g * per:(g + 1) * per]) for g in range(G)]   # per <= 2: all of it
+        best_groups = max(itertools.combinations(range(G), TG),
+                          key=lambda c: sum(gscore[g] for g in c))
+        allowed = [e for g in best_groups for e in range(g * per, (g + 1) * per)]
+        best = max(itertools.combinations(allowed, k), key=lambda c: sum(sb[t, e] for e in c))
+        assert info["margin"][t] > 1e-9
+        assert sorted(best) == list(ids[t]), t
