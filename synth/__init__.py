@@ -298,3 +298,52 @@ def make_custom(geom: dict, T: int, wfmt: str, bias: str, seed: int,
     if geom.get("n_shared_experts", 0):
         shared = make_experts(seed, 1, H, geom["shared_inter"], wfmt, device, tag=11)
     return LayerInputs("custom", seed, dict(geom), wfmt, T, x, router_w, b, routed, shared)
+
+
+# ----------------------------------------------------------------------------
+# Raw packed bytes: every code the formats admit, not only what the encoders
+# above emit (int4 code 0, i.e. q = -8; E2M1 -0; negative block scales)
+# ----------------------------------------------------------------------------
+
+def raw_int4_proj(E: int, N: int, K: int, seed: int, device="cpu") -> QProj:
+    """Uniformly random code bytes and fp16 scales of either sign with
+    magnitudes 2^U(-12, -4)."""
+    g = _gen("cpu", seed)
+    q = torch.randint(0, 256, (E, N, K // 2), generator=g, dtype=torch.int32).to(torch.uint8)
+    mag = torch.exp2(torch.rand((E, N, K // 32), generator=g) * 8.0 - 12.0)
+    sign = torch.where(torch.rand((E, N, K // 32), generator=g) < 0.5, -1.0, 1.0)
+    return QProj(q.to(device), (mag * sign).to(torch.float16).to(device), None)
+
+
+def raw_nvfp4_proj(E: int, N: int, K: int, seed: int, gscale: float,
+                   device="cpu") -> QProj:
+    """Uniformly random code bytes (both zeros of E2M1 included) and random
+    finite E4M3 scale bytes of either sign (the two NaN codes 0x7F and 0xFF
+    excluded); per-tensor scale `gscale` for every expert."""
+    g = _gen("cpu", seed)
+    q = torch.randint(0, 256, (E, N, K // 2), generator=g, dtype=torch.int32).to(torch.uint8)
+    s = torch.randint(0, 254, (E, N, K // 16), generator=g, dtype=torch.int32)
+    s = torch.where(s >= 0x7F, s + 1, s)          # skip 0x7F; 0xFF is out of range
+    gs = torch.full((E,), gscale, dtype=torch.float32)
+    return QProj(q.to(device), s.to(torch.uint8).to(device), gs.to(device))
+
+
+def make_raw(geom: dict, T: int, wfmt: str, seed: int, device="cpu",
+             gscale: float = 2e-4) -> LayerInputs:
+    """A small layer whose expert weights are raw random bytes (see above);
+    router and activations as in make_custom, zero bias."""
+    H, E, I = geom["hidden"], geom["n_routed_experts"], geom["moe_inter"]
+
+    def experts(n, inter, tag):
+        shapes = ((inter, H), (inter, H), (H, inter))
+        ps = []
+        for p, (N, K) in enumerate(shapes):
+            s = sub_seed(seed, tag, p)
+            ps.append(raw_int4_proj(n, N, K, s, device) if wfmt == "int4"
+                      else raw_nvfp4_proj(n, N, K, s, gscale, device))
+        return QExperts(*ps)
+    x = to_bf16(randn((T, H), sub_seed(seed, 1, T), device))
+    router_w = randn((E, H), sub_seed(seed, 2), device, WEIGHT_STD)
+    b = make_bias("zero", E, seed, device)
+    shared = experts(1, geom["shared_inter"], 21) if geom.get("n_shared_experts", 0) else None
+    return LayerInputs("raw", seed, dict(geom), wfmt, T, x, router_w, b, experts(E, I, 20), shared)
