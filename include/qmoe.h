@@ -21,9 +21,11 @@
  *   except `cfg`, the moe_qexperts structs, and the `bytes` output of
  *   moe_workspace_size, which are HOST pointers read or written during the
  *   call only.  The caller owns every buffer, including the workspace.  The
- *   library never allocates or frees memory and keeps no mutable global state,
- *   so calls on different streams are independent as long as their workspaces
- *   and outputs do not overlap.
+ *   library never allocates or frees memory; its only global state is a
+ *   per-device record of how many workgroups of the single-token kernel fit
+ *   on the device (computed once, read-only after).  Calls on different
+ *   streams are independent as long as their workspaces and outputs do not
+ *   overlap.
  * Alignment.  Packed weight arrays (`q`), scale arrays and `x` must be 16-byte
  *   aligned; the workspace 256-byte aligned.  Otherwise MOE_ERR_INVALID_ARG.
  * Asynchrony.  Every call only enqueues kernels on `stream` and returns
@@ -94,7 +96,21 @@ typedef struct {
   int32_t shared_inter;            /* Is: inter size of the shared expert */
   float routed_scaling_factor;     /* rsf: multiplies the renormalised routed weights */
   int32_t wfmt;                    /* moe_wfmt of routed and shared experts */
+  uint32_t options;                /* MOE_OPT_* bits; 0 for the defaults */
 } moe_config;
+
+/* moe_config.options.  Unknown bits are MOE_ERR_INVALID_ARG.
+ * MOE_OPT_NO_GRID_WAIT   moe_layer never runs the single-token kernel whose
+ *                        workgroups wait for each other (see moe_layer); one
+ *                        token then takes kernels that do not, with results
+ *                        identical bit for bit.  For callers that share the
+ *                        device with other work while the layer runs.
+ * MOE_OPT_GRID_WAIT_NONE that kernel's workgroups give up on the wait at once
+ *                        (no poll): every row of y is NaN and the workspace
+ *                        flag MOE_FLAG_GRID_WAIT_TIMEOUT is raised.  Exists to
+ *                        exercise the give-up path; never needed otherwise. */
+#define MOE_OPT_NO_GRID_WAIT 1u
+#define MOE_OPT_GRID_WAIT_NONE 2u
 
 /* One projection of E experts (device pointers; see the formats above). */
 typedef struct {
@@ -118,6 +134,17 @@ moe_status moe_workspace_size(const moe_config* cfg, int32_t T, size_t* bytes);
 
 /* Static, human-readable name of a status code. */
 const char* moe_status_string(moe_status s);
+
+/* Flags raised by the last moe_layer call that used workspace `ws` (host
+ * output `flags`); the first 4 bytes of every workspace hold them, and
+ * moe_layer clears them before it does anything else.  The call enqueues a
+ * copy on `stream` and waits for it, so it returns after all work queued on
+ * `stream` before it has finished.
+ * MOE_FLAG_GRID_WAIT_TIMEOUT  the single-token kernel's workgroups waited for
+ *   each other in vain (other work on the device kept some from starting);
+ *   the rows of y that they owned are NaN.  Rerun with MOE_OPT_NO_GRID_WAIT. */
+#define MOE_FLAG_GRID_WAIT_TIMEOUT 1u
+moe_status moe_layer_flags(const void* ws, uint32_t* flags, hipStream_t stream);
 
 /* Router (page "Show HN: Menjalankan GLM 5.2 ...", section "Fitur utama":
  * DeepSeek-V3-style sigmoid router, noaux_tc, routed_scaling_factor).
@@ -188,11 +215,10 @@ moe_status moe_combine(const moe_config* cfg, int32_t T, const float* expert_out
  * kernels sizes its grid to what the device holds at once and has its
  * workgroups wait for each other; it expects the device to itself while it
  * runs.  If other work keeps some of its workgroups from starting, the wait
- * gives up after a bounded time and the rows of y it could not finish are
- * NaN.  Setting QMOE_DECODE_FUSED=0 in the environment selects kernels that
- * do not wait for each other (same results, bit for bit); QMOE_BARRIER_SPINS
- * (at most 65536, the default) lowers the number of polls before giving up,
- * which tests use to reach that path. */
+ * gives up after a bounded time (2^16 polls), the rows of y it could not
+ * finish are NaN, and MOE_FLAG_GRID_WAIT_TIMEOUT is raised in the workspace
+ * (moe_layer_flags).  cfg->options MOE_OPT_NO_GRID_WAIT selects kernels that
+ * do not wait for each other (same results, bit for bit). */
 moe_status moe_layer(const moe_config* cfg, int32_t T, const uint16_t* x,
                      const float* router_w, const float* bias, const moe_qexperts* routed,
                      const moe_qexperts* shared, void* y, int32_t out_dtype,

@@ -21,6 +21,8 @@ LIB_PATH = os.environ.get("QMOE_LIBRARY") or os.path.join(_HERE, "libqmoe.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP = range(5)
 MOE_WFMT_INT4_G32_F16, MOE_WFMT_NVFP4 = 0, 1
 MOE_OUT_F32, MOE_OUT_BF16 = 0, 1
+MOE_OPT_NO_GRID_WAIT, MOE_OPT_GRID_WAIT_NONE = 1, 2
+MOE_FLAG_GRID_WAIT_TIMEOUT = 1
 MOE_MAX_TOKENS = 262144
 WFMT = {"int4": MOE_WFMT_INT4_G32_F16, "nvfp4": MOE_WFMT_NVFP4}
 
@@ -36,7 +38,8 @@ class MoeConfig(ctypes.Structure):
                 ("n_routed_experts", ctypes.c_int32), ("n_group", ctypes.c_int32),
                 ("topk_group", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("n_shared_experts", ctypes.c_int32), ("shared_inter", ctypes.c_int32),
-                ("routed_scaling_factor", ctypes.c_float), ("wfmt", ctypes.c_int32)]
+                ("routed_scaling_factor", ctypes.c_float), ("wfmt", ctypes.c_int32),
+                ("options", ctypes.c_uint32)]
 
 
 class MoeQProj(ctypes.Structure):
@@ -78,6 +81,7 @@ def lib() -> ctypes.CDLL:
             "moe_layer": [cfgp, i32, vp, vp, vp, exp, exp, vp, i32, vp, vp, vp, sz, vp],
             "moe_layer_trace": [cfgp, i32, vp, vp, vp, exp, exp, vp, i32, vp, vp, vp, sz, vp,
                                 ctypes.POINTER(MoeTrace)],
+            "moe_layer_flags": [vp, ctypes.POINTER(ctypes.c_uint32), vp],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -108,11 +112,11 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
-def make_config(geom: dict, wfmt: str) -> MoeConfig:
+def make_config(geom: dict, wfmt: str, options: int = 0) -> MoeConfig:
     return MoeConfig(geom["hidden"], geom["moe_inter"], geom["n_routed_experts"],
                      geom["n_group"], geom["topk_group"], geom["top_k"],
                      geom["n_shared_experts"], geom.get("shared_inter", 0),
-                     float(geom["routed_scaling_factor"]), WFMT.get(wfmt, wfmt))
+                     float(geom["routed_scaling_factor"]), WFMT.get(wfmt, wfmt), options)
 
 
 def qexperts(gate, up, down) -> MoeQExperts:
@@ -181,3 +185,12 @@ def moe_layer_trace(cfg, T, x, router_w, bias, routed: MoeQExperts, shared: Opti
                                  out_dtype, _p(topk_ids_out), _p(topk_w_out), _p(ws),
                                  0 if ws is None else ws.numel(), _stream(stream),
                                  ctypes.byref(trace)), "moe_layer_trace")
+
+
+def moe_layer_flags(ws, stream=None) -> int:
+    """MOE_FLAG_* bits raised by the last moe_layer call on workspace `ws`
+    (waits for the work queued on `stream`)."""
+    f = ctypes.c_uint32(0)
+    _check(lib().moe_layer_flags(_p(ws), ctypes.byref(f), _stream(stream)), "moe_layer_flags")
+    return f.value
+

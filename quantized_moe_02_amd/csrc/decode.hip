@@ -295,6 +295,7 @@ __global__ void __launch_bounds__(256) dec_router_kernel(DecodeArgs a) {
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   for (int i = (int)blockIdx.x * 256 + (int)threadIdx.x; i <= kDecFusedMaxGrid; i += (int)gridDim.x * 256)
     a.bar[kDecFlagStride * i] = 0u;
+  if (blockIdx.x == 0 && threadIdx.x == 0) a.flags[0] = 0u;
   {
     // expert e's logits: the four waves take quarters of the hidden dimension
     const int e = blockIdx.x;
@@ -790,6 +791,9 @@ __device__ __forceinline__ void down_t1_rows(const DecodeArgs& a, uint4* hl, int
   };
   if (gw < H) load_row(std::integral_constant<int, 0>{}, gw);
   const bool fine = before_h();
+  // a workgroup that gave up raises the layer's flag (plain vector store: any
+  // number of workgroups may write the same value)
+  if (FUSED && !fine && threadIdx.x == 0) a.flags[0] = MOE_FLAG_GRID_WAIT_TIMEOUT;
   if constexpr (FUSED) load_h();   // first, so that it does not queue behind the second row
   if (FUSED && gw + nw < H) load_row(std::integral_constant<int, 1>{}, gw + nw);
 #pragma unroll
@@ -1291,23 +1295,6 @@ hipError_t launch_fused(const DecodeArgs& a, hipStream_t s, size_t lds, int grid
   return hipGetLastError();
 }
 
-// QMOE_DECODE_FUSED=0 in the environment turns dec_fused_t1 off (one token
-// then takes K3 and dec_down_t1).
-bool fused_enabled() {
-  const char* v = std::getenv("QMOE_DECODE_FUSED");
-  return !(v && v[0] == '0' && v[1] == '\0');
-}
-
-// Polls a workgroup of dec_fused_t1 makes before it gives up on the barrier:
-// kBarrierSpins, or QMOE_BARRIER_SPINS from the environment (a test sets it to
-// 0 to exercise the give-up path without waiting).
-uint32_t barrier_spins() {
-  const char* v = std::getenv("QMOE_BARRIER_SPINS");
-  if (!v || !*v) return kBarrierSpins;
-  char* end = nullptr;
-  const unsigned long n = std::strtoul(v, &end, 10);
-  return (end && *end == '\0' && n <= kBarrierSpins) ? (uint32_t)n : kBarrierSpins;
-}
 
 }  // namespace
 
@@ -1321,7 +1308,9 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
   // one token: selection, the shared expert's gate/up and K3/K4 in
   // dec_fused_t1 when the device's resident grid is known
   int fgrid = 0;
-  if (down_t1_fits(a) && fused_enabled()) {
+  // MOE_OPT_NO_GRID_WAIT turns dec_fused_t1 off (one token then takes K2, K3
+  // and dec_down_t1)
+  if (down_t1_fits(a) && !(a.options & MOE_OPT_NO_GRID_WAIT)) {
     switch (gpl) {
       case 1: fgrid = fused_grid<1>(f4); break;
       case 2: fgrid = fused_grid<2>(f4); break;
@@ -1335,7 +1324,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
   const size_t lds1 = (size_t)(a.K + (a.has_shared ? 1 : 0)) * a.routed.inter * 2;
   if (fgrid > 0) {
     DecodeArgs af = a;
-    af.barrier_spins = barrier_spins();
+    // MOE_OPT_GRID_WAIT_NONE: no poll at all, to exercise the give-up path
+    af.barrier_spins = (a.options & MOE_OPT_GRID_WAIT_NONE) ? 0u : kBarrierSpins;
     switch (gpl) {
       case 1: e = launch_fused<1>(af, s, lds1, fgrid); break;
       case 2: e = launch_fused<2>(af, s, lds1, fgrid); break;

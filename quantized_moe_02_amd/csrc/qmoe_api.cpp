@@ -32,6 +32,7 @@ moe_status check_cfg(const moe_config* c) {
   if (!std::isfinite(c->routed_scaling_factor) || !(c->routed_scaling_factor > 0.0f))
     return MOE_ERR_INVALID_ARG;
   if (c->wfmt != MOE_WFMT_INT4_G32_F16 && c->wfmt != MOE_WFMT_NVFP4) return MOE_ERR_INVALID_ARG;
+  if (c->options & ~(MOE_OPT_NO_GRID_WAIT | MOE_OPT_GRID_WAIT_NONE)) return MOE_ERR_INVALID_ARG;
   // kernel limits
   if (c->n_routed_experts > 256 || c->n_group > 64 || c->top_k > 16) return MOE_ERR_UNSUPPORTED;
   if (c->hidden > 65536 || c->moe_inter > 65536) return MOE_ERR_UNSUPPORTED;
@@ -134,6 +135,7 @@ Workspace carve_workspace(const moe_config& c, int T, void* base) {
     off = round_up(off + bytes, kAlign);
     return o;
   };
+  const size_t o_flags = take(sizeof(uint32_t));   // offset 0, as moe_layer_flags documents
   const size_t o_logits =
       take((size_t)route_splits(T, c.hidden, (int)E) * T * E * sizeof(double));
   const size_t o_ids = take(P * sizeof(int32_t));
@@ -157,6 +159,7 @@ Workspace carve_workspace(const moe_config& c, int T, void* base) {
   w.total = off;
   if (base) {
     char* b = static_cast<char*>(base);
+    w.flags = reinterpret_cast<uint32_t*>(b + o_flags);
     w.logits = reinterpret_cast<double*>(b + o_logits);
     w.ids = reinterpret_cast<int32_t*>(b + o_ids);
     w.tw = reinterpret_cast<float*>(b + o_tw);
@@ -177,6 +180,24 @@ Workspace carve_workspace(const moe_config& c, int T, void* base) {
     w.phist = reinterpret_cast<int32_t*>(b + o_phist);
   }
   return w;
+}
+
+moe_status check_layer_args(const moe_config* cfg, int32_t T, const uint16_t* x,
+                            const float* router_w, const moe_qexperts* routed,
+                            const moe_qexperts* shared, const void* y, int32_t out_dtype) {
+  moe_status s;
+  if ((s = check_cfg(cfg)) != MOE_OK) return s;
+  if ((s = check_T(T)) != MOE_OK) return s;
+  if (!x || !router_w || !y) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(router_w, 16) || !aligned(y, 16)) return MOE_ERR_INVALID_ARG;
+  if (out_dtype != MOE_OUT_F32 && out_dtype != MOE_OUT_BF16) return MOE_ERR_INVALID_ARG;
+  if ((s = check_experts(routed, cfg->wfmt)) != MOE_OK) return s;
+  if (cfg->n_shared_experts == 1) {
+    if ((s = check_experts(shared, cfg->wfmt)) != MOE_OK) return s;
+  } else if (shared) {
+    return MOE_ERR_INVALID_ARG;
+  }
+  return MOE_OK;
 }
 
 }  // namespace qmoe
@@ -205,6 +226,17 @@ const char* moe_status_string(moe_status s) {
   return "MOE_ERR_UNKNOWN";
 }
 
+moe_status moe_layer_flags(const void* ws, uint32_t* flags, hipStream_t stream) {
+  if (!ws || !flags) return MOE_ERR_INVALID_ARG;
+  if (!aligned(ws, kAlign)) return MOE_ERR_INVALID_ARG;
+  uint32_t v = 0;
+  if (hipMemcpyAsync(&v, ws, sizeof(v), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return MOE_ERR_HIP;
+  *flags = v;
+  return MOE_OK;
+}
+
 moe_status moe_route(const moe_config* cfg, int32_t T, const uint16_t* x, const float* router_w,
                      const float* bias, int32_t* topk_ids, float* topk_w, void* ws,
                      size_t ws_bytes, hipStream_t stream) {
@@ -218,7 +250,7 @@ moe_status moe_route(const moe_config* cfg, int32_t T, const uint16_t* x, const 
   const Workspace w = carve_workspace(*cfg, T, ws);
   RouteArgs a{x, router_w, bias, topk_ids, topk_w, w.logits, T, cfg->hidden,
               cfg->n_routed_experts, cfg->n_group, cfg->topk_group, cfg->top_k,
-              cfg->routed_scaling_factor};
+              cfg->routed_scaling_factor, nullptr};
   return hip_status(launch_route(a, stream));
 }
 
@@ -320,17 +352,7 @@ moe_status layer_impl(const moe_config* cfg, int32_t T, const uint16_t* x, const
                       void* y, int32_t out_dtype, int32_t* topk_ids_out, float* topk_w_out,
                       void* ws, size_t ws_bytes, hipStream_t stream, moe_trace* trace) {
   moe_status s;
-  if ((s = check_cfg(cfg)) != MOE_OK) return s;
-  if ((s = check_T(T)) != MOE_OK) return s;
-  if (!x || !router_w || !y) return MOE_ERR_INVALID_ARG;
-  if (!aligned(x, 16) || !aligned(router_w, 16) || !aligned(y, 16)) return MOE_ERR_INVALID_ARG;
-  if (out_dtype != MOE_OUT_F32 && out_dtype != MOE_OUT_BF16) return MOE_ERR_INVALID_ARG;
-  if ((s = check_experts(routed, cfg->wfmt)) != MOE_OK) return s;
-  if (cfg->n_shared_experts == 1) {
-    if ((s = check_experts(shared, cfg->wfmt)) != MOE_OK) return s;
-  } else if (shared) {
-    return MOE_ERR_INVALID_ARG;
-  }
+  if ((s = check_layer_args(cfg, T, x, router_w, routed, shared, y, out_dtype)) != MOE_OK) return s;
   if ((s = check_ws(*cfg, T, ws, ws_bytes)) != MOE_OK) return s;
   if (trace) {
     for (int i = 0; i <= MOE_TRACE_MAX; ++i)
@@ -381,6 +403,8 @@ moe_status layer_impl(const moe_config* cfg, int32_t T, const uint16_t* x, const
     d.slots = w.dslots;
     d.sorted_et = w.dpick;
     d.bar = w.dbar;
+    d.options = cfg->options;
+    d.flags = w.flags;
     d.routed = expert_set(*routed, cfg->moe_inter);
     d.has_shared = has_shared;
     if (has_shared) d.shared = expert_set(*shared, cfg->shared_inter);
@@ -393,7 +417,7 @@ moe_status layer_impl(const moe_config* cfg, int32_t T, const uint16_t* x, const
     return hip_status(launch_decode(d, stream, tr));
   }
   RouteArgs ra{x, router_w, bias, ids, tw, w.logits, T, cfg->hidden, cfg->n_routed_experts,
-               cfg->n_group, cfg->topk_group, cfg->top_k, cfg->routed_scaling_factor};
+               cfg->n_group, cfg->topk_group, cfg->top_k, cfg->routed_scaling_factor, w.flags};
   if ((e = launch_route(ra, stream, tr)) != hipSuccess) return MOE_ERR_HIP;
   PermuteArgs pa{ids, w.offsets, w.sorted_token, w.inv_perm, w.active, w.n_active,
                  T, cfg->top_k, cfg->n_routed_experts, w.phist};

@@ -36,6 +36,7 @@ static_assert(sizeof(DecSlot) == 48, "three 16-byte loads");
 constexpr int kDecMaxSlots = 64;
 
 struct Workspace {
+  uint32_t* flags;        // [1] at offset 0: MOE_FLAG_* of the last moe_layer call
   double* logits;         // [T][E]   router logits (fp64)
   int32_t* ids;           // [T][k]   routing when the caller keeps none
   float* tw;              // [T][k]
@@ -79,6 +80,10 @@ struct Tracer {
 
 // Lays the workspace out from `base` (nullptr: only sizes it).
 Workspace carve_workspace(const moe_config& c, int T, void* base);
+// moe_layer's argument checks other than the workspace's (no HIP call).
+moe_status check_layer_args(const moe_config* cfg, int32_t T, const uint16_t* x,
+                            const float* router_w, const moe_qexperts* routed,
+                            const moe_qexperts* shared, const void* y, int32_t out_dtype);
 
 struct RouteArgs {
   const uint16_t* x;
@@ -89,6 +94,7 @@ struct RouteArgs {
   double* logits;
   int T, H, E, G, TG, K;
   float rsf;
+  uint32_t* flags;    // nullable: moe_layer's flags word, cleared by the selection kernel
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t s, Tracer* tr = nullptr);
 // Number of hidden-dimension slices route_logits uses (its logits buffer
@@ -174,6 +180,8 @@ struct DecodeArgs {
   int32_t* sorted_et;     // [P] expert (low 16 bits) and token (high 16 bits) of sorted pick p
   uint32_t* bar;          // grid-barrier count and flags of the fused single-token kernel
   uint32_t barrier_spins; // polls before a workgroup of that kernel gives up on the barrier
+  uint32_t options;       // moe_config.options
+  uint32_t* flags;        // moe_layer's flags word: cleared by K1, raised on a barrier give-up
   ExpertSet routed;
   bool has_shared;
   ExpertSet shared;

@@ -111,11 +111,13 @@ __global__ void __launch_bounds__(256) route_select_kernel(const double* __restr
                                                            int32_t* __restrict__ ids,
                                                            float* __restrict__ tw, int T, int E,
                                                            int G, int TG, int K, float rsf,
-                                                           int nsplit) {
+                                                           int nsplit, uint32_t* __restrict__ flags) {
   __shared__ SelectScratch sc[4];
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wv;
+  // moe_layer's flags word: nothing on this path raises one
+  if (flags && blockIdx.x == 0 && threadIdx.x == 0) flags[0] = 0u;
   if (t >= T) return;
   int id, rank;
   float w;
@@ -151,7 +153,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s, Tracer* tr) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (tr && (e = tr->mark("route_logits")) != hipSuccess) return e;
   hipLaunchKernelGGL(route_select_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, a.logits, a.bias,
-                     a.ids, a.tw, a.T, a.E, a.G, a.TG, a.K, a.rsf, S_used);
+                     a.ids, a.tw, a.T, a.E, a.G, a.TG, a.K, a.rsf, S_used, a.flags);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (tr && (e = tr->mark("route_select")) != hipSuccess) return e;
   return hipSuccess;

@@ -22,13 +22,13 @@ def qexp(qe):
     return q.qexperts(proj_tuple(qe.gate), proj_tuple(qe.up), proj_tuple(qe.down))
 
 
-def run_layer(L, out_dtype=q.MOE_OUT_F32, x=None, T=None):
+def run_layer(L, out_dtype=q.MOE_OUT_F32, x=None, T=None, options=0, ws=None):
     """moe_layer on the GPU; returns (y, ids, tw) as torch tensors on the GPU."""
-    cfg = q.make_config(L.geom, L.wfmt)
+    cfg = q.make_config(L.geom, L.wfmt, options)
     x = L.x if x is None else x
     T = x.shape[0] if T is None else T
     H, k = L.geom["hidden"], L.geom["top_k"]
-    ws = q.workspace(cfg, T)
+    ws = q.workspace(cfg, T) if ws is None else ws
     y = torch.empty(T, H, device="cuda",
                     dtype=torch.float32 if out_dtype == q.MOE_OUT_F32 else torch.bfloat16)
     ids = torch.empty(T, k, dtype=torch.int32, device="cuda")

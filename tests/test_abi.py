@@ -37,8 +37,9 @@ def test_status_strings():
 def _cfg(**over):
     g = dict(synth.WORKLOADS["tiny"]["geom"])
     wfmt = over.pop("wfmt", "int4")
+    options = over.pop("options", 0)
     g.update(over)
-    return q.make_config(g, wfmt)
+    return q.make_config(g, wfmt, options)
 
 
 def _size(cfg, T):
@@ -60,6 +61,8 @@ def _size(cfg, T):
     (dict(routed_scaling_factor=0.0), q.MOE_ERR_INVALID_ARG),
     (dict(routed_scaling_factor=float("nan")), q.MOE_ERR_INVALID_ARG),
     (dict(wfmt=7), q.MOE_ERR_INVALID_ARG),
+    (dict(options=4), q.MOE_ERR_INVALID_ARG),              # unknown option bit
+    (dict(options=3), q.MOE_OK),
     (dict(n_routed_experts=512, n_group=8, topk_group=4), q.MOE_ERR_UNSUPPORTED),
     (dict(n_routed_experts=128, n_group=128, topk_group=4), q.MOE_ERR_UNSUPPORTED),
     (dict(n_routed_experts=64, n_group=2, topk_group=2, top_k=20), q.MOE_ERR_UNSUPPORTED),
@@ -142,6 +145,9 @@ def test_entry_point_validation_paths():
     assert L.moe_combine(ctypes.byref(c), 8, FAKE, FAKE, FAKE, None, FAKE, 3, None) == q.MOE_ERR_INVALID_ARG
     assert L.moe_combine(ctypes.byref(c), 8, None, FAKE, FAKE, None, FAKE, 0, None) == q.MOE_ERR_INVALID_ARG
     assert L.moe_combine(ctypes.byref(c), 0, FAKE, FAKE, FAKE, None, FAKE, 0, None) == q.MOE_OK
+    f = ctypes.c_uint32(7)
+    assert L.moe_layer_flags(ctypes.c_void_p(FAKE.value + 4), ctypes.byref(f), None) == q.MOE_ERR_INVALID_ARG
+    assert L.moe_layer_flags(FAKE, None, None) == q.MOE_ERR_INVALID_ARG and f.value == 7
 
 
 def test_layer_rejects_buffers_beyond_descriptor_range():
@@ -149,3 +155,4 @@ def test_layer_rejects_buffers_beyond_descriptor_range():
     # the large-batch kernels: rejected before any device call
     c = _cfg(hidden=16384)
     assert _layer(c, T=262144) == q.MOE_ERR_UNSUPPORTED
+

@@ -13,8 +13,9 @@ import torch
 import oracle
 import quantized_moe_02_amd as q
 import synth
-from gpu_common import TOL, check_outputs, check_routing, qexp, run_layer
-from helpers import oracle_inputs, row_rel_err
+from gpu_common import (TOL, FFNCache, check_outputs, check_routing, cover_tokens,
+                        expert_slots_to_check, qexp, run_layer)
+from helpers import np_u16, oracle_inputs, row_rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -60,19 +61,25 @@ def test_tiny_bf16_output_is_rne_of_fp32(T):
     assert torch.equal(y32.to(torch.bfloat16), y16)
 
 
-def test_tiny_entry_points():
-    L = layer("tiny")
+def entry_point_chain(L, T=None, x=None, pool=False):
+    """moe_route -> moe_permute -> moe_expert_ffn_q4 (routed, then dense on the
+    shared expert) -> moe_combine, each result against the oracle: ids exact,
+    permutation exact, expert outputs per sorted slot within TOL, combine
+    within 1e-6 of its own fp64 sum."""
     g = L.geom
-    T, H, E, k = L.T, g["hidden"], g["n_routed_experts"], g["top_k"]
+    x = L.x if x is None else x
+    T = x.shape[0] if T is None else T
+    H, E, k = g["hidden"], g["n_routed_experts"], g["top_k"]
     P = T * k
     cfg = q.make_config(g, L.wfmt)
     ws = q.workspace(cfg, T)
     dev = dict(device="cuda")
     ids = torch.empty(T, k, dtype=torch.int32, **dev)
     tw = torch.empty(T, k, dtype=torch.float32, **dev)
-    q.moe_route(cfg, T, L.x, L.router_w, L.bias, ids, tw, ws)
+    q.moe_route(cfg, T, x, L.router_w, L.bias, ids, tw, ws)
     torch.cuda.synchronize()
-    ids_g, _ = check_routing(L, ids, tw)
+    x_np = np_u16(x)
+    ids_g, _ = check_routing(L, ids, tw, x_np=x_np)
 
     offs = torch.empty(E + 1, dtype=torch.int32, **dev)
     st = torch.empty(P, dtype=torch.int32, **dev)
@@ -88,32 +95,49 @@ def test_tiny_entry_points():
     assert int(na.item()) == len(r_act)
     assert np.array_equal(act.cpu().numpy()[: len(r_act)], r_act)
 
-    x_np, Wr, b, rcfg, routed, shared = oracle_inputs(L)
+    _, _, _, _, routed, shared = oracle_inputs(L, lazy=True)
     X = oracle.bf16_bits_to_f64(x_np)
     out = torch.empty(P, H, dtype=torch.float32, **dev)
-    q.moe_expert_ffn_q4(cfg, T, L.x, qexp(L.routed), offs, st, act, na, out, ws)
+    q.moe_expert_ffn_q4(cfg, T, x, qexp(L.routed), offs, st, act, na, out, ws)
     torch.cuda.synchronize()
+    jobs = [(routed, int(e), X[r_st[r_off[e]:r_off[e + 1]]]) for e in r_act]
+    jobs.append((shared, 0, X))
+    refs = FFNCache()(jobs) if pool else [oracle.expert_ffn(*j) for j in jobs]
     ref = np.zeros((P, H))
-    for e in range(E):
-        lo, hi = r_off[e], r_off[e + 1]
-        if hi > lo:
-            W = [routed.weight(p, e) for p in ("gate", "up", "down")]
-            ref[lo:hi] = oracle.swiglu_ffn(X[r_st[lo:hi]], *W)
-    assert row_rel_err(out.cpu().numpy(), ref).max() <= TOL
+    for e, F in zip(r_act, refs):
+        ref[r_off[e]:r_off[e + 1]] = F
+    err = row_rel_err(out.cpu().numpy(), ref)
+    assert err.max() <= TOL, (err.max(), int(err.argmax()))
 
     outs = torch.empty(T, H, dtype=torch.float32, **dev)
-    q.moe_expert_ffn_q4(cfg, T, L.x, qexp(L.shared), None, None, None, None, outs, ws)
+    q.moe_expert_ffn_q4(cfg, T, x, qexp(L.shared), None, None, None, None, outs, ws)
     torch.cuda.synchronize()
-    refs = oracle.swiglu_ffn(X, *[shared.weight(p, 0) for p in ("gate", "up", "down")])
-    assert row_rel_err(outs.cpu().numpy(), refs).max() <= TOL
+    assert row_rel_err(outs.cpu().numpy(), refs[-1]).max() <= TOL
 
     y = torch.empty(T, H, dtype=torch.float32, **dev)
     q.moe_combine(cfg, T, out, inv, tw, outs, y)
+    y16 = torch.empty(T, H, dtype=torch.bfloat16, **dev)
+    q.moe_combine(cfg, T, out, inv, tw, outs, y16, q.MOE_OUT_BF16)
     torch.cuda.synchronize()
     o64, s64 = out.double().cpu().numpy(), outs.double().cpu().numpy()
     w64 = tw.double().cpu().numpy()
     yref = s64 + np.einsum("tk,tkh->th", w64, o64[r_inv.reshape(T, k)])
     assert row_rel_err(y.cpu().numpy(), yref).max() <= 1e-6
+    assert torch.equal(y.to(torch.bfloat16), y16)
+    return err.max()
+
+
+def test_tiny_entry_points():
+    entry_point_chain(layer("tiny"))
+
+
+@pytest.mark.parametrize("wfmt", ["int4", "nvfp4"])
+@pytest.mark.parametrize("T", [1, 2, 3, 4])
+def test_small_batch_entry_points(T, wfmt):
+    """moe_expert_ffn_q4 at 1-4 tokens runs the GEMV kernels (routed and dense
+    mode), then combine."""
+    L = synth.make_custom(synth.small_geom(), T, wfmt, "normal0.1", seed=400 + T, device="cuda")
+    entry_point_chain(L)
 
 
 @pytest.mark.parametrize("T,k,E,dist", [
@@ -235,18 +259,21 @@ def test_edge_geometries(case):
 # full GLM-5.2-shaped workloads
 # ---------------------------------------------------------------------------
 
-def _full(name, sample):
+def _full(name):
+    """Every token's routing exactly; at up to 64 tokens every token's output,
+    else the outputs of a set of tokens that covers every selected expert."""
     L = layer(name)
     y, ids, tw = run_layer(L)
     ids_g, near = check_routing(L, ids, tw)
     T = L.T
-    idx = np.unique(np.linspace(0, T - 1, min(sample, T)).astype(int))
-    err = check_outputs(L, y, ids_g, token_idx=idx)
-    print(f"{name}: T={T} near-ties={near} sampled={len(idx)} max_row_err={err:.2e}", flush=True)
+    idx = np.arange(T) if T <= 64 else cover_tokens(ids_g, always=(0, T - 1))
+    _, _, _, _, routed, shared = oracle_inputs(L, lazy=True)
+    err = check_outputs(L, y, ids_g, token_idx=idx, ffn_map=FFNCache(), srcs=(routed, shared))
+    print(f"{name}: T={T} near-ties={near} checked={len(idx)} max_row_err={err:.2e}", flush=True)
 
 
 def test_full_decode():
-    _full("decode", 1)
+    _full("decode")
 
 
 def test_decode_poisoned_workspace_reused():
@@ -278,9 +305,9 @@ def test_decode_poisoned_workspace_reused():
 
 
 @pytest.mark.parametrize("case", ["T1", "nvfp4_T1", "decode"])
-def test_single_token_fused_matches_two_launches(case, monkeypatch):
+def test_single_token_fused_matches_two_launches(case):
     """One token runs gate/up and down in one launch with a grid barrier
-    between them; QMOE_DECODE_FUSED=0 selects the two-launch kernels, which
+    between them; MOE_OPT_NO_GRID_WAIT selects the kernels without one, which
     sum in the same order.  Both match the oracle, and each other bit for
     bit."""
     if case == "decode":
@@ -289,71 +316,199 @@ def test_single_token_fused_matches_two_launches(case, monkeypatch):
         over, T, wfmt, bias = EDGE[case]
         L = synth.make_custom(synth.small_geom(**over), T, wfmt, bias, seed=300, device="cuda")
     fused = run_layer(L)
-    monkeypatch.setenv("QMOE_DECODE_FUSED", "0")
-    split = run_layer(L)
+    split = run_layer(L, options=q.MOE_OPT_NO_GRID_WAIT)
     ids_g, _ = check_routing(L, split[1], split[2])
     check_outputs(L, split[0], ids_g)
     for u, v in zip(fused, split):
         assert torch.equal(u, v)
 
 
-def test_fused_decode_gives_up_to_nan(monkeypatch):
-    """The fused single-token kernel's barrier wait is bounded.  With the bound
-    forced to zero polls from the host, no workgroup waits: every row of y is
-    NaN (never a sum over an incomplete h), the routing outputs are still
-    written, and the next call is exact again."""
+def test_fused_decode_gives_up_to_nan():
+    """The fused single-token kernel's barrier wait is bounded.  With no poll
+    allowed (MOE_OPT_GRID_WAIT_NONE, set from the host), no workgroup waits:
+    every row of y is NaN (never a sum over an incomplete h), the routing
+    outputs are still written, and the workspace flag says so.  The next call
+    on the same workspace clears the flag and is exact again."""
     over, T, wfmt, bias = EDGE["T1"]
     L = synth.make_custom(synth.small_geom(**over), T, wfmt, bias, seed=301, device="cuda")
-    monkeypatch.setenv("QMOE_BARRIER_SPINS", "0")
-    y, ids, tw = run_layer(L)
+    ws = q.workspace(q.make_config(L.geom, L.wfmt), T)
+    y, ids, tw = run_layer(L, options=q.MOE_OPT_GRID_WAIT_NONE, ws=ws)
     assert torch.isnan(y).all()
     check_routing(L, ids, tw)
-    monkeypatch.delenv("QMOE_BARRIER_SPINS")
-    y, ids, tw = run_layer(L)
+    assert q.moe_layer_flags(ws) == q.MOE_FLAG_GRID_WAIT_TIMEOUT
+    y, ids, tw = run_layer(L, ws=ws)
+    assert q.moe_layer_flags(ws) == 0
     ids_g, _ = check_routing(L, ids, tw)
     check_outputs(L, y, ids_g)
+    # a large-batch call clears a raised flag too (the flags word is at offset
+    # 0 of every workspace)
+    L8 = layer("tiny")
+    ws8 = q.workspace(q.make_config(L8.geom, L8.wfmt), L8.T)
+    run_layer(L, options=q.MOE_OPT_GRID_WAIT_NONE, ws=ws8)
+    assert q.moe_layer_flags(ws8) == q.MOE_FLAG_GRID_WAIT_TIMEOUT
+    run_layer(L8, ws=ws8)
+    assert q.moe_layer_flags(ws8) == 0
 
 
 def test_full_verify4():
-    _full("verify4", 4)
+    _full("verify4")
+
+
+def test_full_verify4_entry_points():
+    """The GEMV kernels behind moe_expert_ffn_q4 at 4 tokens at full size."""
+    entry_point_chain(layer("verify4"), pool=True)
 
 
 def test_full_verify64():
-    _full("verify64", 3)
+    _full("verify64")
 
 
-def test_full_prefill4k():
-    _full("prefill4k", 2)
-
-
-def test_full_nvfp4_512():
-    _full("nvfp4_512", 2)
-
-
-def test_full_prefill16k_routing_and_permutation():
-    """T = 16384: every token's routing and the permutation exactly; one
-    sampled token's output."""
-    L = layer("prefill16k")
+def _full_large(name):
+    """A large batch at full size, through the entry points and the layer:
+      * routing of every token exactly, and the permutation of the GPU's ids;
+      * moe_expert_ffn_q4's routed output at every sorted slot of eight
+        experts (the most and least loaded, ragged last work units) and at the
+        first, a middle and the last slot of every other active expert;
+      * its dense output (the shared expert) on 256 tokens, the last included;
+      * moe_layer's output on tokens that together cover every selected
+        expert.
+    Each expert is dequantised once by the oracle (worker processes)."""
+    L = layer(name)
     g = L.geom
-    T, E, k = L.T, g["n_routed_experts"], g["top_k"]
+    T, H, E, k = L.T, g["hidden"], g["n_routed_experts"], g["top_k"]
+    P = T * k
     cfg = q.make_config(g, L.wfmt)
+    y, ids, tw = run_layer(L)
+    ids_g, near = check_routing(L, ids, tw)
     ws = q.workspace(cfg, T)
-    ids = torch.empty(T, k, dtype=torch.int32, device="cuda")
-    tw = torch.empty(T, k, dtype=torch.float32, device="cuda")
-    q.moe_route(cfg, T, L.x, L.router_w, L.bias, ids, tw, ws)
-    offs = torch.empty(E + 1, dtype=torch.int32, device="cuda")
-    st = torch.empty(T * k, dtype=torch.int32, device="cuda")
-    inv = torch.empty(T * k, dtype=torch.int32, device="cuda")
-    act = torch.empty(E, dtype=torch.int32, device="cuda")
-    na = torch.empty(1, dtype=torch.int32, device="cuda")
+    dev = dict(device="cuda")
+    offs = torch.empty(E + 1, dtype=torch.int32, **dev)
+    st = torch.empty(P, dtype=torch.int32, **dev)
+    inv = torch.empty(P, dtype=torch.int32, **dev)
+    act = torch.empty(E, dtype=torch.int32, **dev)
+    na = torch.empty(1, dtype=torch.int32, **dev)
     q.moe_permute(cfg, T, ids, offs, st, inv, act, na, ws)
     torch.cuda.synchronize()
-    ids_g, near = check_routing(L, ids, tw)
     r_off, r_st, r_inv, r_act = oracle.permute(ids_g, E)
     assert np.array_equal(offs.cpu().numpy(), r_off)
     assert np.array_equal(st.cpu().numpy(), r_st)
     assert np.array_equal(inv.cpu().numpy(), r_inv)
+    assert int(na.item()) == len(r_act)
+    out = torch.empty(P, H, dtype=torch.float32, **dev)
+    q.moe_expert_ffn_q4(cfg, T, L.x, qexp(L.routed), offs, st, act, na, out, ws)
+    outs = torch.empty(T, H, dtype=torch.float32, **dev)
+    q.moe_expert_ffn_q4(cfg, T, L.x, qexp(L.shared), None, None, None, None, outs, ws)
+    torch.cuda.synchronize()
     del ws
-    y, ids2, _ = run_layer(L)
-    assert torch.equal(ids2, ids)
-    check_outputs(L, y, ids_g, token_idx=[T // 2])
+
+    slots = expert_slots_to_check(r_off, seed=T)
+    cover = cover_tokens(ids_g, always=(0, T - 1))
+    dense_rows = np.unique(np.append(np.linspace(0, T - 1, 255).astype(int), T - 1))
+    x_np, _, _, _, routed, shared = oracle_inputs(L, lazy=True)
+    X = oracle.bf16_bits_to_f64(x_np)
+    # every expert's rows for all three checks in one job, so it is dequantised once
+    cov_ids = ids_g[cover]
+    jobs = []
+    for e, sl in slots.items():
+        toks = np.union1d(r_st[sl], cover[np.any(cov_ids == e, axis=1)])
+        jobs.append((routed, e, X[toks]))
+    jobs.append((shared, 0, X[np.union1d(dense_rows, cover)]))
+    cache = FFNCache()
+    cache.fill(jobs)
+
+    all_sl = np.concatenate([slots[e] for e in sorted(slots)])
+    got = out[torch.from_numpy(all_sl).to("cuda")].double().cpu().numpy()
+    ref = np.concatenate(cache([(routed, e, X[r_st[slots[e]]]) for e in sorted(slots)]))
+    err_o = row_rel_err(got, ref)
+    assert err_o.max() <= TOL, f"expert output row error {err_o.max():.3e} at slot {all_sl[err_o.argmax()]}"
+    err_s = row_rel_err(outs.cpu().numpy()[dense_rows], cache([(shared, 0, X[dense_rows])])[0])
+    assert err_s.max() <= TOL, err_s.max()
+    err_y = check_outputs(L, y, ids_g, token_idx=cover, ffn_map=cache, srcs=(routed, shared))
+    print(f"{name}: T={T} near-ties={near} expert rows={len(all_sl)} ({len(slots)} experts) "
+          f"max err {err_o.max():.2e}; shared rows {len(dense_rows)} {err_s.max():.2e}; "
+          f"layer tokens {len(cover)} {err_y:.2e}", flush=True)
+
+
+def test_full_nvfp4_512():
+    _full_large("nvfp4_512")
+
+
+def test_full_nvfp4_4_entry_points():
+    """NVFP4 GEMV kernels at 4 tokens at full size (the NVFP4 layer's first
+    four tokens)."""
+    L = layer("nvfp4_512")
+    entry_point_chain(L, x=L.x[:4].contiguous(), pool=True)
+
+
+def test_full_prefill4k():
+    _full_large("prefill4k")
+
+
+def test_full_prefill16k():
+    _full_large("prefill16k")
+
+
+# ---------------------------------------------------------------------------
+# raw packed bytes and exact router ties
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("wfmt", ["int4", "nvfp4"])
+@pytest.mark.parametrize("T", [1, 3, 8, 40, 640])
+def test_raw_weight_bytes(T, wfmt):
+    """Uniformly random code bytes (int4 code 0, E2M1 -0 included) and random
+    scales of either sign (finite E4M3 codes for NVFP4) through every path:
+    one token (fused kernel), 3 tokens (small-batch kernels), 8 and 40 tokens
+    (thin GEMM units), 640 tokens (fat units)."""
+    L = synth.make_raw(synth.small_geom(), T, wfmt, seed=500 + T, device="cuda")
+    y, ids, tw = run_layer(L)
+    ids_g, _ = check_routing(L, ids, tw)
+    check_outputs(L, y, ids_g)
+    if T <= 4:
+        entry_point_chain(L)
+
+
+TIE_BIAS = {
+    "zero": lambda E: np.zeros(E),
+    "mod3": lambda E: 0.125 * (np.arange(E) % 3),
+    "pairs": lambda E: 0.0625 * ((np.arange(E) * 5) % 4),
+}
+
+
+@pytest.mark.parametrize("bias", sorted(TIE_BIAS))
+@pytest.mark.parametrize("T", [1, 3, 37])
+def test_exact_router_ties(T, bias):
+    """Zero router weights make every sigmoid score exactly 1/2, so the
+    selection is decided by biases with exact ties (equal group scores, equal
+    biased scores): the ids must equal the oracle's tie-break (lower group,
+    lower id) exactly, with no near-tie leniency, and every weight is
+    rsf / top_k."""
+    geom = synth.small_geom()
+    L = synth.make_custom(geom, T, "int4", "zero", seed=600 + T, device="cuda")
+    L.router_w.zero_()
+    L.bias.copy_(torch.from_numpy(TIE_BIAS[bias](geom["n_routed_experts"])).float())
+    y, ids, tw = run_layer(L)
+    x, Wr, b, cfg, _, _ = oracle_inputs(L)
+    ids_ref, w_ref, info = oracle.route(oracle.bf16_bits_to_f64(x), Wr, b, cfg)
+    assert np.all(info["margin"] == 0) or bias != "zero"
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    assert np.array_equal(tw.cpu().numpy(), w_ref.astype(np.float32))
+    check_outputs(L, y, ids_ref)
+
+
+def test_exact_router_ties_full_decode():
+    """The same at the GLM-5.2 decode shape (one token, fused kernel)."""
+    L = layer("decode")
+    rw, b0 = L.router_w.clone(), L.bias.clone()
+    try:
+        L.router_w.zero_()
+        E = L.geom["n_routed_experts"]
+        L.bias.copy_(torch.from_numpy(0.0625 * ((np.arange(E) * 5) % 4)).float())
+        y, ids, tw = run_layer(L)
+        x, Wr, b, cfg, _, _ = oracle_inputs(L, lazy=True)
+        ids_ref, w_ref, _ = oracle.route(oracle.bf16_bits_to_f64(x), Wr, b, cfg)
+        assert np.array_equal(ids.cpu().numpy(), ids_ref)
+        assert np.array_equal(tw.cpu().numpy(), w_ref.astype(np.float32))
+        check_outputs(L, y, ids_ref)
+    finally:
+        L.router_w.copy_(rw)
+        L.bias.copy_(b0)
