@@ -23,9 +23,9 @@
  *   call only.  The caller owns every buffer, including the workspace.  The
  *   library never allocates or frees memory; its only global state is a
  *   per-device record of how many workgroups of the single-token kernel fit
- *   on the device (computed once, read-only after).  Calls on different
- *   streams are independent as long as their workspaces and outputs do not
- *   overlap.
+ *   on the device (computed once, read-only after) and the device buffer of
+ *   moe_layer_noalloc.  Calls on different streams are independent as long
+ *   as their workspaces and outputs do not overlap.
  * Alignment.  Packed weight arrays (`q`), scale arrays and `x` must be 16-byte
  *   aligned; the workspace 256-byte aligned.  Otherwise MOE_ERR_INVALID_ARG.
  * Asynchrony.  Every call only enqueues kernels on `stream` and returns
@@ -139,7 +139,8 @@ const char* moe_status_string(moe_status s);
  * output `flags`); the first 4 bytes of every workspace hold them, and
  * moe_layer clears them before it does anything else.  The call enqueues a
  * copy on `stream` and waits for it, so it returns after all work queued on
- * `stream` before it has finished.
+ * `stream` before it has finished.  ws == NULL reads the flags of
+ * moe_layer_noalloc's workspace on the current device.
  * MOE_FLAG_GRID_WAIT_TIMEOUT  the single-token kernel's workgroups waited for
  *   each other in vain (other work on the device kept some from starting);
  *   the rows of y that they owned are NaN.  Rerun with MOE_OPT_NO_GRID_WAIT. */
@@ -247,6 +248,26 @@ moe_status moe_layer_trace(const moe_config* cfg, int32_t T, const uint16_t* x,
                            const moe_qexperts* routed, const moe_qexperts* shared, void* y,
                            int32_t out_dtype, int32_t* topk_ids_out, float* topk_w_out,
                            void* ws, size_t ws_bytes, hipStream_t stream, moe_trace* trace);
+
+/* moe_layer without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, serving loops and harnesses
+ * that forbid hipMalloc.  The workspace is a buffer inside the library's
+ * device code, MOE_NOALLOC_WS_BYTES on every GPU the library runs on, held
+ * until the process ends; the call allocates nothing (no hipMalloc, no
+ * allocating library routine).  The caller still passes inputs and outputs.
+ * Calls whose moe_workspace_size(cfg, T) exceeds MOE_NOALLOC_WS_BYTES return
+ * MOE_ERR_UNSUPPORTED before any HIP call (the GLM-5.2 layer shape fits up to
+ * 64 tokens).  All calls on one device share its buffer: calls that overlap
+ * on one device (other streams, other threads) race and give wrong results.
+ * Each call writes every workspace word it reads, so a call's results do not
+ * depend on the previous call.  Otherwise as moe_layer (same kernels, same
+ * results); moe_layer_flags(NULL, ...) reads its flags. */
+#define MOE_NOALLOC_WS_BYTES (32u << 20)
+moe_status moe_layer_noalloc(const moe_config* cfg, int32_t T, const uint16_t* x,
+                             const float* router_w, const float* bias,
+                             const moe_qexperts* routed, const moe_qexperts* shared, void* y,
+                             int32_t out_dtype, int32_t* topk_ids_out, float* topk_w_out,
+                             hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -24,6 +24,7 @@ MOE_OUT_F32, MOE_OUT_BF16 = 0, 1
 MOE_OPT_NO_GRID_WAIT, MOE_OPT_GRID_WAIT_NONE = 1, 2
 MOE_FLAG_GRID_WAIT_TIMEOUT = 1
 MOE_MAX_TOKENS = 262144
+MOE_NOALLOC_WS_BYTES = 32 << 20
 WFMT = {"int4": MOE_WFMT_INT4_G32_F16, "nvfp4": MOE_WFMT_NVFP4}
 
 
@@ -82,6 +83,7 @@ def lib() -> ctypes.CDLL:
             "moe_layer_trace": [cfgp, i32, vp, vp, vp, exp, exp, vp, i32, vp, vp, vp, sz, vp,
                                 ctypes.POINTER(MoeTrace)],
             "moe_layer_flags": [vp, ctypes.POINTER(ctypes.c_uint32), vp],
+            "moe_layer_noalloc": [cfgp, i32, vp, vp, vp, exp, exp, vp, i32, vp, vp, vp],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -194,3 +196,13 @@ def moe_layer_flags(ws, stream=None) -> int:
     _check(lib().moe_layer_flags(_p(ws), ctypes.byref(f), _stream(stream)), "moe_layer_flags")
     return f.value
 
+
+def moe_layer_noalloc(cfg, T, x, router_w, bias, routed: MoeQExperts,
+                      shared: Optional[MoeQExperts], y, out_dtype=MOE_OUT_F32, topk_ids_out=None,
+                      topk_w_out=None, stream=None):
+    """moe_layer on the library's own device workspace (no workspace argument)."""
+    _check(lib().moe_layer_noalloc(ctypes.byref(cfg), T, _p(x), _p(router_w), _p(bias),
+                                   ctypes.byref(routed),
+                                   None if shared is None else ctypes.byref(shared), _p(y),
+                                   out_dtype, _p(topk_ids_out), _p(topk_w_out), _stream(stream)),
+           "moe_layer_noalloc")

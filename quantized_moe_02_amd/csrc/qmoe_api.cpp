@@ -227,8 +227,9 @@ const char* moe_status_string(moe_status s) {
 }
 
 moe_status moe_layer_flags(const void* ws, uint32_t* flags, hipStream_t stream) {
-  if (!ws || !flags) return MOE_ERR_INVALID_ARG;
-  if (!aligned(ws, kAlign)) return MOE_ERR_INVALID_ARG;
+  if (!flags) return MOE_ERR_INVALID_ARG;
+  if (ws && !aligned(ws, kAlign)) return MOE_ERR_INVALID_ARG;
+  if (!ws && !(ws = noalloc_workspace())) return MOE_ERR_HIP;
   uint32_t v = 0;
   if (hipMemcpyAsync(&v, ws, sizeof(v), hipMemcpyDeviceToHost, stream) != hipSuccess ||
       hipStreamSynchronize(stream) != hipSuccess)

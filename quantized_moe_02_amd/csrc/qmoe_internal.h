@@ -84,6 +84,9 @@ Workspace carve_workspace(const moe_config& c, int T, void* base);
 moe_status check_layer_args(const moe_config* cfg, int32_t T, const uint16_t* x,
                             const float* router_w, const moe_qexperts* routed,
                             const moe_qexperts* shared, const void* y, int32_t out_dtype);
+// moe_layer_noalloc's workspace on the current device (its device address,
+// looked up on the first call on that device); nullptr if the lookup failed.
+void* noalloc_workspace();
 
 struct RouteArgs {
   const uint16_t* x;

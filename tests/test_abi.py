@@ -156,3 +156,21 @@ def test_layer_rejects_buffers_beyond_descriptor_range():
     c = _cfg(hidden=16384)
     assert _layer(c, T=262144) == q.MOE_ERR_UNSUPPORTED
 
+
+def test_noalloc_validation_and_size_limit():
+    """moe_layer_noalloc checks its arguments and its workspace bound before
+    any HIP call: the GLM-5.2 shape fits at 64 tokens, not at 128."""
+    L = q.lib()
+    g = synth.WORKLOADS["decode"]["geom"]
+    c = q.make_config(g, "int4")
+    assert q.moe_workspace_size(c, 64) <= q.MOE_NOALLOC_WS_BYTES < q.moe_workspace_size(c, 128)
+    e = _experts()
+
+    def call(T, x=FAKE, cfg=c):
+        return L.moe_layer_noalloc(ctypes.byref(cfg), T, x, FAKE, None, ctypes.byref(e),
+                                   ctypes.byref(e), FAKE, 0, None, None, None)
+    assert call(128) == q.MOE_ERR_UNSUPPORTED
+    assert call(4096) == q.MOE_ERR_UNSUPPORTED
+    assert call(8, x=None) == q.MOE_ERR_INVALID_ARG
+    assert call(-1) == q.MOE_ERR_INVALID_ARG
+    assert call(0) == q.MOE_OK
