@@ -27,5 +27,6 @@ from .moe import (  # noqa: F401
     bf16_bits_to_f64, fp16_bits_to_f64, decode_e2m1, decode_e4m3fn,
     unpack_int4_codes, unpack_nvfp4_codes, dequant_int4, dequant_nvfp4,
     RouterConfig, route, route_weights, route_margins, valid_under_perturbation,
+    apply_top_p, valid_top_p,
     permute, swiglu_ffn, expert_ffn, layer, dense_layer, ExpertSource,
 )

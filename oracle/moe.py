@@ -9,6 +9,9 @@ fusion or reordering beyond what the definition states.  Page references:
               batch-union MoE; int4 kernels with dequant-on-use).
   [P2-Cara]   same page, section "Cara kerja eksekusi MoE berbasis streaming
               disk" (routed experts vs the always-resident shared expert).
+  [P2-Unduh]  same page, section "Mengunduh model dan menjalankannya"
+              (the --topp 0.7 option: adaptive expert top-p), and section
+              "Benchmark komunitas" (its measured effect).
   [P5-Tech]   page "NVIDIA stellt neues GLM-5.2 NVFP4 Modell vor", section
               "Technische Details und Quantisierungsansatz" (expert FFNs in
               NVFP4 with FP8 scales per 16 elements; router kept in BF16/FP32).
@@ -150,6 +153,7 @@ class RouterConfig:
     top_k: int
     routed_scaling_factor: float
     group_top: int = 2          # reading: a group's score is the sum of its top-2 biased scores
+    top_p: float = 0.0          # adaptive expert top-p; 0 (or >= 1) keeps all top_k
 
 
 def _router_scores(x: np.ndarray, Wr: np.ndarray, b: np.ndarray):
@@ -180,6 +184,9 @@ def route(x: np.ndarray, Wr: np.ndarray, b: np.ndarray, cfg: RouterConfig):
        experts always come from the kept groups.
     7. report ids in ascending expert id.
     8. weights: w_i = s[id_i] / sum_j s[id_j] * routed_scaling_factor.
+    9. adaptive expert top-p (0 < top_p < 1), see `apply_top_p`: only a
+       prefix of the chosen experts stays; the others get id -1 and weight 0,
+       after the kept ids.
     Returns (ids int64 [T,k], w float64 [T,k], info dict)."""
     x = np.asarray(x, np.float64)
     T = x.shape[0]
@@ -193,16 +200,56 @@ def route(x: np.ndarray, Wr: np.ndarray, b: np.ndarray, cfg: RouterConfig):
     masked = np.where(allowed, sb, -np.inf)
     eorder = np.argsort(-masked, axis=1, kind="stable")
     ids = np.sort(eorder[:, :k], axis=1)
+    margin = route_margins(sb, gscore, keep, cfg)
+    if 0.0 < cfg.top_p < 1.0:
+        ids, pmargin = apply_top_p(s, ids, cfg.top_p)
+        margin = np.minimum(margin, pmargin)
     w = route_weights(s, ids, cfg.routed_scaling_factor)
-    info = dict(logits=logits, s=s, sb=sb, gscore=gscore, keep=keep,
-                margin=route_margins(sb, gscore, keep, cfg))
+    info = dict(logits=logits, s=s, sb=sb, gscore=gscore, keep=keep, margin=margin)
     return ids, w, info
+
+
+def apply_top_p(s: np.ndarray, ids: np.ndarray, p: float):
+    """Adaptive expert top-p [P2-Unduh: --topp].  The pages name the option
+    only; the reading taken: order a token's chosen experts by their share
+    s_e / sum(s over the chosen) (descending; equal shares: lower id first),
+    keep the shortest prefix whose shares add up to at least p -- at least
+    one expert -- and drop the rest (id -1, after the kept ids, which stay in
+    ascending order).  The kept weights are renormalised by `route_weights`.
+    Also returns each token's decision margin: the smallest distance of a
+    prefix sum from p, and the share gap between the last kept and the first
+    dropped expert."""
+    ids = np.asarray(ids)
+    T, k = ids.shape
+    out = np.full_like(ids, -1)
+    margin = np.full(T, np.inf)
+    for t in range(T):
+        sel = [int(e) for e in ids[t]]
+        sv = [float(s[t, e]) for e in sel]
+        total = sum(sv)
+        order = sorted(range(k), key=lambda i: (-sv[i], sel[i]))
+        shares = [sv[i] / total for i in order]
+        csum, keep = 0.0, k
+        for j in range(k):
+            csum += shares[j]
+            margin[t] = min(margin[t], abs(csum - p))
+            if csum >= p and keep == k:
+                keep = j + 1
+        if keep < k:
+            margin[t] = min(margin[t], shares[keep - 1] - shares[keep])
+        kept = sorted(sel[i] for i in order[:keep])
+        out[t, :keep] = kept
+    return out, margin
 
 
 def route_weights(s: np.ndarray, ids: np.ndarray, rsf: float) -> np.ndarray:
     """Renormalised unbiased sigmoid scores of the chosen experts times
-    routed_scaling_factor (no epsilon: every s > 0)."""
-    sel = np.take_along_axis(np.asarray(s, np.float64), np.asarray(ids), axis=1)
+    routed_scaling_factor (no epsilon: every s > 0).  Slots with id -1
+    (dropped by the adaptive top-p) get weight 0 and do not enter the sum."""
+    ids = np.asarray(ids)
+    valid = ids >= 0
+    sel = np.take_along_axis(np.asarray(s, np.float64), np.where(valid, ids, 0), axis=1)
+    sel = np.where(valid, sel, 0.0)
     return sel / sel.sum(axis=1, keepdims=True) * float(rsf)
 
 
@@ -236,6 +283,7 @@ def valid_under_perturbation(ids_t: np.ndarray, sb_t: np.ndarray, cfg: RouterCon
     ids_t = np.asarray(ids_t)
     if len(set(ids_t.tolist())) != k or ids_t.min() < 0 or ids_t.max() >= E:
         return False
+    # (with the adaptive top-p, check the kept prefix with valid_top_p)
     per = E // G
     gscore = _group_scores(sb_t[None, :], cfg)[0]
     chosen_groups = sorted(set((ids_t // per).tolist()))
@@ -264,24 +312,29 @@ def valid_under_perturbation(ids_t: np.ndarray, sb_t: np.ndarray, cfg: RouterCon
 
 def permute(ids: np.ndarray, n_experts: int):
     """Group the T*k picks by expert, keeping pick order (t*k+i) inside an
-    expert: a counting sort written out.
-    Returns expert_offsets [E+1], sorted_token [T*k] (token of the pick at each
-    sorted position), inv_perm [T*k] (sorted position of pick t*k+i),
-    active_experts (ascending ids with at least one pick)."""
+    expert: a counting sort written out.  Picks with id -1 (dropped by the
+    adaptive top-p) take no slot; their inv_perm is -1.
+    Returns expert_offsets [E+1], sorted_token [P'] (token of the pick at each
+    sorted position, P' valid picks), inv_perm [T*k] (sorted position of pick
+    t*k+i), active_experts (ascending ids with at least one pick)."""
     ids = np.asarray(ids)
     T, k = ids.shape
     flat = ids.reshape(-1).tolist()
     counts = [0] * n_experts
     for e in flat:
+        if e < 0:
+            continue
         counts[e] += 1
     offsets = [0] * (n_experts + 1)
     for e in range(n_experts):
         offsets[e + 1] = offsets[e] + counts[e]
     cursor = offsets[:-1]
     cursor = list(cursor)
-    sorted_token = [0] * (T * k)
-    inv_perm = [0] * (T * k)
+    sorted_token = [0] * offsets[n_experts]
+    inv_perm = [-1] * (T * k)
     for p, e in enumerate(flat):
+        if e < 0:
+            continue
         pos = cursor[e]
         cursor[e] += 1
         sorted_token[pos] = p // k
@@ -334,7 +387,7 @@ def layer(x_bits, Wr, b, cfg: RouterConfig, routed: ExpertSource,
         ids = np.asarray(ids)
         w = route_weights(s, ids, cfg.routed_scaling_factor)
     T, H = X.shape
-    experts = [int(e) for e in np.unique(ids)]
+    experts = [int(e) for e in np.unique(ids) if e >= 0]
     jobs = [(routed, e, X[np.nonzero(ids == e)[0]]) for e in experts]
     if shared is not None:
         jobs.append((shared, 0, X))
@@ -362,10 +415,37 @@ def dense_layer(x_bits, Wr, b, cfg: RouterConfig, routed: ExpertSource,
     ids, w, _ = route(X, Wr, b, cfg)
     T, H = X.shape
     gate = np.zeros((T, cfg.n_experts))
-    np.put_along_axis(gate, ids, w, axis=1)
+    for t in range(T):
+        for e, we in zip(ids[t], w[t]):
+            if e >= 0:
+                gate[t, e] = we
     y = np.zeros((T, H))
     for e in range(cfg.n_experts):
         y += gate[:, e:e + 1] * swiglu_ffn(X, *_expert_weights(routed, e))
     if shared is not None:
         y += swiglu_ffn(X, *_expert_weights(shared, 0))
     return y
+
+
+def valid_top_p(ids_t: np.ndarray, s_t: np.ndarray, chosen_t: np.ndarray, p: float,
+                tau: float) -> bool:
+    """Whether `ids_t` (one token's ids after the adaptive top-p, -1 for
+    dropped slots) is what `apply_top_p` keeps from the chosen experts
+    `chosen_t` for some shares within `tau` of the exact ones -- the check for
+    tokens whose top-p decision margin is below rounding level."""
+    kept = [int(e) for e in ids_t if e >= 0]
+    chosen = [int(e) for e in chosen_t]
+    if not kept or not set(kept) <= set(chosen) or list(ids_t[len(kept):]) != [-1] * (len(ids_t) - len(kept)):
+        return False
+    if kept != sorted(kept):
+        return False
+    total = sum(float(s_t[e]) for e in chosen)
+    share = {e: float(s_t[e]) / total for e in chosen}
+    dropped = [e for e in chosen if e not in kept]
+    if dropped and min(share[e] for e in kept) < max(share[e] for e in dropped) - 2 * tau:
+        return False
+    ks = sorted((share[e] for e in kept), reverse=True)
+    csum = sum(ks)
+    if csum < p - len(chosen) * tau:
+        return False
+    return len(kept) == 1 or csum - ks[-1] < p + len(chosen) * tau

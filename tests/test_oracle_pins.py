@@ -477,3 +477,97 @@ def test_router_small_groups_brute_force(E, G, TG, k):
         best = max(itertools.combinations(allowed, k), key=lambda c: sum(sb[t, e] for e in c))
         assert info["margin"][t] > 1e-9
         assert sorted(best) == list(ids[t]), t
+
+
+# ---------------------------------------------------------------------------
+# Adaptive expert top-p
+# ---------------------------------------------------------------------------
+
+def test_top_p_hand_example():
+    """Chosen experts 0..3 with scores .5, .25, .125, .125 (shares exactly
+    1/2, 1/4, 1/8, 1/8): the shortest share-ordered prefix reaching p."""
+    s = np.array([[0.5, 0.25, 0.125, 0.125]])
+    ids = np.array([[0, 1, 2, 3]])
+    cases = {0.5: [0], 0.6: [0, 1], 0.75: [0, 1], 0.76: [0, 1, 2], 0.9: [0, 1, 2, 3],
+             0.01: [0]}
+    for p, kept in cases.items():
+        out, _ = oracle.apply_top_p(s, ids, p)
+        assert list(out[0]) == kept + [-1] * (4 - len(kept)), p
+    out, _ = oracle.apply_top_p(s, ids, 0.75)
+    w = oracle.route_weights(s, out, 2.0)
+    assert np.allclose(w[0], [2.0 * 2 / 3, 2.0 / 3, 0, 0], rtol=1e-15)
+    # scores given in another id order: ties still go to the lower id
+    s2 = np.array([[0.125, 0.25, 0.125, 0.5]])
+    out, _ = oracle.apply_top_p(s2, ids, 0.76)
+    assert list(out[0]) == [0, 1, 3, -1]
+
+
+def test_top_p_brute_force():
+    """Random tokens: the kept set is the smallest set of chosen experts that
+    contains every expert with a larger share than any member and whose
+    shares reach p (found by enumerating all subsets)."""
+    rng = np.random.default_rng(11)
+    for _ in range(200):
+        k = int(rng.integers(1, 7))
+        E = 12
+        ids = np.sort(rng.choice(E, size=k, replace=False))[None, :]
+        s = rng.random((1, E)) * 0.9 + 0.05
+        p = float(rng.random())
+        out, _ = oracle.apply_top_p(s, ids, p)
+        chosen = list(ids[0])
+        total = sum(s[0, e] for e in chosen)
+        best = None
+        for r in range(1, k + 1):
+            for sub in itertools.combinations(chosen, r):
+                rest = [e for e in chosen if e not in sub]
+                closed = not rest or min(s[0, e] for e in sub) >= max(s[0, e] for e in rest)
+                if closed and sum(s[0, e] for e in sub) / total >= p - 1e-12:
+                    best = sorted(sub)
+                    break
+            if best:
+                break
+        assert [e for e in out[0] if e >= 0] == best
+
+
+def test_top_p_off_is_plain_routing_and_layer_is_dense_definition():
+    L = synth.make_custom(synth.small_geom(), 8, "int4", "normal0.1", seed=51)
+    x, Wr, b, cfg, routed, shared = oracle_inputs(L)
+    X = oracle.bf16_bits_to_f64(x)
+    ids0, w0, _ = oracle.route(X, Wr, b, cfg)
+    for p in (0.0, 1.0):
+        c = oracle.RouterConfig(cfg.n_experts, cfg.n_group, cfg.topk_group, cfg.top_k,
+                                cfg.routed_scaling_factor, top_p=p)
+        ids1, w1, _ = oracle.route(X, Wr, b, c)
+        assert np.array_equal(ids0, ids1) and np.array_equal(w0, w1)
+    c = oracle.RouterConfig(cfg.n_experts, cfg.n_group, cfg.topk_group, cfg.top_k,
+                            cfg.routed_scaling_factor, top_p=0.6)
+    ids, w, _ = oracle.route(X, Wr, b, c)
+    n_kept = (ids >= 0).sum(1)
+    assert n_kept.min() >= 1 and n_kept.max() <= cfg.top_k and (n_kept < cfg.top_k).any()
+    assert np.allclose(w.sum(1), cfg.routed_scaling_factor, rtol=1e-13)
+    assert np.all((w > 0) == (ids >= 0))
+    # kept ids are a subset of the plain choice, in ascending order, -1 after
+    for t in range(ids.shape[0]):
+        kept = [e for e in ids[t] if e >= 0]
+        assert kept == sorted(kept) and set(kept) <= set(ids0[t])
+        assert list(ids[t][len(kept):]) == [-1] * (cfg.top_k - len(kept))
+    y, _, _ = oracle.layer(x, Wr, b, c, routed, shared)
+    assert np.allclose(y, oracle.dense_layer(x, Wr, b, c, routed, shared), rtol=1e-12, atol=1e-14)
+    # permutation of the kept picks: stable argsort of the valid ones
+    offs, st, inv, act = oracle.permute(ids, cfg.n_experts)
+    flat = ids.reshape(-1)
+    valid = np.nonzero(flat >= 0)[0]
+    order = valid[np.argsort(flat[valid], kind="stable")]
+    assert np.array_equal(st, order // cfg.top_k)
+    assert offs[-1] == len(valid) and np.all(inv[flat < 0] == -1)
+    assert np.array_equal(order[inv[valid]], valid)
+
+
+def test_valid_top_p():
+    s = np.array([0.5, 0.25, 0.125, 0.125])
+    chosen = np.array([0, 1, 2, 3])
+    assert oracle.valid_top_p(np.array([0, 1, -1, -1]), s, chosen, 0.75, 1e-9)
+    assert oracle.valid_top_p(np.array([0, 1, 2, -1]), s, chosen, 0.75, 1e-9)     # at the boundary
+    assert not oracle.valid_top_p(np.array([0, 1, 2, -1]), s, chosen, 0.6, 1e-9)
+    assert not oracle.valid_top_p(np.array([0, 2, -1, -1]), s, chosen, 0.6, 1e-9)
+    assert oracle.valid_top_p(np.array([0, 1, 3, -1]), s, chosen, 0.76, 1e-9)     # tie
