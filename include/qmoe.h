@@ -97,7 +97,22 @@ typedef struct {
   float routed_scaling_factor;     /* rsf: multiplies the renormalised routed weights */
   int32_t wfmt;                    /* moe_wfmt of routed and shared experts */
   uint32_t options;                /* MOE_OPT_* bits; 0 for the defaults */
+  float expert_top_p;              /* adaptive expert top-p p in [0, 1]; 0 (or 1): off */
 } moe_config;
+
+/* Adaptive expert top-p (page "Show HN: Menjalankan GLM 5.2 ...", section
+ * "Mengunduh model dan menjalankannya": the --topp option; the pages name it
+ * without a definition, and the reading taken here is the following).  With
+ * 0 < expert_top_p < 1, after the top_k selection each token keeps only the
+ * shortest prefix of its chosen experts, ordered by share s / sum(s over the
+ * chosen) (descending; equal shares: lower id first), whose shares add up to
+ * at least expert_top_p -- at least one expert; the kept weights are
+ * renormalised (s / sum(s over the kept) * rsf).  topk_ids then hold the kept
+ * ids in ascending order followed by -1, topk_w the weights followed by 0;
+ * moe_permute gives dropped picks no slot (inv_perm -1), moe_combine skips
+ * them, and their experts' weights are not read.  The decision is taken in
+ * float64 on the float32 value of expert_top_p.  NaN or values outside
+ * [0, 1] are MOE_ERR_INVALID_ARG. */
 
 /* moe_config.options.  Unknown bits are MOE_ERR_INVALID_ARG.
  * MOE_OPT_NO_GRID_WAIT   moe_layer never runs the single-token kernel whose
@@ -169,10 +184,14 @@ moe_status moe_route(const moe_config* cfg, int32_t T, const uint16_t* x,
  * of the batch is read once and applied to every position routed to it).
  * Stable counting sort of the P = T*k picks by expert id, keeping pick order
  * p = t*k + i inside each expert.
- *   topk_ids       int32 [T][k] in: values in [0, E) (else results undefined)
- *   expert_offsets int32 [E+1] out: exclusive prefix sum of per-expert counts
+ *   topk_ids       int32 [T][k] in: values in [0, E), or -1 for a pick the
+ *                                   adaptive top-p dropped (else results
+ *                                   undefined)
+ *   expert_offsets int32 [E+1] out: exclusive prefix sum of per-expert counts;
+ *                                   offsets[E] is the number of kept picks
  *   sorted_token   int32 [P]   out: token index of the pick at each sorted slot
- *   inv_perm       int32 [P]   out: sorted slot of pick p
+ *                                   (slots past offsets[E] unspecified)
+ *   inv_perm       int32 [P]   out: sorted slot of pick p, -1 if dropped
  *   active_experts int32 [E]   out: experts with >= 1 pick, ascending; the tail
  *                                   beyond n_active is left unspecified
  *   n_active       int32 [1]   out */
@@ -198,7 +217,8 @@ moe_status moe_expert_ffn_q4(const moe_config* cfg, int32_t T, const uint16_t* x
                              size_t ws_bytes, hipStream_t stream);
 
 /* Weighted combine: y_t = sum_i topk_w[t][i] * expert_out[inv_perm[t*k+i]]
- *                         + shared_out[t]   (shared_out may be NULL).
+ *                         + shared_out[t]   (shared_out may be NULL);
+ * picks with inv_perm -1 (dropped by the adaptive top-p) are skipped.
  *   expert_out fp32 [T*k][H] (sorted order); y [T][H] fp32 or bf16 (RNE). */
 moe_status moe_combine(const moe_config* cfg, int32_t T, const float* expert_out,
                        const int32_t* inv_perm, const float* topk_w,

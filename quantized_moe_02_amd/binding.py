@@ -40,7 +40,7 @@ class MoeConfig(ctypes.Structure):
                 ("topk_group", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("n_shared_experts", ctypes.c_int32), ("shared_inter", ctypes.c_int32),
                 ("routed_scaling_factor", ctypes.c_float), ("wfmt", ctypes.c_int32),
-                ("options", ctypes.c_uint32)]
+                ("options", ctypes.c_uint32), ("expert_top_p", ctypes.c_float)]
 
 
 class MoeQProj(ctypes.Structure):
@@ -118,7 +118,8 @@ def make_config(geom: dict, wfmt: str, options: int = 0) -> MoeConfig:
     return MoeConfig(geom["hidden"], geom["moe_inter"], geom["n_routed_experts"],
                      geom["n_group"], geom["topk_group"], geom["top_k"],
                      geom["n_shared_experts"], geom.get("shared_inter", 0),
-                     float(geom["routed_scaling_factor"]), WFMT.get(wfmt, wfmt), options)
+                     float(geom["routed_scaling_factor"]), WFMT.get(wfmt, wfmt), options,
+                     float(geom.get("expert_top_p", 0.0)))
 
 
 def qexperts(gate, up, down) -> MoeQExperts:

@@ -387,13 +387,17 @@ __global__ void __launch_bounds__(256) dec_select_permute_kernel(DecodeArgs a) {
     // ascending-id order select_token ranks them in, and every record follows
     // from (id, weight, rank) in the picking lanes.
     if (wv != 0) return;
-    int id, rank;
+    int id, rank, n_kept;
     float w;
-    select_token<true>(a.logits, a.bias, a.E, a.G, a.TG, K, a.rsf, sc[0], id, w, rank);
+    select_token<true>(a.logits, a.bias, a.E, a.G, a.TG, K, a.rsf, a.top_p, sc[0], id, w, rank,
+                       n_kept);
     if (lane < K) {
       a.ids[rank] = id;
       a.tw[rank] = w;
+      // picks the adaptive top-p dropped (ranks from n_kept on) have no h row
       a.sorted_et[rank] = id;
+    }
+    if (lane < K && rank < n_kept) {
       DecSlot sl;
       sl.e = id;
       sl.p0 = rank;
@@ -406,14 +410,14 @@ __global__ void __launch_bounds__(256) dec_select_permute_kernel(DecodeArgs a) {
       }
       a.slots[rank] = sl;
     }
-    if (lane == 0) a.n_active[0] = K;
+    if (lane == 0) a.n_active[0] = n_kept;
     return;
   }
   if (wv < a.T) {
-    int id, rank;
+    int id, rank, n_kept;
     float w;
-    select_token<true>(a.logits + (size_t)wv * a.E, a.bias, a.E, a.G, a.TG, K, a.rsf, sc[wv], id, w,
-                 rank);
+    select_token<true>(a.logits + (size_t)wv * a.E, a.bias, a.E, a.G, a.TG, K, a.rsf, a.top_p,
+                       sc[wv], id, w, rank, n_kept);
     if (lane < K) {
       a.ids[wv * K + rank] = id;
       a.tw[wv * K + rank] = w;
@@ -428,8 +432,11 @@ __global__ void __launch_bounds__(256) dec_select_permute_kernel(DecodeArgs a) {
   // one, are found with one ballot per id bit, from the top bit down: `eq`
   // keeps the lanes that agree with this one on the bits so far, and a lane
   // that agrees so far but has 0 where this one has 1 is smaller.
-  const bool have = lane < P;
-  const int e = have ? pid[lane] : 0;
+  // picks the adaptive top-p dropped (id -1) take no slot; sorted picks run
+  // to the number of kept ones, and K3's blocks past them exit
+  const int pe = lane < P ? pid[lane] : -1;
+  const bool have = pe >= 0;
+  const int e = have ? pe : 0;
   int nbits = 0;
   while ((1 << nbits) < a.E) ++nbits;
   uint64_t eq = __ballot(have), lt = 0;
@@ -444,6 +451,7 @@ __global__ void __launch_bounds__(256) dec_select_permute_kernel(DecodeArgs a) {
   const bool first = have && (eq & below) == 0;
   const uint64_t firsts = __ballot(first);
   if (have) a.sorted_et[pos] = e | ((lane / K) << 16);
+  if (lane < P && lane >= __popcll(__ballot(have))) a.sorted_et[lane] = -1;
   if (first) {
     // the expert's record: its picks (the lanes in eq) in pick order, at most
     // one per token, so at most four
@@ -476,6 +484,7 @@ template <int FMT, int GPL>
 __global__ void __launch_bounds__(256) dec_gateup_kernel(DecodeArgs a) {
   const int p = (int)blockIdx.y;
   const int et = __builtin_amdgcn_readfirstlane(a.sorted_et[p]);
+  if (et < 0) return;   // a pick the adaptive top-p dropped
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const ExpertSet& R = a.routed;
   const int pair0 = blockIdx.x * kPairsPerBlock + wv * kPairsPerWave;
@@ -709,10 +718,12 @@ __device__ __forceinline__ void store_y(const DecodeArgs& a, int t, int row, flo
 template <int FMT, bool FUSED, int NT, class BeforeH>
 __device__ __forceinline__ void down_t1_rows(const DecodeArgs& a, uint4* hl, int gw, int nw,
                                              BeforeH before_h, const int* sel_e = nullptr,
-                                             const float* sel_w = nullptr) {
+                                             const float* sel_w = nullptr, int sel_n = 0) {
   const int lane = threadIdx.x & 63;
   const int H = a.H;
-  const int nr = a.K;                       // one token: k distinct experts
+  // one token: its distinct selected experts (k, or fewer after the adaptive
+  // top-p)
+  const int nr = FUSED ? sel_n : __builtin_amdgcn_readfirstlane(*a.n_active);
   const bool shared = a.has_shared;
   const int ns = nr + (shared ? 1 : 0);
   const int inter = a.routed.inter;         // routed and shared inter are equal here
@@ -752,17 +763,20 @@ __device__ __forceinline__ void down_t1_rows(const DecodeArgs& a, uint4* hl, int
   // h rows 0..k (the shared expert's row follows the k routed ones); FUSED:
   // device-scope loads, as the rows were written in this launch
   uint4 hv[kHPerThread];
-  const rsrc_t hr = make_rsrc(a.h_routed, (uint32_t)(ns * a.ldh * 2));
+  // the shared expert's h row is row k (its place after all k picks), also
+  // when the adaptive top-p kept fewer: slot s < nr reads row s, slot nr row k
+  const rsrc_t hr = make_rsrc(a.h_routed, (uint32_t)((a.K + 1) * a.ldh * 2));
   auto load_h = [&] {
 #pragma unroll
     for (int j = 0; j < kHPerThread; ++j) {
       const int i = threadIdx.x + NT * j;
       const int sl = i / hper, rem = i - sl * hper;
-      const uint32_t off = (uint32_t)(sl * a.ldh + rem * 8) * 2u;
+      const int hrow = sl < nr ? sl : a.K;
+      const uint32_t off = (uint32_t)(hrow * a.ldh + rem * 8) * 2u;
       if constexpr (FUSED)
         hv[j] = i < ns * hper ? bload16_device(hr, off, 0) : make_uint4(0, 0, 0, 0);
       else
-        hv[j] = i < ns * hper ? *reinterpret_cast<const uint4*>(a.h_routed + (size_t)sl * a.ldh + rem * 8)
+        hv[j] = i < ns * hper ? *reinterpret_cast<const uint4*>(a.h_routed + (size_t)hrow * a.ldh + rem * 8)
                               : make_uint4(0, 0, 0, 0);
     }
   };
@@ -945,6 +959,7 @@ __global__ void __launch_bounds__(64 * kFusedWaves, kFusedBlocksPerCU) dec_fused
   __shared__ SelectScratch sc;
   __shared__ int sel_e[kD1MaxRouted];
   __shared__ float sel_w[kD1MaxRouted];
+  __shared__ int sel_n;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int gw = blockIdx.x * kFusedWaves + wv, nw = gridDim.x * kFusedWaves;
@@ -952,9 +967,11 @@ __global__ void __launch_bounds__(64 * kFusedWaves, kFusedBlocksPerCU) dec_fused
     // every workgroup selects the token's experts itself (the same result
     // everywhere), so no workgroup waits for another to publish them;
     // workgroup 0 writes the layer's ids and weights
-    int id, rank;
+    int id, rank, n_kept;
     float w;
-    select_token<true>(a.logits, a.bias, a.E, a.G, a.TG, a.K, a.rsf, sc, id, w, rank);
+    select_token<true>(a.logits, a.bias, a.E, a.G, a.TG, a.K, a.rsf, a.top_p, sc, id, w, rank,
+                       n_kept);
+    if (lane == 0) sel_n = n_kept;
     if (lane < a.K) {
       sel_e[rank] = id;
       sel_w[rank] = w;
@@ -978,7 +995,7 @@ __global__ void __launch_bounds__(64 * kFusedWaves, kFusedBlocksPerCU) dec_fused
   // wave item it: pick p = it / per_pick (rank p of the k distinct experts),
   // row pairs [8 m, 8 m + 8) with m = it % per_pick
   const int per_pick = R.inter / kFusedPairs;
-  for (int it = gw; it < a.K * per_pick; it += nw) {
+  for (int it = gw; it < sel_n * per_pick; it += nw) {
     const int p = it / per_pick;
     const int e = sel_e[p];
     const float gg = (FMT == MOE_WFMT_NVFP4) ? R.gate.g[e] : 1.0f;
@@ -989,7 +1006,7 @@ __global__ void __launch_bounds__(64 * kFusedWaves, kFusedBlocksPerCU) dec_fused
   }
   grid_arrive(a.bar, gridDim.x);
   down_t1_rows<FMT, true, 64 * kFusedWaves>(a, hl, gw, nw, [&] { return grid_wait(a.bar, a.barrier_spins); },
-                                            sel_e, sel_w);
+                                            sel_e, sel_w, sel_n);
 }
 
 // ---------------------------------------------------------------------------

@@ -260,9 +260,11 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
   if (n >= H) return;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int i = 0; i < K; ++i) {
+    // inv_perm -1: a pick the adaptive top-p dropped (weight 0, no row)
     const int p = a.inv_perm[(size_t)t * K + i];
     const float w = a.tw[(size_t)t * K + i];
-    const float4 o = *reinterpret_cast<const float4*>(a.expert_out + (size_t)p * H + n);
+    float4 o = *reinterpret_cast<const float4*>(a.expert_out + (size_t)(p < 0 ? 0 : p) * H + n);
+    if (p < 0) o = make_float4(0.f, 0.f, 0.f, 0.f);
     acc.x = fmaf(w, o.x, acc.x);
     acc.y = fmaf(w, o.y, acc.y);
     acc.z = fmaf(w, o.z, acc.z);

@@ -29,7 +29,10 @@ __global__ void __launch_bounds__(256) perm_hist_kernel(const int32_t* __restric
   for (int e = threadIdx.x; e < kMaxE; e += 256) h[e] = 0;
   __syncthreads();
   const int p0 = b * chunk * K, p1 = min(T, (b + 1) * chunk) * K;
-  for (int p = p0 + threadIdx.x; p < p1; p += 256) atomicAdd(&h[ids[p]], 1);
+  for (int p = p0 + threadIdx.x; p < p1; p += 256) {
+    const int e = ids[p];
+    if (e >= 0) atomicAdd(&h[e], 1);   // -1: a pick the adaptive top-p dropped
+  }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += 256) hist[(size_t)b * E + e] = h[e];
 }
@@ -143,8 +146,11 @@ __global__ void __launch_bounds__(64) perm_scatter_kernel(const int32_t* __restr
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (q0 + 64 * j >= p1) break;
-      const int p = q0 + 64 * j + lane, e = v[j];
-      const bool valid = p < p1;
+      const int p = q0 + 64 * j + lane;
+      const bool in = p < p1;
+      const bool valid = in && v[j] >= 0;   // -1: dropped pick, no slot
+      const int e = valid ? v[j] : 0;
+      if (in && !valid) inv_perm[p] = -1;
       uint64_t m = __builtin_amdgcn_ballot_w64(valid);
       for (int bit = 0; bit < nbits; ++bit) {
         const bool set = (e >> bit) & 1;
@@ -182,7 +188,10 @@ __global__ void __launch_bounds__(64 * kSmallWaves) perm_small_kernel(
   const int p0 = min(P, w * chunk), p1 = min(P, p0 + chunk);
   for (int i = threadIdx.x; i < kSmallWaves * kMaxE; i += 64 * kSmallWaves) (&cnt[0][0])[i] = 0;
   __syncthreads();
-  for (int p = p0 + lane; p < p1; p += 64) atomicAdd(&cnt[w][ids[p]], 1);
+  for (int p = p0 + lane; p < p1; p += 64) {
+    const int e = ids[p];
+    if (e >= 0) atomicAdd(&cnt[w][e], 1);   // -1: a pick the adaptive top-p dropped
+  }
   __syncthreads();
   // per expert: exclusive prefix over the chunks, and the total
   if (threadIdx.x < kMaxE) {
@@ -234,8 +243,10 @@ __global__ void __launch_bounds__(64 * kSmallWaves) perm_small_kernel(
   const uint64_t below = (1ull << lane) - 1;
   for (int q = p0; q < p1; q += 64) {
     const int p = q + lane;
-    const bool valid = p < p1;
-    const int e = valid ? ids[p] : 0;
+    const int ev = p < p1 ? ids[p] : 0;
+    const bool valid = p < p1 && ev >= 0;   // -1: dropped pick, no slot
+    const int e = valid ? ev : 0;
+    if (p < p1 && !valid) inv_perm[p] = -1;
     uint64_t m = __builtin_amdgcn_ballot_w64(valid);
     for (int bit = 0; bit < nbits; ++bit) {
       const bool set = (e >> bit) & 1;

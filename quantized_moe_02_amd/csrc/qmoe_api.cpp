@@ -33,6 +33,7 @@ moe_status check_cfg(const moe_config* c) {
     return MOE_ERR_INVALID_ARG;
   if (c->wfmt != MOE_WFMT_INT4_G32_F16 && c->wfmt != MOE_WFMT_NVFP4) return MOE_ERR_INVALID_ARG;
   if (c->options & ~(MOE_OPT_NO_GRID_WAIT | MOE_OPT_GRID_WAIT_NONE)) return MOE_ERR_INVALID_ARG;
+  if (!(c->expert_top_p >= 0.0f && c->expert_top_p <= 1.0f)) return MOE_ERR_INVALID_ARG;   // NaN too
   // kernel limits
   if (c->n_routed_experts > 256 || c->n_group > 64 || c->top_k > 16) return MOE_ERR_UNSUPPORTED;
   if (c->hidden > 65536 || c->moe_inter > 65536) return MOE_ERR_UNSUPPORTED;
@@ -251,7 +252,7 @@ moe_status moe_route(const moe_config* cfg, int32_t T, const uint16_t* x, const 
   const Workspace w = carve_workspace(*cfg, T, ws);
   RouteArgs a{x, router_w, bias, topk_ids, topk_w, w.logits, T, cfg->hidden,
               cfg->n_routed_experts, cfg->n_group, cfg->topk_group, cfg->top_k,
-              cfg->routed_scaling_factor, nullptr};
+              cfg->routed_scaling_factor, nullptr, cfg->expert_top_p};
   return hip_status(launch_route(a, stream));
 }
 
@@ -390,6 +391,7 @@ moe_status layer_impl(const moe_config* cfg, int32_t T, const uint16_t* x, const
     d.TG = cfg->topk_group;
     d.K = cfg->top_k;
     d.rsf = cfg->routed_scaling_factor;
+    d.top_p = cfg->expert_top_p;
     d.router_w = router_w;
     d.bias = bias;
     d.logits = w.logits;
@@ -418,7 +420,8 @@ moe_status layer_impl(const moe_config* cfg, int32_t T, const uint16_t* x, const
     return hip_status(launch_decode(d, stream, tr));
   }
   RouteArgs ra{x, router_w, bias, ids, tw, w.logits, T, cfg->hidden, cfg->n_routed_experts,
-               cfg->n_group, cfg->topk_group, cfg->top_k, cfg->routed_scaling_factor, w.flags};
+               cfg->n_group, cfg->topk_group, cfg->top_k, cfg->routed_scaling_factor, w.flags,
+               cfg->expert_top_p};
   if ((e = launch_route(ra, stream, tr)) != hipSuccess) return MOE_ERR_HIP;
   PermuteArgs pa{ids, w.offsets, w.sorted_token, w.inv_perm, w.active, w.n_active,
                  T, cfg->top_k, cfg->n_routed_experts, w.phist};

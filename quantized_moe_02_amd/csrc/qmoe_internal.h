@@ -98,6 +98,7 @@ struct RouteArgs {
   int T, H, E, G, TG, K;
   float rsf;
   uint32_t* flags;    // nullable: moe_layer's flags word, cleared by the selection kernel
+  float top_p;        // adaptive expert top-p (0: keep all top_k)
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t s, Tracer* tr = nullptr);
 // Number of hidden-dimension slices route_logits uses (its logits buffer
@@ -168,6 +169,7 @@ struct DecodeArgs {
   const uint16_t* x;
   int T, H, E, G, TG, K;
   float rsf;
+  float top_p;            // adaptive expert top-p (0: keep all top_k)
   const float* router_w;
   const float* bias;
   double* logits;         // [T][E] router scores (sigmoid of the float64 logits)

@@ -111,7 +111,8 @@ __global__ void __launch_bounds__(256) route_select_kernel(const double* __restr
                                                            int32_t* __restrict__ ids,
                                                            float* __restrict__ tw, int T, int E,
                                                            int G, int TG, int K, float rsf,
-                                                           int nsplit, uint32_t* __restrict__ flags) {
+                                                           int nsplit, uint32_t* __restrict__ flags,
+                                                           float top_p) {
   __shared__ SelectScratch sc[4];
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
@@ -119,10 +120,10 @@ __global__ void __launch_bounds__(256) route_select_kernel(const double* __restr
   // moe_layer's flags word: nothing on this path raises one
   if (flags && blockIdx.x == 0 && threadIdx.x == 0) flags[0] = 0u;
   if (t >= T) return;
-  int id, rank;
+  int id, rank, n_kept;
   float w;
-  select_token(logits + (size_t)t * E, bias, E, G, TG, K, rsf, sc[wv], id, w, rank, nsplit,
-               (size_t)T * E);
+  select_token(logits + (size_t)t * E, bias, E, G, TG, K, rsf, top_p, sc[wv], id, w, rank, n_kept,
+               nsplit, (size_t)T * E);
   if (lane < K) {
     ids[(size_t)t * K + rank] = id;
     tw[(size_t)t * K + rank] = w;
@@ -153,7 +154,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s, Tracer* tr) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (tr && (e = tr->mark("route_logits")) != hipSuccess) return e;
   hipLaunchKernelGGL(route_select_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, a.logits, a.bias,
-                     a.ids, a.tw, a.T, a.E, a.G, a.TG, a.K, a.rsf, S_used, a.flags);
+                     a.ids, a.tw, a.T, a.E, a.G, a.TG, a.K, a.rsf, S_used, a.flags, a.top_p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (tr && (e = tr->mark("route_select")) != hipSuccess) return e;
   return hipSuccess;

@@ -116,7 +116,14 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 }
 
 // Lanes < K return their chosen expert in `id`, its weight in `w` and its
-// position in ascending id order in `rank`.  `logits` points at the token's E
+// position in ascending id order in `rank`; every lane returns in `n_kept`
+// how many of the K stay after the adaptive expert top-p (page "Show HN:
+// Menjalankan GLM 5.2 ...", section "Mengunduh model dan menjalankannya",
+// --topp): with 0 < top_p < 1 only the shortest prefix of the chosen experts,
+// ordered by share s / sum(s) (descending; equal shares: lower id first),
+// whose shares reach top_p stays -- at least one; the weights are
+// renormalised over the kept experts, and a dropped expert returns id -1,
+// weight 0 and a rank >= n_kept.  Otherwise n_kept = K.  `logits` points at the token's E
 // float64 logits, given as `nsplit` partial sums `split_stride` apart (added
 // in order); SCORES: at the E sigmoid scores instead (nsplit 1), computed
 // where the logits were, off this wave's critical path.  Must be called by
@@ -124,8 +131,9 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 template <bool SCORES = false>
 __device__ __forceinline__ void select_token(const double* __restrict__ logits,
                                              const float* __restrict__ bias, int E, int G, int TG,
-                                             int K, float rsf, SelectScratch& sc, int& id, float& w,
-                                             int& rank, int nsplit = 1, size_t split_stride = 0) {
+                                             int K, float rsf, float top_p, SelectScratch& sc,
+                                             int& id, float& w, int& rank, int& n_kept,
+                                             int nsplit = 1, size_t split_stride = 0) {
   const int lane = threadIdx.x & 63;
   const int per = E / G;
   const int e0 = 4 * lane;
@@ -301,6 +309,42 @@ __device__ __forceinline__ void select_token(const double* __restrict__ logits,
   }
   const double total = wave_sum(lane < K ? my_s : 0.0);
   id = my_id;
+  n_kept = K;
+  if (top_p > 0.0f && top_p < 1.0f) {
+    // share order: picks with a larger score, or an equal one and a lower id,
+    // come first; the running sum of shares in that order, one pick at a
+    // time, decides how many stay
+    int pos = 0;
+    for (int j = 0; j < K; ++j) {
+      const double o = readlane_d(my_s, j);
+      const int oid = __builtin_amdgcn_readlane(my_id, j);
+      pos += (j != lane && (o > my_s || (o == my_s && oid < my_id))) ? 1 : 0;
+    }
+    const double share = my_s / total;
+    double csum = 0.0;
+    int keep = K;
+    for (int q = 0; q < K; ++q) {
+      const uint64_t at = __ballot(lane < K && pos == q);
+      csum += readlane_d(share, at ? (int)__builtin_ctzll(at) : 0);
+      if (keep == K && csum >= (double)top_p) keep = q + 1;
+    }
+    const bool kept = lane < K && pos < keep;
+    const double total_kept = wave_sum(kept ? my_s : 0.0);
+    // ascending id order among the kept picks; the dropped ones after them
+    // (in lane order)
+    const uint64_t kept_mask = __ballot(kept);
+    int nr = 0;
+    for (int j = 0; j < K; ++j) {
+      const int oid = __builtin_amdgcn_readlane(my_id, j);
+      const bool ok = (kept_mask >> j) & 1ull;
+      nr += kept ? ((ok && oid < my_id) ? 1 : 0) : ((!ok && j < lane) ? 1 : 0);
+    }
+    rank = kept ? nr : keep + nr;
+    id = kept ? my_id : -1;
+    w = kept ? (float)(my_s / total_kept * (double)rsf) : 0.0f;
+    n_kept = keep;
+    return;
+  }
   w = (float)(my_s / total * (double)rsf);
 }
 

@@ -51,10 +51,20 @@ def check_routing(L, ids_gpu, tw_gpu, x_np=None):
     exact = info["margin"] >= TAU
     mism = np.nonzero(exact & np.any(ids_g != ids_ref, axis=1))[0]
     assert len(mism) == 0, f"routing differs at tokens {mism[:8]}: gpu {ids_g[mism[:2]]} ref {ids_ref[mism[:2]]}"
-    for t in np.nonzero(~exact)[0]:
-        assert oracle.valid_under_perturbation(ids_g[t], info["sb"][t], cfg, TAU), t
+    if 0.0 < cfg.top_p < 1.0:
+        plain = oracle.RouterConfig(cfg.n_experts, cfg.n_group, cfg.topk_group, cfg.top_k,
+                                    cfg.routed_scaling_factor)
+        chosen, _, _ = oracle.route(X, Wr, b, plain)
+        for t in np.nonzero(~exact)[0]:
+            assert oracle.valid_top_p(ids_g[t], info["s"][t], chosen[t], cfg.top_p, TAU), t
+    else:
+        for t in np.nonzero(~exact)[0]:
+            assert oracle.valid_under_perturbation(ids_g[t], info["sb"][t], cfg, TAU), t
     w_ref = oracle.route_weights(info["s"], ids_g, cfg.routed_scaling_factor)
-    rel = np.abs(tw_gpu.cpu().numpy() - w_ref) / np.abs(w_ref)
+    tw = tw_gpu.cpu().numpy()
+    kept = ids_g >= 0
+    assert np.all(tw[~kept] == 0.0)
+    rel = np.abs(tw[kept] - w_ref[kept]) / np.abs(w_ref[kept])
     assert rel.max() <= W_TOL, rel.max()
     return ids_g, int((~exact).sum())
 

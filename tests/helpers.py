@@ -13,8 +13,10 @@ def np_u16(t: torch.Tensor) -> np.ndarray:
 
 
 def router_cfg(geom: dict) -> oracle.RouterConfig:
+    # the library decides on the float32 value of the top-p parameter
+    p = float(np.float32(geom.get("expert_top_p", 0.0)))
     return oracle.RouterConfig(geom["n_routed_experts"], geom["n_group"], geom["topk_group"],
-                               geom["top_k"], geom["routed_scaling_factor"])
+                               geom["top_k"], geom["routed_scaling_factor"], top_p=p)
 
 
 def _proj_np(p, wfmt):

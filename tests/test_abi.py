@@ -62,6 +62,10 @@ def _size(cfg, T):
     (dict(routed_scaling_factor=float("nan")), q.MOE_ERR_INVALID_ARG),
     (dict(wfmt=7), q.MOE_ERR_INVALID_ARG),
     (dict(options=4), q.MOE_ERR_INVALID_ARG),              # unknown option bit
+    (dict(expert_top_p=-0.1), q.MOE_ERR_INVALID_ARG),
+    (dict(expert_top_p=1.5), q.MOE_ERR_INVALID_ARG),
+    (dict(expert_top_p=float("nan")), q.MOE_ERR_INVALID_ARG),
+    (dict(expert_top_p=0.7), q.MOE_OK),
     (dict(options=3), q.MOE_OK),
     (dict(n_routed_experts=512, n_group=8, topk_group=4), q.MOE_ERR_UNSUPPORTED),
     (dict(n_routed_experts=128, n_group=128, topk_group=4), q.MOE_ERR_UNSUPPORTED),

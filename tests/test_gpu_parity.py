@@ -90,7 +90,7 @@ def entry_point_chain(L, T=None, x=None, pool=False):
     torch.cuda.synchronize()
     r_off, r_st, r_inv, r_act = oracle.permute(ids_g, E)
     assert np.array_equal(offs.cpu().numpy(), r_off)
-    assert np.array_equal(st.cpu().numpy(), r_st)
+    assert np.array_equal(st.cpu().numpy()[: len(r_st)], r_st)
     assert np.array_equal(inv.cpu().numpy(), r_inv)
     assert int(na.item()) == len(r_act)
     assert np.array_equal(act.cpu().numpy()[: len(r_act)], r_act)
@@ -103,10 +103,11 @@ def entry_point_chain(L, T=None, x=None, pool=False):
     jobs = [(routed, int(e), X[r_st[r_off[e]:r_off[e + 1]]]) for e in r_act]
     jobs.append((shared, 0, X))
     refs = FFNCache()(jobs) if pool else [oracle.expert_ffn(*j) for j in jobs]
-    ref = np.zeros((P, H))
+    Pk = int(r_off[-1])   # kept picks (all P unless the adaptive top-p dropped some)
+    ref = np.zeros((Pk, H))
     for e, F in zip(r_act, refs):
         ref[r_off[e]:r_off[e + 1]] = F
-    err = row_rel_err(out.cpu().numpy(), ref)
+    err = row_rel_err(out.cpu().numpy()[:Pk], ref)
     assert err.max() <= TOL, (err.max(), int(err.argmax()))
 
     outs = torch.empty(T, H, dtype=torch.float32, **dev)
@@ -121,7 +122,8 @@ def entry_point_chain(L, T=None, x=None, pool=False):
     torch.cuda.synchronize()
     o64, s64 = out.double().cpu().numpy(), outs.double().cpu().numpy()
     w64 = tw.double().cpu().numpy()
-    yref = s64 + np.einsum("tk,tkh->th", w64, o64[r_inv.reshape(T, k)])
+    inv2 = r_inv.reshape(T, k)
+    yref = s64 + np.einsum("tk,tkh->th", np.where(inv2 >= 0, w64, 0.0), o64[np.maximum(inv2, 0)])
     assert row_rel_err(y.cpu().numpy(), yref).max() <= 1e-6
     assert torch.equal(y.to(torch.bfloat16), y16)
     return err.max()
@@ -512,3 +514,62 @@ def test_exact_router_ties_full_decode():
     finally:
         L.router_w.copy_(rw)
         L.bias.copy_(b0)
+
+
+# ---------------------------------------------------------------------------
+# adaptive expert top-p
+# ---------------------------------------------------------------------------
+
+TOP_P = {
+    "T1": (1, "int4", 0),
+    "T1_split": (1, "int4", q.MOE_OPT_NO_GRID_WAIT),
+    "T3": (3, "int4", 0),
+    "T4_nvfp4": (4, "nvfp4", 0),
+    "T37": (37, "int4", 0),
+    "T640": (640, "int4", 0),
+    "T40_nvfp4": (40, "nvfp4", 0),
+}
+
+
+@pytest.mark.parametrize("p", [0.35, 0.7])
+@pytest.mark.parametrize("case", sorted(TOP_P))
+def test_top_p_paths(case, p):
+    """Every kernel path with the adaptive top-p: ids exact (kept ids
+    ascending, then -1), weights renormalised over the kept experts, outputs
+    against the oracle; some tokens keep fewer than top_k experts."""
+    T, wfmt, options = TOP_P[case]
+    geom = synth.small_geom(expert_top_p=p, top_k=6, topk_group=4)
+    L = synth.make_custom(geom, T, wfmt, "normal0.1", seed=700 + T, device="cuda")
+    y, ids, tw = run_layer(L, options=options)
+    ids_g, _ = check_routing(L, ids, tw)
+    check_outputs(L, y, ids_g)
+    n_kept = (ids_g >= 0).sum(1)
+    assert n_kept.min() >= 1 and (T < 8 or n_kept.min() < geom["top_k"])
+
+
+def test_top_p_fused_matches_split_and_entry_points():
+    geom = synth.small_geom(expert_top_p=0.6, top_k=6, topk_group=4)
+    L = synth.make_custom(geom, 1, "int4", "normal0.1", seed=720, device="cuda")
+    a = run_layer(L)
+    b = run_layer(L, options=q.MOE_OPT_NO_GRID_WAIT)
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+    L8 = synth.make_custom(geom, 8, "int4", "normal0.1", seed=721, device="cuda")
+    entry_point_chain(L8)
+
+
+def test_top_p_full_size():
+    """The GLM-5.2 decode layer (one token, fused kernel) and the 64-token
+    verify batch with expert_top_p 0.7 (the pages' setting): every token."""
+    for name in ("decode", "verify64"):
+        L = layer(name)
+        L.geom["expert_top_p"] = 0.7
+        try:
+            y, ids, tw = run_layer(L)
+            ids_g, _ = check_routing(L, ids, tw)
+            _, _, _, _, routed, shared = oracle_inputs(L, lazy=True)
+            check_outputs(L, y, ids_g, ffn_map=FFNCache(), srcs=(routed, shared))
+            print(f"{name} top-p 0.7: experts kept per token {(ids_g >= 0).sum(1).mean():.2f} "
+                  f"of {L.geom['top_k']}", flush=True)
+        finally:
+            del L.geom["expert_top_p"]
