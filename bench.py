@@ -29,7 +29,8 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/s + weight-stream HBM GB/s (% peak); prefill MFMA util"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_F16_TFLOPS = 2500.0       # MI355X dense fp16/bf16 MFMA
-ALL_WORKLOADS = ["decode", "verify4", "verify64", "prefill4k", "prefill16k", "nvfp4_512"]
+ALL_WORKLOADS = ["decode", "verify4", "verify64", "prefill4k", "prefill16k", "nvfp4_512",
+                 "decode_topp", "verify64_topp"]
 HEADLINE = "decode"
 
 
@@ -210,43 +211,53 @@ class Bench:
                                self.q.MOE_OUT_F32, self.ids, self.tw, self.ws)
 
     def n_active(self):
-        return int(torch.unique(self.ids).numel())
+        # experts with at least one kept pick (-1: a pick the adaptive top-p dropped)
+        return int(torch.unique(self.ids[self.ids >= 0]).numel())
 
 
 def time_steps(B: Bench, steps, warmup, use_graph):
-    """Whole-step throughput.  Decode-sized steps replay a captured HIP graph of
-    one step per replica, so that Python launch overhead does not idle the GPU."""
+    """Whole-step throughput over exactly `steps` steps.  Decode-sized steps
+    replay captured HIP graphs -- one of a step per replica, replayed
+    steps // R times, and one of the remaining steps % R steps -- so that
+    Python launch overhead does not idle the GPU."""
     R = len(B.qsets)
     for i in range(warmup):
         B.step(i)
     torch.cuda.synchronize()
     if use_graph:
-        g = torch.cuda.CUDAGraph()
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            with torch.cuda.graph(g, stream=s):
-                for i in range(R):
-                    B.step(i)
-        torch.cuda.synchronize()
-        g.replay()
-        torch.cuda.synchronize()
-        reps = max(1, steps // R)
-        n = reps * R
+        def capture(n_steps):
+            g = torch.cuda.CUDAGraph()
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                with torch.cuda.graph(g, stream=s):
+                    for i in range(n_steps):
+                        B.step(i)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            return g
+        g = capture(R)
+        reps, rem = divmod(steps, R)
+        g_rem = capture(rem) if rem else None
         t0 = time.perf_counter()
         for _ in range(reps):
             g.replay()
+        if g_rem is not None:
+            g_rem.replay()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        # per-step spread, from events around each replay (after the timed run)
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        # per-step spread, from events around each replay of R steps (after
+        # the timed run)
+        nrep = max(1, reps)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(nrep + 1)]
         ev[0].record()
-        for j in range(reps):
+        for j in range(nrep):
             g.replay()
             ev[j + 1].record()
         torch.cuda.synchronize()
-        per = [ev[j].elapsed_time(ev[j + 1]) * 1e3 / R for j in range(reps)]
-        return n, (t1 - t0), per
+        per = [ev[j].elapsed_time(ev[j + 1]) * 1e3 / R for j in range(nrep)]
+        return steps, (t1 - t0), per
     t0 = time.perf_counter()
     for i in range(steps):
         B.step(i)
@@ -369,16 +380,31 @@ def cpu_baseline(name, budget_s=10.0, max_calls=16):
 
 
 def copy_calibration():
-    """A plain streaming kernel of known traffic (read 1 GiB, write 1 GiB) whose
-    FETCH_SIZE / WRITE_SIZE readings scale the layer kernels' counters."""
-    n = 1 << 28
-    src = torch.randn(n, device="cuda")
-    dst = torch.empty_like(src)
+    """Kernels of known traffic whose FETCH_SIZE / WRITE_SIZE readings scale the
+    layer kernels' counters (libqmoe_calib.so): whole-line reads of 1 GiB,
+    GEMM-shaped half-line reads (16 rows x 64 bytes per instruction) of
+    349525 rows x 3072 bytes, whole-line writes of 1 GiB; five launches each."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "quantized_moe_02_amd", "libqmoe_calib.so"))
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    lib.qmoe_calib_read_lines.argtypes = [vp, sz, vp, vp]
+    lib.qmoe_calib_read_halflines.argtypes = [vp, sz, ctypes.c_uint32, vp, vp]
+    lib.qmoe_calib_write_lines.argtypes = [vp, sz, vp]
+    n = 1 << 30
+    buf = torch.empty(n, dtype=torch.uint8, device="cuda")
+    buf.random_(0, 256)
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    rows, row_bytes = 349525, 3072
     for _ in range(5):
-        torch.neg(src, out=dst)
+        assert lib.qmoe_calib_read_lines(buf.data_ptr(), n, sink.data_ptr(), st) == 0
+    for _ in range(5):
+        assert lib.qmoe_calib_read_halflines(buf.data_ptr(), rows, row_bytes, sink.data_ptr(), st) == 0
+    for _ in range(5):
+        assert lib.qmoe_calib_write_lines(buf.data_ptr(), n, st) == 0
     torch.cuda.synchronize()
-    print(json.dumps(dict(copy_kernel="torch.neg fp32", bytes_read=n * 4, bytes_written=n * 4,
-                          launches=5)))
+    print(json.dumps(dict(read_lines_kernel=n, read_halflines_kernel=rows * row_bytes,
+                          write_lines_kernel=n, launches=5)))
 
 
 def main():

@@ -49,6 +49,13 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, OUT)
+    # counter-calibration kernels, a library of their own (benchmark only)
+    cal = os.path.join(PKG, "libqmoe_calib.so")
+    cmd = [HIPCC, *COMMON, "-shared", os.path.join(CSRC, "calib.hip"), "-o", cal + ".tmp"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for calib.hip:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(cal + ".tmp", cal)
     if verbose:
         print(f"built {OUT}")
     return OUT

@@ -4,6 +4,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstring>
 
 #include "qmoe_internal.h"
 
@@ -217,7 +218,12 @@ moe_status moe_workspace_size(const moe_config* cfg, int32_t T, size_t* bytes) {
 }
 
 const char* moe_status_string(moe_status s) {
-  switch (s) {
+  // callers may pass any int (the header's other codes, or none of them):
+  // read it as an int, since a value outside the enumerators is not a valid
+  // moe_status in C++
+  int v;
+  std::memcpy(&v, &s, sizeof v);
+  switch (v) {
     case MOE_OK: return "MOE_OK";
     case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
     case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";

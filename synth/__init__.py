@@ -46,6 +46,8 @@ BASE_SEED = 20261203
 _GLM = dict(hidden=6144, moe_inter=2048, n_routed_experts=256, n_group=8,
             topk_group=4, top_k=8, n_shared_experts=1, shared_inter=2048,
             routed_scaling_factor=2.5)
+# the same layer with the adaptive expert top-p at the pages' setting (0.7)
+_GLM_TOPP = dict(_GLM, expert_top_p=0.7)
 _TINY = dict(hidden=256, moe_inter=128, n_routed_experts=16, n_group=4,
              topk_group=2, top_k=4, n_shared_experts=1, shared_inter=128,
              routed_scaling_factor=2.5)
@@ -59,6 +61,8 @@ WORKLOADS: Dict[str, dict] = {
     "prefill4k":  dict(index=3, geom=_GLM,  tokens=4096,  wfmt="int4",  bias="zero"),
     "prefill16k": dict(index=3, geom=_GLM,  tokens=16384, wfmt="int4",  bias="zero"),
     "nvfp4_512":  dict(index=4, geom=_GLM,  tokens=512,   wfmt="nvfp4", bias="zipf"),
+    "decode_topp":   dict(index=1, geom=_GLM_TOPP, tokens=1,  wfmt="int4", bias="zero"),
+    "verify64_topp": dict(index=2, geom=_GLM_TOPP, tokens=64, wfmt="int4", bias="hot16"),
 }
 
 WEIGHT_STD = 0.02       # expert, shared-expert and router weights ~ N(0, 0.02)
