@@ -43,7 +43,11 @@
  *   q     uint8 [E][N][K/2]: per row K/8 little-endian 32-bit words; word j
  *         holds inputs 8j..8j+7, input 8j+2i (i = 0..3) in bits [4i, 4i+4) and
  *         input 8j+2i+1 in bits [16+4i, 16+4i+4).  A code u in 0..15 means
- *         q = u - 8.
+ *         q = u - 8.  This is not the natural order (input 2j in the low
+ *         nibble of byte j): such data must be repacked once, a fixed
+ *         permutation of the eight nibbles of each word (the Python helper
+ *         synth.repack_int4_natural does it); unrepacked, it decodes to
+ *         wrong values without any error.
  *   scale fp16 [E][N][K/32]; weight = (u - 8) * scale.
  *   gscale must be NULL.
  * MOE_WFMT_NVFP4  E2M1 elements, one FP8 E4M3 scale per 16 inputs, one fp32
@@ -54,7 +58,10 @@
  *   gscale float32 [E]; weight = e2m1 * e4m3 * gscale[e].
  * Gate and up have N = inter, K = hidden; down has N = hidden, K = inter.
  *
- * Activations are bfloat16 [T][hidden], row-major.
+ * Activations are bfloat16 [T][hidden], row-major.  For T > 4 the grouped
+ * GEMM multiplies them as fp16: magnitudes of 65520 and above (beyond the
+ * fp16 range) become infinities there; T <= 4 reads the bf16 values
+ * directly.
  */
 #ifndef QMOE_H
 #define QMOE_H

@@ -118,6 +118,14 @@ def pack_int4_words(u: torch.Tensor) -> torch.Tensor:
     return out.reshape(*lead, K // 2)
 
 
+def repack_int4_natural(q: torch.Tensor) -> torch.Tensor:
+    """int4 codes packed in the natural order (byte j = input 2j in its low
+    nibble, input 2j+1 in its high nibble), uint8 [..., K/2] -> the library's
+    word order.  A layout change only (no arithmetic on the codes)."""
+    c = torch.stack([q & 15, q >> 4], dim=-1).reshape(*q.shape[:-1], q.shape[-1] * 2)
+    return pack_int4_words(c)
+
+
 def pack_nibbles_natural(c: torch.Tensor) -> torch.Tensor:
     """c: uint8 codes in [0, 15], shape [..., K] with K even.  Byte j = c[2j] |
     c[2j+1] << 4."""

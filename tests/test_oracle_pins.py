@@ -571,3 +571,13 @@ def test_valid_top_p():
     assert not oracle.valid_top_p(np.array([0, 1, 2, -1]), s, chosen, 0.6, 1e-9)
     assert not oracle.valid_top_p(np.array([0, 2, -1, -1]), s, chosen, 0.6, 1e-9)
     assert oracle.valid_top_p(np.array([0, 1, 3, -1]), s, chosen, 0.76, 1e-9)     # tie
+
+
+def test_repack_int4_natural():
+    """Natural-order bytes repacked to the word order decode, through the
+    oracle, to the codes they held."""
+    rng = np.random.default_rng(12)
+    codes = rng.integers(0, 16, size=(3, 64)).astype(np.uint8)
+    natural = torch.from_numpy((codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8))
+    q = synth.repack_int4_natural(natural).numpy()
+    assert np.array_equal(oracle.unpack_int4_codes(q), codes)
