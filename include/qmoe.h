@@ -20,16 +20,19 @@
  * Memory.  All array arguments are DEVICE pointers on the current HIP device,
  *   except `cfg`, the moe_qexperts structs, and the `bytes` output of
  *   moe_workspace_size, which are HOST pointers read or written during the
- *   call only.  The caller owns every buffer, including the workspace.  The
- *   library never allocates or frees memory; its only global state is a
- *   per-device record of how many workgroups of the single-token kernel fit
- *   on the device (computed once, read-only after) and the device buffer of
- *   moe_layer_noalloc.  Calls on different streams are independent as long
+ *   call only (the expert cache's host store and id lists are HOST memory
+ *   too, as stated there).  The caller owns every buffer, including the
+ *   workspace.  The library never allocates or frees device memory; host
+ *   memory only for a moe_expert_cache's bookkeeping.  Its only global state
+ *   is a per-device record of how many workgroups of the single-token kernel
+ *   fit on the device (computed once, read-only after) and the device buffer
+ *   of moe_layer_noalloc.  Calls on different streams are independent as long
  *   as their workspaces and outputs do not overlap.
  * Alignment.  Packed weight arrays (`q`), scale arrays and `x` must be 16-byte
  *   aligned; the workspace 256-byte aligned.  Otherwise MOE_ERR_INVALID_ARG.
- * Asynchrony.  Every call only enqueues kernels on `stream` and returns
- *   without synchronising.  A launch failure returns MOE_ERR_HIP; a fault
+ * Asynchrony.  Every call only enqueues work on `stream` and returns without
+ *   synchronising, except moe_layer_flags and moe_layer_cached, which wait as
+ *   they state.  A launch failure returns MOE_ERR_HIP; a fault
  *   inside a kernel surfaces at the caller's next synchronisation.
  * Validation.  All argument checks run before any HIP call, so an invalid call
  *   has no effect on the device and can be made without one.
@@ -295,6 +298,94 @@ moe_status moe_layer_noalloc(const moe_config* cfg, int32_t T, const uint16_t* x
                              const moe_qexperts* routed, const moe_qexperts* shared, void* y,
                              int32_t out_dtype, int32_t* topk_ids_out, float* topk_w_out,
                              hipStream_t stream);
+
+/* Expert streaming from host memory (page "Show HN: Menjalankan GLM 5.2 ...",
+ * section "Cara kerja eksekusi MoE berbasis streaming disk": the routed experts
+ * stay in a slow tier and come in through a least-recently-used cache per
+ * layer, with an optional pinned hot store; section "Fitur utama": readahead
+ * while an expert is multiplied, a router lookahead that prefetches).  The
+ * slow tier here is host RAM and the fast one HBM: for layers, or models,
+ * whose experts do not all fit on the device.
+ *
+ * A moe_expert_cache serves ONE layer on one device and owns no device memory:
+ *   host_store  the E routed experts in the formats above, HOST pointers; they
+ *               should be page-locked (hipHostMalloc) so that the copies are
+ *               asynchronous DMA (pageable memory works, copied synchronously);
+ *   slots       DEVICE arrays in the same layout for n_slots experts:
+ *               q [n_slots][N][K/2], scale [n_slots][N][...], gscale [n_slots].
+ * Both stay the caller's and must outlive the cache.  The cache itself is
+ * host bookkeeping plus two HIP events, created by its first call that makes
+ * HIP calls, on the device then current (later calls on another device:
+ * MOE_ERR_INVALID_ARG).  Not thread-safe: one thread at a time per cache.
+ *
+ * Slot policy.  A call needs the distinct experts its tokens picked (or the
+ * experts a prefetch lists); resident ones are hits.  The misses are placed
+ * in ascending expert order into the free slot of lowest index, else into the
+ * least recently used slot that is neither pinned nor needed by the same call
+ * (equal age: lowest slot).  Every slot a call or prefetch uses becomes the
+ * most recently used. */
+typedef struct moe_expert_cache moe_expert_cache;
+
+typedef struct {
+  uint64_t calls;        /* moe_layer_cached calls that ran their experts */
+  uint64_t hits;         /* experts those calls needed and found resident */
+  uint64_t misses;       /* experts those calls loaded */
+  uint64_t prefetched;   /* experts loaded by moe_cache_prefetch and moe_cache_pin */
+  uint64_t evictions;    /* loads that replaced a resident expert */
+  uint64_t bytes_loaded; /* host-to-device bytes of all loads */
+} moe_cache_stats;
+
+/* 1 <= n_slots <= n_routed_experts; host_store and slots as above (checked
+ * like moe_layer's experts: non-NULL, aligned, gscale iff NVFP4).  *cache
+ * (host) receives the new cache, NULL on error.  Makes no HIP call. */
+moe_status moe_cache_create(const moe_config* cfg, int32_t n_slots,
+                            const moe_qexperts* host_store, const moe_qexperts* slots,
+                            moe_expert_cache** cache);
+
+/* Frees the cache (NULL: nothing).  Waits for nothing: work already queued
+ * keeps reading the caller's slots. */
+moe_status moe_cache_destroy(moe_expert_cache* cache);
+
+/* The layer, as moe_layer, with the routed experts read from the cache's
+ * slots.  It routes on the device, waits on the host for the routing (the call
+ * synchronises `stream`), places the missing experts and enqueues their copies
+ * on `stream`, then enqueues the permutation, the expert FFNs over the slots,
+ * the shared expert and the combine, and returns without waiting for them.
+ * The routing (topk ids and weights) equals moe_layer's; y agrees with it
+ * within the layer's tolerance (these are the kernels moe_layer runs for T > 4
+ * and those of moe_expert_ffn_q4 for T <= 4).  If the call needs more
+ * distinct experts than the slots that are not pinned, it returns
+ * MOE_ERR_UNSUPPORTED after writing the routing, and loads nothing. */
+moe_status moe_layer_cached(moe_expert_cache* cache, int32_t T, const uint16_t* x,
+                            const float* router_w, const float* bias,
+                            const moe_qexperts* shared, void* y, int32_t out_dtype,
+                            int32_t* topk_ids_out, float* topk_w_out, void* ws,
+                            size_t ws_bytes, hipStream_t stream);
+
+/* Readahead / router lookahead: loads the listed experts now (HOST array of
+ * n ids in priority order; resident ones and repeats cost nothing), with the
+ * copies on `stream`, which may be another stream than the layer's so that
+ * they overlap its kernels.  It never evicts an expert of the latest
+ * moe_layer_cached call (whose kernels may still run; every earlier call has
+ * finished), its copies wait for the previous prefetch, and the next
+ * moe_layer_cached waits for them.  Experts that find no slot are skipped;
+ * *n_loaded (host, may be NULL) receives the number of experts loaded. */
+moe_status moe_cache_prefetch(moe_expert_cache* cache, const int32_t* experts, int32_t n,
+                              int32_t* n_loaded, hipStream_t stream);
+
+/* Pinned hot store: loads the listed experts as moe_cache_prefetch does and
+ * pins their slots, which are then never evicted (until moe_cache_unpin_all).
+ * All or nothing: MOE_ERR_UNSUPPORTED, with nothing loaded or pinned, if they
+ * do not all find slots. */
+moe_status moe_cache_pin(moe_expert_cache* cache, const int32_t* experts, int32_t n,
+                         hipStream_t stream);
+moe_status moe_cache_unpin_all(moe_expert_cache* cache);
+
+/* Counters since creation (host output). */
+moe_status moe_cache_get_stats(const moe_expert_cache* cache, moe_cache_stats* stats);
+
+/* Slot holding `expert` (host output), or -1 if it is not resident. */
+moe_status moe_cache_slot_of(const moe_expert_cache* cache, int32_t expert, int32_t* slot);
 
 #ifdef __cplusplus
 }

@@ -59,6 +59,12 @@ class MoeTrace(ctypes.Structure):
                 ("names", ctypes.c_char_p * MOE_TRACE_MAX)]
 
 
+class MoeCacheStats(ctypes.Structure):
+    _fields_ = [("calls", ctypes.c_uint64), ("hits", ctypes.c_uint64), ("misses", ctypes.c_uint64),
+                ("prefetched", ctypes.c_uint64), ("evictions", ctypes.c_uint64),
+                ("bytes_loaded", ctypes.c_uint64)]
+
+
 _lib = None
 
 
@@ -84,6 +90,14 @@ def lib() -> ctypes.CDLL:
                                 ctypes.POINTER(MoeTrace)],
             "moe_layer_flags": [vp, ctypes.POINTER(ctypes.c_uint32), vp],
             "moe_layer_noalloc": [cfgp, i32, vp, vp, vp, exp, exp, vp, i32, vp, vp, vp],
+            "moe_cache_create": [cfgp, i32, exp, exp, ctypes.POINTER(vp)],
+            "moe_cache_destroy": [vp],
+            "moe_layer_cached": [vp, i32, vp, vp, vp, exp, vp, i32, vp, vp, vp, sz, vp],
+            "moe_cache_prefetch": [vp, ctypes.POINTER(i32), i32, ctypes.POINTER(i32), vp],
+            "moe_cache_pin": [vp, ctypes.POINTER(i32), i32, vp],
+            "moe_cache_unpin_all": [vp],
+            "moe_cache_get_stats": [vp, ctypes.POINTER(MoeCacheStats)],
+            "moe_cache_slot_of": [vp, i32, ctypes.POINTER(i32)],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -123,7 +137,8 @@ def make_config(geom: dict, wfmt: str, options: int = 0) -> MoeConfig:
 
 
 def qexperts(gate, up, down) -> MoeQExperts:
-    """Each argument: (q, scale, gscale-or-None) tensors."""
+    """Each argument: (q, scale, gscale-or-None) tensors (device tensors; for
+    an expert cache's host store, pinned CPU tensors)."""
     def proj(p):
         return MoeQProj(p[0].data_ptr(), p[1].data_ptr(), None if p[2] is None else p[2].data_ptr())
     return MoeQExperts(proj(gate), proj(up), proj(down))
@@ -207,3 +222,59 @@ def moe_layer_noalloc(cfg, T, x, router_w, bias, routed: MoeQExperts,
                                    None if shared is None else ctypes.byref(shared), _p(y),
                                    out_dtype, _p(topk_ids_out), _p(topk_w_out), _stream(stream)),
            "moe_layer_noalloc")
+
+
+def _id_array(experts):
+    arr = (ctypes.c_int32 * max(len(experts), 1))(*[int(e) for e in experts])
+    return arr, len(experts)
+
+
+def moe_cache_create(cfg: MoeConfig, n_slots: int, host_store: MoeQExperts,
+                     slots: MoeQExperts) -> ctypes.c_void_p:
+    h = ctypes.c_void_p(None)
+    _check(lib().moe_cache_create(ctypes.byref(cfg), n_slots, ctypes.byref(host_store),
+                                  ctypes.byref(slots), ctypes.byref(h)), "moe_cache_create")
+    return h
+
+
+def moe_cache_destroy(cache) -> None:
+    _check(lib().moe_cache_destroy(cache), "moe_cache_destroy")
+
+
+def moe_layer_cached(cache, T, x, router_w, bias, shared: Optional[MoeQExperts], y,
+                     out_dtype=MOE_OUT_F32, topk_ids_out=None, topk_w_out=None, ws=None,
+                     stream=None):
+    _check(lib().moe_layer_cached(cache, T, _p(x), _p(router_w), _p(bias),
+                                  None if shared is None else ctypes.byref(shared), _p(y),
+                                  out_dtype, _p(topk_ids_out), _p(topk_w_out), _p(ws),
+                                  0 if ws is None else ws.numel(), _stream(stream)),
+           "moe_layer_cached")
+
+
+def moe_cache_prefetch(cache, experts, stream=None) -> int:
+    arr, n = _id_array(experts)
+    loaded = ctypes.c_int32(0)
+    _check(lib().moe_cache_prefetch(cache, arr, n, ctypes.byref(loaded), _stream(stream)),
+           "moe_cache_prefetch")
+    return loaded.value
+
+
+def moe_cache_pin(cache, experts, stream=None) -> None:
+    arr, n = _id_array(experts)
+    _check(lib().moe_cache_pin(cache, arr, n, _stream(stream)), "moe_cache_pin")
+
+
+def moe_cache_unpin_all(cache) -> None:
+    _check(lib().moe_cache_unpin_all(cache), "moe_cache_unpin_all")
+
+
+def moe_cache_get_stats(cache) -> dict:
+    st = MoeCacheStats()
+    _check(lib().moe_cache_get_stats(cache, ctypes.byref(st)), "moe_cache_get_stats")
+    return {name: getattr(st, name) for name, _ in MoeCacheStats._fields_}
+
+
+def moe_cache_slot_of(cache, expert: int) -> int:
+    s = ctypes.c_int32(0)
+    _check(lib().moe_cache_slot_of(cache, expert, ctypes.byref(s)), "moe_cache_slot_of")
+    return s.value

@@ -263,7 +263,23 @@ __global__ void __launch_bounds__(64 * kSmallWaves) perm_small_kernel(
   }
 }
 
+// Expert id -> cache slot of every pick (the map travels as a kernel argument).
+__global__ void __launch_bounds__(256) remap_ids_kernel(const int32_t* __restrict__ ids,
+                                                        int32_t* __restrict__ out, int P, SlotMap map) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= P) return;
+  const int e = ids[i];
+  out[i] = e < 0 ? -1 : map.slot[e];
+}
+
 }  // namespace
+
+hipError_t launch_remap_ids(const int32_t* ids, int32_t* out, int P, const SlotMap& map,
+                            hipStream_t s) {
+  if (P == 0) return hipSuccess;
+  hipLaunchKernelGGL(remap_ids_kernel, dim3((P + 255) / 256), dim3(256), 0, s, ids, out, P, map);
+  return hipGetLastError();
+}
 
 int permute_chunk(int T) { return std::max(64, (T + kMaxChunks - 1) / kMaxChunks); }
 size_t permute_hist_ints(int T, int E) {

@@ -15,6 +15,8 @@ constexpr size_t kAlign = 256;
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+}  // namespace
+
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 moe_status check_cfg(const moe_config* c) {
@@ -123,8 +125,6 @@ hipError_t run_gemm_ffn(const moe_config& c, int T, const uint16_t* x, const Wor
   return launch_gemm(g, K, E, stream, tr);
 }
 
-}  // namespace
-
 Workspace carve_workspace(const moe_config& c, int T, void* base) {
   Workspace w{};
   if (T == 0) return w;
@@ -158,6 +158,7 @@ Workspace carve_workspace(const moe_config& c, int T, void* base) {
   const size_t o_dpick = take(kDecMaxSlots * sizeof(int32_t));
   const size_t o_dbar = take(kDecBarrierWords * sizeof(uint32_t));
   const size_t o_phist = take(permute_hist_ints(T, (int)E) * sizeof(int32_t));
+  const size_t o_cids = take(P * sizeof(int32_t));
   w.total = off;
   if (base) {
     char* b = static_cast<char*>(base);
@@ -180,6 +181,7 @@ Workspace carve_workspace(const moe_config& c, int T, void* base) {
     w.dpick = reinterpret_cast<int32_t*>(b + o_dpick);
     w.dbar = reinterpret_cast<uint32_t*>(b + o_dbar);
     w.phist = reinterpret_cast<int32_t*>(b + o_phist);
+    w.cache_ids = reinterpret_cast<int32_t*>(b + o_cids);
   }
   return w;
 }

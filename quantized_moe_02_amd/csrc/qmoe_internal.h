@@ -55,6 +55,7 @@ struct Workspace {
   uint32_t* dbar;         // [kDecBarrierWords] decode path: grid-barrier count and flags
   int32_t* n_tiles;       // [4]
   int32_t* phist;         // [permute_hist_ints] permutation scratch
+  int32_t* cache_ids;     // [P] moe_layer_cached: the picks' slot ids
   size_t total;
 };
 
@@ -84,6 +85,14 @@ Workspace carve_workspace(const moe_config& c, int T, void* base);
 moe_status check_layer_args(const moe_config* cfg, int32_t T, const uint16_t* x,
                             const float* router_w, const moe_qexperts* routed,
                             const moe_qexperts* shared, const void* y, int32_t out_dtype);
+// Argument checks shared by the entry points (no HIP call).
+bool aligned(const void* p, size_t a);
+moe_status check_cfg(const moe_config* c);
+moe_status check_T(int32_t T);
+moe_status check_experts(const moe_qexperts* w, int wfmt);
+moe_status check_ws(const moe_config& c, int T, const void* ws, size_t ws_bytes);
+ExpertSet expert_set(const moe_qexperts& w, int inter);
+moe_status hip_status(hipError_t e);
 // moe_layer_noalloc's workspace on the current device (its device address,
 // looked up on the first call on that device); nullptr if the lookup failed.
 void* noalloc_workspace();
@@ -229,5 +238,20 @@ hipError_t launch_build_units(const int32_t* offsets, const int32_t* active,
                               int K, int E, bool has_shared, hipStream_t s);
 hipError_t launch_x_to_f16(const uint16_t* x, uint16_t* y, int T, int H, int ldx, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs& g, int K, int E, hipStream_t s, Tracer* tr = nullptr);
+// Expert FFNs of a T > kDecodeMaxTokens call on the grouped GEMM: work units
+// from the permutation (E = c.n_routed_experts experts) and/or the shared
+// expert, fp16 activations, gate/up, down into o.
+hipError_t run_gemm_ffn(const moe_config& c, int T, const uint16_t* x, const Workspace& w,
+                        bool has_routed, const ExpertSet& routed, const int32_t* offsets,
+                        const int32_t* active, const int32_t* n_active,
+                        const int32_t* sorted_token, bool has_shared, const ExpertSet& shared,
+                        int P, int ldh, uint16_t* h, float* o, hipStream_t stream, Tracer* tr);
+
+// Replaces each pick's expert id by its cache slot (map[id]); -1 stays -1.
+struct SlotMap {
+  int32_t slot[256];
+};
+hipError_t launch_remap_ids(const int32_t* ids, int32_t* out, int P, const SlotMap& map,
+                            hipStream_t s);
 
 }  // namespace qmoe

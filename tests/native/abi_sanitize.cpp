@@ -159,6 +159,48 @@ int main() {
          MOE_ERR_UNSUPPORTED);
   EXPECT(moe_layer_noalloc(&big, 8, nullptr, f, f, &e, &e, fake, 0, nullptr, nullptr, nullptr),
          MOE_ERR_INVALID_ARG);
+  // expert cache: creation and the host-only calls need no device; invalid
+  // calls return before any HIP call
+  moe_expert_cache* cache = reinterpret_cast<moe_expert_cache*>(fake);
+  EXPECT(moe_cache_create(&c, 0, &e, &e, &cache), MOE_ERR_INVALID_ARG);
+  if (cache) ++failures;   // NULL on error
+  EXPECT(moe_cache_create(&c, 17, &e, &e, &cache), MOE_ERR_INVALID_ARG);   // > E
+  EXPECT(moe_cache_create(&c, 4, &mis, &e, &cache), MOE_ERR_INVALID_ARG);
+  EXPECT(moe_cache_create(&c, 4, &e, nullptr, &cache), MOE_ERR_INVALID_ARG);
+  EXPECT(moe_cache_create(&c, 4, &e, &e, nullptr), MOE_ERR_INVALID_ARG);
+  EXPECT(moe_cache_create(&c, 4, &e, &e, &cache), MOE_OK);
+  if (cache) {
+    int32_t slot = 7;
+    EXPECT(moe_cache_slot_of(cache, 3, &slot), MOE_OK);
+    if (slot != -1) ++failures;
+    EXPECT(moe_cache_slot_of(cache, 16, &slot), MOE_ERR_INVALID_ARG);
+    moe_cache_stats st{};
+    EXPECT(moe_cache_get_stats(cache, &st), MOE_OK);
+    if (st.calls || st.hits || st.misses || st.prefetched || st.evictions || st.bytes_loaded)
+      ++failures;
+    const int32_t ids[6] = {0, 1, 2, 3, 4, 16};
+    int32_t loaded = 9;
+    EXPECT(moe_cache_prefetch(cache, ids, 0, &loaded, nullptr), MOE_OK);
+    if (loaded != 0) ++failures;
+    EXPECT(moe_cache_prefetch(cache, ids, 6, &loaded, nullptr), MOE_ERR_INVALID_ARG);   // id 16
+    EXPECT(moe_cache_prefetch(cache, nullptr, 2, &loaded, nullptr), MOE_ERR_INVALID_ARG);
+    EXPECT(moe_cache_pin(cache, ids, 5, nullptr), MOE_ERR_UNSUPPORTED);   // 5 experts, 4 slots
+    EXPECT(moe_cache_pin(cache, ids, -1, nullptr), MOE_ERR_INVALID_ARG);
+    EXPECT(moe_cache_unpin_all(cache), MOE_OK);
+    EXPECT(moe_layer_cached(cache, 8, x, f, f, &e, fake, 2, nullptr, nullptr, fake, n, nullptr),
+           MOE_ERR_INVALID_ARG);   // out dtype
+    EXPECT(moe_layer_cached(cache, 8, x, f, f, nullptr, fake, 0, nullptr, nullptr, fake, n, nullptr),
+           MOE_ERR_INVALID_ARG);   // shared expert missing
+    EXPECT(moe_layer_cached(cache, 8, x, f, f, &e, fake, 0, nullptr, nullptr, fake, n - 1, nullptr),
+           MOE_ERR_WORKSPACE_TOO_SMALL);
+    EXPECT(moe_layer_cached(cache, 0, x, f, f, &e, fake, 0, nullptr, nullptr, nullptr, 0, nullptr),
+           MOE_OK);
+    EXPECT(moe_cache_destroy(cache), MOE_OK);
+  }
+  EXPECT(moe_layer_cached(nullptr, 1, x, f, f, &e, fake, 0, nullptr, nullptr, fake, n, nullptr),
+         MOE_ERR_INVALID_ARG);
+  EXPECT(moe_cache_destroy(nullptr), MOE_OK);
+
   for (int s = 0; s <= 7; ++s)   // the values a moe_status can hold in C++
     if (!moe_status_string(static_cast<moe_status>(s))) ++failures;
 

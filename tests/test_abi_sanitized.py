@@ -1,4 +1,4 @@
-"""The C-ABI boundary code (csrc/qmoe_api.cpp) built with AddressSanitizer and
+"""The C-ABI boundary code (csrc/qmoe_api.cpp, csrc/expert_cache.cpp) built with AddressSanitizer and
 UndefinedBehaviorSanitizer on the host, driven by tests/native/abi_sanitize.cpp
 through every entry point's validation and the workspace sizing.  CPU only:
 none of these calls reaches the device.  The kernels' objects come from the
@@ -17,22 +17,26 @@ SAN = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-
 
 @pytest.mark.slow
 def test_abi_under_host_sanitizers(tmp_path):
+    boundary = ("qmoe_api", "expert_cache")   # host-only sources of the boundary
     objs = [o for o in glob.glob(os.path.join(ROOT, "_build", "*.o"))
-            if not o.endswith("qmoe_api.o")]
+            if os.path.splitext(os.path.basename(o))[0] not in boundary]
     if not shutil.which(CLANG) or len(objs) < 5:
         pytest.skip("needs the regular build (_build/*.o) and the ROCm clang")
     inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(ROOT, "quantized_moe_02_amd", "csrc"),
            "-I", "/opt/rocm/include", "-D__HIP_PLATFORM_AMD__"]
-    api = str(tmp_path / "qmoe_api_san.o")
     drv = str(tmp_path / "abi_sanitize.o")
     exe = str(tmp_path / "abi_sanitize")
     # host-only C++ (the boundary holds no device code)
-    subprocess.run([CLANG, "-x", "c++", "-std=c++17", "-O1", "-g", *SAN, *inc, "-c",
-                    os.path.join(ROOT, "quantized_moe_02_amd", "csrc", "qmoe_api.cpp"), "-o", api],
-                   check=True)
+    san_objs = []
+    for name in boundary:
+        o = str(tmp_path / f"{name}_san.o")
+        subprocess.run([CLANG, "-x", "c++", "-std=c++17", "-O1", "-g", *SAN, *inc, "-c",
+                        os.path.join(ROOT, "quantized_moe_02_amd", "csrc", f"{name}.cpp"), "-o", o],
+                       check=True)
+        san_objs.append(o)
     subprocess.run([CLANG, "-std=c++17", "-O1", "-g", *SAN, *inc, "-c",
                     os.path.join(ROOT, "tests", "native", "abi_sanitize.cpp"), "-o", drv], check=True)
-    subprocess.run([CLANG, *SAN, drv, api, *objs, "-L/opt/rocm/lib", "-lamdhip64",
+    subprocess.run([CLANG, *SAN, drv, *san_objs, *objs, "-L/opt/rocm/lib", "-lamdhip64",
                     "-Wl,-rpath,/opt/rocm/lib", "-o", exe], check=True)
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=1",
                UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
