@@ -13,7 +13,8 @@ What it follows (page "Show HN: Menjalankan GLM 5.2 di komputer lambat"):
   * section "Fitur utama": batch-union MoE, where each unique expert of a batch
     is applied to every position routed to it (the permutation);
   * sections "Cara kerja eksekusi MoE" and "Fitur utama": int4 expert weights
-    dequantised on use;
+    dequantised on use, and the per-row-scale int8 / packed int4 / packed int2
+    formats of the quantisation kernels;
 and page "NVIDIA stellt neues GLM-5.2 NVFP4 Modell vor", section "Technische
 Details": the expert FFNs in 4-bit with one FP8 scale per 16 elements.
 
@@ -26,6 +27,7 @@ reference implementation and trained weights are not available.
 from .moe import (  # noqa: F401
     bf16_bits_to_f64, fp16_bits_to_f64, decode_e2m1, decode_e4m3fn,
     unpack_int4_codes, unpack_nvfp4_codes, dequant_int4, dequant_nvfp4,
+    unpack_int2_codes, dequant_int4_row, dequant_int8_row, dequant_int2_row, ROW_FORMATS,
     RouterConfig, route, route_weights, route_margins, valid_under_perturbation,
     apply_top_p, valid_top_p,
     permute, swiglu_ffn, expert_ffn, layer, dense_layer, ExpertSource,

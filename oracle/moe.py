@@ -120,11 +120,62 @@ def dequant_nvfp4(q: np.ndarray, scale_e4m3: np.ndarray, gscale: float) -> np.nd
     return (v.reshape(N, K // 16, 16) * s[:, :, None]).reshape(N, K) * g
 
 
+# Per-row-scale formats.  [P2-Fitur: the quantisation kernels handle int8,
+# packed int4 and packed int2 with one scale per row, dequantised on use.]  The
+# pages name these formats without a layout; the reading taken: symmetric
+# integer codes with one float32 scale per output row, w = q * scale[row];
+# int8 codes are two's-complement bytes in input order; int4 codes use the
+# int4 word layout above (q = u - 8); int2 codes use the word layout below
+# (q = u - 2).
+
+def unpack_int2_codes(q: np.ndarray) -> np.ndarray:
+    """uint8 [..., K/4] -> codes [..., K] in 0..3.  Each group of 4 bytes is a
+    little-endian 32-bit word covering inputs 16j..16j+15; input 16j+2i
+    (i = 0..7) sits in bits [2i, 2i+2) and input 16j+2i+1 in bits
+    [16+2i, 16+2i+2)."""
+    q = np.asarray(q, dtype=np.uint8)
+    *lead, quarter = q.shape
+    K = quarter * 4
+    b = q.reshape(*lead, K // 16, 4).astype(np.uint32)
+    word = b[..., 0] | (b[..., 1] << 8) | (b[..., 2] << 16) | (b[..., 3] << 24)
+    out = np.empty((*lead, K // 16, 16), dtype=np.uint8)
+    for i in range(8):
+        out[..., 2 * i] = (word >> (2 * i)) & 3
+        out[..., 2 * i + 1] = (word >> (16 + 2 * i)) & 3
+    return out.reshape(*lead, K)
+
+
+def _row_scale(scale) -> np.ndarray:
+    return np.asarray(scale, dtype=np.float32).astype(np.float64)[:, None]
+
+
+def dequant_int4_row(q: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """int4 codes (word layout of unpack_int4_codes), one fp32 scale per row:
+    w = (u - 8) * scale[n].  q: uint8 [N, K/2]; scale: float32 [N]."""
+    return (unpack_int4_codes(q).astype(np.float64) - 8.0) * _row_scale(scale)
+
+
+def dequant_int8_row(q: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """int8 two's-complement codes in input order, one fp32 scale per row:
+    w = q * scale[n].  q: uint8/int8 [N, K]; scale: float32 [N]."""
+    return np.asarray(q).view(np.int8).astype(np.float64) * _row_scale(scale)
+
+
+def dequant_int2_row(q: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """int2 codes (word layout of unpack_int2_codes), one fp32 scale per row:
+    w = (u - 2) * scale[n].  q: uint8 [N, K/4]; scale: float32 [N]."""
+    return (unpack_int2_codes(q).astype(np.float64) - 2.0) * _row_scale(scale)
+
+
+ROW_FORMATS = {"int4_row": dequant_int4_row, "int8_row": dequant_int8_row,
+               "int2_row": dequant_int2_row}
+
+
 @dataclasses.dataclass
 class ExpertSource:
     """Packed weights of E experts as NumPy arrays, decoded on demand.
-    proj -> (q uint8 [E,N,K/2], scale [E,N,K/g], gscale float32 [E] or None)."""
-    wfmt: str                      # "int4" or "nvfp4"
+    proj -> (q uint8 [E,N,...], scale [E,N,...], gscale float32 [E] or None)."""
+    wfmt: str                      # "int4", "nvfp4" or one of ROW_FORMATS
     gate: tuple
     up: tuple
     down: tuple
@@ -133,6 +184,8 @@ class ExpertSource:
         q, s, g = getattr(self, proj)
         if self.wfmt == "int4":
             return dequant_int4(q[e], s[e])
+        if self.wfmt in ROW_FORMATS:
+            return ROW_FORMATS[self.wfmt](q[e], s[e])
         return dequant_nvfp4(q[e], s[e], g[e])
 
     @property

@@ -150,6 +150,64 @@ def quantize_int4_g32(W: torch.Tensor):
     return pack_int4_words(u), s16
 
 
+def pack_int2_words(u: torch.Tensor) -> torch.Tensor:
+    """u: uint8 codes in [0, 3], shape [..., K] with K % 16 == 0.  Returns
+    uint8 [..., K/4]: per 16 inputs one little-endian 32-bit word, input
+    16j+2i (i = 0..7) in bits [2i, 2i+2), input 16j+2i+1 in bits
+    [16+2i, 16+2i+2)."""
+    *lead, K = u.shape
+    assert K % 16 == 0
+    c = u.to(torch.int64).reshape(*lead, K // 16, 8, 2)
+    sh = 2 * torch.arange(8, dtype=torch.int64, device=u.device)
+    word = ((c[..., 0] << sh) | (c[..., 1] << (sh + 16))).sum(-1)     # disjoint bits
+    b = torch.stack([(word >> (8 * j)) & 255 for j in range(4)], dim=-1).to(torch.uint8)
+    return b.reshape(*lead, K // 4)
+
+
+def repack_int2_natural(q: torch.Tensor) -> torch.Tensor:
+    """int2 codes packed in the natural order (byte j holds inputs 4j..4j+3 in
+    bits 0-1, 2-3, 4-5, 6-7), uint8 [..., K/4] -> the library's word order.
+    A layout change only."""
+    c = torch.stack([(q >> (2 * i)) & 3 for i in range(4)], dim=-1)
+    return pack_int2_words(c.reshape(*q.shape[:-1], q.shape[-1] * 4))
+
+
+def _row_quantize(W: torch.Tensor, qmin: int, qmax: int, div: float):
+    """scale = absmax(row) / div (fp32); q = clamp(round_half_even(w/scale),
+    qmin, qmax); a zero row encodes q = 0."""
+    Wf = W.float()
+    s = Wf.abs().amax(-1) / div
+    sd = torch.where(s > 0, s, torch.ones_like(s)).unsqueeze(-1)
+    q = torch.where(s.unsqueeze(-1) > 0, torch.round(Wf / sd), torch.zeros_like(Wf))
+    return q.clamp_(qmin, qmax), s
+
+
+def quantize_int4_row(W: torch.Tensor):
+    """int4 codes with one fp32 scale per row: scale = absmax/7, q in -7..7,
+    u = q + 8, word layout of pack_int4_words.  W: float [..., N, K].
+    Returns (uint8 [..., N, K/2], float32 [..., N])."""
+    q, s = _row_quantize(W, -7, 7, 7.0)
+    return pack_int4_words((q + 8).to(torch.uint8)), s
+
+
+def quantize_int8_row(W: torch.Tensor):
+    """int8 two's-complement codes in input order with one fp32 scale per row:
+    scale = absmax/127, q in -127..127.  Returns (uint8 [..., N, K], float32 [..., N])."""
+    q, s = _row_quantize(W, -127, 127, 127.0)
+    return q.to(torch.int8).view(torch.uint8), s
+
+
+def quantize_int2_row(W: torch.Tensor):
+    """int2 codes with one fp32 scale per row: scale = absmax/2, q in -2..1
+    (the positive side saturates at 1), u = q + 2, word layout of
+    pack_int2_words.  Returns (uint8 [..., N, K/4], float32 [..., N])."""
+    q, s = _row_quantize(W, -2, 1, 2.0)
+    return pack_int2_words((q + 2).to(torch.uint8)), s
+
+
+ROW_FORMATS = ("int4_row", "int8_row", "int2_row")
+
+
 def _e2m1_encode(v: torch.Tensor) -> torch.Tensor:
     """Round-to-nearest-even onto the E2M1 grid {0,.5,1,1.5,2,3,4,6}, saturating
     at 6; returns uint8 codes (bit 3 = sign)."""
@@ -191,9 +249,10 @@ def quantize_nvfp4(W: torch.Tensor):
 @dataclasses.dataclass
 class QProj:
     """One projection of E experts: N output rows, K inputs."""
-    q: torch.Tensor                   # uint8 [E, N, K/2]
-    scale: torch.Tensor               # int4: float16 [E, N, K/32]; nvfp4: uint8 [E, N, K/16]
-    gscale: Optional[torch.Tensor]    # nvfp4: float32 [E]; int4: None
+    q: torch.Tensor                   # uint8 [E, N, K * bits / 8]
+    scale: torch.Tensor               # int4: float16 [E, N, K/32]; nvfp4: uint8 [E, N, K/16];
+                                      # per-row formats: float32 [E, N]
+    gscale: Optional[torch.Tensor]    # nvfp4: float32 [E]; otherwise None
 
 
 @dataclasses.dataclass
@@ -220,6 +279,10 @@ class LayerInputs:
 def _quantize(W: torch.Tensor, wfmt: str) -> QProj:
     if wfmt == "int4":
         q, s = quantize_int4_g32(W)
+        return QProj(q, s, None)
+    if wfmt in ROW_FORMATS:
+        q, s = {"int4_row": quantize_int4_row, "int8_row": quantize_int8_row,
+                "int2_row": quantize_int2_row}[wfmt](W)
         return QProj(q, s, None)
     q, s, g = quantize_nvfp4(W)
     return QProj(q, s, g)
@@ -340,6 +403,16 @@ def raw_nvfp4_proj(E: int, N: int, K: int, seed: int, gscale: float,
     return QProj(q.to(device), s.to(torch.uint8).to(device), gs.to(device))
 
 
+def raw_row_proj(E: int, N: int, K: int, bits: int, seed: int, device="cpu") -> QProj:
+    """Uniformly random code bytes (every code of the format) and fp32 row
+    scales of either sign with magnitudes 2^U(-14, -6) / 2^(bits-4)."""
+    g = _gen("cpu", seed)
+    q = torch.randint(0, 256, (E, N, K * bits // 8), generator=g, dtype=torch.int32).to(torch.uint8)
+    mag = torch.exp2(torch.rand((E, N), generator=g) * 8.0 - 14.0 - (bits - 4))
+    sign = torch.where(torch.rand((E, N), generator=g) < 0.5, -1.0, 1.0)
+    return QProj(q.to(device), (mag * sign).float().to(device), None)
+
+
 def make_raw(geom: dict, T: int, wfmt: str, seed: int, device="cpu",
              gscale: float = 2e-4) -> LayerInputs:
     """A small layer whose expert weights are raw random bytes (see above);
@@ -351,8 +424,13 @@ def make_raw(geom: dict, T: int, wfmt: str, seed: int, device="cpu",
         ps = []
         for p, (N, K) in enumerate(shapes):
             s = sub_seed(seed, tag, p)
-            ps.append(raw_int4_proj(n, N, K, s, device) if wfmt == "int4"
-                      else raw_nvfp4_proj(n, N, K, s, gscale, device))
+            if wfmt == "int4":
+                ps.append(raw_int4_proj(n, N, K, s, device))
+            elif wfmt in ROW_FORMATS:
+                bits = {"int4_row": 4, "int8_row": 8, "int2_row": 2}[wfmt]
+                ps.append(raw_row_proj(n, N, K, bits, s, device))
+            else:
+                ps.append(raw_nvfp4_proj(n, N, K, s, gscale, device))
         return QExperts(*ps)
     x = to_bf16(randn((T, H), sub_seed(seed, 1, T), device))
     router_w = randn((E, H), sub_seed(seed, 2), device, WEIGHT_STD)

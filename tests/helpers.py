@@ -26,7 +26,7 @@ def _proj_np(p, wfmt):
         g = None
     else:
         s = p.scale.detach().cpu().numpy()
-        g = p.gscale.detach().cpu().numpy()
+        g = None if p.gscale is None else p.gscale.detach().cpu().numpy()
     return (q, s, g)
 
 
@@ -54,6 +54,8 @@ class LazyExperts:
             q = p.q[e:e + 1].detach().cpu().numpy()
             if self.wfmt == "int4":
                 out.append((q, np_u16(p.scale[e:e + 1]), None))
+            elif self.wfmt in oracle.ROW_FORMATS:
+                out.append((q, p.scale[e:e + 1].detach().cpu().numpy(), None))
             else:
                 out.append((q, p.scale[e:e + 1].detach().cpu().numpy(),
                             p.gscale[e:e + 1].detach().cpu().numpy()))
@@ -66,6 +68,8 @@ class LazyExperts:
             q = p.q[e].detach().cpu().numpy()
             if self.wfmt == "int4":
                 w = oracle.dequant_int4(q, np_u16(p.scale[e]))
+            elif self.wfmt in oracle.ROW_FORMATS:
+                w = oracle.ROW_FORMATS[self.wfmt](q, p.scale[e].detach().cpu().numpy())
             else:
                 w = oracle.dequant_nvfp4(q, p.scale[e].detach().cpu().numpy(),
                                          float(p.gscale[e].item()))

@@ -581,3 +581,112 @@ def test_repack_int4_natural():
     natural = torch.from_numpy((codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8))
     q = synth.repack_int4_natural(natural).numpy()
     assert np.array_equal(oracle.unpack_int4_codes(q), codes)
+
+
+# ---------------------------------------------------------------------------
+# Per-row-scale formats (int4, int8, packed int2)
+# ---------------------------------------------------------------------------
+
+def _int2_bytes_from_codes_by_position(codes):
+    """Independent packer for the int2 word layout, bit by bit from the
+    layout's statement (input 16j + r: r even in bits r, r+1 of word j; r odd
+    in bits 16 + r - 1, 16 + r)."""
+    N, K = codes.shape
+    out = np.zeros((N, K // 4), np.uint8)
+    for n in range(N):
+        for k in range(K):
+            j, r = divmod(k, 16)
+            bit = (r - r % 2) + 16 * (r % 2)
+            byte, sh = 4 * j + bit // 8, bit % 8
+            out[n, byte] |= np.uint8(int(codes[n, k]) << sh)
+    return out
+
+
+def test_int2_layout_one_hot_probe():
+    K = 48
+    for k in range(K):
+        codes = np.full((1, K), 2, np.uint8)
+        codes[0, k] = 3                        # q = +1 at input k only
+        q = _int2_bytes_from_codes_by_position(codes)
+        w = oracle.dequant_int2_row(q, np.array([0.25], np.float32))
+        expect = np.zeros((1, K))
+        expect[0, k] = 0.25
+        assert np.array_equal(w, expect), k
+        assert np.array_equal(synth.pack_int2_words(torch.from_numpy(codes)).numpy(), q)
+
+
+def test_int2_hand_words():
+    """Word 0x00000001: input 0 has code 1 (q = -1), every other input code 0
+    (q = -2).  Word 0xC0000000: input 15 has code 3 (q = 1).  Byte order is
+    little-endian."""
+    q = np.array([[0x01, 0x00, 0x00, 0x00], [0x00, 0x00, 0x00, 0xC0]], np.uint8)
+    w = oracle.dequant_int2_row(q, np.array([1.0, 2.0], np.float32))
+    assert np.array_equal(w[0], np.array([-1.0] + [-2.0] * 15))
+    assert np.array_equal(w[1], np.array([-4.0] * 15 + [2.0]))
+
+
+def test_int8_hand_bytes():
+    q = np.array([[0x00, 0x01, 0x7F, 0x80, 0xFF, 0xFE]], np.uint8)
+    w = oracle.dequant_int8_row(q, np.array([0.5], np.float32))
+    assert np.array_equal(w[0], 0.5 * np.array([0, 1, 127, -128, -1, -2]))
+
+
+def test_int4_row_equals_group_scales_when_all_equal():
+    """Per-row int4 is int4 g32 with every group scale equal to the row scale
+    (scales exact in fp16)."""
+    rng = np.random.default_rng(7)
+    codes = rng.integers(0, 16, size=(5, 96)).astype(np.uint8)
+    q = _int4_bytes_from_codes_by_position(codes)
+    srow = np.array([0.5, 0.25, 2.0, 1.0, 0.125], np.float32)
+    sg = np.repeat(srow[:, None], 3, axis=1).astype(np.float16).view(np.uint16)
+    assert np.array_equal(oracle.dequant_int4_row(q, srow), oracle.dequant_int4(q, sg))
+    assert np.array_equal(oracle.dequant_int4_row(q, srow), (codes - 8.0) * srow[:, None])
+
+
+@pytest.mark.parametrize("fmt,qmax", [("int4_row", 7), ("int8_row", 127)])
+def test_row_roundtrip_bound(fmt, qmax):
+    W = torch.randn(32, 256) * 0.02
+    W[5] = 0.0                                  # an all-zero row
+    qp = synth._quantize(W.unsqueeze(0), fmt)
+    w = oracle.ROW_FORMATS[fmt](qp.q[0].numpy(), qp.scale[0].numpy())
+    s = qp.scale[0].double().numpy()[:, None]
+    assert np.all(np.abs(w - W.double().numpy()) <= s / 2 * (1 + 1e-6))
+    assert np.all(w[5] == 0.0)
+    # the row's absmax is on the grid
+    assert np.allclose(np.abs(w).max(1)[s[:, 0] > 0], (qmax * s[:, 0])[s[:, 0] > 0], rtol=1e-6)
+
+
+def test_int2_on_grid_roundtrip_exact():
+    rng = np.random.default_rng(3)
+    qv = rng.integers(-2, 2, size=(8, 64)).astype(np.float64)
+    qv[:, 0] = -2                                # every row reaches absmax = 2 s
+    s = np.float32(2.0 ** -7) * (1 + np.arange(8) % 3)
+    W = qv * s.astype(np.float64)[:, None]
+    qp = synth._quantize(torch.from_numpy(W).float().unsqueeze(0), "int2_row")
+    assert np.array_equal(oracle.dequant_int2_row(qp.q[0].numpy(), qp.scale[0].numpy()), W)
+
+
+def test_repack_int2_natural():
+    rng = np.random.default_rng(13)
+    codes = rng.integers(0, 4, size=(3, 64)).astype(np.uint8)
+    natural = (codes[:, 0::4] | (codes[:, 1::4] << 2) | (codes[:, 2::4] << 4)
+               | (codes[:, 3::4] << 6)).astype(np.uint8)
+    q = synth.repack_int2_natural(torch.from_numpy(natural)).numpy()
+    assert np.array_equal(oracle.unpack_int2_codes(q), codes)
+
+
+@pytest.mark.parametrize("fmt", ["int4_row", "int8_row", "int2_row"])
+def test_row_format_layer_dense_equivalence(fmt):
+    """The batch-union layer equals the dense definition (every expert applied
+    to every token, weights zero off the chosen ones) for the per-row formats."""
+    geom = synth.small_geom()
+    L = synth.make_custom(geom, 5, fmt, "normal0.1", seed=21)
+    x, Wr, b, cfg, routed, shared = oracle_inputs(L)
+    y, _, _ = oracle.layer(x, Wr, b, cfg, routed, shared)
+    assert np.allclose(y, oracle.dense_layer(x, Wr, b, cfg, routed, shared), rtol=1e-12, atol=1e-14)
+    # doubling every down-projection row scale doubles the routed part exactly
+    d = routed.down
+    routed2 = oracle.ExpertSource(fmt, routed.gate, routed.up, (d[0], d[1] * 2, None))
+    y0, _, _ = oracle.layer(x, Wr, b, cfg, routed, None)
+    y2, _, _ = oracle.layer(x, Wr, b, cfg, routed2, None)
+    assert np.allclose(y2, 2 * y0, rtol=1e-12, atol=1e-14)
