@@ -56,9 +56,14 @@ def parse():
 # algorithmic bytes and flops
 # ---------------------------------------------------------------------------
 
+ROW_BITS = {"int4_row": 4, "int8_row": 8, "int2_row": 2}
+
+
 def proj_bytes(N, K, wfmt):
     if wfmt == "int4":
         return N * K // 2 + (N * K // 32) * 2
+    if wfmt in ROW_BITS:
+        return N * K * ROW_BITS[wfmt] // 8 + 4 * N
     return N * K // 2 + N * K // 16 + 4
 
 

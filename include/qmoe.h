@@ -59,6 +59,24 @@
  *          2j+1 in the high nibble; a nibble is an E2M1 code (bit 3 sign).
  *   scale  uint8 [E][N][K/16] E4M3 "fn" codes (bias 7, no infinities).
  *   gscale float32 [E]; weight = e2m1 * e4m3 * gscale[e].
+ * Per-row-scale formats (page "Show HN: Menjalankan GLM 5.2 ...", section
+ * "Fitur utama": the quantisation kernels take int8, packed int4 and packed
+ * int2 with one scale per row, dequantised on use; the pages give no layout,
+ * so these are the library's): symmetric integer codes and one float32 scale
+ * per output row, weight = q * scale[e][n]; gscale must be NULL.
+ *   MOE_WFMT_INT4_ROW_F32  q as MOE_WFMT_INT4_G32_F16 (q = u - 8);
+ *                          scale float32 [E][N].
+ *   MOE_WFMT_INT8_ROW_F32  q int8 [E][N][K], two's complement, input order;
+ *                          scale float32 [E][N].
+ *   MOE_WFMT_INT2_ROW_F32  q uint8 [E][N][K/4]: per row K/16 little-endian
+ *                          32-bit words; word j holds inputs 16j..16j+15,
+ *                          input 16j+2i (i = 0..7) in bits [2i, 2i+2) and
+ *                          input 16j+2i+1 in bits [16+2i, 16+2i+2); a code u
+ *                          in 0..3 means q = u - 2 (natural order, four inputs
+ *                          per byte from bit 0 up, must be repacked:
+ *                          synth.repack_int2_natural); scale float32 [E][N].
+ *   The per-row formats run on the grouped GEMV for T <= 4 and on the grouped
+ *   GEMM for larger T (moe_layer's single-token kernel takes the other two).
  * Gate and up have N = inter, K = hidden; down has N = hidden, K = inter.
  *
  * Activations are bfloat16 [T][hidden], row-major.  For T > 4 the grouped
@@ -85,7 +103,13 @@ typedef enum {
   MOE_ERR_HIP = 4                  /* a HIP runtime call or launch failed */
 } moe_status;
 
-typedef enum { MOE_WFMT_INT4_G32_F16 = 0, MOE_WFMT_NVFP4 = 1 } moe_wfmt;
+typedef enum {
+  MOE_WFMT_INT4_G32_F16 = 0,
+  MOE_WFMT_NVFP4 = 1,
+  MOE_WFMT_INT4_ROW_F32 = 2,
+  MOE_WFMT_INT8_ROW_F32 = 3,
+  MOE_WFMT_INT2_ROW_F32 = 4
+} moe_wfmt;
 typedef enum { MOE_OUT_F32 = 0, MOE_OUT_BF16 = 1 } moe_out_dtype;
 
 /* Layer geometry.  Limits (else MOE_ERR_INVALID_ARG): hidden, moe_inter and

@@ -64,8 +64,11 @@ struct ProjBytes {
 
 ProjBytes proj_bytes(int wfmt, int N, int K) {
   ProjBytes b;
-  b.q = (size_t)N * K / 2;
-  b.s = wfmt == MOE_WFMT_NVFP4 ? (size_t)N * K / 16 : (size_t)N * (K / 32) * 2;
+  b.q = (size_t)N * K * wfmt_bits(wfmt) / 8;
+  if (wfmt_row(wfmt))
+    b.s = (size_t)N * sizeof(float);
+  else
+    b.s = wfmt == MOE_WFMT_NVFP4 ? (size_t)N * K / 16 : (size_t)N * (K / 32) * 2;
   b.g = wfmt == MOE_WFMT_NVFP4 ? sizeof(float) : 0;
   return b;
 }
@@ -303,45 +306,11 @@ moe_status moe_layer_cached(moe_expert_cache* cache, int32_t T, const uint16_t* 
   SlotMap map;
   for (int e = 0; e < cfg.n_routed_experts; ++e) map.slot[e] = cache->policy.slot_of(e);
   if (launch_remap_ids(ids, w.cache_ids, P, map, stream) != hipSuccess) return MOE_ERR_HIP;
-  PermuteArgs pa{w.cache_ids, w.offsets, w.sorted_token, w.inv_perm, w.active, w.n_active,
-                 T, K, S, w.phist};
-  if (launch_permute(pa, stream) != hipSuccess) return MOE_ERR_HIP;
-
   const ExpertSet rset = expert_set(cache->slots, cfg.moe_inter);
   const ExpertSet sset = has_shared ? expert_set(*shared, cfg.shared_inter) : ExpertSet{};
-  float* o_shared = has_shared ? w.O + (size_t)P * cfg.hidden : nullptr;
-  if (small) {
-    FfnArgs a{};
-    a.x = x;
-    a.T = T;
-    a.H = cfg.hidden;
-    a.K = K;
-    a.wfmt = cfg.wfmt;
-    a.ldh = ldh;
-    a.has_routed = true;
-    a.routed = rset;
-    a.max_slots = std::min(S, P);
-    a.offsets = w.offsets;
-    a.sorted_token = w.sorted_token;
-    a.active = w.active;
-    a.n_active = w.n_active;
-    a.h_routed = w.h;
-    a.o_routed = w.O;
-    a.has_dense = has_shared;
-    a.dense = sset;
-    a.h_dense = w.h + (size_t)P * ldh;
-    a.o_dense = o_shared;
-    if (launch_ffn(a, stream) != hipSuccess) return MOE_ERR_HIP;
-  } else {
-    moe_config slot_cfg = cfg;
-    slot_cfg.n_routed_experts = S;
-    if (run_gemm_ffn(slot_cfg, T, x, w, true, rset, w.offsets, w.active, w.n_active,
-                     w.sorted_token, has_shared, sset, P, ldh, w.h, w.O, stream, nullptr) !=
-        hipSuccess)
-      return MOE_ERR_HIP;
-  }
-  CombineArgs ca{w.O, w.inv_perm, tw, o_shared, y, out_dtype == MOE_OUT_BF16, T, cfg.hidden, K};
-  if (launch_combine(ca, stream) != hipSuccess) return MOE_ERR_HIP;
+  if (run_ffn_combine(cfg, T, x, w, w.cache_ids, S, rset, has_shared, sset, tw, y,
+                      out_dtype == MOE_OUT_BF16, small, stream, nullptr) != hipSuccess)
+    return MOE_ERR_HIP;
   if (hipEventRecord(cache->ev_call, stream) != hipSuccess) return MOE_ERR_HIP;
   cache->call_recorded = true;
   return MOE_OK;

@@ -101,6 +101,41 @@ __device__ __forceinline__ half8 dequant_word(uint32_t w, uint32_t scale2) {
   return r;
 }
 
+// Per-row-scale formats: the 8 inputs of one K step of one row -> fp16 A
+// operand, exact integers q (the row scale multiplies the accumulator in the
+// epilogue).  w: the lane's code words of the K block; ks: the K step.
+//   int4: word ks, 1024 + u (or 1024 + 16 u), then u - 8 as for int4 g32;
+//   int8: words 2 ks, 2 ks + 1, sign bits flipped (u = q + 128), bytes into
+//         the mantissa of fp16 1024 (1024 + u), minus 1152;
+//   int2: half (ks & 1) of word ks / 2, pairs into the mantissa of fp16 1024
+//         (1024 + u), minus 1026.
+template <int FMT>
+__device__ __forceinline__ half8 dequant_row(const uint32_t* w, int ks) {
+  uint32_t p[4];
+  if constexpr (FMT == MOE_WFMT_INT4_ROW_F32) {
+    const uint32_t x = w[ks], x8 = x >> 8;
+    p[0] = pk_add_f16(and_or(x, 0x000F000Fu, 0x64006400u), 0xE408E408u);
+    p[1] = pk_fma_f16(and_or(x, 0x00F000F0u, 0x64006400u), 0x2C002C00u, 0xD480D480u);
+    p[2] = pk_add_f16(and_or(x8, 0x000F000Fu, 0x64006400u), 0xE408E408u);
+    p[3] = pk_fma_f16(and_or(x8, 0x00F000F0u, 0x64006400u), 0x2C002C00u, 0xD480D480u);
+  } else if constexpr (FMT == MOE_WFMT_INT8_ROW_F32) {
+    const uint32_t a = w[2 * ks] ^ 0x80808080u, b = w[2 * ks + 1] ^ 0x80808080u;
+    p[0] = pk_add_f16(__builtin_amdgcn_perm(0x64646464u, a, 0x04010400u), 0xE480E480u);
+    p[1] = pk_add_f16(__builtin_amdgcn_perm(0x64646464u, a, 0x04030402u), 0xE480E480u);
+    p[2] = pk_add_f16(__builtin_amdgcn_perm(0x64646464u, b, 0x04010400u), 0xE480E480u);
+    p[3] = pk_add_f16(__builtin_amdgcn_perm(0x64646464u, b, 0x04030402u), 0xE480E480u);
+  } else {
+    const uint32_t x = w[ks >> 1] >> (8 * (ks & 1));
+    p[0] = pk_add_f16(and_or(x, 0x00030003u, 0x64006400u), 0xE402E402u);
+    p[1] = pk_add_f16(and_or(x >> 2, 0x00030003u, 0x64006400u), 0xE402E402u);
+    p[2] = pk_add_f16(and_or(x >> 4, 0x00030003u, 0x64006400u), 0xE402E402u);
+    p[3] = pk_add_f16(and_or(x >> 6, 0x00030003u, 0x64006400u), 0xE402E402u);
+  }
+  half8 r;
+  __builtin_memcpy(&r, p, 16);
+  return r;
+}
+
 struct Unit {
   int e;        // expert index in its weight set (0 for the shared expert)
   int p0;       // first row of the unit in the h / O buffers
@@ -218,14 +253,26 @@ __device__ __forceinline__ int xcd_item(int L, int total) {
 // Otherwise (ragged K) each lane loads its own 2 bytes per block.
 constexpr int kSclBytesPerWave = 3 * 2 * 1024;   // three super-blocks x two 1 KB copies
 
+// int8 codes take twice the ring registers: its thin units run one
+// workgroup per CU, which leaves them the registers they need unspilled.
+template <int FMT, int BM>
+constexpr int gemm_wgs_per_cu() {
+  return BM == kBMThin && FMT != MOE_WFMT_INT8_ROW_F32 ? QMOE_THIN_WGS : 1;
+}
+
 template <int FMT, int PROJ, int BM, int NS, bool SL>
-__global__ void __launch_bounds__(256, BM == kBMThin ? QMOE_THIN_WGS : 1) moe_gemm_kernel(GemmArgs g) {
+__global__ void __launch_bounds__(256, (gemm_wgs_per_cu<FMT, BM>())) moe_gemm_kernel(GemmArgs g) {
   constexpr int RT = kRT;
   constexpr int NA = act_loads<BM>();
+  constexpr bool ROW = wfmt_row(FMT);
+  constexpr int BITS = wfmt_bits(FMT);
+  constexpr int WPL = BITS;                  // code words per lane per K block (32 inputs)
+  constexpr int CL = BITS == 8 ? 2 : 1;      // code loads per row tile per K block
   static_assert(NS == 4, "the scale copies ride on K blocks 0 and 2 of each group of four");
+  static_assert(!(ROW && SL), "per-row scales are read in the epilogue");
   // vector memory ops per thread issued for K blocks kb + 2 and kb + 3: all
   // that may still be in flight once block kb + 1 has landed
-  constexpr int WAITN = 2 * (NA + RT) + (SL ? 1 : 2 * RT);
+  constexpr int WAITN = 2 * (NA + RT * CL + (SL || ROW ? 0 : RT)) + (SL ? 1 : 0);
   __shared__ __attribute__((aligned(16))) uint16_t xs[NS][BM * kBK];
   __shared__ __attribute__((aligned(16))) uint8_t scl[SL ? 4 * kSclBytesPerWave : 16];
   const int lane = threadIdx.x & 63;
@@ -247,9 +294,9 @@ __global__ void __launch_bounds__(256, BM == kBMThin ? QMOE_THIN_WGS : 1) moe_ge
   // first output row of this wave (gate/up: row pairs)
   const int wrow = PROJ == 0 ? nt * kGateUpPairs + wv * 32 : nt * kDownRows + wv * 64;
   if (nt * (PROJ == 0 ? kGateUpPairs : kDownRows) >= nrow_out) return;
-  const uint32_t rowBytes = (uint32_t)K / 2;
+  const uint32_t rowBytes = (uint32_t)K * BITS / 8;
   const int sgpr = FMT == MOE_WFMT_INT4_G32_F16 ? 32 : 16;   // inputs per scale
-  const uint32_t scaleRowBytes = (uint32_t)(K / sgpr) * (FMT == MOE_WFMT_INT4_G32_F16 ? 2 : 1);
+  const uint32_t scaleRowBytes = ROW ? 4u : (uint32_t)(K / sgpr) * (FMT == MOE_WFMT_INT4_G32_F16 ? 2 : 1);
 
   // One buffer per projection over this expert's whole matrix (codes and
   // scales); rows past the end read as zero through the range check.
@@ -282,7 +329,7 @@ __global__ void __launch_bounds__(256, BM == kBMThin ? QMOE_THIN_WGS : 1) moe_ge
   uint32_t qoff[RT], soff[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    qoff[rt] = (uint32_t)(rbase[rt] + lrow) * rowBytes + (uint32_t)lq * 16u;
+    qoff[rt] = (uint32_t)(rbase[rt] + lrow) * rowBytes + (uint32_t)lq * (4u * WPL);
     soff[rt] = (uint32_t)(rbase[rt] + lrow) * scaleRowBytes + (uint32_t)lq * 2u;   // !SL
   }
   // SL: copy q (0, 1) of a super-block holds 32 rows x 32 bytes; lane l
@@ -303,7 +350,7 @@ __global__ void __launch_bounds__(256, BM == kBMThin ? QMOE_THIN_WGS : 1) moe_ge
     const int j = PROJ == 0 ? q : 0;
     lds_copy16(sb[j], sclw + (sbk % 3) * 2048 + q * 1024, scopy[q] + (uint32_t)sbk * 32u);
   };
-  uint32_t wcode[NS][RT][4], wsc[NS][RT];
+  uint32_t wcode[NS][RT][WPL], wsc[NS][RT];
   const rsrc_t ar = PROJ == 0 ? make_rsrc(g.x16, (uint32_t)g.T * (uint32_t)g.ldx * 2u)
                               : make_rsrc(g.hin, (uint32_t)(g.P + g.T) * (uint32_t)g.ldh * 2u);
   uint32_t arow[NA];
@@ -317,8 +364,15 @@ __global__ void __launch_bounds__(256, BM == kBMThin ? QMOE_THIN_WGS : 1) moe_ge
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       const int j = PROJ == 0 ? rt >> 1 : 0;
-      bload16(wcode[st][rt], qb[j], qoff[rt] + (uint32_t)kb * 64u, 0);
-      if constexpr (!SL) wsc[st][rt] = bload_u16(sb[j], soff[rt] + (uint32_t)kb * 8u, 0);
+      const uint32_t kq = qoff[rt] + (uint32_t)kb * (16u * WPL);
+      if constexpr (BITS == 2) {
+        bload8(wcode[st][rt], qb[j], kq, 0);
+      } else {
+#pragma unroll
+        for (int h = 0; h < CL; ++h)
+          bload16(*reinterpret_cast<uint32_t(*)[4]>(&wcode[st][rt][4 * h]), qb[j], kq + 16u * h, 0);
+      }
+      if constexpr (!SL && !ROW) wsc[st][rt] = bload_u16(sb[j], soff[rt] + (uint32_t)kb * 8u, 0);
     }
     if constexpr (SL && (st & 1) == 0) copy_scales(st >> 1, (kb >> 2) + 1);
   };
@@ -337,6 +391,10 @@ __global__ void __launch_bounds__(256, BM == kBMThin ? QMOE_THIN_WGS : 1) moe_ge
     constexpr int st = decltype(S)::value;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
+      if constexpr (ROW) {
+        A[rt] = dequant_row<FMT>(wcode[st][rt], ks);
+        continue;
+      }
       uint32_t s2;
       const uint32_t sw = wsc[st][rt];
       if constexpr (FMT == MOE_WFMT_INT4_G32_F16) {
@@ -347,7 +405,7 @@ __global__ void __launch_bounds__(256, BM == kBMThin ? QMOE_THIN_WGS : 1) moe_ge
         const uint32_t b = __builtin_bit_cast(uint16_t, sh);
         s2 = b * 0x00010001u;
       }
-      A[rt] = dequant_word<FMT>(wcode[st][rt][ks], s2);
+      A[rt] = dequant_word<FMT == MOE_WFMT_NVFP4 ? FMT : MOE_WFMT_INT4_G32_F16>(wcode[st][rt][ks], s2);
     }
   };
 
@@ -427,6 +485,22 @@ __global__ void __launch_bounds__(256, BM == kBMThin ? QMOE_THIN_WGS : 1) moe_ge
       });
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
+    // per-row formats: the scales of this lane's four rows of each tile
+    // (rows past the matrix read zeros through the range check)
+    float rsc[RT][4];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      if constexpr (ROW) {
+        uint32_t v[4];
+        bload16(v, sb[PROJ == 0 ? rt >> 1 : 0], (uint32_t)(rbase[rt] + 4 * lq) * 4u, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rsc[rt][i] = __uint_as_float(v[i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rsc[rt][i] = gsc[PROJ == 0 ? rt >> 1 : 0];
+      }
+    }
+
     // epilogue
 #pragma unroll
     for (int c = 0; c < CT; ++c) {
@@ -439,8 +513,9 @@ __global__ void __launch_bounds__(256, BM == kBMThin ? QMOE_THIN_WGS : 1) moe_ge
           uint32_t packed[2];
 #pragma unroll
           for (int i = 0; i < 4; i += 2) {
-            const float h0 = silu_mul(acc[rt][c][i] * gsc[0], acc[rt + 2][c][i] * gsc[1]);
-            const float h1 = silu_mul(acc[rt][c][i + 1] * gsc[0], acc[rt + 2][c][i + 1] * gsc[1]);
+            const float h0 = silu_mul(acc[rt][c][i] * rsc[rt][i], acc[rt + 2][c][i] * rsc[rt + 2][i]);
+            const float h1 = silu_mul(acc[rt][c][i + 1] * rsc[rt][i + 1],
+                                      acc[rt + 2][c][i + 1] * rsc[rt + 2][i + 1]);
             const _Float16 a0 = (_Float16)h0, a1 = (_Float16)h1;
             packed[i / 2] = (uint32_t)__builtin_bit_cast(uint16_t, a0) |
                             ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
@@ -460,10 +535,10 @@ __global__ void __launch_bounds__(256, BM == kBMThin ? QMOE_THIN_WGS : 1) moe_ge
           const int col = rbase[rt] + 4 * lq;
           if (col < g.H) {
             float4 o;
-            o.x = acc[rt][c][0] * gsc[0];
-            o.y = acc[rt][c][1] * gsc[0];
-            o.z = acc[rt][c][2] * gsc[0];
-            o.w = acc[rt][c][3] * gsc[0];
+            o.x = acc[rt][c][0] * rsc[rt][0];
+            o.y = acc[rt][c][1] * rsc[rt][1];
+            o.z = acc[rt][c][2] * rsc[rt][2];
+            o.w = acc[rt][c][3] * rsc[rt][3];
             *reinterpret_cast<float4*>(g.o_out + (size_t)orow * g.H + col) = o;
           }
         }
@@ -655,19 +730,18 @@ hipError_t launch_gemm_kernel(const GemmArgs& g, long units, int nt, hipStream_t
   else
     sdw = g.routed.inter % 512 == 0 && (!g.has_shared || g.shared.inter % 512 == 0);
   sdw = sdw && BM == kBMThin;
-  if (g.wfmt == MOE_WFMT_NVFP4) {
-    if (sdw)
-      hipLaunchKernelGGL((moe_gemm_kernel<MOE_WFMT_NVFP4, PROJ, BM, NS, true>), grid, dim3(256), 0, s, g);
-    else
-      hipLaunchKernelGGL((moe_gemm_kernel<MOE_WFMT_NVFP4, PROJ, BM, NS, false>), grid, dim3(256), 0, s, g);
-  } else {
-    if (sdw)
-      hipLaunchKernelGGL((moe_gemm_kernel<MOE_WFMT_INT4_G32_F16, PROJ, BM, NS, true>), grid, dim3(256),
-                         0, s, g);
-    else
-      hipLaunchKernelGGL((moe_gemm_kernel<MOE_WFMT_INT4_G32_F16, PROJ, BM, NS, false>), grid,
-                         dim3(256), 0, s, g);
-  }
+  dispatch_wfmt(g.wfmt, [&](auto F) {
+    constexpr int fmt = decltype(F)::value;
+    if constexpr (wfmt_row(fmt)) {   // no per-block scales to copy
+      hipLaunchKernelGGL((moe_gemm_kernel<fmt, PROJ, BM, NS, false>), grid, dim3(256), 0, s, g);
+    } else {
+      if (sdw)
+        hipLaunchKernelGGL((moe_gemm_kernel<fmt, PROJ, BM, NS, true>), grid, dim3(256), 0, s, g);
+      else
+        hipLaunchKernelGGL((moe_gemm_kernel<fmt, PROJ, BM, NS, false>), grid, dim3(256), 0, s, g);
+    }
+    return 0;
+  });
   return hipGetLastError();
 }
 

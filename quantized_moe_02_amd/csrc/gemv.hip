@@ -115,6 +115,96 @@ __device__ __forceinline__ uint32_t load_scale(const void* s, size_t row, int nG
   }
 }
 
+// Per-row-scale formats: one 32-input group of one row (BITS 32-bit code
+// words) against kTB activation groups, without the row scale (applied once
+// per row after the reduction).  acc[tb] += sum_k q_k * act_k.
+//   int4: 1 + u/16 pairs, sum (u-8) a = 16 (d - 1.5 A)
+//   int2: 1 + u/4 pairs,  sum (u-2) a = 4 (d - 1.5 A)
+//   int8: u = q + 128; bf16 activations: fp32 products, sum q a = d - 128 A;
+//         fp16 activations: 1024 + u pairs, sum q a = d - 1152 A
+// with d the dot product of the formed values and A the activation sum.
+template <int FMT, bool F16ACT>
+__device__ __forceinline__ void group_dot_row(const uint32_t* wq, const uint32_t (&act)[kTB][16],
+                                              const float (&asum)[kTB], float (&acc)[kTB]) {
+  if constexpr (FMT == MOE_WFMT_INT8_ROW_F32 && !F16ACT) {
+    float d[kTB];
+#pragma unroll
+    for (int tb = 0; tb < kTB; ++tb) d[tb] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t w = wq[j] ^ 0x80808080u;
+      float u[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) u[b] = (float)((w >> (8 * b)) & 0xffu);
+#pragma unroll
+      for (int tb = 0; tb < kTB; ++tb) {
+        const uint32_t x01 = act[tb][2 * j], x23 = act[tb][2 * j + 1];
+        d[tb] = fmaf(u[0], __uint_as_float(x01 << 16), d[tb]);
+        d[tb] = fmaf(u[1], __uint_as_float(x01 & 0xffff0000u), d[tb]);
+        d[tb] = fmaf(u[2], __uint_as_float(x23 << 16), d[tb]);
+        d[tb] = fmaf(u[3], __uint_as_float(x23 & 0xffff0000u), d[tb]);
+      }
+    }
+#pragma unroll
+    for (int tb = 0; tb < kTB; ++tb) acc[tb] += fmaf(-128.0f, asum[tb], d[tb]);
+  } else {
+    uint32_t p[16];
+    float mul, off;
+    if constexpr (FMT == MOE_WFMT_INT8_ROW_F32) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t w = wq[j] ^ 0x80808080u;
+        p[2 * j] = int8_pair_f16(w, 0x04010400u);
+        p[2 * j + 1] = int8_pair_f16(w, 0x04030402u);
+      }
+      mul = 1.0f;
+      off = -1152.0f;
+    } else if constexpr (FMT == MOE_WFMT_INT2_ROW_F32) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          p[8 * j + k] = F16ACT ? int2_pair_f16(wq[j], k, 0x3C003C00u) : int2_pair_bf16(wq[j], k, 0x3F803F80u);
+      mul = 4.0f;
+      off = -1.5f;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          p[4 * j + k] = F16ACT ? int4_pair_f16(wq[j], k) : int4_pair_bf16(wq[j], k);
+      mul = 16.0f;
+      off = -1.5f;
+    }
+#pragma unroll
+    for (int tb = 0; tb < kTB; ++tb) {
+      float d = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) d = F16ACT ? dot2_f16(p[i], act[tb][i], d) : dot2_bf16(p[i], act[tb][i], d);
+      acc[tb] = fmaf(mul, fmaf(off, asum[tb], d), acc[tb]);
+    }
+  }
+}
+
+// The code words of one 32-input group: 32 * bits / 8 bytes at p.
+template <int FMT>
+__device__ __forceinline__ void load_codes(uint32_t* dst, const uint8_t* p) {
+  constexpr int BITS = wfmt_bits(FMT);
+  if constexpr (BITS == 2) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    dst[0] = v.x;
+    dst[1] = v.y;
+  } else {
+#pragma unroll
+    for (int i = 0; i < BITS / 4; ++i) load16(dst + 4 * i, p + 16 * i);
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ float row_scale(const void* s, size_t row) {
+  return wfmt_row(FMT) ? reinterpret_cast<const float*>(s)[row] : 1.0f;
+}
+
 template <int FMT>
 __global__ void __launch_bounds__(256) gateup_gemv_kernel(FfnArgs a) {
   const int lane = threadIdx.x & 63;
@@ -127,7 +217,9 @@ __global__ void __launch_bounds__(256) gateup_gemv_kernel(FfnArgs a) {
   if (row0 >= inter) return;
   const int H = a.H;
   const int nG = H / 32;
-  const size_t rowBytes = (size_t)H / 2;
+  constexpr int BITS = wfmt_bits(FMT);
+  constexpr bool ROW = wfmt_row(FMT);
+  const size_t rowBytes = (size_t)H * BITS / 8;
   const size_t rbase = (size_t)sl.e * inter;
   const float gg = (FMT == MOE_WFMT_NVFP4) ? X.gate.g[sl.e] : 1.0f;
   const float gu = (FMT == MOE_WFMT_NVFP4) ? X.up.g[sl.e] : 1.0f;
@@ -152,7 +244,7 @@ __global__ void __launch_bounds__(256) gateup_gemv_kernel(FfnArgs a) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) load16(&xw[tb][4 * q], xp + 8 * q);
         float s = 0.0f;
-        if constexpr (FMT == MOE_WFMT_INT4_G32_F16) {
+        if constexpr (FMT != MOE_WFMT_NVFP4) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) s = dot2_bf16(xw[tb][i], 0x3F803F80u, s);
         }
@@ -161,19 +253,30 @@ __global__ void __launch_bounds__(256) gateup_gemv_kernel(FfnArgs a) {
 #pragma unroll
       for (int r = 0; r < kRPW; ++r) {
         const size_t row = rbase + row0 + r;
-        uint32_t wq[4];
-        load16(wq, X.gate.q + row * rowBytes + (size_t)c * 16);
-        group_dot<FMT, false>(wq, load_scale<FMT>(X.gate.s, row, nG, c), xw, xs, gg, ag[r]);
-        load16(wq, X.up.q + row * rowBytes + (size_t)c * 16);
-        group_dot<FMT, false>(wq, load_scale<FMT>(X.up.s, row, nG, c), xw, xs, gu, au[r]);
+        uint32_t wq[BITS];
+        load_codes<FMT>(wq, X.gate.q + row * rowBytes + (size_t)c * (4 * BITS));
+        if constexpr (ROW) {
+          group_dot_row<FMT, false>(wq, xw, xs, ag[r]);
+        } else {
+          group_dot<FMT, false>(*reinterpret_cast<const uint32_t(*)[4]>(wq),
+                                load_scale<FMT>(X.gate.s, row, nG, c), xw, xs, gg, ag[r]);
+        }
+        load_codes<FMT>(wq, X.up.q + row * rowBytes + (size_t)c * (4 * BITS));
+        if constexpr (ROW) {
+          group_dot_row<FMT, false>(wq, xw, xs, au[r]);
+        } else {
+          group_dot<FMT, false>(*reinterpret_cast<const uint32_t(*)[4]>(wq),
+                                load_scale<FMT>(X.up.s, row, nG, c), xw, xs, gu, au[r]);
+        }
       }
     }
 #pragma unroll
     for (int r = 0; r < kRPW; ++r)
 #pragma unroll
       for (int tb = 0; tb < kTB; ++tb) {
-        const float g = wave_sum(ag[r][tb]);
-        const float u = wave_sum(au[r][tb]);
+        const size_t row = rbase + row0 + r;
+        const float g = wave_sum(ag[r][tb]) * row_scale<FMT>(X.gate.s, row);
+        const float u = wave_sum(au[r][tb]) * row_scale<FMT>(X.up.s, row);
         if (lane == r * kTB + tb && m0 + tb < sl.M) {
           const _Float16 hv = (_Float16)silu_mul(g, u);
           hbase[(size_t)(m0 + tb) * a.ldh + row0 + r] = __builtin_bit_cast(uint16_t, hv);
@@ -194,7 +297,9 @@ __global__ void __launch_bounds__(256) down_gemv_kernel(FfnArgs a) {
   const int row0 = blockIdx.x * kRowsPerBlock + wv * kRPW;
   if (row0 >= H) return;
   const int nG = inter / 32;
-  const size_t rowBytes = (size_t)inter / 2;
+  constexpr int BITS = wfmt_bits(FMT);
+  constexpr bool ROW = wfmt_row(FMT);
+  const size_t rowBytes = (size_t)inter * BITS / 8;
   const size_t rbase = (size_t)sl.e * H;
   const float gd = (FMT == MOE_WFMT_NVFP4) ? X.down.g[sl.e] : 1.0f;
   const uint16_t* hbase = sl.routed ? a.h_routed + (size_t)sl.tok_begin * a.ldh : a.h_dense;
@@ -218,7 +323,7 @@ __global__ void __launch_bounds__(256) down_gemv_kernel(FfnArgs a) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) load16(&hw[tb][4 * q], hp + 8 * q);
         float s = 0.0f;
-        if constexpr (FMT == MOE_WFMT_INT4_G32_F16) {
+        if constexpr (FMT != MOE_WFMT_NVFP4) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) s = dot2_f16(hw[tb][i], 0x3C003C00u, s);
         }
@@ -227,16 +332,21 @@ __global__ void __launch_bounds__(256) down_gemv_kernel(FfnArgs a) {
 #pragma unroll
       for (int r = 0; r < kRPW; ++r) {
         const size_t row = rbase + row0 + r;
-        uint32_t wq[4];
-        load16(wq, X.down.q + row * rowBytes + (size_t)c * 16);
-        group_dot<FMT, true>(wq, load_scale<FMT>(X.down.s, row, nG, c), hw, hs, gd, acc[r]);
+        uint32_t wq[BITS];
+        load_codes<FMT>(wq, X.down.q + row * rowBytes + (size_t)c * (4 * BITS));
+        if constexpr (ROW) {
+          group_dot_row<FMT, true>(wq, hw, hs, acc[r]);
+        } else {
+          group_dot<FMT, true>(*reinterpret_cast<const uint32_t(*)[4]>(wq),
+                               load_scale<FMT>(X.down.s, row, nG, c), hw, hs, gd, acc[r]);
+        }
       }
     }
 #pragma unroll
     for (int r = 0; r < kRPW; ++r)
 #pragma unroll
       for (int tb = 0; tb < kTB; ++tb) {
-        const float v = wave_sum(acc[r][tb]);
+        const float v = wave_sum(acc[r][tb]) * row_scale<FMT>(X.down.s, rbase + row0 + r);
         if (lane == r * kTB + tb && m0 + tb < sl.M) obase[(size_t)(m0 + tb) * H + row0 + r] = v;
       }
   }
@@ -299,17 +409,19 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, Tracer* tr) {
   dim3 g1((max_inter + kRowsPerBlock - 1) / kRowsPerBlock, slots);
   dim3 g2((a.H + kRowsPerBlock - 1) / kRowsPerBlock, slots);
   hipError_t e;
-  if (a.wfmt == MOE_WFMT_INT4_G32_F16)
-    hipLaunchKernelGGL(gateup_gemv_kernel<MOE_WFMT_INT4_G32_F16>, g1, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(gateup_gemv_kernel<MOE_WFMT_NVFP4>, g1, dim3(256), 0, s, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  auto launch = [&](auto F) {
+    constexpr int fmt = decltype(F)::value;
+    hipLaunchKernelGGL(gateup_gemv_kernel<fmt>, g1, dim3(256), 0, s, a);
+    return hipGetLastError();
+  };
+  auto launch_down = [&](auto F) {
+    constexpr int fmt = decltype(F)::value;
+    hipLaunchKernelGGL(down_gemv_kernel<fmt>, g2, dim3(256), 0, s, a);
+    return hipGetLastError();
+  };
+  if ((e = dispatch_wfmt(a.wfmt, launch)) != hipSuccess) return e;
   if (tr && (e = tr->mark("gateup_gemv")) != hipSuccess) return e;
-  if (a.wfmt == MOE_WFMT_INT4_G32_F16)
-    hipLaunchKernelGGL(down_gemv_kernel<MOE_WFMT_INT4_G32_F16>, g2, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(down_gemv_kernel<MOE_WFMT_NVFP4>, g2, dim3(256), 0, s, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = dispatch_wfmt(a.wfmt, launch_down)) != hipSuccess) return e;
   if (tr && (e = tr->mark("down_gemv")) != hipSuccess) return e;
   return hipSuccess;
 }

@@ -34,7 +34,8 @@ moe_status check_cfg(const moe_config* c) {
   if (c->top_k < 1 || c->top_k > allowed) return MOE_ERR_INVALID_ARG;
   if (!std::isfinite(c->routed_scaling_factor) || !(c->routed_scaling_factor > 0.0f))
     return MOE_ERR_INVALID_ARG;
-  if (c->wfmt != MOE_WFMT_INT4_G32_F16 && c->wfmt != MOE_WFMT_NVFP4) return MOE_ERR_INVALID_ARG;
+  if (c->wfmt != MOE_WFMT_INT4_G32_F16 && c->wfmt != MOE_WFMT_NVFP4 && !wfmt_row(c->wfmt))
+    return MOE_ERR_INVALID_ARG;
   if (c->options & ~(MOE_OPT_NO_GRID_WAIT | MOE_OPT_GRID_WAIT_NONE)) return MOE_ERR_INVALID_ARG;
   if (!(c->expert_top_p >= 0.0f && c->expert_top_p <= 1.0f)) return MOE_ERR_INVALID_ARG;   // NaN too
   // kernel limits
@@ -123,6 +124,51 @@ hipError_t run_gemm_ffn(const moe_config& c, int T, const uint16_t* x, const Wor
   g.P = P;
   g.wfmt = c.wfmt;
   return launch_gemm(g, K, E, stream, tr);
+}
+
+hipError_t run_ffn_combine(const moe_config& c, int T, const uint16_t* x, const Workspace& w,
+                           const int32_t* picks, int n_experts, const ExpertSet& routed,
+                           bool has_shared, const ExpertSet& shared, const float* tw, void* y,
+                           bool out_bf16, bool gemv, hipStream_t stream, Tracer* tr) {
+  hipError_t e;
+  const int K = c.top_k, P = T * K;
+  const int ldh = pad_k(std::max(c.moe_inter, has_shared ? c.shared_inter : 0));
+  PermuteArgs pa{picks, w.offsets, w.sorted_token, w.inv_perm, w.active, w.n_active,
+                 T, K, n_experts, w.phist};
+  if ((e = launch_permute(pa, stream, tr)) != hipSuccess) return e;
+  float* o_shared = has_shared ? w.O + (size_t)P * c.hidden : nullptr;
+  if (gemv) {
+    FfnArgs a{};
+    a.x = x;
+    a.T = T;
+    a.H = c.hidden;
+    a.K = K;
+    a.wfmt = c.wfmt;
+    a.ldh = ldh;
+    a.has_routed = true;
+    a.routed = routed;
+    a.max_slots = std::min(n_experts, P);
+    a.offsets = w.offsets;
+    a.sorted_token = w.sorted_token;
+    a.active = w.active;
+    a.n_active = w.n_active;
+    a.h_routed = w.h;
+    a.o_routed = w.O;
+    a.has_dense = has_shared;
+    a.dense = shared;
+    a.h_dense = w.h + (size_t)P * ldh;
+    a.o_dense = o_shared;
+    if ((e = launch_ffn(a, stream, tr)) != hipSuccess) return e;
+  } else {
+    moe_config ce = c;
+    ce.n_routed_experts = n_experts;
+    if ((e = run_gemm_ffn(ce, T, x, w, true, routed, w.offsets, w.active, w.n_active,
+                          w.sorted_token, has_shared, shared, P, ldh, w.h, w.O, stream, tr)) !=
+        hipSuccess)
+      return e;
+  }
+  CombineArgs ca{w.O, w.inv_perm, tw, o_shared, y, out_bf16, T, c.hidden, K};
+  return launch_combine(ca, stream, tr);
 }
 
 Workspace carve_workspace(const moe_config& c, int T, void* base) {
@@ -376,8 +422,11 @@ moe_status layer_impl(const moe_config* cfg, int32_t T, const uint16_t* x, const
   const bool has_shared = cfg->n_shared_experts == 1;
   const int ldh = pad_k(std::max(cfg->moe_inter, has_shared ? cfg->shared_inter : 0));
   const size_t P = (size_t)T * cfg->top_k;
-  const bool small = T <= kDecodeMaxTokens && decode_supported(cfg->hidden);
-  if (!small && !gemm_fits(T, (int64_t)P + (has_shared ? T : 0), pad_k(cfg->hidden), ldh))
+  // the single-token and small-batch kernels take the group-scaled formats;
+  // small batches in the per-row formats take the grouped GEMV
+  const bool small = T <= kDecodeMaxTokens && decode_supported(cfg->hidden) && !wfmt_row(cfg->wfmt);
+  const bool gemv = T <= kDecodeMaxTokens && wfmt_row(cfg->wfmt);
+  if (!small && !gemv && !gemm_fits(T, (int64_t)P + (has_shared ? T : 0), pad_k(cfg->hidden), ldh))
     return MOE_ERR_UNSUPPORTED;
 
   const Workspace w = carve_workspace(*cfg, T, ws);
@@ -431,19 +480,10 @@ moe_status layer_impl(const moe_config* cfg, int32_t T, const uint16_t* x, const
                cfg->n_group, cfg->topk_group, cfg->top_k, cfg->routed_scaling_factor, w.flags,
                cfg->expert_top_p};
   if ((e = launch_route(ra, stream, tr)) != hipSuccess) return MOE_ERR_HIP;
-  PermuteArgs pa{ids, w.offsets, w.sorted_token, w.inv_perm, w.active, w.n_active,
-                 T, cfg->top_k, cfg->n_routed_experts, w.phist};
-  if ((e = launch_permute(pa, stream, tr)) != hipSuccess) return MOE_ERR_HIP;
-
   const ExpertSet rset = expert_set(*routed, cfg->moe_inter);
   const ExpertSet sset = has_shared ? expert_set(*shared, cfg->shared_inter) : ExpertSet{};
-  if ((e = run_gemm_ffn(*cfg, T, x, w, true, rset, w.offsets, w.active, w.n_active,
-                        w.sorted_token, has_shared, sset, (int)P, ldh, w.h, w.O, stream, tr)) !=
-      hipSuccess)
-    return MOE_ERR_HIP;
-  CombineArgs ca{w.O, w.inv_perm, tw, has_shared ? w.O + P * cfg->hidden : nullptr, y,
-                 out_dtype == MOE_OUT_BF16, T, cfg->hidden, cfg->top_k};
-  return hip_status(launch_combine(ca, stream, tr));
+  return hip_status(run_ffn_combine(*cfg, T, x, w, ids, cfg->n_routed_experts, rset, has_shared,
+                                    sset, tw, y, out_dtype == MOE_OUT_BF16, gemv, stream, tr));
 }
 
 }  // namespace

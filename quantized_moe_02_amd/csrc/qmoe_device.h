@@ -67,6 +67,25 @@ __device__ __forceinline__ uint32_t int4_pair_f16(uint32_t w, int k, uint32_t on
   const uint32_t s = (k == 0) ? (w << 6) : (k == 1) ? (w << 2) : (w >> (4 * k - 6));
   return and_or(s, 0x03C003C0u, one);
 }
+// int2 codes (word layout of MOE_WFMT_INT2_ROW_F32: pair k = inputs 2k, 2k+1
+// of the word's 16 in bits [2k, 2k+2) and [16+2k, 16+2k+2)) into the top two
+// mantissa bits of a 16-bit float of exponent 1.0: 1 + u/4 exactly.
+__device__ __forceinline__ uint32_t int2_pair_bf16(uint32_t w, int k, uint32_t one) {
+  // bf16: code goes to bits [5,7) of each half
+  const uint32_t s = (k <= 2) ? (w << (5 - 2 * k)) : (w >> (2 * k - 5));
+  return and_or(s, 0x00600060u, one);
+}
+__device__ __forceinline__ uint32_t int2_pair_f16(uint32_t w, int k, uint32_t one) {
+  // fp16: code goes to bits [8,10) of each half
+  const uint32_t s = (k <= 4) ? (w << (8 - 2 * k)) : (w >> (2 * k - 8));
+  return and_or(s, 0x03000300u, one);
+}
+// int8 bytes b0, b1 (selector 0x04010400) or b2, b3 (0x04030402) of a word
+// whose sign bits were flipped (u = q + 128) into the mantissa of fp16 1024:
+// 1024 + u exactly.
+__device__ __forceinline__ uint32_t int8_pair_f16(uint32_t wflip, uint32_t sel) {
+  return __builtin_amdgcn_perm(0x64646464u, wflip, sel);
+}
 __device__ __forceinline__ uint32_t int4_pair_bf16(uint32_t w, int k) {
   return int4_pair_bf16(w, k, 0x3F803F80u);
 }
@@ -133,6 +152,11 @@ __device__ __forceinline__ uint4 bload16_device(rsrc_t r, uint32_t voff, uint32_
   constexpr int kSc1 = 16;   // cache-policy bit of device (agent) scope
   const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kSc1);
   return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void bload8(uint32_t* d, rsrc_t r, uint32_t voff, uint32_t soff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+  d[0] = v[0];
+  d[1] = v[1];
 }
 __device__ __forceinline__ uint32_t bload_u16(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);

@@ -7,9 +7,31 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <type_traits>
+
 #include "../../include/qmoe.h"
 
 namespace qmoe {
+
+// Per-row-scale weight formats: code bits, and whether a format is one.
+__host__ __device__ constexpr bool wfmt_row(int f) {
+  return f == MOE_WFMT_INT4_ROW_F32 || f == MOE_WFMT_INT8_ROW_F32 || f == MOE_WFMT_INT2_ROW_F32;
+}
+__host__ __device__ constexpr int wfmt_bits(int f) {
+  return f == MOE_WFMT_INT8_ROW_F32 ? 8 : f == MOE_WFMT_INT2_ROW_F32 ? 2 : 4;
+}
+
+// Calls f(std::integral_constant<int, fmt>{}) for the runtime format.
+template <class F>
+inline auto dispatch_wfmt(int wfmt, F&& f) {
+  switch (wfmt) {
+    case MOE_WFMT_NVFP4: return f(std::integral_constant<int, MOE_WFMT_NVFP4>{});
+    case MOE_WFMT_INT4_ROW_F32: return f(std::integral_constant<int, MOE_WFMT_INT4_ROW_F32>{});
+    case MOE_WFMT_INT8_ROW_F32: return f(std::integral_constant<int, MOE_WFMT_INT8_ROW_F32>{});
+    case MOE_WFMT_INT2_ROW_F32: return f(std::integral_constant<int, MOE_WFMT_INT2_ROW_F32>{});
+    default: return f(std::integral_constant<int, MOE_WFMT_INT4_G32_F16>{});
+  }
+}
 
 struct ProjPtr {
   const uint8_t* q;
@@ -246,6 +268,15 @@ hipError_t run_gemm_ffn(const moe_config& c, int T, const uint16_t* x, const Wor
                         const int32_t* active, const int32_t* n_active,
                         const int32_t* sorted_token, bool has_shared, const ExpertSet& shared,
                         int P, int ldh, uint16_t* h, float* o, hipStream_t stream, Tracer* tr);
+
+// The layer after routing: permutation of `picks` (ids in [0, n_experts) or
+// -1) over n_experts experts whose weights are `routed`, the expert FFNs
+// (grouped GEMV if `gemv`, else the grouped GEMM) with the shared expert, and
+// the weighted combine into y.
+hipError_t run_ffn_combine(const moe_config& c, int T, const uint16_t* x, const Workspace& w,
+                           const int32_t* picks, int n_experts, const ExpertSet& routed,
+                           bool has_shared, const ExpertSet& shared, const float* tw, void* y,
+                           bool out_bf16, bool gemv, hipStream_t stream, Tracer* tr);
 
 // Replaces each pick's expert id by its cache slot (map[id]); -1 stays -1.
 struct SlotMap {

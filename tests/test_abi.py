@@ -128,6 +128,11 @@ def test_layer_validation_paths():
     assert _layer(c0) == q.MOE_ERR_INVALID_ARG                                  # shared given but none configured
     cn = _cfg(wfmt="nvfp4")
     assert _layer(cn) == q.MOE_ERR_INVALID_ARG                                  # nvfp4 needs gscale
+    for fmt in ("int4_row", "int8_row", "int2_row"):                            # per-row formats:
+        cr = _cfg(wfmt=fmt)                                                     # no gscale
+        assert _size(cr, 8)[0] == q.MOE_OK
+        assert _layer(cr, routed=_experts(gs=FAKE.value)) == q.MOE_ERR_INVALID_ARG
+        assert _layer(cr, T=0, ws=None, ws_bytes=0) == q.MOE_OK
     # T == 0 is a valid no-op, even with no workspace
     assert _layer(c, T=0, ws=None, ws_bytes=0) == q.MOE_OK
 

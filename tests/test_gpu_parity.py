@@ -14,7 +14,7 @@ import oracle
 import quantized_moe_02_amd as q
 import synth
 from gpu_common import (TOL, FFNCache, check_outputs, check_routing, cover_tokens,
-                        expert_slots_to_check, qexp, run_layer)
+                        entry_point_chain, expert_slots_to_check, qexp, run_layer)
 from helpers import np_u16, oracle_inputs, row_rel_err
 
 pytestmark = pytest.mark.gpu
@@ -59,74 +59,6 @@ def test_tiny_bf16_output_is_rne_of_fp32(T):
     y32, _, _ = run_layer(L, q.MOE_OUT_F32, x=x)
     y16, _, _ = run_layer(L, q.MOE_OUT_BF16, x=x)
     assert torch.equal(y32.to(torch.bfloat16), y16)
-
-
-def entry_point_chain(L, T=None, x=None, pool=False):
-    """moe_route -> moe_permute -> moe_expert_ffn_q4 (routed, then dense on the
-    shared expert) -> moe_combine, each result against the oracle: ids exact,
-    permutation exact, expert outputs per sorted slot within TOL, combine
-    within 1e-6 of its own fp64 sum."""
-    g = L.geom
-    x = L.x if x is None else x
-    T = x.shape[0] if T is None else T
-    H, E, k = g["hidden"], g["n_routed_experts"], g["top_k"]
-    P = T * k
-    cfg = q.make_config(g, L.wfmt)
-    ws = q.workspace(cfg, T)
-    dev = dict(device="cuda")
-    ids = torch.empty(T, k, dtype=torch.int32, **dev)
-    tw = torch.empty(T, k, dtype=torch.float32, **dev)
-    q.moe_route(cfg, T, x, L.router_w, L.bias, ids, tw, ws)
-    torch.cuda.synchronize()
-    x_np = np_u16(x)
-    ids_g, _ = check_routing(L, ids, tw, x_np=x_np)
-
-    offs = torch.empty(E + 1, dtype=torch.int32, **dev)
-    st = torch.empty(P, dtype=torch.int32, **dev)
-    inv = torch.empty(P, dtype=torch.int32, **dev)
-    act = torch.empty(E, dtype=torch.int32, **dev)
-    na = torch.empty(1, dtype=torch.int32, **dev)
-    q.moe_permute(cfg, T, ids, offs, st, inv, act, na, ws)
-    torch.cuda.synchronize()
-    r_off, r_st, r_inv, r_act = oracle.permute(ids_g, E)
-    assert np.array_equal(offs.cpu().numpy(), r_off)
-    assert np.array_equal(st.cpu().numpy()[: len(r_st)], r_st)
-    assert np.array_equal(inv.cpu().numpy(), r_inv)
-    assert int(na.item()) == len(r_act)
-    assert np.array_equal(act.cpu().numpy()[: len(r_act)], r_act)
-
-    _, _, _, _, routed, shared = oracle_inputs(L, lazy=True)
-    X = oracle.bf16_bits_to_f64(x_np)
-    out = torch.empty(P, H, dtype=torch.float32, **dev)
-    q.moe_expert_ffn_q4(cfg, T, x, qexp(L.routed), offs, st, act, na, out, ws)
-    torch.cuda.synchronize()
-    jobs = [(routed, int(e), X[r_st[r_off[e]:r_off[e + 1]]]) for e in r_act]
-    jobs.append((shared, 0, X))
-    refs = FFNCache()(jobs) if pool else [oracle.expert_ffn(*j) for j in jobs]
-    Pk = int(r_off[-1])   # kept picks (all P unless the adaptive top-p dropped some)
-    ref = np.zeros((Pk, H))
-    for e, F in zip(r_act, refs):
-        ref[r_off[e]:r_off[e + 1]] = F
-    err = row_rel_err(out.cpu().numpy()[:Pk], ref)
-    assert err.max() <= TOL, (err.max(), int(err.argmax()))
-
-    outs = torch.empty(T, H, dtype=torch.float32, **dev)
-    q.moe_expert_ffn_q4(cfg, T, x, qexp(L.shared), None, None, None, None, outs, ws)
-    torch.cuda.synchronize()
-    assert row_rel_err(outs.cpu().numpy(), refs[-1]).max() <= TOL
-
-    y = torch.empty(T, H, dtype=torch.float32, **dev)
-    q.moe_combine(cfg, T, out, inv, tw, outs, y)
-    y16 = torch.empty(T, H, dtype=torch.bfloat16, **dev)
-    q.moe_combine(cfg, T, out, inv, tw, outs, y16, q.MOE_OUT_BF16)
-    torch.cuda.synchronize()
-    o64, s64 = out.double().cpu().numpy(), outs.double().cpu().numpy()
-    w64 = tw.double().cpu().numpy()
-    inv2 = r_inv.reshape(T, k)
-    yref = s64 + np.einsum("tk,tkh->th", np.where(inv2 >= 0, w64, 0.0), o64[np.maximum(inv2, 0)])
-    assert row_rel_err(y.cpu().numpy(), yref).max() <= 1e-6
-    assert torch.equal(y.to(torch.bfloat16), y16)
-    return err.max()
 
 
 def test_tiny_entry_points():
