@@ -30,7 +30,9 @@ METRIC = "MoE-layer tokens/s + weight-stream HBM GB/s (% peak); prefill MFMA uti
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_F16_TFLOPS = 2500.0       # MI355X dense fp16/bf16 MFMA
 ALL_WORKLOADS = ["decode", "verify4", "verify64", "prefill4k", "prefill16k", "nvfp4_512",
-                 "decode_topp", "verify64_topp", "decode_stream", "decode_stream_warm"]
+                 "decode_topp", "verify64_topp", "decode_stream", "decode_stream_warm",
+                 "decode_int4_row", "decode_int8_row", "decode_int2_row", "prefill4k_int4_row",
+                 "prefill4k_int8_row"]
 HEADLINE = "decode"
 # expert streaming from host memory: the decode layer with its 256 routed
 # experts in page-locked host RAM and this many HBM slots (moe_layer_cached)
@@ -527,7 +529,8 @@ def main():
         "metric": METRIC, "value": h["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
         "steps": h["steps"], "warmup": h["warmup"], "ms_per_step": h["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "int4*bf16->f32" if synth.WORKLOADS[base]["wfmt"] == "int4" else "fp4*bf16->f32",
+        "dtype": {"int4": "int4*bf16->f32", "nvfp4": "fp4*bf16->f32"}.get(
+            synth.WORKLOADS[base]["wfmt"], synth.WORKLOADS[base]["wfmt"] + "*bf16->f32"),
         "data": "synthetic",
         "config": {"workload": head, "tokens": h["tokens"], "hidden": geom["hidden"],
                    "moe_inter": geom["moe_inter"], "experts": geom["n_routed_experts"],

@@ -63,6 +63,12 @@ WORKLOADS: Dict[str, dict] = {
     "nvfp4_512":  dict(index=4, geom=_GLM,  tokens=512,   wfmt="nvfp4", bias="zipf"),
     "decode_topp":   dict(index=1, geom=_GLM_TOPP, tokens=1,  wfmt="int4", bias="zero"),
     "verify64_topp": dict(index=2, geom=_GLM_TOPP, tokens=64, wfmt="int4", bias="hot16"),
+    # the per-row-scale formats on the decode and prefill shapes
+    "decode_int4_row":    dict(index=1, geom=_GLM, tokens=1,    wfmt="int4_row", bias="zero"),
+    "decode_int8_row":    dict(index=1, geom=_GLM, tokens=1,    wfmt="int8_row", bias="zero"),
+    "decode_int2_row":    dict(index=1, geom=_GLM, tokens=1,    wfmt="int2_row", bias="zero"),
+    "prefill4k_int4_row": dict(index=3, geom=_GLM, tokens=4096, wfmt="int4_row", bias="zero"),
+    "prefill4k_int8_row": dict(index=3, geom=_GLM, tokens=4096, wfmt="int8_row", bias="zero"),
 }
 
 WEIGHT_STD = 0.02       # expert, shared-expert and router weights ~ N(0, 0.02)
