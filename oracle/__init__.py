@@ -14,7 +14,8 @@ What it follows (page "Show HN: Menjalankan GLM 5.2 di komputer lambat"):
     is applied to every position routed to it (the permutation);
   * sections "Cara kerja eksekusi MoE" and "Fitur utama": int4 expert weights
     dequantised on use, and the per-row-scale int8 / packed int4 / packed int2
-    formats of the quantisation kernels;
+    formats of the quantisation kernels, and the integer-dot path with int8
+    activations;
 and page "NVIDIA stellt neues GLM-5.2 NVFP4 Modell vor", section "Technische
 Details": the expert FFNs in 4-bit with one FP8 scale per 16 elements.
 
@@ -28,6 +29,7 @@ from .moe import (  # noqa: F401
     bf16_bits_to_f64, fp16_bits_to_f64, decode_e2m1, decode_e4m3fn,
     unpack_int4_codes, unpack_nvfp4_codes, dequant_int4, dequant_nvfp4,
     unpack_int2_codes, dequant_int4_row, dequant_int8_row, dequant_int2_row, ROW_FORMATS,
+    A8_FORMATS, quantize_rows_int8, w4a8_ffn,
     RouterConfig, route, route_weights, route_margins, valid_under_perturbation,
     apply_top_p, valid_top_p,
     permute, swiglu_ffn, expert_ffn, layer, dense_layer, ExpertSource,

@@ -169,6 +169,9 @@ def dequant_int2_row(q: np.ndarray, scale: np.ndarray) -> np.ndarray:
 
 ROW_FORMATS = {"int4_row": dequant_int4_row, "int8_row": dequant_int8_row,
                "int2_row": dequant_int2_row}
+# W4A8 (integer-dot) sources: per-row int4 weights whose FFN takes int8
+# activations (w4a8_ffn); their weights decode as the base format.
+A8_FORMATS = {"int4_row_a8": "int4_row"}
 
 
 @dataclasses.dataclass
@@ -186,6 +189,8 @@ class ExpertSource:
             return dequant_int4(q[e], s[e])
         if self.wfmt in ROW_FORMATS:
             return ROW_FORMATS[self.wfmt](q[e], s[e])
+        if self.wfmt in A8_FORMATS:
+            return ROW_FORMATS[A8_FORMATS[self.wfmt]](q[e], s[e])
         return dequant_nvfp4(q[e], s[e], g[e])
 
     @property
@@ -455,8 +460,61 @@ def layer(x_bits, Wr, b, cfg: RouterConfig, routed: ExpertSource,
 
 
 def expert_ffn(src: ExpertSource, e: int, X: np.ndarray) -> np.ndarray:
-    """FFN of expert e of `src` (dequantised from its packed bytes) on rows X."""
+    """FFN of expert e of `src` (dequantised from its packed bytes) on rows X;
+    W4A8 sources take their integer-dot FFN."""
+    if src.wfmt in A8_FORMATS:
+        return w4a8_ffn(src, e, X)
     return swiglu_ffn(X, *_expert_weights(src, e))
+
+
+# ---------------------------------------------------------------------------
+# W4A8 integer-dot FFN.  [P2-Fitur: an integer-dot kernel with int8
+# activations in the Q8_0 manner (1.4-2.5x faster than float; int4 weights
+# 1.8x faster on batches, single rows kept in float).]  Reading: the weights
+# are the pages' own container (int4 codes, one scale per row); activations are
+# quantised to int8 with one scale per row -- the input x per token, and the
+# SwiGLU output h (held in fp16) per (token, expert) row -- instead of Q8_0's one
+# scale per 32 inputs, so that both scales factor out of an integer dot product
+# over the whole row.  The quantiser's decisions are taken in float32 (the
+# precision the kernels use), so both sides form the same codes from the same
+# values.
+# ---------------------------------------------------------------------------
+
+def quantize_rows_int8(a: np.ndarray):
+    """Symmetric int8 codes per row, in float32 arithmetic: amax = max |a|,
+    q = clamp(rint(a * (127 / amax)), -127, 127) (ties to even), scale =
+    amax / 127; an all-zero row gives q = 0 and scale 0.
+    a: float32 [M, K] -> (q int64 [M, K], scale float32 [M])."""
+    a = np.asarray(a, dtype=np.float32)
+    amax = np.abs(a).max(axis=1)
+    safe = np.where(amax > 0, amax, np.float32(1.0)).astype(np.float32)
+    inv = np.where(amax > 0, np.float32(127.0) / safe, np.float32(0.0)).astype(np.float32)
+    q = np.clip(np.rint(a * inv[:, None]), -127, 127).astype(np.int64)
+    return q, (amax / np.float32(127.0)).astype(np.float32)
+
+
+def _int4_row_codes(src: ExpertSource, proj: str, e: int):
+    q, s, _ = getattr(src, proj)
+    codes = unpack_int4_codes(q[e]).astype(np.int64) - 8
+    return codes, np.asarray(s[e], dtype=np.float32).astype(np.float64)
+
+
+def w4a8_ffn(src: ExpertSource, e: int, X: np.ndarray) -> np.ndarray:
+    """SwiGLU FFN of expert e with int8 activations: G = s_x s_g (q_x . q_g),
+    U likewise, h = silu(G) U rounded to fp16, then quantised per row, and
+    O = s_h s_d (q_h . q_d); the integer dot products are exact.
+    X: float64 rows holding bf16 values."""
+    cg, sg = _int4_row_codes(src, "gate", e)
+    cu, su = _int4_row_codes(src, "up", e)
+    cd, sd = _int4_row_codes(src, "down", e)
+    xq, sx = quantize_rows_int8(np.asarray(X, dtype=np.float32))
+    sx = sx.astype(np.float64)[:, None]
+    G = (xq @ cg.T).astype(np.float64) * sg[None, :] * sx
+    U = (xq @ cu.T).astype(np.float64) * su[None, :] * sx
+    with np.errstate(over="ignore"):
+        h = G / (1.0 + np.exp(-G)) * U
+    hq, sh = quantize_rows_int8(h.astype(np.float16).astype(np.float32))
+    return (hq @ cd.T).astype(np.float64) * sd[None, :] * sh.astype(np.float64)[:, None]
 
 
 def dense_layer(x_bits, Wr, b, cfg: RouterConfig, routed: ExpertSource,
@@ -474,9 +532,9 @@ def dense_layer(x_bits, Wr, b, cfg: RouterConfig, routed: ExpertSource,
                 gate[t, e] = we
     y = np.zeros((T, H))
     for e in range(cfg.n_experts):
-        y += gate[:, e:e + 1] * swiglu_ffn(X, *_expert_weights(routed, e))
+        y += gate[:, e:e + 1] * expert_ffn(routed, e, X)
     if shared is not None:
-        y += swiglu_ffn(X, *_expert_weights(shared, 0))
+        y += expert_ffn(shared, 0, X)
     return y
 
 

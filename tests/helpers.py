@@ -54,7 +54,7 @@ class LazyExperts:
             q = p.q[e:e + 1].detach().cpu().numpy()
             if self.wfmt == "int4":
                 out.append((q, np_u16(p.scale[e:e + 1]), None))
-            elif self.wfmt in oracle.ROW_FORMATS:
+            elif self.wfmt in oracle.ROW_FORMATS or self.wfmt in oracle.A8_FORMATS:
                 out.append((q, p.scale[e:e + 1].detach().cpu().numpy(), None))
             else:
                 out.append((q, p.scale[e:e + 1].detach().cpu().numpy(),
@@ -68,8 +68,9 @@ class LazyExperts:
             q = p.q[e].detach().cpu().numpy()
             if self.wfmt == "int4":
                 w = oracle.dequant_int4(q, np_u16(p.scale[e]))
-            elif self.wfmt in oracle.ROW_FORMATS:
-                w = oracle.ROW_FORMATS[self.wfmt](q, p.scale[e].detach().cpu().numpy())
+            elif self.wfmt in oracle.ROW_FORMATS or self.wfmt in oracle.A8_FORMATS:
+                base = oracle.A8_FORMATS.get(self.wfmt, self.wfmt)
+                w = oracle.ROW_FORMATS[base](q, p.scale[e].detach().cpu().numpy())
             else:
                 w = oracle.dequant_nvfp4(q, p.scale[e].detach().cpu().numpy(),
                                          float(p.gscale[e].item()))

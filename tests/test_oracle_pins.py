@@ -690,3 +690,100 @@ def test_row_format_layer_dense_equivalence(fmt):
     y0, _, _ = oracle.layer(x, Wr, b, cfg, routed, None)
     y2, _, _ = oracle.layer(x, Wr, b, cfg, routed2, None)
     assert np.allclose(y2, 2 * y0, rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# W4A8 integer-dot path: the int8 row quantiser and the FFN
+# ---------------------------------------------------------------------------
+
+def test_quantize_rows_int8_hand_values():
+    """Row 0: amax 1, so a * 127: 63.5 -> 64 and 31.75 -> 32 (ties to even);
+    row 1 all zero; row 2: amax 254, so a * 0.5: 0.5 -> 0, -1.5 -> -2, 2.5 -> 2."""
+    a = np.array([[0.5, -1.0, 0.25, 0.0],
+                  [0.0, 0.0, 0.0, 0.0],
+                  [254.0, 1.0, -3.0, 5.0]], np.float32)
+    q, s = oracle.quantize_rows_int8(a)
+    assert q.tolist() == [[64, -127, 32, 0], [0, 0, 0, 0], [127, 0, -2, 2]]
+    assert s.dtype == np.float32
+    assert s[0] == np.float32(1.0) / np.float32(127.0) and s[1] == 0 and s[2] == 2.0
+
+
+def test_quantize_rows_int8_on_grid_exact():
+    """Rows k * 2^-e with integer k in [-127, 127] reaching |k| = 127 come
+    back as k exactly, with scale 2^-e."""
+    rng = np.random.default_rng(31)
+    k = rng.integers(-127, 128, size=(6, 64))
+    k[:, 5] = 127 * np.where(np.arange(6) % 2 == 0, 1, -1)
+    s = np.float32(2.0) ** -np.arange(3, 9, dtype=np.float32)
+    a = (k * s[:, None]).astype(np.float32)
+    q, sc = oracle.quantize_rows_int8(a)
+    assert np.array_equal(q, k) and np.array_equal(sc, s)
+
+
+def _a8_source(seed, E=3, H=64, I=32):
+    """Per-row int4 experts (as the synthetic encoder makes them) viewed as a
+    W4A8 source and as a plain one."""
+    torch.manual_seed(seed)
+    projs = [synth._quantize(torch.randn(E, n, k) * 0.02, "int4_row") for n, k in ((I, H), (I, H), (H, I))]
+    arrs = [(p.q.numpy(), p.scale.numpy(), None) for p in projs]
+    return oracle.ExpertSource("int4_row_a8", *arrs), oracle.ExpertSource("int4_row", *arrs)
+
+
+def test_w4a8_ffn_on_grid_input_bound():
+    """Inputs on the int8 grid are quantised exactly, so gate and up equal the
+    float64 ones; the result then differs from the float64 FFN only through
+    h's fp16 rounding and int8 quantisation: |dO[n]| <= sum_k |Wd[n,k]| (s_h/2 +
+    2^-11 |h_k|) per token."""
+    a8, plain = _a8_source(41)
+    rng = np.random.default_rng(42)
+    k = rng.integers(-127, 128, size=(5, 64))
+    k[:, 0] = 127
+    X = k * np.float64(2.0 ** -6)
+    for e in range(3):
+        Wg, Wu, Wd = (plain.weight(p, e) for p in ("gate", "up", "down"))
+        G, U = X @ Wg.T, X @ Wu.T
+        h = G / (1.0 + np.exp(-G)) * U
+        ref = h @ Wd.T
+        got = oracle.w4a8_ffn(a8, e, X)
+        sh = np.abs(h).max(1) / 127.0
+        bound = (sh[:, None] / 2 + 2.0 ** -11 * np.abs(h)) @ np.abs(Wd).T
+        assert np.all(np.abs(got - ref) <= bound * (1 + 1e-6) + 1e-300), e
+        assert not np.allclose(got, ref, rtol=1e-12, atol=0)      # h really was quantised
+
+
+def test_w4a8_integer_core_brute_force():
+    """The integer dot products against a loop over the decoded codes, on a
+    two-token example (every step of w4a8_ffn recomputed by hand)."""
+    a8, _ = _a8_source(43, E=1, H=32, I=32)
+    X = np.random.default_rng(44).standard_normal((2, 32)).astype(np.float32).astype(np.float64)
+    q, s = oracle.quantize_rows_int8(X.astype(np.float32))
+    codes = {p: oracle.unpack_int4_codes(getattr(a8, p)[0][0]).astype(int) - 8 for p in ("gate", "up", "down")}
+    rs = {p: getattr(a8, p)[1][0].astype(np.float64) for p in ("gate", "up", "down")}
+    out = np.zeros((2, 32))
+    for t in range(2):
+        G = [sum(int(q[t, i]) * int(codes["gate"][r, i]) for i in range(32)) * rs["gate"][r] * float(s[t])
+             for r in range(32)]
+        U = [sum(int(q[t, i]) * int(codes["up"][r, i]) for i in range(32)) * rs["up"][r] * float(s[t])
+             for r in range(32)]
+        h = np.array([g / (1 + math.exp(-g)) * u for g, u in zip(G, U)])
+        h16 = h.astype(np.float16).astype(np.float32)
+        amax = np.float32(np.abs(h16).max())
+        inv = np.float32(127.0) / amax
+        hq = [int(np.clip(np.rint(np.float32(v) * inv), -127, 127)) for v in h16]
+        sh = float(amax / np.float32(127.0))
+        for n in range(32):
+            out[t, n] = sum(hq[i] * int(codes["down"][n, i]) for i in range(32)) * rs["down"][n] * sh
+    assert np.allclose(oracle.w4a8_ffn(a8, 0, X), out, rtol=1e-12, atol=1e-15)
+
+
+def test_w4a8_layer_dense_equivalence():
+    geom = synth.small_geom()
+    L = synth.make_custom(geom, 5, "int4_row", "normal0.1", seed=47)
+    x, Wr, b, cfg, routed, shared = oracle_inputs(L)
+    a8 = lambda src: oracle.ExpertSource("int4_row_a8", src.gate, src.up, src.down)
+    y, _, _ = oracle.layer(x, Wr, b, cfg, a8(routed), a8(shared))
+    yd = oracle.dense_layer(x, Wr, b, cfg, a8(routed), a8(shared))
+    assert np.allclose(y, yd, rtol=1e-12, atol=1e-14)
+    # and it stays close to the float-activation layer (int8 rounding only)
+    y0, _, _ = oracle.layer(x, Wr, b, cfg, routed, shared)
+    assert np.abs(y - y0).max() <= 0.05 * np.abs(y0).max()
