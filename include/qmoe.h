@@ -160,6 +160,17 @@ typedef struct {
  *                        exercise the give-up path; never needed otherwise. */
 #define MOE_OPT_NO_GRID_WAIT 1u
 #define MOE_OPT_GRID_WAIT_NONE 2u
+/* MOE_OPT_INT8_ACTIVATIONS  W4A8 integer-dot path (page "Show HN: ...", section
+ *   "Fitur utama": int8 activations in the Q8_0 manner against int4 weights,
+ *   faster on batches; single rows stay in float).  Requires
+ *   wfmt == MOE_WFMT_INT4_ROW_F32 (else MOE_ERR_INVALID_ARG).  For T > 4 the
+ *   expert FFNs quantise their inputs to int8 with one fp32 scale per row --
+ *   x per token, the fp16 SwiGLU output per (token, expert) row: scale =
+ *   amax / 127, q = rint(a * (127 / amax)) clamped to +-127, in fp32 -- and
+ *   multiply on the int8 matrix cores with exact int32 sums; the results
+ *   then carry the activations' int8 rounding (the layer's bar is measured
+ *   against a reference that rounds the same way).  T <= 4 is unaffected. */
+#define MOE_OPT_INT8_ACTIVATIONS 4u
 
 /* One projection of E experts (device pointers; see the formats above). */
 typedef struct {

@@ -7,6 +7,7 @@ from .binding import (  # noqa: F401
     MOE_ERR_HIP, MOE_WFMT_INT4_G32_F16, MOE_WFMT_NVFP4, MOE_OUT_F32, MOE_OUT_BF16,
     MOE_WFMT_INT4_ROW_F32, MOE_WFMT_INT8_ROW_F32, MOE_WFMT_INT2_ROW_F32,
     MOE_MAX_TOKENS, WFMT, moe_layer_flags, MOE_OPT_NO_GRID_WAIT, MOE_OPT_GRID_WAIT_NONE,
+    MOE_OPT_INT8_ACTIVATIONS,
     MOE_FLAG_GRID_WAIT_TIMEOUT, moe_layer_noalloc, MOE_NOALLOC_WS_BYTES,
     MoeCacheStats, moe_cache_create, moe_cache_destroy, moe_layer_cached, moe_cache_prefetch,
     moe_cache_pin, moe_cache_unpin_all, moe_cache_get_stats, moe_cache_slot_of,

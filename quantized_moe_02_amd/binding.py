@@ -22,7 +22,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, M
 MOE_WFMT_INT4_G32_F16, MOE_WFMT_NVFP4 = 0, 1
 MOE_WFMT_INT4_ROW_F32, MOE_WFMT_INT8_ROW_F32, MOE_WFMT_INT2_ROW_F32 = 2, 3, 4
 MOE_OUT_F32, MOE_OUT_BF16 = 0, 1
-MOE_OPT_NO_GRID_WAIT, MOE_OPT_GRID_WAIT_NONE = 1, 2
+MOE_OPT_NO_GRID_WAIT, MOE_OPT_GRID_WAIT_NONE, MOE_OPT_INT8_ACTIVATIONS = 1, 2, 4
 MOE_FLAG_GRID_WAIT_TIMEOUT = 1
 MOE_MAX_TOKENS = 262144
 MOE_NOALLOC_WS_BYTES = 32 << 20

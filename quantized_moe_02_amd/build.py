@@ -20,7 +20,7 @@ OUT = os.path.join(PKG, "libqmoe.so")
 BUILD = os.path.join(ROOT, "_build")
 
 SOURCES = ["qmoe_api.cpp", "route.hip", "permute.hip", "gemv.hip", "decode.hip", "gemm.hip",
-           "noalloc.hip", "expert_cache.cpp"]
+           "gemm_i8.hip", "noalloc.hip", "expert_cache.cpp"]
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

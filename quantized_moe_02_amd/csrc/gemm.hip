@@ -24,7 +24,7 @@
 #include <type_traits>
 #include <utility>
 
-#include "qmoe_device.h"
+#include "gemm_common.h"
 
 namespace qmoe {
 namespace {
@@ -33,7 +33,6 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 
-constexpr int kBM = 128;          // tokens per unit
 constexpr int kBK = 128;          // inputs per K block
 constexpr int kChunks = kBK / 8;  // 16-byte chunks per activation row of a K block
 // Thin units: up to kBMThin tokens of an expert with few tokens, run by the
@@ -43,15 +42,7 @@ constexpr int kChunks = kBK / 8;  // 16-byte chunks per activation row of a K bl
 #ifndef QMOE_THIN_NS
 #define QMOE_THIN_NS 4
 #endif
-constexpr int kBMThin = 32;
-// With fewer fat units than this (gate/up: 16 work items each) the fat
-// launches would leave most of the chip idle, so the experts they would hold
-// are cut into thin units, which run in the thin launch with the bulk of the
-// work (their weights are then read once per 32 tokens).
-constexpr int kFewFat = 16;
 constexpr int kNSThin = QMOE_THIN_NS;
-constexpr int kGateUpPairs = 128; // row pairs per gate/up unit
-constexpr int kDownRows = 256;    // output rows per down unit
 
 __device__ __forceinline__ uint32_t pk_fma_f16(uint32_t a, uint32_t b, uint32_t c) {
   const half2v r = __builtin_bit_cast(half2v, a) * __builtin_bit_cast(half2v, b) +
@@ -136,33 +127,6 @@ __device__ __forceinline__ half8 dequant_row(const uint32_t* w, int ks) {
   return r;
 }
 
-struct Unit {
-  int e;        // expert index in its weight set (0 for the shared expert)
-  int p0;       // first row of the unit in the h / O buffers
-  int M;        // tokens in the unit (<= the kernel's unit rows)
-  int tok0;     // routed: first sorted slot (index into sorted_token); shared: first token
-  bool routed;
-};
-
-// The unit is the same for the whole workgroup; readfirstlane puts it in
-// SGPRs, so that the buffer descriptors built from it are uniform (a
-// descriptor in VGPRs turns every buffer load into a waterfall loop).
-__device__ __forceinline__ Unit load_unit(const int4* tiles, int idx) {
-  const int4 t = tiles[idx];
-  Unit u;
-  const int x = __builtin_amdgcn_readfirstlane(t.x);
-  u.routed = x >= 0;
-  u.e = u.routed ? x : 0;
-  u.p0 = __builtin_amdgcn_readfirstlane(t.y);
-  u.M = __builtin_amdgcn_readfirstlane(t.z);
-  u.tok0 = __builtin_amdgcn_readfirstlane(t.w);
-  return u;
-}
-
-// Activation rows past M start at this offset, past the range of every
-// activation descriptor (the host keeps those buffers below 2 GiB), so their
-// loads return zeros at every K block.
-constexpr uint32_t kOOBRow = 0x80000000u;
 
 // Activations go from HBM straight into LDS (buffer_load ... lds: lane l of a
 // load writes 16 bytes at base + 16 l).  Stage layout: 128 token rows of 16
@@ -212,20 +176,10 @@ __device__ __forceinline__ void lds_copy16(const rsrc_t& r, uint8_t* dst, uint32
                                            0, 0, 0);
 }
 
-template <int N>
-using ic = std::integral_constant<int, N>;
 
 constexpr int kNS = 4;            // K blocks in flight (LDS stages, weight register ring)
 constexpr int kRT = 4;            // 16-row weight tiles per wave
 
-// Work item -> (unit, n tile).  Workgroups are dispatched round-robin over
-// the 8 XCDs; this maps the items that one XCD receives onto a contiguous
-// range, n tile fastest, so that the n tiles of one token tile run on the same
-// XCD at about the same time and share its L2 copy of the activations.
-__device__ __forceinline__ int xcd_item(int L, int total) {
-  const int x = L & 7, q = total >> 3, r = total & 7;
-  return x * q + min(x, r) + (L >> 3);
-}
 
 // PROJ 0: gate/up (+SwiGLU), PROJ 1: down.
 //
@@ -666,6 +620,8 @@ __global__ void __launch_bounds__(64) build_units_kernel(const int32_t* __restri
   }
 }
 
+}  // namespace
+
 // Most work units of each kind: fat units hold up to kBM tokens of an expert
 // with more than kBMThin of them, thin units up to kBMThin tokens of an
 // expert (or the shared expert) with at most kBMThin, or of any expert when
@@ -684,8 +640,6 @@ long thin_units_max(int T, int K, int E, bool has_shared) {
   // kBM / kBMThin thin units
   return std::min<long>(E, P) + (has_shared ? 1 : 0) + (long)(kFewFat - 1) * (kBM / kBMThin);
 }
-
-}  // namespace
 
 hipError_t launch_build_units(const int32_t* offsets, const int32_t* active,
                               const int32_t* n_active, int4* tiles, int32_t* n_tiles, int T, int P,

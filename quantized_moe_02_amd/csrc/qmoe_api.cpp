@@ -36,7 +36,10 @@ moe_status check_cfg(const moe_config* c) {
     return MOE_ERR_INVALID_ARG;
   if (c->wfmt != MOE_WFMT_INT4_G32_F16 && c->wfmt != MOE_WFMT_NVFP4 && !wfmt_row(c->wfmt))
     return MOE_ERR_INVALID_ARG;
-  if (c->options & ~(MOE_OPT_NO_GRID_WAIT | MOE_OPT_GRID_WAIT_NONE)) return MOE_ERR_INVALID_ARG;
+  if (c->options & ~(MOE_OPT_NO_GRID_WAIT | MOE_OPT_GRID_WAIT_NONE | MOE_OPT_INT8_ACTIVATIONS))
+    return MOE_ERR_INVALID_ARG;
+  if ((c->options & MOE_OPT_INT8_ACTIVATIONS) && c->wfmt != MOE_WFMT_INT4_ROW_F32)
+    return MOE_ERR_INVALID_ARG;
   if (!(c->expert_top_p >= 0.0f && c->expert_top_p <= 1.0f)) return MOE_ERR_INVALID_ARG;   // NaN too
   // kernel limits
   if (c->n_routed_experts > 256 || c->n_group > 64 || c->top_k > 16) return MOE_ERR_UNSUPPORTED;
@@ -103,6 +106,46 @@ hipError_t run_gemm_ffn(const moe_config& c, int T, const uint16_t* x, const Wor
                               has_routed ? n_active : nullptr, w.tiles, w.n_tiles, T, P, K, E,
                               has_shared, stream)) != hipSuccess)
     return e;
+  if (c.options & MOE_OPT_INT8_ACTIVATIONS) {
+    // W4A8: x -> int8 rows, gate/up (fp16 h), h -> int8 rows, down
+    GemmQArgs q{};
+    q.tiles = w.tiles;
+    q.n_tiles = w.n_tiles;
+    q.thin_off = gemm_thin_offset(T, K, E, has_shared);
+    q.xq = reinterpret_cast<const int8_t*>(w.x16);
+    q.ldxq = pad_k(c.hidden);
+    q.xs = w.xs;
+    q.xsum = w.xsum;
+    q.sorted_token = sorted_token;
+    q.hq = w.hq;
+    q.ldhq = ldh;
+    q.hs = w.hs;
+    q.hsum = w.hsum;
+    q.routed = routed;
+    q.has_shared = has_shared;
+    q.shared = shared;
+    q.h_out = h;
+    q.ldh = ldh;
+    q.o_out = o;
+    q.T = T;
+    q.H = c.hidden;
+    q.P = P;
+    if ((e = launch_quant_rows(x, c.hidden, true, T, T, c.hidden, c.hidden,
+                               reinterpret_cast<int8_t*>(w.x16), q.ldxq, w.xs, w.xsum, stream)) !=
+        hipSuccess)
+      return e;
+    if (tr && (e = tr->mark("gemm_prep")) != hipSuccess) return e;
+    if ((e = launch_gemm_q(q, 0, K, E, stream)) != hipSuccess) return e;
+    if (tr && (e = tr->mark("gemm_gateup")) != hipSuccess) return e;
+    if ((e = launch_quant_rows(h, ldh, false, P + (has_shared ? T : 0), P, routed.inter,
+                               has_shared ? shared.inter : routed.inter, w.hq, ldh, w.hs, w.hsum,
+                               stream)) != hipSuccess)
+      return e;
+    if (tr && (e = tr->mark("quant_h")) != hipSuccess) return e;
+    if ((e = launch_gemm_q(q, 1, K, E, stream)) != hipSuccess) return e;
+    if (tr && (e = tr->mark("gemm_down")) != hipSuccess) return e;
+    return hipSuccess;
+  }
   if ((e = launch_x_to_f16(x, w.x16, T, c.hidden, pad_k(c.hidden), stream)) != hipSuccess) return e;
   if (tr && (e = tr->mark("gemm_prep")) != hipSuccess) return e;
   GemmArgs g{};
@@ -205,6 +248,12 @@ Workspace carve_workspace(const moe_config& c, int T, void* base) {
   const size_t o_dbar = take(kDecBarrierWords * sizeof(uint32_t));
   const size_t o_phist = take(permute_hist_ints(T, (int)E) * sizeof(int32_t));
   const size_t o_cids = take(P * sizeof(int32_t));
+  const bool a8 = (c.options & MOE_OPT_INT8_ACTIVATIONS) != 0;
+  const size_t o_xs = take(a8 ? (size_t)T * sizeof(float) : 0);
+  const size_t o_xsum = take(a8 ? (size_t)T * sizeof(int32_t) : 0);
+  const size_t o_hq = take(a8 ? (P + T) * imax : 0);
+  const size_t o_hs = take(a8 ? (P + T) * sizeof(float) : 0);
+  const size_t o_hsum = take(a8 ? (P + T) * sizeof(int32_t) : 0);
   w.total = off;
   if (base) {
     char* b = static_cast<char*>(base);
@@ -228,6 +277,13 @@ Workspace carve_workspace(const moe_config& c, int T, void* base) {
     w.dbar = reinterpret_cast<uint32_t*>(b + o_dbar);
     w.phist = reinterpret_cast<int32_t*>(b + o_phist);
     w.cache_ids = reinterpret_cast<int32_t*>(b + o_cids);
+    if (a8) {
+      w.xs = reinterpret_cast<float*>(b + o_xs);
+      w.xsum = reinterpret_cast<int32_t*>(b + o_xsum);
+      w.hq = reinterpret_cast<int8_t*>(b + o_hq);
+      w.hs = reinterpret_cast<float*>(b + o_hs);
+      w.hsum = reinterpret_cast<int32_t*>(b + o_hsum);
+    }
   }
   return w;
 }

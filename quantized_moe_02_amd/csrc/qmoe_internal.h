@@ -78,6 +78,12 @@ struct Workspace {
   int32_t* n_tiles;       // [4]
   int32_t* phist;         // [permute_hist_ints] permutation scratch
   int32_t* cache_ids;     // [P] moe_layer_cached: the picks' slot ids
+  // int8 activations (MOE_OPT_INT8_ACTIVATIONS only; x codes reuse x16)
+  float* xs;              // [T]
+  int32_t* xsum;          // [T]
+  int8_t* hq;             // [P+T][Imax]
+  float* hs;              // [P+T]
+  int32_t* hsum;          // [P+T]
   size_t total;
 };
 
@@ -247,6 +253,37 @@ struct GemmArgs {
   float* o_out;               // fp32 [P+T][H] (down output)
   int T, H, P, wfmt;
 };
+// W4A8 grouped GEMM (csrc/gemm_i8.hip): per-row int4 weights, int8
+// activations with one fp32 scale and one code sum per row.
+struct GemmQArgs {
+  const int4* tiles;
+  const int32_t* n_tiles;
+  int thin_off;
+  const int8_t* xq;           // int8 x [T][ldxq] (bytes), chunk order of the kernel
+  int ldxq;
+  const float* xs;            // [T] scales
+  const int32_t* xsum;        // [T] code sums
+  const int32_t* sorted_token;
+  const int8_t* hq;           // int8 h [P+T][ldhq]
+  int ldhq;
+  const float* hs;            // [P+T]
+  const int32_t* hsum;        // [P+T]
+  ExpertSet routed;
+  bool has_shared;
+  ExpertSet shared;
+  uint16_t* h_out;            // fp16 h [P+T][ldh] (gate/up output)
+  int ldh;
+  float* o_out;               // fp32 [P+T][H] (down output)
+  int T, H, P;
+};
+// Row quantiser: rows of bf16 (x) or fp16 (h; width n below row `split`, n2
+// from there) -> int8 codes [rows][ld_dst] in the W4A8 GEMM's chunk order,
+// scale and code sum per row.
+hipError_t launch_quant_rows(const uint16_t* src, int ld_src, bool bf16, int rows, int split, int n,
+                             int n2, int8_t* dst, int ld_dst, float* scale, int32_t* sum, hipStream_t s);
+// proj 0: gate/up (+SwiGLU into h_out); 1: down (into o_out).
+hipError_t launch_gemm_q(const GemmQArgs& g, int proj, int K, int E, hipStream_t s);
+
 int gemm_max_units(int T, int K, int E, bool has_shared);
 // Row strides (elements) of the fp16 activation and intermediate buffers: a
 // multiple of the GEMM's K block, the padding held at zero.

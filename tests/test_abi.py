@@ -128,6 +128,10 @@ def test_layer_validation_paths():
     assert _layer(c0) == q.MOE_ERR_INVALID_ARG                                  # shared given but none configured
     cn = _cfg(wfmt="nvfp4")
     assert _layer(cn) == q.MOE_ERR_INVALID_ARG                                  # nvfp4 needs gscale
+    assert _size(_cfg(wfmt="int4", options=q.MOE_OPT_INT8_ACTIVATIONS), 8)[0] == q.MOE_ERR_INVALID_ARG
+    assert _size(_cfg(wfmt="int8_row", options=q.MOE_OPT_INT8_ACTIVATIONS), 8)[0] == q.MOE_ERR_INVALID_ARG
+    c8 = _cfg(wfmt="int4_row", options=q.MOE_OPT_INT8_ACTIVATIONS)              # W4A8: its own
+    assert _size(c8, 64)[0] == q.MOE_OK and _size(c8, 64)[1] > _size(_cfg(wfmt="int4_row"), 64)[1]
     for fmt in ("int4_row", "int8_row", "int2_row"):                            # per-row formats:
         cr = _cfg(wfmt=fmt)                                                     # no gscale
         assert _size(cr, 8)[0] == q.MOE_OK
