@@ -29,10 +29,11 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/s + weight-stream HBM GB/s (% peak); prefill MFMA util"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_F16_TFLOPS = 2500.0       # MI355X dense fp16/bf16 MFMA
+PEAK_I8_TOPS = 5000.0          # MI355X dense int8 MFMA
 ALL_WORKLOADS = ["decode", "verify4", "verify64", "prefill4k", "prefill16k", "nvfp4_512",
                  "decode_topp", "verify64_topp", "decode_stream", "decode_stream_warm",
                  "decode_int4_row", "decode_int8_row", "decode_int2_row", "prefill4k_int4_row",
-                 "prefill4k_int8_row"]
+                 "prefill4k_int8_row", "prefill4k_w4a8", "prefill16k_w4a8", "verify64_w4a8"]
 HEADLINE = "decode"
 # expert streaming from host memory: the decode layer with its 256 routed
 # experts in page-locked host RAM and this many HBM slots (moe_layer_cached)
@@ -125,6 +126,8 @@ def algorithmic(geom, wfmt, T, n_active):
         "combine": dict(bytes=rows * H * 4 + P * 8 + y_b, flops=2 * P * H),
         # moe_expert_ffn_q4 on few tokens
         "gateup_gemv": dict(bytes=w_gu + x_b + rows * I * 2, flops=f_gu),
+        # W4A8: the SwiGLU outputs to int8 rows between the projections
+        "quant_h": dict(bytes=rows * I * 3 + rows * 8, flops=0),
         "down_gemv": dict(bytes=w_dn + rows * I * 2 + rows * H * 4, flops=f_dn),
     })
     return layer_bytes, layer_flops, kern
@@ -195,7 +198,8 @@ class Bench:
         self.L = L = synth.make_layer(name, "cuda")
         self.geom, self.T, self.wfmt = L.geom, L.T, L.wfmt
         g = self.geom
-        self.cfg = q.make_config(g, L.wfmt)
+        self.options = synth.WORKLOADS[name].get("options", 0)
+        self.cfg = q.make_config(g, L.wfmt, self.options)
         self.sets = [(L.router_w, L.bias, L.routed, L.shared)]
         for _ in range(replicas - 1):
             self.sets.append((L.router_w.clone(), L.bias.clone(), clone_experts(L.routed),
@@ -343,8 +347,11 @@ def run_workload(name, args):
         dur = kt[dom] * 1e-6
         if roofline_bound(kb) == "mfma":
             ach = kb["flops"] / dur / 1e12
-            res["roofline"] = dict(kernel=dom, bound="mfma", achieved=ach, peak=PEAK_F16_TFLOPS,
-                                   unit="TFLOP/s", frac=ach / PEAK_F16_TFLOPS,
+            # the W4A8 path multiplies on the int8 matrix cores
+            i8 = bool(B.options & 4)
+            peak = PEAK_I8_TOPS if i8 else PEAK_F16_TFLOPS
+            res["roofline"] = dict(kernel=dom, bound="mfma", achieved=ach, peak=peak,
+                                   unit="TOP/s" if i8 else "TFLOP/s", frac=ach / peak,
                                    traffic=traffic_for(dom, name),
                                    algorithmic=kb["flops"], avg_us=kt[dom])
         else:

@@ -69,6 +69,11 @@ WORKLOADS: Dict[str, dict] = {
     "decode_int2_row":    dict(index=1, geom=_GLM, tokens=1,    wfmt="int2_row", bias="zero"),
     "prefill4k_int4_row": dict(index=3, geom=_GLM, tokens=4096, wfmt="int4_row", bias="zero"),
     "prefill4k_int8_row": dict(index=3, geom=_GLM, tokens=4096, wfmt="int8_row", bias="zero"),
+    # the W4A8 integer-dot path (per-row int4 weights, int8 activations;
+    # options = the library's MOE_OPT_INT8_ACTIVATIONS bit)
+    "prefill4k_w4a8":     dict(index=3, geom=_GLM, tokens=4096, wfmt="int4_row", bias="zero", options=4),
+    "prefill16k_w4a8":    dict(index=3, geom=_GLM, tokens=16384, wfmt="int4_row", bias="zero", options=4),
+    "verify64_w4a8":      dict(index=2, geom=_GLM, tokens=64, wfmt="int4_row", bias="hot16", options=4),
 }
 
 WEIGHT_STD = 0.02       # expert, shared-expert and router weights ~ N(0, 0.02)
