@@ -69,10 +69,31 @@ __device__ __forceinline__ void load16(uint32_t (&d)[4], const void* p) {
 // sum_k w_k * a_k over one 32-input group.  wq: the group's 16 code bytes;
 // sc: its scale word (int4: fp16 bits; nvfp4: two E4M3 bytes); act: 16 pairs
 // of 16-bit activations; asum: sum of the 32 activations (int4 only).
+// Per-row formats (scale applied per row after the reduction): int4 as
+// above with no group scale; int2 (two code words per group) as 1 + u/4
+// pairs, sum (u - 2) a = 4 (d - 1.5 A).
 template <int FMT, bool F16ACT>
 __device__ __forceinline__ float group_dot(const uint32_t (&wq)[4], uint32_t sc,
                                            const uint32_t (&act)[16], float asum, float gs) {
-  if constexpr (FMT == MOE_WFMT_INT4_G32_F16) {
+  if constexpr (FMT == MOE_WFMT_INT4_ROW_F32) {
+    float d = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        d = F16ACT ? dot2_f16(int4_pair_f16(wq[j], k), act[4 * j + k], d)
+                   : dot2_bf16(int4_pair_bf16(wq[j], k), act[4 * j + k], d);
+    return 16.0f * fmaf(-1.5f, asum, d);
+  } else if constexpr (FMT == MOE_WFMT_INT2_ROW_F32) {
+    float d = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        d = F16ACT ? dot2_f16(int2_pair_f16(wq[j], k, 0x3C003C00u), act[8 * j + k], d)
+                   : dot2_bf16(int2_pair_bf16(wq[j], k, 0x3F803F80u), act[8 * j + k], d);
+    return 4.0f * fmaf(-1.5f, asum, d);
+  } else if constexpr (FMT == MOE_WFMT_INT4_G32_F16) {
     float d = 0.0f;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -151,17 +172,36 @@ __device__ __forceinline__ float int4_offset(const uint32_t (&act)[16]) {
 template <int FMT>
 __device__ __forceinline__ float group_dot_h(const uint32_t (&wq)[4], uint32_t sc,
                                              const uint32_t (&act)[16], float off, float gs) {
-  if constexpr (FMT == MOE_WFMT_INT4_G32_F16) {
+  if constexpr (FMT == MOE_WFMT_INT4_G32_F16 || FMT == MOE_WFMT_INT4_ROW_F32) {
     uint32_t wf[16];
     int4_f16_1024(wq, wf);
-    return half_bits_to_f32(sc & 0xffffu) * (int4_dot_1024(wf, act) - off);
+    const float d = int4_dot_1024(wf, act) - off;
+    return FMT == MOE_WFMT_INT4_G32_F16 ? half_bits_to_f32(sc & 0xffffu) * d : d;
+  } else if constexpr (FMT == MOE_WFMT_INT2_ROW_F32) {
+    return group_dot<FMT, true>(wq, sc, act, off, gs);   // off: the sum of h
   } else {
     return group_dot<FMT, true>(wq, sc, act, 0.0f, gs);
   }
 }
 template <int FMT>
 __device__ __forceinline__ float offset_h(const uint32_t (&act)[16]) {
-  return FMT == MOE_WFMT_INT4_G32_F16 ? int4_offset(act) : 0.0f;
+  if constexpr (FMT == MOE_WFMT_INT2_ROW_F32) return act_sum<true>(act);
+  return (FMT == MOE_WFMT_INT4_G32_F16 || FMT == MOE_WFMT_INT4_ROW_F32) ? int4_offset(act) : 0.0f;
+}
+// Bytes of codes per 32-input group; scale bytes per row (per-row formats) or
+// per group.
+template <int FMT>
+__host__ __device__ constexpr uint32_t group_code_bytes() { return 4u * (uint32_t)wfmt_bits(FMT); }
+__device__ __forceinline__ uint32_t bload_u32(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+// The code words of one group: 16 bytes, or 8 for int2 (words 2, 3 unused).
+template <int FMT>
+__device__ __forceinline__ void load_group(uint32_t (&d)[4], rsrc_t r, uint32_t voff, uint32_t soff) {
+  if constexpr (wfmt_bits(FMT) == 2)
+    bload8(d, r, voff, soff);
+  else
+    bload16(d, r, voff, soff);
 }
 
 // ---------------------------------------------------------------------------
@@ -182,18 +222,27 @@ struct GateUpBufs {
   uint32_t rowBytes, scaleRowBytes;
 };
 
-template <int GPL, int RP>
+// Per-row formats: sg[r][0] / su[r][0] hold the rows' fp32 scales (the same
+// address in every lane).
+template <int FMT, int GPL, int RP>
 __device__ __forceinline__ void gu_load(GateUpItem<GPL, RP>& it, const GateUpBufs& b,
                                         const uint32_t (&off)[GPL], int pair0) {
+  constexpr uint32_t CB = group_code_bytes<FMT>();
 #pragma unroll
   for (int r = 0; r < RP; ++r) {
     const uint32_t row = (uint32_t)(pair0 + r);
 #pragma unroll
     for (int j = 0; j < GPL; ++j) {
-      bload16(it.wg[r][j], b.qg, off[j] * 16u, row * b.rowBytes);
-      bload16(it.wu[r][j], b.qu, off[j] * 16u, row * b.rowBytes);
-      it.sg[r][j] = bload_u16(b.sg, off[j] * 2u, row * b.scaleRowBytes);
-      it.su[r][j] = bload_u16(b.su, off[j] * 2u, row * b.scaleRowBytes);
+      load_group<FMT>(it.wg[r][j], b.qg, off[j] * CB, row * b.rowBytes);
+      load_group<FMT>(it.wu[r][j], b.qu, off[j] * CB, row * b.rowBytes);
+      if constexpr (!wfmt_row(FMT)) {
+        it.sg[r][j] = bload_u16(b.sg, off[j] * 2u, row * b.scaleRowBytes);
+        it.su[r][j] = bload_u16(b.su, off[j] * 2u, row * b.scaleRowBytes);
+      }
+    }
+    if constexpr (wfmt_row(FMT)) {
+      it.sg[r][0] = bload_u32(b.sg, 0u, row * 4u);
+      it.su[r][0] = bload_u32(b.su, 0u, row * 4u);
     }
   }
 }
@@ -218,6 +267,10 @@ __device__ __forceinline__ void gu_compute(const GateUpItem<GPL, RP>& it,
     }
     g = wave_sum(g);
     u = wave_sum(u);
+    if constexpr (wfmt_row(FMT)) {
+      g *= __uint_as_float(it.sg[r][0]);
+      u *= __uint_as_float(it.su[r][0]);
+    }
     if (lane == r) {
       // a device-scope store: dec_fused_t1 reads h in the same launch
       const _Float16 hv = (_Float16)silu_mul(g, u);
@@ -238,12 +291,14 @@ __device__ __forceinline__ void gateup_wave(const uint16_t* __restrict__ x, int 
   const int lane = threadIdx.x & 63;
   const int nG = H / 32;
   GateUpBufs b;
-  b.rowBytes = (uint32_t)H / 2;
-  b.scaleRowBytes = (uint32_t)nG * 2;
+  b.rowBytes = (uint32_t)H * wfmt_bits(FMT) / 8;
+  b.scaleRowBytes = wfmt_row(FMT) ? 4u : (uint32_t)nG * 2;
   b.qg = make_rsrc(Pg.q + row_base * b.rowBytes, (uint32_t)inter * b.rowBytes);
   b.qu = make_rsrc(Pu.q + row_base * b.rowBytes, (uint32_t)inter * b.rowBytes);
-  b.sg = make_rsrc(reinterpret_cast<const uint16_t*>(Pg.s) + row_base * nG, (uint32_t)inter * b.scaleRowBytes);
-  b.su = make_rsrc(reinterpret_cast<const uint16_t*>(Pu.s) + row_base * nG, (uint32_t)inter * b.scaleRowBytes);
+  b.sg = make_rsrc(reinterpret_cast<const uint8_t*>(Pg.s) + row_base * b.scaleRowBytes,
+                   (uint32_t)inter * b.scaleRowBytes);
+  b.su = make_rsrc(reinterpret_cast<const uint8_t*>(Pu.s) + row_base * b.scaleRowBytes,
+                   (uint32_t)inter * b.scaleRowBytes);
   const rsrc_t xr = make_rsrc(x, (uint32_t)H * 2u);
   uint32_t cc[GPL];
   bool ok[GPL];
@@ -254,8 +309,8 @@ __device__ __forceinline__ void gateup_wave(const uint16_t* __restrict__ x, int 
     cc[j] = ok[j] ? c : nG - 1;
   }
   GateUpItem<GPL, RP> A, B;
-  gu_load<GPL, RP>(A, b, cc, pair_begin);
-  gu_load<GPL, RP>(B, b, cc, pair_begin + RP);
+  gu_load<FMT, GPL, RP>(A, b, cc, pair_begin);
+  gu_load<FMT, GPL, RP>(B, b, cc, pair_begin + RP);
   uint32_t xw[GPL][16];
   float xs[GPL];
 #pragma unroll
@@ -270,17 +325,17 @@ __device__ __forceinline__ void gateup_wave(const uint16_t* __restrict__ x, int 
   }
 #pragma unroll
   for (int j = 0; j < GPL; ++j)
-    xs[j] = (FMT == MOE_WFMT_INT4_G32_F16) ? act_sum<false>(xw[j]) : 0.0f;
+    xs[j] = (FMT != MOE_WFMT_NVFP4) ? act_sum<false>(xw[j]) : 0.0f;
 #pragma unroll
   for (int i = 0; i < ITEMS; i += 2) {
     const int p = pair_begin + i * RP;
     gu_compute<FMT, GPL, RP>(A, xw, xs, ok, gg, gu, p, hrow);
     __builtin_amdgcn_sched_barrier(0);
-    if (i + 2 < ITEMS) gu_load<GPL, RP>(A, b, cc, p + 2 * RP);
+    if (i + 2 < ITEMS) gu_load<FMT, GPL, RP>(A, b, cc, p + 2 * RP);
     __builtin_amdgcn_sched_barrier(0);
     gu_compute<FMT, GPL, RP>(B, xw, xs, ok, gg, gu, p + RP, hrow);
     __builtin_amdgcn_sched_barrier(0);
-    if (i + 3 < ITEMS) gu_load<GPL, RP>(B, b, cc, p + 3 * RP);
+    if (i + 3 < ITEMS) gu_load<FMT, GPL, RP>(B, b, cc, p + 3 * RP);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -728,7 +783,9 @@ __device__ __forceinline__ void down_t1_rows(const DecodeArgs& a, uint4* hl, int
   const int ns = nr + (shared ? 1 : 0);
   const int inter = a.routed.inter;         // routed and shared inter are equal here
   const int nG = inter / 32;
-  const uint32_t rowBytes = (uint32_t)inter / 2;
+  constexpr bool ROW = wfmt_row(FMT);
+  constexpr uint32_t CB = group_code_bytes<FMT>();
+  const uint32_t rowBytes = (uint32_t)inter * wfmt_bits(FMT) / 8;
 
   // slots in ascending expert order (expert, weight; nvfp4: the expert's
   // tensor scale), FUSED: from the workgroup's own selection (sel_e, sel_w in
@@ -783,7 +840,7 @@ __device__ __forceinline__ void down_t1_rows(const DecodeArgs& a, uint4* hl, int
   if constexpr (!FUSED) load_h();
   const bool ok = lane < nG;
   const uint32_t c = ok ? (uint32_t)lane : 0u;
-  const uint32_t srow = (uint32_t)nG * 2u;
+  const uint32_t srow = ROW ? 4u : (uint32_t)nG * 2u;
 
   // B: buffer; routed slots 0..7 and the shared slot
   constexpr int NB = 2;                     // row buffers
@@ -794,13 +851,14 @@ __device__ __forceinline__ void down_t1_rows(const DecodeArgs& a, uint4* hl, int
     for (int s = 0; s < kD1MaxRouted; ++s) {
       if (s < nr) {
         const uint32_t row = (uint32_t)(es[s] * H + r);
-        bload16(wq[b][s], rq, c * 16u, row * rowBytes);
-        wsc[b][s] = bload_u16(rs, c * 2u, row * srow);
+        load_group<FMT>(wq[b][s], rq, c * CB, row * rowBytes);
+        // per-row formats: the row's fp32 scale (the same word in every lane)
+        wsc[b][s] = ROW ? bload_u32(rs, 0u, row * 4u) : bload_u16(rs, c * 2u, row * srow);
       }
     }
     if (shared) {
-      bload16(wqs[b], sq, c * 16u, (uint32_t)r * rowBytes);
-      wscs[b] = bload_u16(ss, c * 2u, (uint32_t)r * srow);
+      load_group<FMT>(wqs[b], sq, c * CB, (uint32_t)r * rowBytes);
+      wscs[b] = ROW ? bload_u32(ss, 0u, (uint32_t)r * 4u) : bload_u16(ss, c * 2u, (uint32_t)r * srow);
     }
   };
   if (gw < H) load_row(std::integral_constant<int, 0>{}, gw);
@@ -829,16 +887,16 @@ __device__ __forceinline__ void down_t1_rows(const DecodeArgs& a, uint4* hl, int
 #pragma unroll
   for (int s = 0; s < kD1MaxRouted; ++s) {
     hsum[s] = 0.0f;
-    if (FMT == MOE_WFMT_INT4_G32_F16 && s < nr) {
+    if (FMT != MOE_WFMT_NVFP4 && s < nr) {
       uint32_t hm[16];
       h_of(s, hm);
-      hsum[s] = int4_offset(hm);
+      hsum[s] = offset_h<FMT>(hm);
     }
   }
-  if (FMT == MOE_WFMT_INT4_G32_F16 && shared) {
+  if (FMT != MOE_WFMT_NVFP4 && shared) {
     uint32_t hm[16];
     h_of(nr, hm);
-    hsums = int4_offset(hm);
+    hsums = offset_h<FMT>(hm);
   }
   // row r from buffer B; row r + nw requested into the other buffer first, or
   // (FUSED, both buffers filled before the first row) row r + 2 nw into this
@@ -853,14 +911,15 @@ __device__ __forceinline__ void down_t1_rows(const DecodeArgs& a, uint4* hl, int
         uint32_t hm[16];
         h_of(s, hm);
         const float d = group_dot_h<FMT>(wq[b][s], wsc[b][s], hm, hsum[s], gsl[s]);
-        acc += ok ? wsl[s] * d : 0.0f;
+        const float ws = ROW ? wsl[s] * __uint_as_float(wsc[b][s]) : wsl[s];
+        acc += ok ? ws * d : 0.0f;
       }
     }
     if (shared) {
       uint32_t hm[16];
       h_of(nr, hm);
       const float d = group_dot_h<FMT>(wqs[b], wscs[b], hm, hsums, gsh);
-      acc += ok ? d : 0.0f;
+      acc += ok ? (ROW ? __uint_as_float(wscs[b]) * d : d) : 0.0f;
     }
     if (FUSED && r + NB * nw < H) load_row(B, r + NB * nw);
     const float v = wave_sum(acc);
@@ -1255,23 +1314,34 @@ __host__ __device__ inline bool down_multi_fits(const DecodeArgs& a) {
          (long long)a.E * a.H * nG * 2 < 0xFFFFFFFFll;
 }
 
+// The formats the small-batch kernels take: f(integral_constant<fmt>).  The
+// per-row int4 and int2 formats run the single-token kernels only (the
+// caller routes other shapes and int8 to the grouped GEMV).
+template <class F>
+auto dec_fmt(int wfmt, F&& f) {
+  switch (wfmt) {
+    case MOE_WFMT_NVFP4: return f(std::integral_constant<int, MOE_WFMT_NVFP4>{});
+    case MOE_WFMT_INT4_ROW_F32: return f(std::integral_constant<int, MOE_WFMT_INT4_ROW_F32>{});
+    case MOE_WFMT_INT2_ROW_F32: return f(std::integral_constant<int, MOE_WFMT_INT2_ROW_F32>{});
+    default: return f(std::integral_constant<int, MOE_WFMT_INT4_G32_F16>{});
+  }
+}
+
 template <int GPL>
 hipError_t launch_k2(const DecodeArgs& a, hipStream_t s, int blocks) {
-  if (a.wfmt == MOE_WFMT_NVFP4)
-    hipLaunchKernelGGL((dec_select_permute_kernel<MOE_WFMT_NVFP4, GPL>), dim3(blocks), dim3(256), 0, s,
-                       a);
-  else
-    hipLaunchKernelGGL((dec_select_permute_kernel<MOE_WFMT_INT4_G32_F16, GPL>), dim3(blocks), dim3(256),
-                       0, s, a);
+  dec_fmt(a.wfmt, [&](auto F) {
+    hipLaunchKernelGGL((dec_select_permute_kernel<decltype(F)::value, GPL>), dim3(blocks), dim3(256), 0, s, a);
+    return 0;
+  });
   return hipGetLastError();
 }
 
 template <int GPL>
 hipError_t launch_k3(const DecodeArgs& a, hipStream_t s, dim3 grid) {
-  if (a.wfmt == MOE_WFMT_NVFP4)
-    hipLaunchKernelGGL((dec_gateup_kernel<MOE_WFMT_NVFP4, GPL>), grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((dec_gateup_kernel<MOE_WFMT_INT4_G32_F16, GPL>), grid, dim3(256), 0, s, a);
+  dec_fmt(a.wfmt, [&](auto F) {
+    hipLaunchKernelGGL((dec_gateup_kernel<decltype(F)::value, GPL>), grid, dim3(256), 0, s, a);
+    return 0;
+  });
   return hipGetLastError();
 }
 
@@ -1297,18 +1367,17 @@ int fused_grid_of() {
   return v > 0 ? v : 0;
 }
 template <int GPL>
-int fused_grid(bool f4) {
-  return f4 ? fused_grid_of<MOE_WFMT_NVFP4, GPL>() : fused_grid_of<MOE_WFMT_INT4_G32_F16, GPL>();
+int fused_grid(int wfmt) {
+  return dec_fmt(wfmt, [&](auto F) { return fused_grid_of<decltype(F)::value, GPL>(); });
 }
 
 template <int GPL>
 hipError_t launch_fused(const DecodeArgs& a, hipStream_t s, size_t lds, int grid) {
-  if (a.wfmt == MOE_WFMT_NVFP4)
-    hipLaunchKernelGGL((dec_fused_t1_kernel<MOE_WFMT_NVFP4, GPL>), dim3(grid), dim3(64 * kFusedWaves),
+  dec_fmt(a.wfmt, [&](auto F) {
+    hipLaunchKernelGGL((dec_fused_t1_kernel<decltype(F)::value, GPL>), dim3(grid), dim3(64 * kFusedWaves),
                        lds, s, a);
-  else
-    hipLaunchKernelGGL((dec_fused_t1_kernel<MOE_WFMT_INT4_G32_F16, GPL>), dim3(grid),
-                       dim3(64 * kFusedWaves), lds, s, a);
+    return 0;
+  });
   return hipGetLastError();
 }
 
@@ -1317,11 +1386,28 @@ hipError_t launch_fused(const DecodeArgs& a, hipStream_t s, size_t lds, int grid
 
 bool decode_supported(int H) { return H / 32 <= 64 * kDecodeMaxGPL; }
 
+bool decode_row_format_ok(const moe_config& c, int T) {
+  if (c.wfmt != MOE_WFMT_INT4_ROW_F32 && c.wfmt != MOE_WFMT_INT2_ROW_F32) return false;
+  if (T != 1 || !decode_supported(c.hidden)) return false;
+  DecodeArgs a{};
+  a.T = 1;
+  a.K = c.top_k;
+  a.E = c.n_routed_experts;
+  a.H = c.hidden;
+  a.routed.inter = c.moe_inter;
+  a.has_shared = c.n_shared_experts == 1;
+  a.shared.inter = c.shared_inter;
+  return down_t1_fits(a);
+}
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
   if (a.T == 0) return hipSuccess;
   hipError_t e;
   const int gpl = (a.H / 32 + 63) / 64;
   const bool f4 = a.wfmt == MOE_WFMT_NVFP4;
+  // per-row formats: single tokens whose down rows fit dec_down_t1 only
+  if (wfmt_row(a.wfmt) && (a.wfmt == MOE_WFMT_INT8_ROW_F32 || a.T != 1 || !down_t1_fits(a)))
+    return hipErrorInvalidValue;
   // one token: selection, the shared expert's gate/up and K3/K4 in
   // dec_fused_t1 when the device's resident grid is known
   int fgrid = 0;
@@ -1329,10 +1415,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
   // and dec_down_t1)
   if (down_t1_fits(a) && !(a.options & MOE_OPT_NO_GRID_WAIT)) {
     switch (gpl) {
-      case 1: fgrid = fused_grid<1>(f4); break;
-      case 2: fgrid = fused_grid<2>(f4); break;
-      case 3: fgrid = fused_grid<3>(f4); break;
-      default: fgrid = fused_grid<4>(f4); break;
+      case 1: fgrid = fused_grid<1>(a.wfmt); break;
+      case 2: fgrid = fused_grid<2>(a.wfmt); break;
+      case 3: fgrid = fused_grid<3>(a.wfmt); break;
+      default: fgrid = fused_grid<4>(a.wfmt); break;
     }
   }
   hipLaunchKernelGGL(dec_router_kernel, dim3(a.E), dim3(256), 0, s, a);
@@ -1378,11 +1464,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
   dim3 g4(a.H / kDownRows);
   if (down_t1_fits(a)) {
     const int blocks = std::min((a.H + 3) / 4, 512);
-    if (f4)
-      hipLaunchKernelGGL((dec_down_t1_kernel<MOE_WFMT_NVFP4>), dim3(blocks), dim3(256), lds1, s, a);
-    else
-      hipLaunchKernelGGL((dec_down_t1_kernel<MOE_WFMT_INT4_G32_F16>), dim3(blocks), dim3(256), lds1, s,
-                         a);
+    dec_fmt(a.wfmt, [&](auto F) {
+      hipLaunchKernelGGL((dec_down_t1_kernel<decltype(F)::value>), dim3(blocks), dim3(256), lds1, s, a);
+      return 0;
+    });
   } else if (a.T > 1 && down_multi_fits<kDMRows>(a)) {
     const int blocks = std::min((a.H + kDMWaves - 1) / kDMWaves, kDMBlocks);
     if (f4)

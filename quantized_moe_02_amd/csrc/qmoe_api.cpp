@@ -480,8 +480,9 @@ moe_status layer_impl(const moe_config* cfg, int32_t T, const uint16_t* x, const
   const size_t P = (size_t)T * cfg->top_k;
   // the single-token and small-batch kernels take the group-scaled formats;
   // small batches in the per-row formats take the grouped GEMV
-  const bool small = T <= kDecodeMaxTokens && decode_supported(cfg->hidden) && !wfmt_row(cfg->wfmt);
-  const bool gemv = T <= kDecodeMaxTokens && wfmt_row(cfg->wfmt);
+  const bool small = T <= kDecodeMaxTokens && decode_supported(cfg->hidden) &&
+                     (!wfmt_row(cfg->wfmt) || decode_row_format_ok(*cfg, T));
+  const bool gemv = T <= kDecodeMaxTokens && wfmt_row(cfg->wfmt) && !small;
   if (!small && !gemv && !gemm_fits(T, (int64_t)P + (has_shared ? T : 0), pad_k(cfg->hidden), ldh))
     return MOE_ERR_UNSUPPORTED;
 

@@ -201,6 +201,9 @@ constexpr int kDecFlagStride = 64;
 constexpr int kDecFusedMaxGrid = 1024;
 constexpr size_t kDecBarrierWords = (size_t)kDecFlagStride * (kDecFusedMaxGrid + 1);
 bool decode_supported(int hidden);
+// Whether a per-row format call of T tokens takes the single-token kernels
+// (per-row int4 and int2, one token, down rows within dec_down_t1's limits).
+bool decode_row_format_ok(const moe_config& c, int T);
 
 struct DecodeArgs {
   const uint16_t* x;

@@ -113,3 +113,18 @@ def test_row_format_cached_layer():
         assert q.moe_cache_get_stats(cache)["evictions"] > 0
     finally:
         q.moe_cache_destroy(cache)
+
+
+@pytest.mark.parametrize("fmt", ["int4_row", "int2_row"])
+@pytest.mark.parametrize("shape", ["tiny", "glm"])
+def test_row_format_single_token_kernels(fmt, shape):
+    """One token in per-row int4 / int2 takes the single-token kernels: the
+    fused kernel and the two-launch form (MOE_OPT_NO_GRID_WAIT) agree bit for
+    bit, and both match the oracle."""
+    geom = synth.small_geom() if shape == "tiny" else dict(synth.WORKLOADS["decode"]["geom"])
+    L = synth.make_custom(geom, 1, fmt, "normal0.1", seed=1600 + len(fmt), device="cuda")
+    y, ids, tw = run_layer(L)
+    y2, ids2, tw2 = run_layer(L, options=q.MOE_OPT_NO_GRID_WAIT)
+    assert torch.equal(y, y2) and torch.equal(ids, ids2) and torch.equal(tw, tw2)
+    ids_g, _ = check_routing(L, ids, tw)
+    check_outputs(L, y, ids_g, ffn_map=FFNCache() if shape == "glm" else None)
