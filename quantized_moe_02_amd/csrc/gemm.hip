@@ -544,6 +544,7 @@ __global__ void __launch_bounds__(256) x_to_f16_kernel(const uint16_t* __restric
 // Work units: for each active expert (ascending) its sorted slots in slices of
 // kBM, then the shared expert's tokens in slices of kBM.
 // tiles[i] = {expert or -1, first h/O row, tokens, first sorted slot or token}.
+template <int BMF>
 __global__ void __launch_bounds__(64) build_units_kernel(const int32_t* __restrict__ offsets,
                                                          const int32_t* __restrict__ active,
                                                          const int32_t* __restrict__ n_active,
@@ -560,11 +561,11 @@ __global__ void __launch_bounds__(64) build_units_kernel(const int32_t* __restri
   for (int a = lane; a < na; a += 64) {
     const int e = active[a];
     const int M = offsets[e + 1] - offsets[e];
-    nfat += M > kBMThin ? (M + kBM - 1) / kBM : 0;
+    nfat += M > kBMThin ? (M + BMF - 1) / BMF : 0;
   }
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) nfat += __shfl_xor(nfat, d, 64);
-  if (has_shared && T > kBMThin) nfat += (T + kBM - 1) / kBM;
+  if (has_shared && T > kBMThin) nfat += (T + BMF - 1) / BMF;
   const int thin_max = nfat < kFewFat ? 0x7fffffff : kBMThin;   // most tokens of a thin-cut expert
   int base = 0, tbase = 0;   // fat units, thin units so far
   for (int a0 = 0; a0 < na; a0 += 64) {
@@ -575,7 +576,7 @@ __global__ void __launch_bounds__(64) build_units_kernel(const int32_t* __restri
       o = offsets[e];
       M = offsets[e + 1] - o;
       nt = M <= thin_max ? (M + kBMThin - 1) / kBMThin : 0;
-      nm = nt ? 0 : (M + kBM - 1) / kBM;
+      nm = nt ? 0 : (M + BMF - 1) / BMF;
     }
     // exclusive prefixes of the fat and thin unit counts across the wave
     int pre = nm, tpre = nt;
@@ -589,8 +590,8 @@ __global__ void __launch_bounds__(64) build_units_kernel(const int32_t* __restri
     }
     const int excl = base + pre - nm;
     for (int i = 0; i < nm; ++i) {
-      const int m0 = i * kBM;
-      tiles[excl + i] = make_int4(e, o + m0, min(kBM, M - m0), o + m0);
+      const int m0 = i * BMF;
+      tiles[excl + i] = make_int4(e, o + m0, min(BMF, M - m0), o + m0);
     }
     for (int i = 0; i < nt; ++i) {
       const int m0 = i * kBMThin;
@@ -606,10 +607,10 @@ __global__ void __launch_bounds__(64) build_units_kernel(const int32_t* __restri
         thin[tbase + i] = make_int4(-1, P + i * kBMThin, min(kBMThin, T - i * kBMThin), i * kBMThin);
       tbase += ns;
     } else {
-      const int ns = (T + kBM - 1) / kBM;
+      const int ns = (T + BMF - 1) / BMF;
       for (int i = lane; i < ns; i += 64) {
-        const int t0 = i * kBM;
-        tiles[base + i] = make_int4(-1, P + t0, min(kBM, T - t0), t0);
+        const int t0 = i * BMF;
+        tiles[base + i] = make_int4(-1, P + t0, min(BMF, T - t0), t0);
       }
       base += ns;
     }
@@ -626,26 +627,31 @@ __global__ void __launch_bounds__(64) build_units_kernel(const int32_t* __restri
 // with more than kBMThin of them, thin units up to kBMThin tokens of an
 // expert (or the shared expert) with at most kBMThin, or of any expert when
 // there would be fewer than kFewFat fat units.
-long fat_units_max(int T, int K, int E, bool has_shared) {
+long fat_units_max(int T, int K, int E, bool has_shared, int bmf) {
   const long P = (long)T * K;
   const long fat_experts = std::min<long>(E, P / (kBMThin + 1));
-  const long routed = (P + kBM - 1) / kBM + fat_experts;
-  const long shared = has_shared && T > kBMThin ? (T + kBM - 1) / kBM : 0;
+  const long routed = (P + bmf - 1) / bmf + fat_experts;
+  const long shared = has_shared && T > kBMThin ? (T + bmf - 1) / bmf : 0;
   return routed + shared;
 }
-long thin_units_max(int T, int K, int E, bool has_shared) {
+long thin_units_max(int T, int K, int E, bool has_shared, int bmf) {
   const long P = (long)T * K;
   // one per expert with at most kBMThin tokens (and the shared expert's one);
   // when fewer than kFewFat fat units are cut up, each gives at most
-  // kBM / kBMThin thin units
-  return std::min<long>(E, P) + (has_shared ? 1 : 0) + (long)(kFewFat - 1) * (kBM / kBMThin);
+  // bmf / kBMThin thin units
+  return std::min<long>(E, P) + (has_shared ? 1 : 0) + (long)(kFewFat - 1) * (bmf / kBMThin);
 }
 
 hipError_t launch_build_units(const int32_t* offsets, const int32_t* active,
                               const int32_t* n_active, int4* tiles, int32_t* n_tiles, int T, int P,
-                              int K, int E, bool has_shared, hipStream_t s) {
-  hipLaunchKernelGGL(build_units_kernel, dim3(1), dim3(64), 0, s, offsets, active, n_active, tiles,
-                     n_tiles, T, P, has_shared ? 1 : 0, (int)fat_units_max(T, K, E, has_shared));
+                              int K, int E, bool has_shared, hipStream_t s, int bmf) {
+  const int thin_off = (int)fat_units_max(T, K, E, has_shared, bmf);
+  if (bmf == kBMQ)
+    hipLaunchKernelGGL(build_units_kernel<kBMQ>, dim3(1), dim3(64), 0, s, offsets, active, n_active, tiles,
+                       n_tiles, T, P, has_shared ? 1 : 0, thin_off);
+  else
+    hipLaunchKernelGGL(build_units_kernel<kBM>, dim3(1), dim3(64), 0, s, offsets, active, n_active, tiles,
+                       n_tiles, T, P, has_shared ? 1 : 0, thin_off);
   return hipGetLastError();
 }
 
@@ -655,10 +661,12 @@ hipError_t launch_build_units(const int32_t* offsets, const int32_t* active,
 // tiles[i] = {expert or -1, first h/O row, tokens, first sorted slot or
 // token}; the thin units start at tiles[thin_off].
 int gemm_max_units(int T, int K, int E, bool has_shared) {
-  return (int)(fat_units_max(T, K, E, has_shared) + thin_units_max(T, K, E, has_shared));
+  // the larger of the two unit tables (fat units of kBM or kBMQ tokens)
+  return (int)std::max(fat_units_max(T, K, E, has_shared, kBM) + thin_units_max(T, K, E, has_shared, kBM),
+                       fat_units_max(T, K, E, has_shared, kBMQ) + thin_units_max(T, K, E, has_shared, kBMQ));
 }
-int gemm_thin_offset(int T, int K, int E, bool has_shared) {
-  return (int)fat_units_max(T, K, E, has_shared);
+int gemm_thin_offset(int T, int K, int E, bool has_shared, int bmf) {
+  return (int)fat_units_max(T, K, E, has_shared, bmf);
 }
 bool gemm_fits(int64_t T, int64_t rows, int64_t ldx, int64_t ldh) {
   return T * ldx * 2 <= (int64_t)kOOBRow && rows * ldh * 2 <= (int64_t)kOOBRow;
@@ -703,8 +711,8 @@ hipError_t launch_gemm(const GemmArgs& g, int K, int E, hipStream_t s, Tracer* t
   hipError_t e;
   int max_inter = g.routed.inter;
   if (g.has_shared && g.shared.inter > max_inter) max_inter = g.shared.inter;
-  const long fat = fat_units_max(g.T, K, E, g.has_shared);
-  const long thin = thin_units_max(g.T, K, E, g.has_shared);
+  const long fat = fat_units_max(g.T, K, E, g.has_shared, kBM);
+  const long thin = thin_units_max(g.T, K, E, g.has_shared, kBM);
   // one workgroup per work item (unit, n tile); items past the actual number
   // of units exit at once
   const int ntg = (max_inter + kGateUpPairs - 1) / kGateUpPairs;

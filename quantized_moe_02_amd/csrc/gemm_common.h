@@ -12,6 +12,7 @@ namespace qmoe {
 
 constexpr int kBM = 128;          // tokens per unit
 constexpr int kBMThin = 32;
+constexpr int kBMQ = kGemmUnitTokensQ;   // fat units of the W4A8 GEMM
 // With fewer fat units than this (gate/up: 16 work items each) the fat
 // launches would leave most of the chip idle, so the experts they would hold
 // are cut into thin units, which run in the thin launch with the bulk of the
@@ -62,7 +63,7 @@ __device__ __forceinline__ int xcd_item(int L, int total) {
 
 // Most work units of each kind for T tokens, top-k K and E experts (the
 // launches are sized to these; units past the built ones exit at once).
-long fat_units_max(int T, int K, int E, bool has_shared);
-long thin_units_max(int T, int K, int E, bool has_shared);
+long fat_units_max(int T, int K, int E, bool has_shared, int bmf);
+long thin_units_max(int T, int K, int E, bool has_shared, int bmf);
 
 }  // namespace qmoe

@@ -104,10 +104,13 @@ __global__ void __launch_bounds__(256) quant_rows_kernel(const uint16_t* __restr
 }
 
 // ---------------------------------------------------------------------------
-// The GEMM.  Same units, work items, XCD mapping and K pipeline as the fp16
-// grouped GEMM (csrc/gemm.hip): four waves, each 64 weight rows x BM tokens;
-// NS K blocks in flight, codes into a register ring, activations straight
-// into LDS.  Stage layout: BM rows of 8 chunks of 16 bytes, chunk c of row r
+// The GEMM.  Same work items, XCD mapping and K pipeline as the fp16 grouped
+// GEMM (csrc/gemm.hip): four waves, each 64 weight rows x BM tokens; NS K
+// blocks in flight, codes into a register ring, activations straight into
+// LDS.  Its fat units hold kBMQ = 192 tokens instead of 128 (the int8 path
+// has the registers, its dequantisation being two masks): at 4096 tokens an
+// expert's weights are then read once instead of twice for most experts
+// (2.95 -> 2.61 ms per layer; 256-token units spill and ran 2.79).  Stage layout: BM rows of 8 chunks of 16 bytes, chunk c of row r
 // at slot r * 8 + (c ^ ((r >> 1) & 7)), so the 16 rows of one B read (two
 // rows per 256-byte bank row) fall on distinct banks.  Load i of wave w covers
 // slots (w NA + i) * 64 .. +63: rows 8 (w NA + i) + lane / 8, slot lane % 8.
@@ -333,6 +336,21 @@ __global__ void __launch_bounds__(256, BM == kBMThin ? 2 : 1) moe_gemm_q_kernel(
     else
       run(ic<1>{});
   } else {
+    if constexpr (BM >= 256) {
+      if (nct > 12) {
+        run(ic<16>{});
+        return;
+      }
+      if (nct > 8) {
+        run(ic<12>{});
+        return;
+      }
+    } else if constexpr (BM > 128) {
+      if (nct > 8) {
+        run(ic<BM / 16>{});
+        return;
+      }
+    }
     if (nct > 4)
       run(ic<8>{});
     else if (nct > 2)
@@ -364,17 +382,17 @@ hipError_t launch_quant_rows(const uint16_t* src, int ld_src, bool bf16, int row
 }
 
 hipError_t launch_gemm_q(const GemmQArgs& g, int proj, int K, int E, hipStream_t s) {
-  const long fat = fat_units_max(g.T, K, E, g.has_shared);
-  const long thin = thin_units_max(g.T, K, E, g.has_shared);
+  const long fat = fat_units_max(g.T, K, E, g.has_shared, kBMQ);
+  const long thin = thin_units_max(g.T, K, E, g.has_shared, kBMQ);
   hipError_t e;
   if (proj == 0) {
     const int max_inter = std::max(g.routed.inter, g.has_shared ? g.shared.inter : 0);
     const int ntg = (max_inter + kGateUpPairs - 1) / kGateUpPairs;
-    if ((e = launch_q<0, kBM>(g, fat, ntg, s)) != hipSuccess) return e;
+    if ((e = launch_q<0, kBMQ>(g, fat, ntg, s)) != hipSuccess) return e;
     return launch_q<0, kBMThin>(g, thin, ntg, s);
   }
   const int ntd = (g.H + kDownRows - 1) / kDownRows;
-  if ((e = launch_q<1, kBM>(g, fat, ntd, s)) != hipSuccess) return e;
+  if ((e = launch_q<1, kBMQ>(g, fat, ntd, s)) != hipSuccess) return e;
   return launch_q<1, kBMThin>(g, thin, ntd, s);
 }
 

@@ -102,16 +102,18 @@ hipError_t run_gemm_ffn(const moe_config& c, int T, const uint16_t* x, const Wor
                         int P, int ldh, uint16_t* h, float* o, hipStream_t stream, Tracer* tr) {
   hipError_t e;
   const int K = has_routed ? c.top_k : 0, E = has_routed ? c.n_routed_experts : 0;
+  const bool a8 = (c.options & MOE_OPT_INT8_ACTIVATIONS) != 0;
+  const int bmf = a8 ? kGemmUnitTokensQ : 128;
   if ((e = launch_build_units(offsets, has_routed ? active : nullptr,
                               has_routed ? n_active : nullptr, w.tiles, w.n_tiles, T, P, K, E,
-                              has_shared, stream)) != hipSuccess)
+                              has_shared, stream, bmf)) != hipSuccess)
     return e;
-  if (c.options & MOE_OPT_INT8_ACTIVATIONS) {
+  if (a8) {
     // W4A8: x -> int8 rows, gate/up (fp16 h), h -> int8 rows, down
     GemmQArgs q{};
     q.tiles = w.tiles;
     q.n_tiles = w.n_tiles;
-    q.thin_off = gemm_thin_offset(T, K, E, has_shared);
+    q.thin_off = gemm_thin_offset(T, K, E, has_shared, bmf);
     q.xq = reinterpret_cast<const int8_t*>(w.x16);
     q.ldxq = pad_k(c.hidden);
     q.xs = w.xs;
