@@ -135,7 +135,8 @@ def algorithmic(geom, wfmt, T, n_active):
 
 KERNEL_SOURCES = {
     "dec_": ["decode.hip", "select_token.h", "qmoe_device.h", "qmoe_internal.h"],
-    "gemm_": ["gemm.hip", "qmoe_device.h", "qmoe_internal.h"],
+    "gemm_": ["gemm.hip", "gemm_i8.hip", "gemm_common.h", "qmoe_device.h", "qmoe_internal.h"],
+    "quant_h": ["gemm_i8.hip", "gemm_common.h", "qmoe_device.h", "qmoe_internal.h"],
     "route_": ["route.hip", "select_token.h", "qmoe_device.h", "qmoe_internal.h"],
     "permute": ["permute.hip", "qmoe_device.h", "qmoe_internal.h"],
     "combine": ["gemv.hip", "qmoe_device.h", "qmoe_internal.h"],
