@@ -32,7 +32,8 @@ PEAK_F16_TFLOPS = 2500.0       # MI355X dense fp16/bf16 MFMA
 PEAK_I8_TOPS = 5000.0          # MI355X dense int8 MFMA
 ALL_WORKLOADS = ["decode", "verify4", "verify64", "prefill4k", "prefill16k", "nvfp4_512",
                  "decode_topp", "verify64_topp", "decode_stream", "decode_stream_warm",
-                 "decode_int4_row", "decode_int8_row", "decode_int2_row", "prefill4k_int4_row",
+                 "decode_int4_row", "decode_int8_row", "decode_int2_row", "verify4_int2_row",
+                 "prefill4k_int4_row",
                  "prefill4k_int8_row", "prefill4k_w4a8", "prefill16k_w4a8", "verify64_w4a8"]
 HEADLINE = "decode"
 # expert streaming from host memory: the decode layer with its 256 routed

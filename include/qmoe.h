@@ -75,8 +75,10 @@
  *                          in 0..3 means q = u - 2 (natural order, four inputs
  *                          per byte from bit 0 up, must be repacked:
  *                          synth.repack_int2_natural); scale float32 [E][N].
- *   The per-row formats run on the grouped GEMV for T <= 4 and on the grouped
- *   GEMM for larger T (moe_layer's single-token kernel takes the other two).
+ *   In moe_layer, per-row int4 and int2 take the small-batch kernels for
+ *   T <= 4 (as the group-scaled formats do), int8 the grouped GEMV
+ *   (moe_expert_ffn_q4 uses the GEMV for all three); the grouped GEMM takes
+ *   all of them for larger T.
  * Gate and up have N = inter, K = hidden; down has N = hidden, K = inter.
  *
  * Activations are bfloat16 [T][hidden], row-major.  For T > 4 the grouped
@@ -352,6 +354,8 @@ moe_status moe_layer_noalloc(const moe_config* cfg, int32_t T, const uint16_t* x
  * host bookkeeping plus two HIP events, created by its first call that makes
  * HIP calls, on the device then current (later calls on another device:
  * MOE_ERR_INVALID_ARG).  Not thread-safe: one thread at a time per cache.
+ * After a call returns MOE_ERR_HIP the slots may not hold what the cache
+ * records: destroy the cache and create a new one.
  *
  * Slot policy.  A call needs the distinct experts its tokens picked (or the
  * experts a prefetch lists); resident ones are hits.  The misses are placed

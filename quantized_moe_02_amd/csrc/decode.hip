@@ -1117,7 +1117,9 @@ __global__ void __launch_bounds__(64 * kDMWaves) dec_down_multi_kernel(DecodeArg
   const int ns = nr + (shared ? 1 : 0);
   const int nG = a.routed.inter / 32;
   const int nrows = P + (shared ? T : 0);
-  const uint32_t rowBytes = (uint32_t)nG * 16u, srow = (uint32_t)nG * 2u;
+  constexpr bool ROW = wfmt_row(FMT);
+  constexpr uint32_t CB = group_code_bytes<FMT>();
+  const uint32_t rowBytes = (uint32_t)nG * CB, srow = (uint32_t)nG * 2u;
 
   // slot `lane`'s record: weight row base, tokens, weights, first h row
   const bool sh_lane = shared && lane == nr;
@@ -1182,8 +1184,9 @@ __global__ void __launch_bounds__(64 * kDMWaves) dec_down_multi_kernel(DecodeArg
     const int sl = __builtin_amdgcn_readfirstlane(is);
     const bool sh = shared && sl == nr;
     const uint32_t row = (uint32_t)__builtin_amdgcn_readlane((int)m_row, sl) + (uint32_t)ir;
-    bload16(wq[b], sh ? sq : rq, c * 16u, row * rowBytes);
-    wsc[b] = bload_u16(sh ? ss : rs, c * 2u, row * srow);
+    load_group<FMT>(wq[b], sh ? sq : rq, c * CB, row * rowBytes);
+    // per-row formats: the row's fp32 scale (the same word in every lane)
+    wsc[b] = ROW ? bload_u32(sh ? ss : rs, 0u, row * 4u) : bload_u16(sh ? ss : rs, c * 2u, row * srow);
     if (iss < N - 1) {
       ++iss;
       if (++is == ns) {
@@ -1203,7 +1206,8 @@ __global__ void __launch_bounds__(64 * kDMWaves) dec_down_multi_kernel(DecodeArg
     hl[L] = in ? make_uint4(hv[u][0], hv[u][1], hv[u][2], hv[u][3]) : make_uint4(0, 0, 0, 0);
   });
   __syncthreads();
-  if (FMT == MOE_WFMT_INT4_G32_F16) {
+  if (FMT != MOE_WFMT_NVFP4) {
+    // each (row, group)'s offset term: int4's, or (int2) the sum of h
     for (int i = threadIdx.x; i < ROWS * 64; i += NT) {
       const int j = i >> 6, g = i & 63;
       uint32_t hm[16];
@@ -1212,7 +1216,7 @@ __global__ void __launch_bounds__(64 * kDMWaves) dec_down_multi_kernel(DecodeArg
         const uint4 v = hl[(j * 4 + q) * 64 + g];
         hm[4 * q] = v.x; hm[4 * q + 1] = v.y; hm[4 * q + 2] = v.z; hm[4 * q + 3] = v.w;
       }
-      hsl[i] = int4_offset(hm);
+      hsl[i] = offset_h<FMT>(hm);
     }
     __syncthreads();
   }
@@ -1232,9 +1236,15 @@ __global__ void __launch_bounds__(64 * kDMWaves) dec_down_multi_kernel(DecodeArg
     // the codes as 16-bit float pairs, once for all tokens of the slot
     uint32_t wf[16];
     float sc0, sc1 = 0.0f;
-    if constexpr (FMT == MOE_WFMT_INT4_G32_F16) {
+    if constexpr (FMT == MOE_WFMT_INT4_G32_F16 || FMT == MOE_WFMT_INT4_ROW_F32) {
       int4_f16_1024(wq[b], wf);
-      sc0 = half_bits_to_f32(wsc[b] & 0xffffu);
+      sc0 = ROW ? __uint_as_float(wsc[b]) : half_bits_to_f32(wsc[b] & 0xffffu);
+    } else if constexpr (FMT == MOE_WFMT_INT2_ROW_F32) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) wf[8 * j + k] = int2_pair_f16(wq[b][j], k, 0x3C003C00u);
+      sc0 = 4.0f * __uint_as_float(wsc[b]);
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -1257,8 +1267,13 @@ __global__ void __launch_bounds__(64 * kDMWaves) dec_down_multi_kernel(DecodeArg
           hm[4 * q] = v.x; hm[4 * q + 1] = v.y; hm[4 * q + 2] = v.z; hm[4 * q + 3] = v.w;
         }
         float v;
-        if constexpr (FMT == MOE_WFMT_INT4_G32_F16) {
+        if constexpr (FMT == MOE_WFMT_INT4_G32_F16 || FMT == MOE_WFMT_INT4_ROW_F32) {
           v = sc0 * (int4_dot_1024(wf, hm) - hslane[j * 64]);   // offset staged with h
+        } else if constexpr (FMT == MOE_WFMT_INT2_ROW_F32) {
+          float d = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) d = dot2_f16(wf[i], hm[i], d);
+          v = sc0 * fmaf(-1.5f, hslane[j * 64], d);   // 4 s (d - 1.5 sum h)
         } else {
           float d0 = 0.0f, d1 = 0.0f;
 #pragma unroll
@@ -1388,16 +1403,16 @@ bool decode_supported(int H) { return H / 32 <= 64 * kDecodeMaxGPL; }
 
 bool decode_row_format_ok(const moe_config& c, int T) {
   if (c.wfmt != MOE_WFMT_INT4_ROW_F32 && c.wfmt != MOE_WFMT_INT2_ROW_F32) return false;
-  if (T != 1 || !decode_supported(c.hidden)) return false;
+  if (T < 1 || T > kDecodeMaxTokens || !decode_supported(c.hidden)) return false;
   DecodeArgs a{};
-  a.T = 1;
+  a.T = T;
   a.K = c.top_k;
   a.E = c.n_routed_experts;
   a.H = c.hidden;
   a.routed.inter = c.moe_inter;
   a.has_shared = c.n_shared_experts == 1;
   a.shared.inter = c.shared_inter;
-  return down_t1_fits(a);
+  return T == 1 ? down_t1_fits(a) : down_multi_fits<kDMRows>(a);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
@@ -1405,8 +1420,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
   hipError_t e;
   const int gpl = (a.H / 32 + 63) / 64;
   const bool f4 = a.wfmt == MOE_WFMT_NVFP4;
-  // per-row formats: single tokens whose down rows fit dec_down_t1 only
-  if (wfmt_row(a.wfmt) && (a.wfmt == MOE_WFMT_INT8_ROW_F32 || a.T != 1 || !down_t1_fits(a)))
+  // per-row formats: shapes whose down rows fit dec_down_t1 (one token) or
+  // dec_down_multi (2-4 tokens) only
+  if (wfmt_row(a.wfmt) && (a.wfmt == MOE_WFMT_INT8_ROW_F32 ||
+                           !(a.T == 1 ? down_t1_fits(a) : down_multi_fits<kDMRows>(a))))
     return hipErrorInvalidValue;
   // one token: selection, the shared expert's gate/up and K3/K4 in
   // dec_fused_t1 when the device's resident grid is known
@@ -1470,12 +1487,11 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
     });
   } else if (a.T > 1 && down_multi_fits<kDMRows>(a)) {
     const int blocks = std::min((a.H + kDMWaves - 1) / kDMWaves, kDMBlocks);
-    if (f4)
-      hipLaunchKernelGGL((dec_down_multi_kernel<MOE_WFMT_NVFP4, kDMRows, kDMDepth>), dim3(blocks),
+    dec_fmt(a.wfmt, [&](auto F) {
+      hipLaunchKernelGGL((dec_down_multi_kernel<decltype(F)::value, kDMRows, kDMDepth>), dim3(blocks),
                          dim3(64 * kDMWaves), 0, s, a);
-    else
-      hipLaunchKernelGGL((dec_down_multi_kernel<MOE_WFMT_INT4_G32_F16, kDMRows, kDMDepth>),
-                         dim3(blocks), dim3(64 * kDMWaves), 0, s, a);
+      return 0;
+    });
   } else if (a.T == 1) {
     if (f4)
       hipLaunchKernelGGL((dec_down_combine_kernel<MOE_WFMT_NVFP4, 1>), g4, dim3(256), 0, s, a);

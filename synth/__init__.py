@@ -67,6 +67,7 @@ WORKLOADS: Dict[str, dict] = {
     "decode_int4_row":    dict(index=1, geom=_GLM, tokens=1,    wfmt="int4_row", bias="zero"),
     "decode_int8_row":    dict(index=1, geom=_GLM, tokens=1,    wfmt="int8_row", bias="zero"),
     "decode_int2_row":    dict(index=1, geom=_GLM, tokens=1,    wfmt="int2_row", bias="zero"),
+    "verify4_int2_row":   dict(index=2, geom=_GLM, tokens=4,    wfmt="int2_row", bias="hot16"),
     "prefill4k_int4_row": dict(index=3, geom=_GLM, tokens=4096, wfmt="int4_row", bias="zero"),
     "prefill4k_int8_row": dict(index=3, geom=_GLM, tokens=4096, wfmt="int8_row", bias="zero"),
     # the W4A8 integer-dot path (per-row int4 weights, int8 activations;

@@ -128,3 +128,16 @@ def test_row_format_single_token_kernels(fmt, shape):
     assert torch.equal(y, y2) and torch.equal(ids, ids2) and torch.equal(tw, tw2)
     ids_g, _ = check_routing(L, ids, tw)
     check_outputs(L, y, ids_g, ffn_map=FFNCache() if shape == "glm" else None)
+
+
+@pytest.mark.parametrize("fmt", ["int4_row", "int2_row"])
+@pytest.mark.parametrize("T", [2, 3, 4])
+def test_row_format_small_batch_kernels(fmt, T):
+    """2-4 tokens in per-row int4 / int2 take the small-batch kernels (K2, K3,
+    the multi-token down kernel) at the GLM-5.2 shape: every token against the
+    oracle."""
+    geom = dict(synth.WORKLOADS["verify4"]["geom"])
+    L = synth.make_custom(geom, T, fmt, "hot16", seed=1700 + T, device="cuda")
+    y, ids, tw = run_layer(L)
+    ids_g, _ = check_routing(L, ids, tw)
+    check_outputs(L, y, ids_g, ffn_map=FFNCache())
