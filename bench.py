@@ -138,7 +138,7 @@ KERNEL_SOURCES = {
     "dec_": ["decode.hip", "select_token.h", "qmoe_device.h", "qmoe_internal.h"],
     "gemm_": ["gemm.hip", "gemm_i8.hip", "gemm_common.h", "qmoe_device.h", "qmoe_internal.h"],
     "quant_h": ["gemm_i8.hip", "gemm_common.h", "qmoe_device.h", "qmoe_internal.h"],
-    "route_": ["route.hip", "select_token.h", "qmoe_device.h", "qmoe_internal.h"],
+    "route_": ["route.hip", "decode.hip", "select_token.h", "qmoe_device.h", "qmoe_internal.h"],
     "permute": ["permute.hip", "qmoe_device.h", "qmoe_internal.h"],
     "combine": ["gemv.hip", "qmoe_device.h", "qmoe_internal.h"],
     "gateup_gemv": ["gemv.hip", "qmoe_device.h", "qmoe_internal.h"],

@@ -343,65 +343,78 @@ __device__ __forceinline__ void gateup_wave(const uint16_t* __restrict__ x, int 
 // ---------------------------------------------------------------------------
 // K1: router scores sigmoid(logit) in float64, one block per expert
 // ---------------------------------------------------------------------------
-// The first workgroups also zero dec_fused_t1's barrier count and flags.
-__global__ void __launch_bounds__(256) dec_router_kernel(DecodeArgs a) {
+// scores[t][e] for expert e = blockIdx.x and the T <= kMaxT tokens of x (one
+// block of 256 threads: the four waves take quarters of the hidden dimension,
+// then their partial sums are added in wave order).
+__device__ __forceinline__ void router_scores_block(const uint16_t* __restrict__ x,
+                                                    const float* __restrict__ router_w,
+                                                    double* __restrict__ scores, int T, int H, int E) {
   __shared__ double rpart[4][kMaxT];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int e = blockIdx.x;
+  const int q0 = wv * (H / 4), q1 = q0 + H / 4;
+  const float* wrow = router_w + (size_t)e * H;
+  double acc[kMaxT];
+#pragma unroll
+  for (int t = 0; t < kMaxT; ++t) acc[t] = 0.0;
+  for (int h0 = q0; h0 < q1; h0 += 256 * kRouterUnroll) {
+    float4 w4[kRouterUnroll];
+    uint2 xv[kRouterUnroll][kMaxT];
+    bool ok[kRouterUnroll];
+#pragma unroll
+    for (int i = 0; i < kRouterUnroll; ++i) {
+      const int h_raw = h0 + 256 * i + lane * 4;
+      ok[i] = h_raw < q1;
+      const int h = ok[i] ? h_raw : q0;
+      w4[i] = *reinterpret_cast<const float4*>(wrow + h);
+#pragma unroll
+      for (int t = 0; t < kMaxT; ++t)
+        xv[i][t] = *reinterpret_cast<const uint2*>(x + (size_t)(t < T ? t : 0) * H + h);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < kRouterUnroll; ++i) {
+      if (!ok[i]) continue;
+#pragma unroll
+      for (int t = 0; t < kMaxT; ++t) {
+        double s2 = acc[t];
+        s2 = fma((double)bf16_lo(xv[i][t].x), (double)w4[i].x, s2);
+        s2 = fma((double)bf16_hi(xv[i][t].x), (double)w4[i].y, s2);
+        s2 = fma((double)bf16_lo(xv[i][t].y), (double)w4[i].z, s2);
+        s2 = fma((double)bf16_hi(xv[i][t].y), (double)w4[i].w, s2);
+        acc[t] = s2;
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < kMaxT; ++t) {
+    const double v = wave_sum(acc[t]);
+    if (lane == 0) rpart[wv][t] = v;
+  }
+  __syncthreads();
+  // the sigmoid score: the selection reads scores, not logits
+  if (threadIdx.x < T) {
+    const double l = ((rpart[0][threadIdx.x] + rpart[1][threadIdx.x]) + rpart[2][threadIdx.x]) +
+                     rpart[3][threadIdx.x];
+    scores[(size_t)threadIdx.x * E + e] = 1.0 / (1.0 + exp(-l));
+  }
+}
+
+// The first workgroups also zero dec_fused_t1's barrier count and flags.
+__global__ void __launch_bounds__(256) dec_router_kernel(DecodeArgs a) {
   for (int i = (int)blockIdx.x * 256 + (int)threadIdx.x; i <= kDecFusedMaxGrid; i += (int)gridDim.x * 256)
     a.bar[kDecFlagStride * i] = 0u;
   if (blockIdx.x == 0 && threadIdx.x == 0) a.flags[0] = 0u;
-  {
-    // expert e's logits: the four waves take quarters of the hidden dimension
-    const int e = blockIdx.x;
-    const int H = a.H, T = a.T;
-    const int q0 = wv * (H / 4), q1 = q0 + H / 4;
-    const float* wrow = a.router_w + (size_t)e * H;
-    double acc[kMaxT];
-#pragma unroll
-    for (int t = 0; t < kMaxT; ++t) acc[t] = 0.0;
-    for (int h0 = q0; h0 < q1; h0 += 256 * kRouterUnroll) {
-      float4 w4[kRouterUnroll];
-      uint2 xv[kRouterUnroll][kMaxT];
-      bool ok[kRouterUnroll];
-#pragma unroll
-      for (int i = 0; i < kRouterUnroll; ++i) {
-        const int h_raw = h0 + 256 * i + lane * 4;
-        ok[i] = h_raw < q1;
-        const int h = ok[i] ? h_raw : q0;
-        w4[i] = *reinterpret_cast<const float4*>(wrow + h);
-#pragma unroll
-        for (int t = 0; t < kMaxT; ++t)
-          xv[i][t] = *reinterpret_cast<const uint2*>(a.x + (size_t)(t < T ? t : 0) * H + h);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < kRouterUnroll; ++i) {
-        if (!ok[i]) continue;
-#pragma unroll
-        for (int t = 0; t < kMaxT; ++t) {
-          double s2 = acc[t];
-          s2 = fma((double)bf16_lo(xv[i][t].x), (double)w4[i].x, s2);
-          s2 = fma((double)bf16_hi(xv[i][t].x), (double)w4[i].y, s2);
-          s2 = fma((double)bf16_lo(xv[i][t].y), (double)w4[i].z, s2);
-          s2 = fma((double)bf16_hi(xv[i][t].y), (double)w4[i].w, s2);
-          acc[t] = s2;
-        }
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < kMaxT; ++t) {
-      const double v = wave_sum(acc[t]);
-      if (lane == 0) rpart[wv][t] = v;
-    }
-    __syncthreads();
-    // the sigmoid score: the selection reads scores, not logits
-    if (threadIdx.x < T) {
-      const double l = ((rpart[0][threadIdx.x] + rpart[1][threadIdx.x]) + rpart[2][threadIdx.x]) +
-                       rpart[3][threadIdx.x];
-      a.logits[(size_t)threadIdx.x * a.E + e] = 1.0 / (1.0 + exp(-l));
-    }
-  }
+  router_scores_block(a.x, a.router_w, a.logits, a.T, a.H, a.E);
+}
+
+// The same scores for moe_route and the split path of moe_layer at T <= kMaxT.
+__global__ void __launch_bounds__(256) route_scores_kernel(const uint16_t* __restrict__ x,
+                                                           const float* __restrict__ router_w,
+                                                           double* __restrict__ scores, int T, int H,
+                                                           int E) {
+  router_scores_block(x, router_w, scores, T, H, E);
 }
 
 // ---------------------------------------------------------------------------
@@ -1398,6 +1411,13 @@ hipError_t launch_fused(const DecodeArgs& a, hipStream_t s, size_t lds, int grid
 
 
 }  // namespace
+
+hipError_t launch_route_scores(const uint16_t* x, const float* router_w, double* scores, int T, int H,
+                               int E, hipStream_t s) {
+  if (T < 1 || T > kMaxT || H % 16 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(route_scores_kernel, dim3(E), dim3(256), 0, s, x, router_w, scores, T, H, E);
+  return hipGetLastError();
+}
 
 bool decode_supported(int H) { return H / 32 <= 64 * kDecodeMaxGPL; }
 

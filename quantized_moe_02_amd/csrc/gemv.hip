@@ -12,6 +12,9 @@
 // wave at the end.
 //   gate/up  x (bf16) . deq(Wg), deq(Wu), then h = silu(g) * u, stored fp16.
 //   down     h (fp16) . deq(Wd), fp32 out per pick.
+// A slot's tokens go through the weights two per pass, an odd last one
+// alone (most decode slots hold one token, whose pass then does no extra
+// arithmetic).
 // Grid: (row blocks, expert slots); slot s < max_slots is the s-th active
 // expert of the permutation (blocks past n_active exit), the last slot is the
 // expert applied to every token (shared expert or dense mode).
@@ -20,9 +23,6 @@
 namespace qmoe {
 namespace {
 
-constexpr int kRPW = 4;                  // output rows per wave (gate/up: row pairs)
-constexpr int kRowsPerBlock = 4 * kRPW;  // 4 waves per block
-constexpr int kTB = 2;                   // tokens per pass over the weights
 
 struct Slot {
   bool ok;
@@ -64,12 +64,12 @@ __device__ __forceinline__ void load16(uint32_t* dst, const void* p) {
   dst[3] = v.w;
 }
 
-// One 32-input group of one weight row against kTB activation groups.
+// One 32-input group of one weight row against TB activation groups.
 // acc[tb] += sum_k w_k * act_k for the group.
-template <int FMT, bool F16ACT>
+template <int FMT, bool F16ACT, int TB>
 __device__ __forceinline__ void group_dot(const uint32_t (&wq)[4], uint32_t sc,
-                                          const uint32_t (&act)[kTB][16], const float (&asum)[kTB],
-                                          float gs, float (&acc)[kTB]) {
+                                          const uint32_t (&act)[TB][16], const float (&asum)[TB],
+                                          float gs, float (&acc)[TB]) {
   if constexpr (FMT == MOE_WFMT_INT4_G32_F16) {
     uint32_t p[16];
 #pragma unroll
@@ -79,7 +79,7 @@ __device__ __forceinline__ void group_dot(const uint32_t (&wq)[4], uint32_t sc,
         p[4 * j + k] = F16ACT ? int4_pair_f16(wq[j], k) : int4_pair_bf16(wq[j], k);
     const float s16 = 16.0f * half_bits_to_f32(sc & 0xffffu);
 #pragma unroll
-    for (int tb = 0; tb < kTB; ++tb) {
+    for (int tb = 0; tb < TB; ++tb) {
       float d = 0.0f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) d = F16ACT ? dot2_f16(p[i], act[tb][i], d) : dot2_bf16(p[i], act[tb][i], d);
@@ -94,7 +94,7 @@ __device__ __forceinline__ void group_dot(const uint32_t (&wq)[4], uint32_t sc,
     const float s0 = e4m3_to_f32(sc, 0) * gs;
     const float s1 = e4m3_to_f32(sc, 1) * gs;
 #pragma unroll
-    for (int tb = 0; tb < kTB; ++tb) {
+    for (int tb = 0; tb < TB; ++tb) {
       float d0 = 0.0f, d1 = 0.0f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) d0 = F16ACT ? dot2_f16(p[i], act[tb][i], d0) : dot2_bf16(p[i], act[tb][i], d0);
@@ -116,20 +116,20 @@ __device__ __forceinline__ uint32_t load_scale(const void* s, size_t row, int nG
 }
 
 // Per-row-scale formats: one 32-input group of one row (BITS 32-bit code
-// words) against kTB activation groups, without the row scale (applied once
+// words) against TB activation groups, without the row scale (applied once
 // per row after the reduction).  acc[tb] += sum_k q_k * act_k.
 //   int4: 1 + u/16 pairs, sum (u-8) a = 16 (d - 1.5 A)
 //   int2: 1 + u/4 pairs,  sum (u-2) a = 4 (d - 1.5 A)
 //   int8: u = q + 128; bf16 activations: fp32 products, sum q a = d - 128 A;
 //         fp16 activations: 1024 + u pairs, sum q a = d - 1152 A
 // with d the dot product of the formed values and A the activation sum.
-template <int FMT, bool F16ACT>
-__device__ __forceinline__ void group_dot_row(const uint32_t* wq, const uint32_t (&act)[kTB][16],
-                                              const float (&asum)[kTB], float (&acc)[kTB]) {
+template <int FMT, bool F16ACT, int TB>
+__device__ __forceinline__ void group_dot_row(const uint32_t* wq, const uint32_t (&act)[TB][16],
+                                              const float (&asum)[TB], float (&acc)[TB]) {
   if constexpr (FMT == MOE_WFMT_INT8_ROW_F32 && !F16ACT) {
-    float d[kTB];
+    float d[TB];
 #pragma unroll
-    for (int tb = 0; tb < kTB; ++tb) d[tb] = 0.0f;
+    for (int tb = 0; tb < TB; ++tb) d[tb] = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const uint32_t w = wq[j] ^ 0x80808080u;
@@ -137,7 +137,7 @@ __device__ __forceinline__ void group_dot_row(const uint32_t* wq, const uint32_t
 #pragma unroll
       for (int b = 0; b < 4; ++b) u[b] = (float)((w >> (8 * b)) & 0xffu);
 #pragma unroll
-      for (int tb = 0; tb < kTB; ++tb) {
+      for (int tb = 0; tb < TB; ++tb) {
         const uint32_t x01 = act[tb][2 * j], x23 = act[tb][2 * j + 1];
         d[tb] = fmaf(u[0], __uint_as_float(x01 << 16), d[tb]);
         d[tb] = fmaf(u[1], __uint_as_float(x01 & 0xffff0000u), d[tb]);
@@ -146,7 +146,7 @@ __device__ __forceinline__ void group_dot_row(const uint32_t* wq, const uint32_t
       }
     }
 #pragma unroll
-    for (int tb = 0; tb < kTB; ++tb) acc[tb] += fmaf(-128.0f, asum[tb], d[tb]);
+    for (int tb = 0; tb < TB; ++tb) acc[tb] += fmaf(-128.0f, asum[tb], d[tb]);
   } else {
     uint32_t p[16];
     float mul, off;
@@ -177,7 +177,7 @@ __device__ __forceinline__ void group_dot_row(const uint32_t* wq, const uint32_t
       off = -1.5f;
     }
 #pragma unroll
-    for (int tb = 0; tb < kTB; ++tb) {
+    for (int tb = 0; tb < TB; ++tb) {
       float d = 0.0f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) d = F16ACT ? dot2_f16(p[i], act[tb][i], d) : dot2_bf16(p[i], act[tb][i], d);
@@ -205,16 +205,60 @@ __device__ __forceinline__ float row_scale(const void* s, size_t row) {
   return wfmt_row(FMT) ? reinterpret_cast<const float*>(s)[row] : 1.0f;
 }
 
+#ifndef QMOE_GU_RPW
+#define QMOE_GU_RPW 4
+#endif
+#ifndef QMOE_GU_RPW8
+#define QMOE_GU_RPW8 1
+#endif
+#ifndef QMOE_DN_RPW
+#define QMOE_DN_RPW 4
+#endif
+#ifndef QMOE_DN_RPW8
+#define QMOE_DN_RPW8 4
+#endif
+// Rows (gate/up: row pairs) per wave.  int8's 32-byte groups take one row
+// pair in gate/up: more waves in flight (45 us at one token against 48 with
+// two row pairs and 58 with four); two rows per wave elsewhere measured no
+// better.
 template <int FMT>
-__global__ void __launch_bounds__(256) gateup_gemv_kernel(FfnArgs a) {
+constexpr int gu_rpw() {
+  return wfmt_bits(FMT) == 8 ? QMOE_GU_RPW8 : QMOE_GU_RPW;
+}
+template <int FMT>
+constexpr int dn_rpw() {
+  return wfmt_bits(FMT) == 8 ? QMOE_DN_RPW8 : QMOE_DN_RPW;
+}
+
+// The registers of one group step of a pass: codes (and group scale words) of
+// the wave's RPW rows in NP projections, and the TB tokens' 32 inputs.
+template <int FMT, int TB, int NP, int RPW>
+struct GemvStep {
+  uint32_t q[NP][RPW][wfmt_bits(FMT)];
+  uint32_t sc[NP][RPW];
+  uint32_t act[TB][16];
+};
+
+// The group steps c = lane, lane + 64, ... < nG of a pass.  (Issuing step
+// i + 1's loads before step i is reduced measured slower: 90.4 against 88.9
+// us per int8 single-token call, at half the waves per SIMD.)
+template <class Step, class Load, class Compute>
+__device__ __forceinline__ void group_steps(int nG, Load load, Compute compute) {
+  for (int c = threadIdx.x & 63; c < nG; c += 64) {
+    Step st;
+    load(st, c);
+    compute(st, c);
+  }
+}
+
+// Gate/up of tokens m0 .. m0 + TB - 1 of a slot (TB = 2 while two remain,
+// then 1): each pass streams the wave's rows once.
+template <int FMT, int TB>
+__device__ __forceinline__ void gateup_pass(const FfnArgs& a, const Slot& sl, const ExpertSet& X,
+                                            int row0, int m0) {
+  constexpr int RPW = gu_rpw<FMT>();
   const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
-  const Slot sl = resolve_slot(a, blockIdx.y);
-  if (!sl.ok) return;
-  const ExpertSet& X = sl.routed ? a.routed : a.dense;
   const int inter = X.inter;
-  const int row0 = blockIdx.x * kRowsPerBlock + wv * kRPW;
-  if (row0 >= inter) return;
   const int H = a.H;
   const int nG = H / 32;
   constexpr int BITS = wfmt_bits(FMT);
@@ -224,78 +268,92 @@ __global__ void __launch_bounds__(256) gateup_gemv_kernel(FfnArgs a) {
   const float gg = (FMT == MOE_WFMT_NVFP4) ? X.gate.g[sl.e] : 1.0f;
   const float gu = (FMT == MOE_WFMT_NVFP4) ? X.up.g[sl.e] : 1.0f;
   uint16_t* hbase = sl.routed ? a.h_routed + (size_t)sl.tok_begin * a.ldh : a.h_dense;
+  int tok[TB];
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb) tok[tb] = token_of(a, sl, m0 + tb);
+  float ag[RPW][TB], au[RPW][TB];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r)
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) ag[r][tb] = au[r][tb] = 0.0f;
 
-  for (int m0 = 0; m0 < sl.M; m0 += kTB) {
-    int tok[kTB];
+  using Step = GemvStep<FMT, TB, 2, RPW>;
+  auto load = [&](Step& st, int c) {
 #pragma unroll
-    for (int tb = 0; tb < kTB; ++tb) tok[tb] = token_of(a, sl, min(m0 + tb, sl.M - 1));
-    float ag[kRPW][kTB], au[kRPW][kTB];
-#pragma unroll
-    for (int r = 0; r < kRPW; ++r)
-#pragma unroll
-      for (int tb = 0; tb < kTB; ++tb) ag[r][tb] = au[r][tb] = 0.0f;
-
-    for (int c = lane; c < nG; c += 64) {
-      uint32_t xw[kTB][16];
-      float xs[kTB];
-#pragma unroll
-      for (int tb = 0; tb < kTB; ++tb) {
-        const uint16_t* xp = a.x + (size_t)tok[tb] * H + (size_t)c * 32;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) load16(&xw[tb][4 * q], xp + 8 * q);
-        float s = 0.0f;
-        if constexpr (FMT != MOE_WFMT_NVFP4) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) s = dot2_bf16(xw[tb][i], 0x3F803F80u, s);
-        }
-        xs[tb] = s;
-      }
-#pragma unroll
-      for (int r = 0; r < kRPW; ++r) {
-        const size_t row = rbase + row0 + r;
-        uint32_t wq[BITS];
-        load_codes<FMT>(wq, X.gate.q + row * rowBytes + (size_t)c * (4 * BITS));
-        if constexpr (ROW) {
-          group_dot_row<FMT, false>(wq, xw, xs, ag[r]);
-        } else {
-          group_dot<FMT, false>(*reinterpret_cast<const uint32_t(*)[4]>(wq),
-                                load_scale<FMT>(X.gate.s, row, nG, c), xw, xs, gg, ag[r]);
-        }
-        load_codes<FMT>(wq, X.up.q + row * rowBytes + (size_t)c * (4 * BITS));
-        if constexpr (ROW) {
-          group_dot_row<FMT, false>(wq, xw, xs, au[r]);
-        } else {
-          group_dot<FMT, false>(*reinterpret_cast<const uint32_t(*)[4]>(wq),
-                                load_scale<FMT>(X.up.s, row, nG, c), xw, xs, gu, au[r]);
-        }
+    for (int r = 0; r < RPW; ++r) {
+      const size_t row = rbase + row0 + r;
+      load_codes<FMT>(st.q[0][r], X.gate.q + row * rowBytes + (size_t)c * (4 * BITS));
+      load_codes<FMT>(st.q[1][r], X.up.q + row * rowBytes + (size_t)c * (4 * BITS));
+      if constexpr (!ROW) {
+        st.sc[0][r] = load_scale<FMT>(X.gate.s, row, nG, c);
+        st.sc[1][r] = load_scale<FMT>(X.up.s, row, nG, c);
       }
     }
 #pragma unroll
-    for (int r = 0; r < kRPW; ++r)
+    for (int tb = 0; tb < TB; ++tb) {
+      const uint16_t* xp = a.x + (size_t)tok[tb] * H + (size_t)c * 32;
 #pragma unroll
-      for (int tb = 0; tb < kTB; ++tb) {
-        const size_t row = rbase + row0 + r;
-        const float g = wave_sum(ag[r][tb]) * row_scale<FMT>(X.gate.s, row);
-        const float u = wave_sum(au[r][tb]) * row_scale<FMT>(X.up.s, row);
-        if (lane == r * kTB + tb && m0 + tb < sl.M) {
-          const _Float16 hv = (_Float16)silu_mul(g, u);
-          hbase[(size_t)(m0 + tb) * a.ldh + row0 + r] = __builtin_bit_cast(uint16_t, hv);
-        }
+      for (int q = 0; q < 4; ++q) load16(&st.act[tb][4 * q], xp + 8 * q);
+    }
+  };
+  auto compute = [&](const Step& st, int) {
+    float xs[TB];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      float s = 0.0f;
+      if constexpr (FMT != MOE_WFMT_NVFP4) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s = dot2_bf16(st.act[tb][i], 0x3F803F80u, s);
       }
-  }
+      xs[tb] = s;
+    }
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      if constexpr (ROW) {
+        group_dot_row<FMT, false, TB>(st.q[0][r], st.act, xs, ag[r]);
+        group_dot_row<FMT, false, TB>(st.q[1][r], st.act, xs, au[r]);
+      } else {
+        group_dot<FMT, false, TB>(st.q[0][r], st.sc[0][r], st.act, xs, gg, ag[r]);
+        group_dot<FMT, false, TB>(st.q[1][r], st.sc[1][r], st.act, xs, gu, au[r]);
+      }
+    }
+  };
+  group_steps<Step>(nG, load, compute);
+#pragma unroll
+  for (int r = 0; r < RPW; ++r)
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      const size_t row = rbase + row0 + r;
+      const float g = wave_sum(ag[r][tb]) * row_scale<FMT>(X.gate.s, row);
+      const float u = wave_sum(au[r][tb]) * row_scale<FMT>(X.up.s, row);
+      if (lane == r * TB + tb) {
+        const _Float16 hv = (_Float16)silu_mul(g, u);
+        hbase[(size_t)(m0 + tb) * a.ldh + row0 + r] = __builtin_bit_cast(uint16_t, hv);
+      }
+    }
 }
 
 template <int FMT>
-__global__ void __launch_bounds__(256) down_gemv_kernel(FfnArgs a) {
-  const int lane = threadIdx.x & 63;
+__global__ void __launch_bounds__(256) gateup_gemv_kernel(FfnArgs a) {
   const int wv = threadIdx.x >> 6;
   const Slot sl = resolve_slot(a, blockIdx.y);
   if (!sl.ok) return;
   const ExpertSet& X = sl.routed ? a.routed : a.dense;
+  const int row0 = (blockIdx.x * 4 + wv) * gu_rpw<FMT>();
+  if (row0 >= X.inter) return;
+  int m0 = 0;
+  for (; m0 + 2 <= sl.M; m0 += 2) gateup_pass<FMT, 2>(a, sl, X, row0, m0);
+  if (m0 < sl.M) gateup_pass<FMT, 1>(a, sl, X, row0, m0);
+}
+
+// Down of tokens m0 .. m0 + TB - 1 of a slot, as gateup_pass.
+template <int FMT, int TB>
+__device__ __forceinline__ void down_pass(const FfnArgs& a, const Slot& sl, const ExpertSet& X,
+                                          int row0, int m0) {
+  constexpr int RPW = dn_rpw<FMT>();
+  const int lane = threadIdx.x & 63;
   const int inter = X.inter;
   const int H = a.H;
-  const int row0 = blockIdx.x * kRowsPerBlock + wv * kRPW;
-  if (row0 >= H) return;
   const int nG = inter / 32;
   constexpr int BITS = wfmt_bits(FMT);
   constexpr bool ROW = wfmt_row(FMT);
@@ -304,52 +362,67 @@ __global__ void __launch_bounds__(256) down_gemv_kernel(FfnArgs a) {
   const float gd = (FMT == MOE_WFMT_NVFP4) ? X.down.g[sl.e] : 1.0f;
   const uint16_t* hbase = sl.routed ? a.h_routed + (size_t)sl.tok_begin * a.ldh : a.h_dense;
   float* obase = sl.routed ? a.o_routed + (size_t)sl.tok_begin * H : a.o_dense;
+  float acc[RPW][TB];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r)
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) acc[r][tb] = 0.0f;
 
-  for (int m0 = 0; m0 < sl.M; m0 += kTB) {
-    int mm[kTB];
+  using Step = GemvStep<FMT, TB, 1, RPW>;
+  auto load = [&](Step& st, int c) {
 #pragma unroll
-    for (int tb = 0; tb < kTB; ++tb) mm[tb] = min(m0 + tb, sl.M - 1);
-    float acc[kRPW][kTB];
-#pragma unroll
-    for (int r = 0; r < kRPW; ++r)
-#pragma unroll
-      for (int tb = 0; tb < kTB; ++tb) acc[r][tb] = 0.0f;
-    for (int c = lane; c < nG; c += 64) {
-      uint32_t hw[kTB][16];
-      float hs[kTB];
-#pragma unroll
-      for (int tb = 0; tb < kTB; ++tb) {
-        const uint16_t* hp = hbase + (size_t)mm[tb] * a.ldh + (size_t)c * 32;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) load16(&hw[tb][4 * q], hp + 8 * q);
-        float s = 0.0f;
-        if constexpr (FMT != MOE_WFMT_NVFP4) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) s = dot2_f16(hw[tb][i], 0x3C003C00u, s);
-        }
-        hs[tb] = s;
-      }
-#pragma unroll
-      for (int r = 0; r < kRPW; ++r) {
-        const size_t row = rbase + row0 + r;
-        uint32_t wq[BITS];
-        load_codes<FMT>(wq, X.down.q + row * rowBytes + (size_t)c * (4 * BITS));
-        if constexpr (ROW) {
-          group_dot_row<FMT, true>(wq, hw, hs, acc[r]);
-        } else {
-          group_dot<FMT, true>(*reinterpret_cast<const uint32_t(*)[4]>(wq),
-                               load_scale<FMT>(X.down.s, row, nG, c), hw, hs, gd, acc[r]);
-        }
-      }
+    for (int r = 0; r < RPW; ++r) {
+      const size_t row = rbase + row0 + r;
+      load_codes<FMT>(st.q[0][r], X.down.q + row * rowBytes + (size_t)c * (4 * BITS));
+      if constexpr (!ROW) st.sc[0][r] = load_scale<FMT>(X.down.s, row, nG, c);
     }
 #pragma unroll
-    for (int r = 0; r < kRPW; ++r)
+    for (int tb = 0; tb < TB; ++tb) {
+      const uint16_t* hp = hbase + (size_t)(m0 + tb) * a.ldh + (size_t)c * 32;
 #pragma unroll
-      for (int tb = 0; tb < kTB; ++tb) {
-        const float v = wave_sum(acc[r][tb]) * row_scale<FMT>(X.down.s, rbase + row0 + r);
-        if (lane == r * kTB + tb && m0 + tb < sl.M) obase[(size_t)(m0 + tb) * H + row0 + r] = v;
+      for (int q = 0; q < 4; ++q) load16(&st.act[tb][4 * q], hp + 8 * q);
+    }
+  };
+  auto compute = [&](const Step& st, int) {
+    float hs[TB];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      float s = 0.0f;
+      if constexpr (FMT != MOE_WFMT_NVFP4) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s = dot2_f16(st.act[tb][i], 0x3C003C00u, s);
       }
-  }
+      hs[tb] = s;
+    }
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      if constexpr (ROW)
+        group_dot_row<FMT, true, TB>(st.q[0][r], st.act, hs, acc[r]);
+      else
+        group_dot<FMT, true, TB>(st.q[0][r], st.sc[0][r], st.act, hs, gd, acc[r]);
+    }
+  };
+  group_steps<Step>(nG, load, compute);
+#pragma unroll
+  for (int r = 0; r < RPW; ++r)
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      const float v = wave_sum(acc[r][tb]) * row_scale<FMT>(X.down.s, rbase + row0 + r);
+      if (lane == r * TB + tb) obase[(size_t)(m0 + tb) * H + row0 + r] = v;
+    }
+}
+
+template <int FMT>
+__global__ void __launch_bounds__(256) down_gemv_kernel(FfnArgs a) {
+  const int wv = threadIdx.x >> 6;
+  const Slot sl = resolve_slot(a, blockIdx.y);
+  if (!sl.ok) return;
+  const ExpertSet& X = sl.routed ? a.routed : a.dense;
+  const int row0 = (blockIdx.x * 4 + wv) * dn_rpw<FMT>();
+  if (row0 >= a.H) return;
+  int m0 = 0;
+  for (; m0 + 2 <= sl.M; m0 += 2) down_pass<FMT, 2>(a, sl, X, row0, m0);
+  if (m0 < sl.M) down_pass<FMT, 1>(a, sl, X, row0, m0);
 }
 
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
@@ -406,16 +479,18 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, Tracer* tr) {
   int max_inter = 0;
   if (a.has_routed) max_inter = a.routed.inter;
   if (a.has_dense && a.dense.inter > max_inter) max_inter = a.dense.inter;
-  dim3 g1((max_inter + kRowsPerBlock - 1) / kRowsPerBlock, slots);
-  dim3 g2((a.H + kRowsPerBlock - 1) / kRowsPerBlock, slots);
   hipError_t e;
   auto launch = [&](auto F) {
     constexpr int fmt = decltype(F)::value;
+    constexpr int rows_per_block = 4 * gu_rpw<fmt>();
+    dim3 g1((max_inter + rows_per_block - 1) / rows_per_block, slots);
     hipLaunchKernelGGL(gateup_gemv_kernel<fmt>, g1, dim3(256), 0, s, a);
     return hipGetLastError();
   };
   auto launch_down = [&](auto F) {
     constexpr int fmt = decltype(F)::value;
+    constexpr int rows_per_block = 4 * dn_rpw<fmt>();
+    dim3 g2((a.H + rows_per_block - 1) / rows_per_block, slots);
     hipLaunchKernelGGL(down_gemv_kernel<fmt>, g2, dim3(256), 0, s, a);
     return hipGetLastError();
   };

@@ -201,6 +201,11 @@ constexpr int kDecFlagStride = 64;
 constexpr int kDecFusedMaxGrid = 1024;
 constexpr size_t kDecBarrierWords = (size_t)kDecFlagStride * (kDecFusedMaxGrid + 1);
 bool decode_supported(int hidden);
+// Router scores sigmoid(x . Wr[e]) in float64 for 1 <= T <= kDecodeMaxTokens
+// tokens (one block per expert) into scores[T][E]; launch_route takes it for
+// such T.  hipErrorInvalidValue for other T or H % 16 != 0.
+hipError_t launch_route_scores(const uint16_t* x, const float* router_w, double* scores, int T, int H,
+                               int E, hipStream_t s);
 // Whether a per-row format call of T tokens takes the single-token kernels
 // (per-row int4 and int2, one token, down rows within dec_down_t1's limits).
 bool decode_row_format_ok(const moe_config& c, int T);

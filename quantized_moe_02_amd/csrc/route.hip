@@ -9,6 +9,10 @@
 //                 One wave per 32 tokens x 64 experts x slice of the hidden
 //                 dimension; with several slices (few tokens) each writes its
 //                 partial sums and route_select adds them in slice order.
+//                 For at most four tokens the small-batch router kernel
+//                 (one block per expert, float64 FMAs, the sigmoid applied)
+//                 takes its place: the matrix-core tiles hold 32 tokens, and
+//                 the slices' partial sums cost the selection a long read.
 //   route_select  one wave per token (select_token.h).
 #include <algorithm>
 
@@ -106,6 +110,9 @@ __global__ void __launch_bounds__(256) route_logits_kernel(const uint16_t* __res
     }
 }
 
+// SCORES: the input holds sigmoid scores (one slice), else logits in nsplit
+// slices.
+template <bool SCORES>
 __global__ void __launch_bounds__(256) route_select_kernel(const double* __restrict__ logits,
                                                            const float* __restrict__ bias,
                                                            int32_t* __restrict__ ids,
@@ -122,8 +129,8 @@ __global__ void __launch_bounds__(256) route_select_kernel(const double* __restr
   if (t >= T) return;
   int id, rank, n_kept;
   float w;
-  select_token(logits + (size_t)t * E, bias, E, G, TG, K, rsf, top_p, sc[wv], id, w, rank, n_kept,
-               nsplit, (size_t)T * E);
+  select_token<SCORES>(logits + (size_t)t * E, bias, E, G, TG, K, rsf, top_p, sc[wv], id, w, rank,
+                       n_kept, nsplit, (size_t)T * E);
   if (lane < K) {
     ids[(size_t)t * K + rank] = id;
     tw[(size_t)t * K + rank] = w;
@@ -143,6 +150,15 @@ int route_splits(int T, int H, int E) {
 hipError_t launch_route(const RouteArgs& a, hipStream_t s, Tracer* tr) {
   if (a.T == 0) return hipSuccess;
   hipError_t e;
+  if (a.T <= kDecodeMaxTokens) {
+    if ((e = launch_route_scores(a.x, a.router_w, a.logits, a.T, a.H, a.E, s)) != hipSuccess) return e;
+    if (tr && (e = tr->mark("route_logits")) != hipSuccess) return e;
+    hipLaunchKernelGGL(route_select_kernel<true>, dim3((a.T + 3) / 4), dim3(256), 0, s, a.logits, a.bias,
+                       a.ids, a.tw, a.T, a.E, a.G, a.TG, a.K, a.rsf, 1, a.flags, a.top_p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (tr && (e = tr->mark("route_select")) != hipSuccess) return e;
+    return hipSuccess;
+  }
   const int groups = (a.T + kLogitTok - 1) / kLogitTok;
   const int S = route_splits(a.T, a.H, a.E);
   const int nkb = a.H / 32;
@@ -153,7 +169,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s, Tracer* tr) {
                      a.H, a.E, per);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (tr && (e = tr->mark("route_logits")) != hipSuccess) return e;
-  hipLaunchKernelGGL(route_select_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, a.logits, a.bias,
+  hipLaunchKernelGGL(route_select_kernel<false>, dim3((a.T + 3) / 4), dim3(256), 0, s, a.logits, a.bias,
                      a.ids, a.tw, a.T, a.E, a.G, a.TG, a.K, a.rsf, S_used, a.flags, a.top_p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (tr && (e = tr->mark("route_select")) != hipSuccess) return e;
