@@ -174,13 +174,13 @@ hipError_t run_gemm_ffn(const moe_config& c, int T, const uint16_t* x, const Wor
 hipError_t run_ffn_combine(const moe_config& c, int T, const uint16_t* x, const Workspace& w,
                            const int32_t* picks, int n_experts, const ExpertSet& routed,
                            bool has_shared, const ExpertSet& shared, const float* tw, void* y,
-                           bool out_bf16, bool gemv, hipStream_t stream, Tracer* tr) {
+                           bool out_bf16, bool gemv, hipStream_t stream, Tracer* tr, bool permuted) {
   hipError_t e;
   const int K = c.top_k, P = T * K;
   const int ldh = pad_k(std::max(c.moe_inter, has_shared ? c.shared_inter : 0));
   PermuteArgs pa{picks, w.offsets, w.sorted_token, w.inv_perm, w.active, w.n_active,
                  T, K, n_experts, w.phist};
-  if ((e = launch_permute(pa, stream, tr)) != hipSuccess) return e;
+  if (!permuted && (e = launch_permute(pa, stream, tr)) != hipSuccess) return e;
   float* o_shared = has_shared ? w.O + (size_t)P * c.hidden : nullptr;
   if (gemv) {
     FfnArgs a{};
@@ -538,11 +538,22 @@ moe_status layer_impl(const moe_config* cfg, int32_t T, const uint16_t* x, const
   RouteArgs ra{x, router_w, bias, ids, tw, w.logits, T, cfg->hidden, cfg->n_routed_experts,
                cfg->n_group, cfg->topk_group, cfg->top_k, cfg->routed_scaling_factor, w.flags,
                cfg->expert_top_p};
-  if ((e = launch_route(ra, stream, tr)) != hipSuccess) return MOE_ERR_HIP;
+  // up to four tokens: the selection also sorts the picks (no permutation
+  // launch)
+  const bool fused_perm = route_permute_small_ok(T, cfg->top_k);
+  if (fused_perm) {
+    PermuteArgs pa{ids, w.offsets, w.sorted_token, w.inv_perm, w.active, w.n_active,
+                   T, cfg->top_k, cfg->n_routed_experts, w.phist};
+    e = launch_route_permute_small(ra, pa, stream, tr);
+  } else {
+    e = launch_route(ra, stream, tr);
+  }
+  if (e != hipSuccess) return MOE_ERR_HIP;
   const ExpertSet rset = expert_set(*routed, cfg->moe_inter);
   const ExpertSet sset = has_shared ? expert_set(*shared, cfg->shared_inter) : ExpertSet{};
   return hip_status(run_ffn_combine(*cfg, T, x, w, ids, cfg->n_routed_experts, rset, has_shared,
-                                    sset, tw, y, out_dtype == MOE_OUT_BF16, gemv, stream, tr));
+                                    sset, tw, y, out_dtype == MOE_OUT_BF16, gemv, stream, tr,
+                                    fused_perm));
 }
 
 }  // namespace

@@ -153,6 +153,14 @@ struct PermuteArgs {
   int32_t* hist;   // [permute_hist_ints] per-chunk expert counts (scratch)
 };
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s, Tracer* tr = nullptr);
+// Routing and permutation of 1 <= T <= kDecodeMaxTokens tokens with T*k <=
+// 64 picks (route_permute_small_ok) in two launches: the scores, then one
+// workgroup that selects and sorts; the outputs of launch_route followed by
+// launch_permute (pa.ids is not read: the picks go from the selection to the
+// sort in LDS).
+bool route_permute_small_ok(int T, int K);
+hipError_t launch_route_permute_small(const RouteArgs& a, const PermuteArgs& pa, hipStream_t s,
+                                      Tracer* tr = nullptr);
 // Tokens per chunk of the permutation and the size of its scratch.
 int permute_chunk(int T);
 size_t permute_hist_ints(int T, int E);
@@ -321,13 +329,15 @@ hipError_t run_gemm_ffn(const moe_config& c, int T, const uint16_t* x, const Wor
                         int P, int ldh, uint16_t* h, float* o, hipStream_t stream, Tracer* tr);
 
 // The layer after routing: permutation of `picks` (ids in [0, n_experts) or
-// -1) over n_experts experts whose weights are `routed`, the expert FFNs
+// -1) over n_experts experts whose weights are `routed` (skipped when
+// `permuted`: w's permutation arrays already hold it), the expert FFNs
 // (grouped GEMV if `gemv`, else the grouped GEMM) with the shared expert, and
 // the weighted combine into y.
 hipError_t run_ffn_combine(const moe_config& c, int T, const uint16_t* x, const Workspace& w,
                            const int32_t* picks, int n_experts, const ExpertSet& routed,
                            bool has_shared, const ExpertSet& shared, const float* tw, void* y,
-                           bool out_bf16, bool gemv, hipStream_t stream, Tracer* tr);
+                           bool out_bf16, bool gemv, hipStream_t stream, Tracer* tr,
+                           bool permuted = false);
 
 // Replaces each pick's expert id by its cache slot (map[id]); -1 stays -1.
 struct SlotMap {

@@ -137,7 +137,86 @@ __global__ void __launch_bounds__(256) route_select_kernel(const double* __restr
   }
 }
 
+// At most four tokens (P = T*k <= 64 picks): the selection and the
+// permutation in one workgroup, from the scores of route_scores.  Wave t
+// selects token t; every thread then counts, for its experts e (and E), the
+// kept picks with a smaller id (offsets[e]); wave 0 sorts the picks, one per
+// lane: a ballot per id bit, from the top bit down, leaves each lane the
+// lanes holding its expert (eq) and those holding a smaller one (lt), so its
+// slot is |lt| plus the equal picks on lower lanes -- by expert, then pick
+// order, as the permutation kernels order them.  The outputs are theirs
+// (offsets, sorted tokens, inverse permutation, active experts and count).
+__global__ void __launch_bounds__(256) route_select_permute_kernel(
+    const double* __restrict__ scores, const float* __restrict__ bias, int32_t* __restrict__ ids,
+    float* __restrict__ tw, int T, int E, int G, int TG, int K, float rsf, uint32_t* __restrict__ flags,
+    float top_p, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_token,
+    int32_t* __restrict__ inv_perm, int32_t* __restrict__ active, int32_t* __restrict__ n_active) {
+  __shared__ SelectScratch sc[4];
+  __shared__ int pid[64];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int P = T * K;
+  if (flags && threadIdx.x == 0) flags[0] = 0u;
+  if (wv < T) {
+    int id, rank, n_kept;
+    float w;
+    select_token<true>(scores + (size_t)wv * E, bias, E, G, TG, K, rsf, top_p, sc[wv], id, w, rank,
+                       n_kept);
+    if (lane < K) {
+      ids[wv * K + rank] = id;   // -1: a pick the adaptive top-p dropped
+      tw[wv * K + rank] = w;
+      pid[wv * K + rank] = id;
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e <= E; e += 256) {
+    int c = 0;
+    for (int p = 0; p < P; ++p) {
+      const int v = pid[p];
+      c += (v >= 0 && v < e) ? 1 : 0;
+    }
+    offsets[e] = c;
+  }
+  if (wv != 0) return;
+  const int pe = lane < P ? pid[lane] : -1;
+  const bool have = pe >= 0;
+  const int e = have ? pe : 0;
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  uint64_t eq = __ballot(have), lt = 0;
+  for (int bit = nbits - 1; bit >= 0; --bit) {
+    const bool set = (e >> bit) & 1;
+    const uint64_t b = __ballot(have && set);
+    lt |= set ? (eq & ~b) : 0ull;
+    eq &= set ? b : ~b;
+  }
+  const uint64_t below = (1ull << lane) - 1ull;
+  const int pos = __popcll(lt) + __popcll(eq & below);
+  if (lane < P) inv_perm[lane] = have ? pos : -1;
+  if (have) sorted_token[pos] = lane / K;
+  const bool first = have && (eq & below) == 0;
+  const uint64_t firsts = __ballot(first);
+  if (first) active[__popcll(lt & firsts)] = e;
+  if (lane == 0) n_active[0] = __popcll(firsts);
+}
+
 }  // namespace
+
+bool route_permute_small_ok(int T, int K) { return T >= 1 && T <= kDecodeMaxTokens && T * K <= 64; }
+
+hipError_t launch_route_permute_small(const RouteArgs& a, const PermuteArgs& pa, hipStream_t s,
+                                      Tracer* tr) {
+  if (!route_permute_small_ok(a.T, a.K)) return hipErrorInvalidValue;
+  hipError_t e;
+  if ((e = launch_route_scores(a.x, a.router_w, a.logits, a.T, a.H, a.E, s)) != hipSuccess) return e;
+  if (tr && (e = tr->mark("route_logits")) != hipSuccess) return e;
+  hipLaunchKernelGGL(route_select_permute_kernel, dim3(1), dim3(256), 0, s, a.logits, a.bias, a.ids, a.tw,
+                     a.T, a.E, a.G, a.TG, a.K, a.rsf, a.flags, a.top_p, pa.offsets, pa.sorted_token,
+                     pa.inv_perm, pa.active, pa.n_active);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (tr && (e = tr->mark("route_select")) != hipSuccess) return e;
+  return hipSuccess;
+}
 
 int route_splits(int T, int H, int E) {
   // enough waves to fill the chip, at least 4 K blocks of 32 inputs per wave

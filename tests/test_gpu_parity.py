@@ -429,6 +429,24 @@ def test_exact_router_ties(T, bias):
     check_outputs(L, y, ids_ref)
 
 
+@pytest.mark.parametrize("bias", sorted(TIE_BIAS))
+@pytest.mark.parametrize("T", [1, 4])
+def test_exact_router_ties_split_small(T, bias):
+    """The same on the split path at 1 and 4 tokens (per-row int8: routing and
+    the sort of the picks in one workgroup).  Every token then picks the same
+    experts, so each selected expert holds T picks in token order."""
+    geom = synth.small_geom()
+    L = synth.make_custom(geom, T, "int8_row", "zero", seed=640 + T, device="cuda")
+    L.router_w.zero_()
+    L.bias.copy_(torch.from_numpy(TIE_BIAS[bias](geom["n_routed_experts"])).float())
+    y, ids, tw = run_layer(L)
+    x, Wr, b, cfg, _, _ = oracle_inputs(L)
+    ids_ref, w_ref, _ = oracle.route(oracle.bf16_bits_to_f64(x), Wr, b, cfg)
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    assert np.array_equal(tw.cpu().numpy(), w_ref.astype(np.float32))
+    check_outputs(L, y, ids_ref)
+
+
 def test_exact_router_ties_full_decode():
     """The same at the GLM-5.2 decode shape (one token, fused kernel)."""
     L = layer("decode")
@@ -460,6 +478,9 @@ TOP_P = {
     "T37": (37, "int4", 0),
     "T640": (640, "int4", 0),
     "T40_nvfp4": (40, "nvfp4", 0),
+    # the split path's one-workgroup selection and sort (per-row int8)
+    "T1_int8": (1, "int8_row", 0),
+    "T4_int8": (4, "int8_row", 0),
 }
 
 
