@@ -116,6 +116,9 @@ def algorithmic(geom, wfmt, T, n_active):
     # above together)
     kern["dec_fused_t1"] = {m: sum(kern[k][m] for k in ("dec_select_permute", "dec_gateup", "dec_down_combine"))
                             for m in ("bytes", "flops")}
+    # 2-4 tokens: selection and gate/up in one launch
+    kern["dec_select_gateup"] = {m: sum(kern[k][m] for k in ("dec_select_permute", "dec_gateup"))
+                                 for m in ("bytes", "flops")}
     kern.update({
         # large-batch path
         "route_logits": dict(bytes=router_b + x_b + T * E * 8, flops=T * 2 * H * E),

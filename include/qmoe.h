@@ -151,15 +151,17 @@ typedef struct {
  * [0, 1] are MOE_ERR_INVALID_ARG. */
 
 /* moe_config.options.  Unknown bits are MOE_ERR_INVALID_ARG.
- * MOE_OPT_NO_GRID_WAIT   moe_layer never runs the single-token kernel whose
+ * MOE_OPT_NO_GRID_WAIT   moe_layer never runs the small-batch kernels whose
  *                        workgroups wait for each other (see moe_layer); one
- *                        token then takes kernels that do not, with results
- *                        identical bit for bit.  For callers that share the
- *                        device with other work while the layer runs.
- * MOE_OPT_GRID_WAIT_NONE that kernel's workgroups give up on the wait at once
- *                        (no poll): every row of y is NaN and the workspace
- *                        flag MOE_FLAG_GRID_WAIT_TIMEOUT is raised.  Exists to
- *                        exercise the give-up path; never needed otherwise. */
+ *                        to four tokens then take kernels that do not, with
+ *                        results identical bit for bit.  For callers that
+ *                        share the device with other work while the layer
+ *                        runs.
+ * MOE_OPT_GRID_WAIT_NONE those kernels' workgroups give up on the wait at
+ *                        once (no poll): every row of y is NaN and the
+ *                        workspace flag MOE_FLAG_GRID_WAIT_TIMEOUT is raised.
+ *                        Exists to exercise the give-up path; never needed
+ *                        otherwise. */
 #define MOE_OPT_NO_GRID_WAIT 1u
 #define MOE_OPT_GRID_WAIT_NONE 2u
 /* MOE_OPT_INT8_ACTIVATIONS  W4A8 integer-dot path (page "Show HN: ...", section
@@ -203,9 +205,10 @@ const char* moe_status_string(moe_status s);
  * copy on `stream` and waits for it, so it returns after all work queued on
  * `stream` before it has finished.  ws == NULL reads the flags of
  * moe_layer_noalloc's workspace on the current device.
- * MOE_FLAG_GRID_WAIT_TIMEOUT  the single-token kernel's workgroups waited for
+ * MOE_FLAG_GRID_WAIT_TIMEOUT  a small-batch kernel's workgroups waited for
  *   each other in vain (other work on the device kept some from starting);
- *   the rows of y that they owned are NaN.  Rerun with MOE_OPT_NO_GRID_WAIT. */
+ *   the rows of y that depend on them are NaN.  Rerun with
+ *   MOE_OPT_NO_GRID_WAIT. */
 #define MOE_FLAG_GRID_WAIT_TIMEOUT 1u
 moe_status moe_layer_flags(const void* ws, uint32_t* flags, hipStream_t stream);
 
@@ -285,8 +288,10 @@ moe_status moe_combine(const moe_config* cfg, int32_t T, const float* expert_out
  * runs.  If other work keeps some of its workgroups from starting, the wait
  * gives up after a bounded time (2^16 polls), the rows of y it could not
  * finish are NaN, and MOE_FLAG_GRID_WAIT_TIMEOUT is raised in the workspace
- * (moe_layer_flags).  cfg->options MOE_OPT_NO_GRID_WAIT selects kernels that
- * do not wait for each other (same results, bit for bit). */
+ * (moe_layer_flags).  For 2-4 tokens in those shapes, the gate/up workgroups
+ * wait for the one that selects the experts (the first dispatched), with the
+ * same bound, NaN rows and flag.  cfg->options MOE_OPT_NO_GRID_WAIT selects
+ * kernels that do not wait for each other (same results, bit for bit). */
 moe_status moe_layer(const moe_config* cfg, int32_t T, const uint16_t* x,
                      const float* router_w, const float* bias, const moe_qexperts* routed,
                      const moe_qexperts* shared, void* y, int32_t out_dtype,

@@ -50,8 +50,12 @@ constexpr int kRPW = QMOE_DEC_RPW;           // gate/up row pairs per pipeline i
 constexpr int kItems = QMOE_DEC_ITEMS;       // pipeline items per wave (even)
 constexpr int kPairsPerWave = kRPW * kItems;
 constexpr int kPairsPerBlock = 4 * kPairsPerWave;
+#ifndef QMOE_K2_ITEMS
+#define QMOE_K2_ITEMS 4
+#endif
 constexpr int kSharedRP = 1;                              // K2 shared gate/up: row pairs per item
-constexpr int kSharedPairsPerBlock = 4 * 2 * kSharedRP;   // K2 shared gate/up: two items per wave
+constexpr int kSharedItems = QMOE_K2_ITEMS;               // K2 shared gate/up: items per wave
+constexpr int kSharedPairsPerBlock = 4 * kSharedItems * kSharedRP;
 static_assert(kItems % 2 == 0, "items are double-buffered in pairs");
 static_assert(32 % kPairsPerWave == 0 && 32 % (2 * kRPW) == 0, "a wave never straddles inter (a multiple of 32)");
 constexpr int kDownRows = QMOE_DEC_DOWN_ROWS; // down/combine output rows per block
@@ -417,70 +421,16 @@ __global__ void __launch_bounds__(256) route_scores_kernel(const uint16_t* __res
   router_scores_block(x, router_w, scores, T, H, E);
 }
 
-// ---------------------------------------------------------------------------
-// K2: selection of every token, then the permutation of the P <= 64 picks
-// ---------------------------------------------------------------------------
-// Selection and grouping.  What the later kernels read: the per-token ids
-// and weights (outputs of the layer), the selected experts' records (slots,
-// in ascending expert order, each with its picks in pick order), their count,
-// and for each sorted pick p (grouped by expert) its expert and token; the h
-// rows follow the sorted pick order.
-// The other workgroups run the shared expert's gate/up GEMV, one per (token,
-// row block): it does not depend on the routing, so it streams while block 0
-// selects.  (For 2..4 tokens this measured 2 us per call faster than extra
-// blocks of K3: 141.5 against 143.7 us at four tokens.)
-template <int FMT, int GPL>
-__global__ void __launch_bounds__(256) dec_select_permute_kernel(DecodeArgs a) {
-  if (blockIdx.x > 0) {
-    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const ExpertSet& S = a.shared;
-    const int nsb = (S.inter + kSharedPairsPerBlock - 1) / kSharedPairsPerBlock;   // row blocks
-    const int t = ((int)blockIdx.x - 1) / nsb, rb = ((int)blockIdx.x - 1) - t * nsb;
-    const int pair0 = rb * kSharedPairsPerBlock + wv * (2 * kSharedRP);
-    if (pair0 >= S.inter) return;
-    const float gg = (FMT == MOE_WFMT_NVFP4) ? S.gate.g[0] : 1.0f;
-    const float gu = (FMT == MOE_WFMT_NVFP4) ? S.up.g[0] : 1.0f;
-    gateup_wave<FMT, GPL, 2, kSharedRP>(a.x + (size_t)t * a.H, a.H, S.gate, S.up, 0, S.inter, pair0, gg,
-                                        gu, a.h_shared + (size_t)t * a.ldh);
-    return;
-  }
-  __shared__ SelectScratch sc[4];
-  __shared__ int pid[64];
-  __shared__ float pw[64];
+// Selection of 2..4 tokens (one wave per token) and the grouping of the
+// P <= 64 picks by expert (wave 0): the layer's ids and weights, one record
+// per selected expert, their count, and each sorted pick's (expert, token)
+// word.  The caller's other waves (wv >= T) only pass the barrier.
+template <bool DEV>
+__device__ __forceinline__ void select_group_multi(const DecodeArgs& a, SelectScratch (&sc)[4],
+                                                   int (&pid)[64], float (&pw)[64]) {
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int K = a.K, P = a.T * a.K;
-  if (a.T == 1) {
-    // One token: its k picks are distinct experts, so the sorted order is the
-    // ascending-id order select_token ranks them in, and every record follows
-    // from (id, weight, rank) in the picking lanes.
-    if (wv != 0) return;
-    int id, rank, n_kept;
-    float w;
-    select_token<true>(a.logits, a.bias, a.E, a.G, a.TG, K, a.rsf, a.top_p, sc[0], id, w, rank,
-                       n_kept);
-    if (lane < K) {
-      a.ids[rank] = id;
-      a.tw[rank] = w;
-      // picks the adaptive top-p dropped (ranks from n_kept on) have no h row
-      a.sorted_et[rank] = id;
-    }
-    if (lane < K && rank < n_kept) {
-      DecSlot sl;
-      sl.e = id;
-      sl.p0 = rank;
-      sl.M = 1;
-      sl.pad = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sl.t[i] = 0;
-        sl.w[i] = i == 0 ? w : 0.0f;
-      }
-      a.slots[rank] = sl;
-    }
-    if (lane == 0) a.n_active[0] = n_kept;
-    return;
-  }
   if (wv < a.T) {
     int id, rank, n_kept;
     float w;
@@ -518,8 +468,15 @@ __global__ void __launch_bounds__(256) dec_select_permute_kernel(DecodeArgs a) {
   const int pos = __popcll(lt) + __popcll(eq & below);
   const bool first = have && (eq & below) == 0;
   const uint64_t firsts = __ballot(first);
-  if (have) a.sorted_et[pos] = e | ((lane / K) << 16);
-  if (lane < P && lane >= __popcll(__ballot(have))) a.sorted_et[lane] = -1;
+  // DEV: device-scope stores, read by other workgroups of the same launch
+  auto put_et = [&](int i, int v) {
+    if constexpr (DEV)
+      __hip_atomic_store(a.sorted_et + i, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      a.sorted_et[i] = v;
+  };
+  if (have) put_et(pos, e | ((lane / K) << 16));
+  if (lane < P && lane >= __popcll(__ballot(have))) put_et(lane, -1);
   if (first) {
     // the expert's record: its picks (the lanes in eq) in pick order, at most
     // one per token, so at most four
@@ -542,6 +499,73 @@ __global__ void __launch_bounds__(256) dec_select_permute_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// K2: selection of every token, then the permutation of the P <= 64 picks
+// ---------------------------------------------------------------------------
+// Selection and grouping.  What the later kernels read: the per-token ids
+// and weights (outputs of the layer), the selected experts' records (slots,
+// in ascending expert order, each with its picks in pick order), their count,
+// and for each sorted pick p (grouped by expert) its expert and token; the h
+// rows follow the sorted pick order.
+// The other workgroups run the shared expert's gate/up GEMV, one per (token,
+// row block): it does not depend on the routing, so it streams while block 0
+// selects.  (For 2..4 tokens this measured 2 us per call faster than extra
+// blocks of K3: 141.5 against 143.7 us at four tokens.)
+template <int FMT, int GPL>
+__global__ void __launch_bounds__(256) dec_select_permute_kernel(DecodeArgs a) {
+  if (blockIdx.x > 0) {
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const ExpertSet& S = a.shared;
+    const int nsb = (S.inter + kSharedPairsPerBlock - 1) / kSharedPairsPerBlock;   // row blocks
+    const int t = ((int)blockIdx.x - 1) / nsb, rb = ((int)blockIdx.x - 1) - t * nsb;
+    const int pair0 = rb * kSharedPairsPerBlock + wv * (kSharedItems * kSharedRP);
+    if (pair0 >= S.inter) return;
+    const float gg = (FMT == MOE_WFMT_NVFP4) ? S.gate.g[0] : 1.0f;
+    const float gu = (FMT == MOE_WFMT_NVFP4) ? S.up.g[0] : 1.0f;
+    gateup_wave<FMT, GPL, kSharedItems, kSharedRP>(a.x + (size_t)t * a.H, a.H, S.gate, S.up, 0, S.inter, pair0, gg,
+                                        gu, a.h_shared + (size_t)t * a.ldh);
+    return;
+  }
+  __shared__ SelectScratch sc[4];
+  __shared__ int pid[64];
+  __shared__ float pw[64];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int K = a.K;
+  if (a.T == 1) {
+    // One token: its k picks are distinct experts, so the sorted order is the
+    // ascending-id order select_token ranks them in, and every record follows
+    // from (id, weight, rank) in the picking lanes.
+    if (wv != 0) return;
+    int id, rank, n_kept;
+    float w;
+    select_token<true>(a.logits, a.bias, a.E, a.G, a.TG, K, a.rsf, a.top_p, sc[0], id, w, rank,
+                       n_kept);
+    if (lane < K) {
+      a.ids[rank] = id;
+      a.tw[rank] = w;
+      // picks the adaptive top-p dropped (ranks from n_kept on) have no h row
+      a.sorted_et[rank] = id;
+    }
+    if (lane < K && rank < n_kept) {
+      DecSlot sl;
+      sl.e = id;
+      sl.p0 = rank;
+      sl.M = 1;
+      sl.pad = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sl.t[i] = 0;
+        sl.w[i] = i == 0 ? w : 0.0f;
+      }
+      a.slots[rank] = sl;
+    }
+    if (lane == 0) a.n_active[0] = n_kept;
+    return;
+  }
+  select_group_multi<false>(a, sc, pid, pw);
+}
+
+// ---------------------------------------------------------------------------
 // K3: gate/up of the selected experts.  Block = (row block, sorted pick p):
 // the double-buffered GEMV of the pick's expert over the block's row pairs
 // for the pick's token, written to h row p.  Picks of one expert sit next to
@@ -557,6 +581,86 @@ __global__ void __launch_bounds__(256) dec_gateup_kernel(DecodeArgs a) {
   const ExpertSet& R = a.routed;
   const int pair0 = blockIdx.x * kPairsPerBlock + wv * kPairsPerWave;
   if (pair0 >= R.inter) return;
+  const int e = et & 0xffff, t = et >> 16;
+  const float gg = (FMT == MOE_WFMT_NVFP4) ? R.gate.g[e] : 1.0f;
+  const float gu = (FMT == MOE_WFMT_NVFP4) ? R.up.g[e] : 1.0f;
+  gateup_wave<FMT, GPL>(a.x + (size_t)t * a.H, a.H, R.gate, R.up, (size_t)e * R.inter, R.inter,
+                        pair0, gg, gu, a.h_routed + (size_t)p * a.ldh);
+}
+
+// ---------------------------------------------------------------------------
+// K2 and K3 in one launch for 2..4 tokens (dec_select_gateup).  Grid (row
+// blocks, 1 + T + P): block (0, 0) selects and groups the picks as K2 does,
+// then raises kSelFlags flags; blocks (x, 1..T) run the shared expert's
+// gate/up for token y - 1, which does not depend on the routing and streams
+// while the selection runs; blocks (x, 1 + T + p) wait for a flag and then run
+// K3's GEMV for sorted pick p.  Block (0, 0) is dispatched first, so it runs
+// whatever the waiting blocks occupy.  The pick words that the waiting
+// blocks read are device-scope stores, complete (vmcnt(0), then the
+// workgroup barrier) before the flags are stored at device scope; the
+// waiters read them with device-scope loads issued after their flag has
+// returned.  The other records (ids, weights, expert records) are read by
+// K4, after the launch.  K1 zeroes the flags.  A wait is bounded
+// (barrier_spins polls); a block that gives up writes NaN to its h rows and
+// raises the layer's flag.
+// ---------------------------------------------------------------------------
+constexpr int kSelFlags = 64;
+static_assert(kSelFlags <= kDecFusedMaxGrid, "the flags sit in the barrier words K1 zeroes");
+
+template <int FMT, int GPL>
+__global__ void __launch_bounds__(256) dec_select_gateup_kernel(DecodeArgs a) {
+  const int y = (int)blockIdx.y;
+  const int T = a.T;
+  if (y == 0) {
+    if (blockIdx.x != 0) return;
+    __shared__ SelectScratch sc[4];
+    __shared__ int pid[64];
+    __shared__ float pw[64];
+    select_group_multi<true>(a, sc, pid, pw);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the pick words are stored
+    __syncthreads();
+    if (threadIdx.x < kSelFlags)
+      __hip_atomic_store(a.bar + kDecFlagStride * (1 + threadIdx.x), 1u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int pair0 = blockIdx.x * kPairsPerBlock + wv * kPairsPerWave;
+  if (y <= T) {
+    const ExpertSet& S = a.shared;
+    if (!a.has_shared || pair0 >= S.inter) return;
+    const float gg = (FMT == MOE_WFMT_NVFP4) ? S.gate.g[0] : 1.0f;
+    const float gu = (FMT == MOE_WFMT_NVFP4) ? S.up.g[0] : 1.0f;
+    gateup_wave<FMT, GPL>(a.x + (size_t)(y - 1) * a.H, a.H, S.gate, S.up, 0, S.inter, pair0, gg, gu,
+                          a.h_shared + (size_t)(y - 1) * a.ldh);
+    return;
+  }
+  const int p = y - 1 - T;
+  const ExpertSet& R = a.routed;
+  __shared__ int ready;
+  if (threadIdx.x == 0) {
+    const uint32_t* flag = a.bar + kDecFlagStride * (1 + ((int)blockIdx.x + p) % kSelFlags);
+    int ok = 0;
+    for (uint32_t spin = 0; spin < a.barrier_spins; ++spin) {
+      if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+        ok = 1;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    ready = ok;
+  }
+  __syncthreads();
+  if (!ready) {
+    // the pick is unknown: its h rows of this block become NaN
+    if (threadIdx.x == 0) a.flags[0] = MOE_FLAG_GRID_WAIT_TIMEOUT;
+    const int r = blockIdx.x * kPairsPerBlock + (int)threadIdx.x;
+    if ((int)threadIdx.x < kPairsPerBlock && r < R.inter) a.h_routed[(size_t)p * a.ldh + r] = 0x7E00u;
+    return;
+  }
+  const int et = __builtin_amdgcn_readfirstlane(
+      __hip_atomic_load(a.sorted_et + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  if (et < 0 || pair0 >= R.inter) return;   // et < 0: a pick the adaptive top-p dropped
   const int e = et & 0xffff, t = et >> 16;
   const float gg = (FMT == MOE_WFMT_NVFP4) ? R.gate.g[e] : 1.0f;
   const float gu = (FMT == MOE_WFMT_NVFP4) ? R.up.g[e] : 1.0f;
@@ -1365,6 +1469,15 @@ hipError_t launch_k2(const DecodeArgs& a, hipStream_t s, int blocks) {
 }
 
 template <int GPL>
+hipError_t launch_k23(const DecodeArgs& a, hipStream_t s, dim3 grid) {
+  dec_fmt(a.wfmt, [&](auto F) {
+    hipLaunchKernelGGL((dec_select_gateup_kernel<decltype(F)::value, GPL>), grid, dim3(256), 0, s, a);
+    return 0;
+  });
+  return hipGetLastError();
+}
+
+template <int GPL>
 hipError_t launch_k3(const DecodeArgs& a, hipStream_t s, dim3 grid) {
   dec_fmt(a.wfmt, [&](auto F) {
     hipLaunchKernelGGL((dec_gateup_kernel<decltype(F)::value, GPL>), grid, dim3(256), 0, s, a);
@@ -1435,11 +1548,45 @@ bool decode_row_format_ok(const moe_config& c, int T) {
   return T == 1 ? down_t1_fits(a) : down_multi_fits<kDMRows>(a);
 }
 
+// K4: the down projection with the combine, for the shapes each kernel takes.
+static hipError_t launch_k4(const DecodeArgs& a, hipStream_t s, Tracer* tr, size_t lds1) {
+  hipError_t e;
+  const bool f4 = a.wfmt == MOE_WFMT_NVFP4;
+  dim3 g4(a.H / kDownRows);
+  if (down_t1_fits(a)) {
+    const int blocks = std::min((a.H + 3) / 4, 512);
+    dec_fmt(a.wfmt, [&](auto F) {
+      hipLaunchKernelGGL((dec_down_t1_kernel<decltype(F)::value>), dim3(blocks), dim3(256), lds1, s, a);
+      return 0;
+    });
+  } else if (a.T > 1 && down_multi_fits<kDMRows>(a)) {
+    const int blocks = std::min((a.H + kDMWaves - 1) / kDMWaves, kDMBlocks);
+    dec_fmt(a.wfmt, [&](auto F) {
+      hipLaunchKernelGGL((dec_down_multi_kernel<decltype(F)::value, kDMRows, kDMDepth>), dim3(blocks),
+                         dim3(64 * kDMWaves), 0, s, a);
+      return 0;
+    });
+  } else if (a.T == 1) {
+    if (f4)
+      hipLaunchKernelGGL((dec_down_combine_kernel<MOE_WFMT_NVFP4, 1>), g4, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((dec_down_combine_kernel<MOE_WFMT_INT4_G32_F16, 1>), g4, dim3(256), 0, s, a);
+  } else {
+    if (f4)
+      hipLaunchKernelGGL((dec_down_combine_kernel<MOE_WFMT_NVFP4, kMaxT>), g4, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((dec_down_combine_kernel<MOE_WFMT_INT4_G32_F16, kMaxT>), g4, dim3(256), 0, s,
+                         a);
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (tr && (e = tr->mark("dec_down_combine")) != hipSuccess) return e;
+  return hipSuccess;
+}
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
   if (a.T == 0) return hipSuccess;
   hipError_t e;
   const int gpl = (a.H / 32 + 63) / 64;
-  const bool f4 = a.wfmt == MOE_WFMT_NVFP4;
   // per-row formats: shapes whose down rows fit dec_down_t1 (one token) or
   // dec_down_multi (2-4 tokens) only
   if (wfmt_row(a.wfmt) && (a.wfmt == MOE_WFMT_INT8_ROW_F32 ||
@@ -1476,6 +1623,26 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
     return tr ? tr->mark("dec_fused_t1") : hipSuccess;
   }
 
+#ifndef QMOE_MERGED_K23
+#define QMOE_MERGED_K23 1
+#endif
+  // 2..4 tokens: the selection and gate/up in one launch, unless the caller
+  // asked for kernels whose workgroups never wait for each other
+  if (QMOE_MERGED_K23 && a.T >= 2 && !(a.options & MOE_OPT_NO_GRID_WAIT)) {
+    DecodeArgs am = a;
+    am.barrier_spins = (a.options & MOE_OPT_GRID_WAIT_NONE) ? 0u : kBarrierSpins;
+    const int imax = std::max(a.routed.inter, a.has_shared ? a.shared.inter : 0);
+    dim3 g23((imax + kPairsPerBlock - 1) / kPairsPerBlock, 1 + a.T + a.T * a.K);
+    switch (gpl) {
+      case 1: e = launch_k23<1>(am, s, g23); break;
+      case 2: e = launch_k23<2>(am, s, g23); break;
+      case 3: e = launch_k23<3>(am, s, g23); break;
+      default: e = launch_k23<4>(am, s, g23); break;
+    }
+    if (e != hipSuccess) return e;
+    if (tr && (e = tr->mark("dec_select_gateup")) != hipSuccess) return e;
+    return launch_k4(a, s, tr, lds1);
+  }
   // the shared expert's gate/up in K2, beside the selection
   const int k2_blocks =
       1 + (a.has_shared ? a.T * ((a.shared.inter + kSharedPairsPerBlock - 1) / kSharedPairsPerBlock) : 0);
@@ -1498,35 +1665,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, Tracer* tr) {
   if (e != hipSuccess) return e;
   if (tr && (e = tr->mark("dec_gateup")) != hipSuccess) return e;
 
-  dim3 g4(a.H / kDownRows);
-  if (down_t1_fits(a)) {
-    const int blocks = std::min((a.H + 3) / 4, 512);
-    dec_fmt(a.wfmt, [&](auto F) {
-      hipLaunchKernelGGL((dec_down_t1_kernel<decltype(F)::value>), dim3(blocks), dim3(256), lds1, s, a);
-      return 0;
-    });
-  } else if (a.T > 1 && down_multi_fits<kDMRows>(a)) {
-    const int blocks = std::min((a.H + kDMWaves - 1) / kDMWaves, kDMBlocks);
-    dec_fmt(a.wfmt, [&](auto F) {
-      hipLaunchKernelGGL((dec_down_multi_kernel<decltype(F)::value, kDMRows, kDMDepth>), dim3(blocks),
-                         dim3(64 * kDMWaves), 0, s, a);
-      return 0;
-    });
-  } else if (a.T == 1) {
-    if (f4)
-      hipLaunchKernelGGL((dec_down_combine_kernel<MOE_WFMT_NVFP4, 1>), g4, dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((dec_down_combine_kernel<MOE_WFMT_INT4_G32_F16, 1>), g4, dim3(256), 0, s, a);
-  } else {
-    if (f4)
-      hipLaunchKernelGGL((dec_down_combine_kernel<MOE_WFMT_NVFP4, kMaxT>), g4, dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((dec_down_combine_kernel<MOE_WFMT_INT4_G32_F16, kMaxT>), g4, dim3(256), 0, s,
-                         a);
-  }
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (tr && (e = tr->mark("dec_down_combine")) != hipSuccess) return e;
-  return hipSuccess;
+  return launch_k4(a, s, tr, lds1);
 }
 
 }  // namespace qmoe

@@ -257,6 +257,50 @@ def test_single_token_fused_matches_two_launches(case):
         assert torch.equal(u, v)
 
 
+SMALL_MERGED = {
+    "T2": (dict(), 2, "int4", "normal0.1"),
+    "T3_no_shared": (dict(n_shared_experts=0), 3, "int4", "normal0.1"),
+    "T4": (dict(), 4, "int4", "zipf"),
+    "T4_top_p": (dict(expert_top_p=0.6, top_k=6, topk_group=4), 4, "int4", "normal0.1"),
+    "nvfp4_T3": EDGE["nvfp4_T3"],       # shared inter below moe_inter
+    "T2_wide_shared": (dict(moe_inter=64, shared_inter=96), 2, "int4", "normal0.1"),
+}
+
+
+@pytest.mark.parametrize("case", sorted(SMALL_MERGED))
+def test_small_batch_merged_matches_two_launches(case):
+    """2-4 tokens run the selection and gate/up in one launch, the gate/up
+    workgroups waiting for the selecting one; MOE_OPT_NO_GRID_WAIT runs them as
+    two launches.  Both match the oracle, and each other bit for bit."""
+    over, T, wfmt, bias = SMALL_MERGED[case]
+    L = synth.make_custom(synth.small_geom(**over), T, wfmt, bias, seed=310 + T, device="cuda")
+    ws = q.workspace(q.make_config(L.geom, L.wfmt), T)
+    merged = run_layer(L, ws=ws)
+    assert q.moe_layer_flags(ws) == 0
+    split = run_layer(L, options=q.MOE_OPT_NO_GRID_WAIT)
+    ids_g, _ = check_routing(L, split[1], split[2])
+    check_outputs(L, split[0], ids_g)
+    for u, v in zip(merged, split):
+        assert torch.equal(u, v)
+
+
+def test_small_batch_gives_up_to_nan():
+    """The gate/up workgroups' wait for the selection is bounded: with no poll
+    allowed, every routed h row is NaN, so is y, the routing is written and
+    the flag raised; the next call clears it and is exact."""
+    over, T, wfmt, bias = SMALL_MERGED["T4"]
+    L = synth.make_custom(synth.small_geom(**over), T, wfmt, bias, seed=320, device="cuda")
+    ws = q.workspace(q.make_config(L.geom, L.wfmt), T)
+    y, ids, tw = run_layer(L, options=q.MOE_OPT_GRID_WAIT_NONE, ws=ws)
+    assert torch.isnan(y).all()
+    check_routing(L, ids, tw)
+    assert q.moe_layer_flags(ws) == q.MOE_FLAG_GRID_WAIT_TIMEOUT
+    y, ids, tw = run_layer(L, ws=ws)
+    assert q.moe_layer_flags(ws) == 0
+    ids_g, _ = check_routing(L, ids, tw)
+    check_outputs(L, y, ids_g)
+
+
 def test_fused_decode_gives_up_to_nan():
     """The fused single-token kernel's barrier wait is bounded.  With no poll
     allowed (MOE_OPT_GRID_WAIT_NONE, set from the host), no workgroup waits:
