@@ -149,16 +149,47 @@ KERNEL_SOURCES = {
 }
 
 
+def strip_comments(src):
+    """C/C++ source text without its comments (string and character literals
+    kept as they are), so that a comment edit does not count as a change."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return "".join(out)
+
+
+def source_code(src):
+    """The code lines of a C/C++ source: comments stripped, blank lines and
+    trailing spaces dropped."""
+    return "\n".join(l.rstrip() for l in strip_comments(src).splitlines() if l.strip())
+
+
 def kernel_source_hash(kernel):
-    """sha256 over the sources a kernel is compiled from (None if unknown)."""
+    """sha256 over the code (source_code) of the sources a kernel is compiled
+    from (None if unknown)."""
     import hashlib
     files = next((v for p, v in KERNEL_SOURCES.items() if kernel.startswith(p)), None)
     if files is None:
         return None
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, "quantized_moe_02_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "quantized_moe_02_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(source_code(fh.read()).encode())
     return h.hexdigest()
 
 

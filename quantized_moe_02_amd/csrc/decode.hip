@@ -10,7 +10,9 @@
 //                          every workgroup selects the experts itself, then
 //                          the shared and routed gate/up GEMVs, a grid
 //                          barrier, and the down GEMV with the combine
-//   otherwise:
+//   2..4 tokens: dec_select_gateup -- K2 and K3 below in one launch, the
+//                          gate/up workgroups waiting for the selecting one
+//   otherwise (or under MOE_OPT_NO_GRID_WAIT):
 //   K2 dec_select_permute  one workgroup: per-token selection (one wave per
 //                          token) and the grouping of the <= 64 picks by
 //                          expert (batch union); the shared expert's gate/up

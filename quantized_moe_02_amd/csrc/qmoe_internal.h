@@ -198,9 +198,9 @@ struct CombineArgs {
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s, Tracer* tr = nullptr);
 
-// Small-batch path of moe_layer (T <= kDecodeMaxTokens): four kernels --
-// router logits, selection + grouping of the picks, gate/up, down with the
-// weighted combine.
+// Small-batch path of moe_layer (T <= kDecodeMaxTokens): router scores,
+// selection + grouping of the picks, gate/up, down with the weighted combine
+// (one token: the last three in one launch; 2..4 tokens: the middle two).
 constexpr int kDecodeMaxTokens = 4;
 constexpr int kDecodeMaxGPL = 4;   // hidden <= 64 lanes * 4 groups * 32 = 8192
 // Grid barrier of the fused single-token kernel: an arrival count and one
