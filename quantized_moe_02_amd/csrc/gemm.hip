@@ -4,7 +4,8 @@
 // dequant-on-use, batch-union MoE; NVFP4 per page "NVIDIA stellt neues
 // GLM-5.2 NVFP4 Modell vor", section "Technische Details").
 //
-// Work unit = (m tile of up to 128 tokens of one expert, n tile of weight
+// Work unit = (m tile of up to 192 tokens of one expert, 32 in the thin
+// launch; n tile of weight
 // rows).  Each wave dequantises its own weight rows straight from HBM into
 // fp16 A operands (scale folded in, one rounding) and multiplies them against
 // the unit's activations, staged in LDS as fp16, with
@@ -129,7 +130,7 @@ __device__ __forceinline__ half8 dequant_row(const uint32_t* w, int ks) {
 
 
 // Activations go from HBM straight into LDS (buffer_load ... lds: lane l of a
-// load writes 16 bytes at base + 16 l).  Stage layout: 128 token rows of 16
+// load writes 16 bytes at base + 16 l).  Stage layout: BM token rows of 16
 // chunks of 16 bytes, chunk c of row r at slot r * 16 + (c ^ (r & 15)); the
 // XOR spreads the 16 rows that one B-operand read touches over all banks.
 // Load i of wave w covers slots (8 w + i) * 64 .. +63, i.e. rows 4 (8 w + i)
@@ -179,6 +180,13 @@ __device__ __forceinline__ void lds_copy16(const rsrc_t& r, uint8_t* dst, uint32
 
 constexpr int kNS = 4;            // K blocks in flight (LDS stages, weight register ring)
 constexpr int kRT = 4;            // 16-row weight tiles per wave
+constexpr int kLdsBytes = 160 * 1024;
+// K blocks in flight for units of BM tokens: four LDS stages where they fit
+// (128 tokens: 128 KB), else three (192 tokens: 144 KB)
+template <int BM>
+constexpr int gemm_stages() { return 4 * BM * kBK * 2 <= kLdsBytes - 4096 ? 4 : 3; }
+constexpr int kNSF = gemm_stages<kBMF>();
+static_assert(3 * kBMF * kBK * 2 <= kLdsBytes - 4096, "a fat unit's LDS stages fit");
 
 
 // PROJ 0: gate/up (+SwiGLU), PROJ 1: down.
@@ -189,10 +197,11 @@ constexpr int kRT = 4;            // 16-row weight tiles per wave
 // ring, activations straight into an LDS stage) while block kb is
 // multiplied; within a block, the next K step's B operands (LDS) and A
 // operands (dequantised weights) are produced while the current step's MFMAs
-// run.  The vector memory ops issued per thread for any two consecutive K
-// blocks are the same in number, WAITN (blocks past K read zeros), so "block
-// kb + 1 has landed" is vmcnt <= WAITN once block kb + 3 is requested.  One
-// barrier per K block, before its last K step.
+// run.  Every K block issues the same number of vector memory ops per thread
+// (blocks past K are requested too and never read), so "block kb + 1 has
+// landed" is vmcnt <= WAITN, the ops of the NS - 2 blocks after it, once
+// block kb + NS - 1 is requested.  One barrier per K block, before its last
+// K step.
 #ifndef QMOE_THIN_WGS
 #define QMOE_THIN_WGS 2
 #endif
@@ -222,11 +231,12 @@ __global__ void __launch_bounds__(256, (gemm_wgs_per_cu<FMT, BM>())) moe_gemm_ke
   constexpr int BITS = wfmt_bits(FMT);
   constexpr int WPL = BITS;                  // code words per lane per K block (32 inputs)
   constexpr int CL = BITS == 8 ? 2 : 1;      // code loads per row tile per K block
-  static_assert(NS == 4, "the scale copies ride on K blocks 0 and 2 of each group of four");
+  static_assert(!SL || NS == 4, "the scale copies ride on K blocks 0 and 2 of each group of four");
+  static_assert(NS * BM * kBK * 2 + (SL ? 4 * kSclBytesPerWave : 16) <= kLdsBytes, "LDS stages fit");
   static_assert(!(ROW && SL), "per-row scales are read in the epilogue");
-  // vector memory ops per thread issued for K blocks kb + 2 and kb + 3: all
-  // that may still be in flight once block kb + 1 has landed
-  constexpr int WAITN = 2 * (NA + RT * CL + (SL || ROW ? 0 : RT)) + (SL ? 1 : 0);
+  // vector memory ops per thread issued for K blocks kb + 2 .. kb + NS - 1:
+  // all that may still be in flight once block kb + 1 has landed
+  constexpr int WAITN = (NS - 2) * (NA + RT * CL + (SL || ROW ? 0 : RT)) + (SL ? 1 : 0);
   __shared__ __attribute__((aligned(16))) uint16_t xs[NS][BM * kBK];
   __shared__ __attribute__((aligned(16))) uint8_t scl[SL ? 4 * kSclBytesPerWave : 16];
   const int lane = threadIdx.x & 63;
@@ -507,6 +517,19 @@ __global__ void __launch_bounds__(256, (gemm_wgs_per_cu<FMT, BM>())) moe_gemm_ke
     else
       run(ic<1>{});
   } else {
+    // 129-160 tokens (common at ~128 tokens per expert) take ten column tiles
+    if constexpr (BM / 16 > 10) {
+      if (nct > 10) {
+        run(ic<BM / 16>{});
+        return;
+      }
+    }
+    if constexpr (BM / 16 > 8) {
+      if (nct > 8) {
+        run(ic<(BM / 16 > 10 ? 10 : BM / 16)>{});
+        return;
+      }
+    }
     if (nct > 4)
       run(ic<8>{});
     else if (nct > 2)
@@ -542,7 +565,7 @@ __global__ void __launch_bounds__(256) x_to_f16_kernel(const uint16_t* __restric
 }
 
 // Work units: for each active expert (ascending) its sorted slots in slices of
-// kBM, then the shared expert's tokens in slices of kBM.
+// BMF, then the shared expert's tokens in slices of BMF.
 // tiles[i] = {expert or -1, first h/O row, tokens, first sorted slot or token}.
 template <int BMF>
 __global__ void __launch_bounds__(64) build_units_kernel(const int32_t* __restrict__ offsets,
@@ -623,7 +646,7 @@ __global__ void __launch_bounds__(64) build_units_kernel(const int32_t* __restri
 
 }  // namespace
 
-// Most work units of each kind: fat units hold up to kBM tokens of an expert
+// Most work units of each kind: fat units hold up to bmf tokens of an expert
 // with more than kBMThin of them, thin units up to kBMThin tokens of an
 // expert (or the shared expert) with at most kBMThin, or of any expert when
 // there would be fewer than kFewFat fat units.
@@ -649,20 +672,22 @@ hipError_t launch_build_units(const int32_t* offsets, const int32_t* active,
   if (bmf == kBMQ)
     hipLaunchKernelGGL(build_units_kernel<kBMQ>, dim3(1), dim3(64), 0, s, offsets, active, n_active, tiles,
                        n_tiles, T, P, has_shared ? 1 : 0, thin_off);
-  else
-    hipLaunchKernelGGL(build_units_kernel<kBM>, dim3(1), dim3(64), 0, s, offsets, active, n_active, tiles,
+  else if (bmf == kBMF)
+    hipLaunchKernelGGL(build_units_kernel<kBMF>, dim3(1), dim3(64), 0, s, offsets, active, n_active, tiles,
                        n_tiles, T, P, has_shared ? 1 : 0, thin_off);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
 // Work units: for each active expert (ascending) its sorted slots, in thin
-// units of kBMThin or fat units of kBM; then the shared expert's tokens
+// units of kBMThin or fat units of kBMF (kBMQ); then the shared expert's tokens
 // likewise.
 // tiles[i] = {expert or -1, first h/O row, tokens, first sorted slot or
 // token}; the thin units start at tiles[thin_off].
 int gemm_max_units(int T, int K, int E, bool has_shared) {
-  // the larger of the two unit tables (fat units of kBM or kBMQ tokens)
-  return (int)std::max(fat_units_max(T, K, E, has_shared, kBM) + thin_units_max(T, K, E, has_shared, kBM),
+  // the larger of the two unit tables (fat units of kBMF or kBMQ tokens)
+  return (int)std::max(fat_units_max(T, K, E, has_shared, kBMF) + thin_units_max(T, K, E, has_shared, kBMF),
                        fat_units_max(T, K, E, has_shared, kBMQ) + thin_units_max(T, K, E, has_shared, kBMQ));
 }
 int gemm_thin_offset(int T, int K, int E, bool has_shared, int bmf) {
@@ -694,7 +719,9 @@ hipError_t launch_gemm_kernel(const GemmArgs& g, long units, int nt, hipStream_t
   sdw = sdw && BM == kBMThin;
   dispatch_wfmt(g.wfmt, [&](auto F) {
     constexpr int fmt = decltype(F)::value;
-    if constexpr (wfmt_row(fmt)) {   // no per-block scales to copy
+    // per-row formats have no per-block scales to copy; fat units load them
+    // per block
+    if constexpr (wfmt_row(fmt) || BM != kBMThin) {
       hipLaunchKernelGGL((moe_gemm_kernel<fmt, PROJ, BM, NS, false>), grid, dim3(256), 0, s, g);
     } else {
       if (sdw)
@@ -711,16 +738,16 @@ hipError_t launch_gemm(const GemmArgs& g, int K, int E, hipStream_t s, Tracer* t
   hipError_t e;
   int max_inter = g.routed.inter;
   if (g.has_shared && g.shared.inter > max_inter) max_inter = g.shared.inter;
-  const long fat = fat_units_max(g.T, K, E, g.has_shared, kBM);
-  const long thin = thin_units_max(g.T, K, E, g.has_shared, kBM);
+  const long fat = fat_units_max(g.T, K, E, g.has_shared, kBMF);
+  const long thin = thin_units_max(g.T, K, E, g.has_shared, kBMF);
   // one workgroup per work item (unit, n tile); items past the actual number
   // of units exit at once
   const int ntg = (max_inter + kGateUpPairs - 1) / kGateUpPairs;
   const int ntd = (g.H + kDownRows - 1) / kDownRows;
-  if ((e = launch_gemm_kernel<0, kBM, kNS>(g, fat, ntg, s)) != hipSuccess) return e;
+  if ((e = launch_gemm_kernel<0, kBMF, kNSF>(g, fat, ntg, s)) != hipSuccess) return e;
   if ((e = launch_gemm_kernel<0, kBMThin, kNSThin>(g, thin, ntg, s)) != hipSuccess) return e;
   if (tr && (e = tr->mark("gemm_gateup")) != hipSuccess) return e;
-  if ((e = launch_gemm_kernel<1, kBM, kNS>(g, fat, ntd, s)) != hipSuccess) return e;
+  if ((e = launch_gemm_kernel<1, kBMF, kNSF>(g, fat, ntd, s)) != hipSuccess) return e;
   if ((e = launch_gemm_kernel<1, kBMThin, kNSThin>(g, thin, ntd, s)) != hipSuccess) return e;
   if (tr && (e = tr->mark("gemm_down")) != hipSuccess) return e;
   return hipSuccess;

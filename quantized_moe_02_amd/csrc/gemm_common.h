@@ -1,5 +1,5 @@
 // Work units of the grouped GEMMs (csrc/gemm.hip: fp16 activations;
-// csrc/gemm_i8.hip: int8 activations): units of up to kBM tokens of one expert
+// csrc/gemm_i8.hip: int8 activations): units of up to kBMF or kBMQ tokens of one expert
 // ("fat") or kBMThin ("thin"), built on the device by build_units, and the
 // mapping of work items to XCDs.
 #pragma once
@@ -10,8 +10,8 @@
 
 namespace qmoe {
 
-constexpr int kBM = 128;          // tokens per unit
 constexpr int kBMThin = 32;
+constexpr int kBMF = kGemmUnitTokensF;   // fat units of the fp16 GEMM
 constexpr int kBMQ = kGemmUnitTokensQ;   // fat units of the W4A8 GEMM
 // With fewer fat units than this (gate/up: 16 work items each) the fat
 // launches would leave most of the chip idle, so the experts they would hold

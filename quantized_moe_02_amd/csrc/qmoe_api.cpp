@@ -103,7 +103,7 @@ hipError_t run_gemm_ffn(const moe_config& c, int T, const uint16_t* x, const Wor
   hipError_t e;
   const int K = has_routed ? c.top_k : 0, E = has_routed ? c.n_routed_experts : 0;
   const bool a8 = (c.options & MOE_OPT_INT8_ACTIVATIONS) != 0;
-  const int bmf = a8 ? kGemmUnitTokensQ : 128;
+  const int bmf = a8 ? kGemmUnitTokensQ : kGemmUnitTokensF;
   if ((e = launch_build_units(offsets, has_routed ? active : nullptr,
                               has_routed ? n_active : nullptr, w.tiles, w.n_tiles, T, P, K, E,
                               has_shared, stream, bmf)) != hipSuccess)
@@ -153,7 +153,7 @@ hipError_t run_gemm_ffn(const moe_config& c, int T, const uint16_t* x, const Wor
   GemmArgs g{};
   g.tiles = w.tiles;
   g.n_tiles = w.n_tiles;
-  g.thin_off = gemm_thin_offset(T, K, E, has_shared);
+  g.thin_off = gemm_thin_offset(T, K, E, has_shared, bmf);
   g.x16 = w.x16;
   g.ldx = pad_k(c.hidden);
   g.sorted_token = sorted_token;

@@ -300,11 +300,15 @@ hipError_t launch_quant_rows(const uint16_t* src, int ld_src, bool bf16, int row
 // proj 0: gate/up (+SwiGLU into h_out); 1: down (into o_out).
 hipError_t launch_gemm_q(const GemmQArgs& g, int proj, int K, int E, hipStream_t s);
 
-// Tokens per fat work unit of the W4A8 GEMM (the fp16 GEMM's are 128).
+// Tokens per fat work unit of the W4A8 GEMM and of the fp16 GEMM.
 #ifndef QMOE_Q_BM
 #define QMOE_Q_BM 192
 #endif
+#ifndef QMOE_F16_BM
+#define QMOE_F16_BM 192
+#endif
 constexpr int kGemmUnitTokensQ = QMOE_Q_BM;
+constexpr int kGemmUnitTokensF = QMOE_F16_BM;
 int gemm_max_units(int T, int K, int E, bool has_shared);
 // Row strides (elements) of the fp16 activation and intermediate buffers: a
 // multiple of the GEMM's K block, the padding held at zero.
@@ -312,11 +316,11 @@ __host__ __device__ inline int pad_k(int n) { return (n + 127) & ~127; }
 // Whether the GEMM path's activation buffers (T x ldx fp16 activations, rows x
 // ldh fp16 intermediates) fit its buffer descriptors (2 GiB each).
 bool gemm_fits(int64_t T, int64_t rows, int64_t ldx, int64_t ldh);
-// bmf: tokens per fat unit (128, or kGemmUnitTokensQ for the W4A8 GEMM).
-int gemm_thin_offset(int T, int K, int E, bool has_shared, int bmf = 128);
+// bmf: tokens per fat unit (kGemmUnitTokensF, or kGemmUnitTokensQ for the W4A8 GEMM).
+int gemm_thin_offset(int T, int K, int E, bool has_shared, int bmf);
 hipError_t launch_build_units(const int32_t* offsets, const int32_t* active,
                               const int32_t* n_active, int4* tiles, int32_t* n_tiles, int T, int P,
-                              int K, int E, bool has_shared, hipStream_t s, int bmf = 128);
+                              int K, int E, bool has_shared, hipStream_t s, int bmf);
 hipError_t launch_x_to_f16(const uint16_t* x, uint16_t* y, int T, int H, int ldx, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs& g, int K, int E, hipStream_t s, Tracer* tr = nullptr);
 // Expert FFNs of a T > kDecodeMaxTokens call on the grouped GEMM: work units

@@ -153,13 +153,18 @@ EDGE = {
     # the GEMM's work units: one expert takes every token, so it gets one full
     # thin unit (32 tokens); with few would-be fat units every expert is cut
     # into thin units: a full and a one-token unit (33), two full (64), five
-    # (160; the shared expert likewise); with many (about 160 tokens for each
-    # of 16 experts) a full and a short fat unit each
+    # (160; the shared expert likewise); with many, fat units of up to 192
+    # tokens: 640 and 700 tokens over 16 experts give experts of 33 to 571
+    # tokens (units of two to twelve column tiles, several units per expert),
+    # and one expert with all 1200 tokens (six full units and one of 48) sits
+    # beside experts of 57 to 105
     "hot_thin32": (dict(top_k=2), 32, "int4", "hot1"),
     "hot_cut33": (dict(top_k=2), 33, "int4", "hot1"),
     "hot_cut64": (dict(top_k=2), 64, "int4", "hot1"),
     "hot_cut160": (dict(top_k=2), 160, "int4", "hot1"),
     "fat_units": (dict(), 640, "int4", "normal0.1"),
+    "fat_units_hot": (dict(top_k=2), 1200, "int4", "hot1"),
+    "fat_units_nvfp4": (dict(), 700, "nvfp4", "normal0.1"),
     # 2..4 tokens: the small-batch down kernel that stages h in LDS (several
     # tokens per expert, no shared expert, one group per row, full 64-group
     # rows), and shapes that fall back to the per-block kernel (65 slots,
