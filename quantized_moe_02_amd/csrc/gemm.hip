@@ -565,7 +565,8 @@ __global__ void __launch_bounds__(256) x_to_f16_kernel(const uint16_t* __restric
 }
 
 // Work units: for each active expert (ascending) its sorted slots in slices of
-// BMF, then the shared expert's tokens in slices of BMF.
+// bm, then the shared expert's tokens in slices of bm (bm = BMF, or kBMNarrow
+// when units of BMF would be few).
 // tiles[i] = {expert or -1, first h/O row, tokens, first sorted slot or token}.
 template <int BMF>
 __global__ void __launch_bounds__(64) build_units_kernel(const int32_t* __restrict__ offsets,
@@ -577,18 +578,29 @@ __global__ void __launch_bounds__(64) build_units_kernel(const int32_t* __restri
   const int lane = threadIdx.x;
   const int na = n_active ? *n_active : 0;
   int4* thin = tiles + thin_off;
-  // fat units if every expert with more than kBMThin tokens took them; when
-  // there are fewer than kFewFat, their launch would leave most of the chip
-  // idle, so every expert is cut into thin units instead
-  int nfat = 0;
-  for (int a = lane; a < na; a += 64) {
-    const int e = active[a];
-    const int M = offsets[e + 1] - offsets[e];
-    nfat += M > kBMThin ? (M + BMF - 1) / BMF : 0;
-  }
+  // fat units if every expert with more than kBMThin tokens took units of bm
+  auto count_fat = [&](int bm) {
+    int n = 0;
+    for (int a = lane; a < na; a += 64) {
+      const int e = active[a];
+      const int M = offsets[e + 1] - offsets[e];
+      n += M > kBMThin ? (M + bm - 1) / bm : 0;
+    }
 #pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) nfat += __shfl_xor(nfat, d, 64);
-  if (has_shared && T > kBMThin) nfat += (T + BMF - 1) / BMF;
+    for (int d = 32; d >= 1; d >>= 1) n += __shfl_xor(n, d, 64);
+    if (has_shared && T > kBMThin) n += (T + bm - 1) / bm;
+    return n;
+  };
+  // Units of BMF tokens when there are enough of them to fill the chip for a
+  // few rounds; else units of kBMNarrow, which spread the same experts over
+  // more workgroups.
+  int bm = BMF, nfat = count_fat(BMF);
+  if (BMF > kBMNarrow && nfat < kFewWide) {
+    bm = kBMNarrow;
+    nfat = count_fat(bm);
+  }
+  // when there are fewer than kFewFat fat units, their launch would leave
+  // most of the chip idle, so every expert is cut into thin units instead
   const int thin_max = nfat < kFewFat ? 0x7fffffff : kBMThin;   // most tokens of a thin-cut expert
   int base = 0, tbase = 0;   // fat units, thin units so far
   for (int a0 = 0; a0 < na; a0 += 64) {
@@ -599,7 +611,7 @@ __global__ void __launch_bounds__(64) build_units_kernel(const int32_t* __restri
       o = offsets[e];
       M = offsets[e + 1] - o;
       nt = M <= thin_max ? (M + kBMThin - 1) / kBMThin : 0;
-      nm = nt ? 0 : (M + BMF - 1) / BMF;
+      nm = nt ? 0 : (M + bm - 1) / bm;
     }
     // exclusive prefixes of the fat and thin unit counts across the wave
     int pre = nm, tpre = nt;
@@ -613,8 +625,8 @@ __global__ void __launch_bounds__(64) build_units_kernel(const int32_t* __restri
     }
     const int excl = base + pre - nm;
     for (int i = 0; i < nm; ++i) {
-      const int m0 = i * BMF;
-      tiles[excl + i] = make_int4(e, o + m0, min(BMF, M - m0), o + m0);
+      const int m0 = i * bm;
+      tiles[excl + i] = make_int4(e, o + m0, min(bm, M - m0), o + m0);
     }
     for (int i = 0; i < nt; ++i) {
       const int m0 = i * kBMThin;
@@ -630,10 +642,10 @@ __global__ void __launch_bounds__(64) build_units_kernel(const int32_t* __restri
         thin[tbase + i] = make_int4(-1, P + i * kBMThin, min(kBMThin, T - i * kBMThin), i * kBMThin);
       tbase += ns;
     } else {
-      const int ns = (T + BMF - 1) / BMF;
+      const int ns = (T + bm - 1) / bm;
       for (int i = lane; i < ns; i += 64) {
-        const int t0 = i * BMF;
-        tiles[base + i] = make_int4(-1, P + t0, min(BMF, T - t0), t0);
+        const int t0 = i * bm;
+        tiles[base + i] = make_int4(-1, P + t0, min(bm, T - t0), t0);
       }
       base += ns;
     }
@@ -651,6 +663,7 @@ __global__ void __launch_bounds__(64) build_units_kernel(const int32_t* __restri
 // expert (or the shared expert) with at most kBMThin, or of any expert when
 // there would be fewer than kFewFat fat units.
 long fat_units_max(int T, int K, int E, bool has_shared, int bmf) {
+  bmf = std::min(bmf, kBMNarrow);   // build_units may fall back to narrow units
   const long P = (long)T * K;
   const long fat_experts = std::min<long>(E, P / (kBMThin + 1));
   const long routed = (P + bmf - 1) / bmf + fat_experts;

@@ -18,6 +18,11 @@ constexpr int kBMQ = kGemmUnitTokensQ;   // fat units of the W4A8 GEMM
 // are cut into thin units, which run in the thin launch with the bulk of the
 // work (their weights are then read once per 32 tokens).
 constexpr int kFewFat = 16;
+// Fat units of kBMF (kBMQ) tokens are used when there are at least kFewWide of
+// them; with fewer (a skewed load: a few experts with many tokens) they are
+// cut at kBMNarrow tokens, which gives more work items for the chip.
+constexpr int kBMNarrow = 128;
+constexpr int kFewWide = 64;
 constexpr int kGateUpPairs = 128; // row pairs per gate/up unit
 constexpr int kDownRows = 256;    // output rows per down unit
 

@@ -153,11 +153,11 @@ EDGE = {
     # the GEMM's work units: one expert takes every token, so it gets one full
     # thin unit (32 tokens); with few would-be fat units every expert is cut
     # into thin units: a full and a one-token unit (33), two full (64), five
-    # (160; the shared expert likewise); with many, fat units of up to 192
-    # tokens: 640 and 700 tokens over 16 experts give experts of 33 to 571
-    # tokens (units of two to twelve column tiles, several units per expert),
-    # and one expert with all 1200 tokens (six full units and one of 48) sits
-    # beside experts of 57 to 105
+    # (160; the shared expert likewise).  With 16 to 63 fat units of 192
+    # tokens they are cut at 128: 640 and 700 tokens over 16 experts (experts
+    # of 33 to 571 tokens, several units each) and one expert with all 1200
+    # tokens beside experts of 57 to 105.  With 64 or more, units of up to 192
+    # tokens (ten and twelve column tiles, experts of up to 1536 tokens).
     "hot_thin32": (dict(top_k=2), 32, "int4", "hot1"),
     "hot_cut33": (dict(top_k=2), 33, "int4", "hot1"),
     "hot_cut64": (dict(top_k=2), 64, "int4", "hot1"),
@@ -165,6 +165,10 @@ EDGE = {
     "fat_units": (dict(), 640, "int4", "normal0.1"),
     "fat_units_hot": (dict(top_k=2), 1200, "int4", "hot1"),
     "fat_units_nvfp4": (dict(), 700, "nvfp4", "normal0.1"),
+    "fat_wide": (dict(n_routed_experts=64, n_group=4, topk_group=4, top_k=8), 1152, "int4",
+                 "normal0.1"),
+    "fat_wide_nvfp4": (dict(n_routed_experts=64, n_group=4, topk_group=4, top_k=8), 1536, "nvfp4",
+                       "zipf"),
     # 2..4 tokens: the small-batch down kernel that stages h in LDS (several
     # tokens per expert, no shared expert, one group per row, full 64-group
     # rows), and shapes that fall back to the per-block kernel (65 slots,
