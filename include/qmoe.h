@@ -328,8 +328,8 @@ moe_status moe_layer_trace(const moe_config* cfg, int32_t T, const uint16_t* x,
  * until the process ends; the call allocates nothing (no hipMalloc, no
  * allocating library routine).  The caller still passes inputs and outputs.
  * Calls whose moe_workspace_size(cfg, T) exceeds MOE_NOALLOC_WS_BYTES return
- * MOE_ERR_UNSUPPORTED before any HIP call (the GLM-5.2 layer shape fits up to
- * 64 tokens).  All calls on one device share its buffer: calls that overlap
+ * MOE_ERR_UNSUPPORTED before any HIP call (the GLM-5.2 layer shape, int4
+ * group-32 weights, fits up to 90 tokens).  All calls on one device share its buffer: calls that overlap
  * on one device (other streams, other threads) race and give wrong results.
  * Each call writes every workspace word it reads, so a call's results do not
  * depend on the previous call.  Otherwise as moe_layer (same kernels, same
