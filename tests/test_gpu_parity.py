@@ -181,6 +181,12 @@ EDGE = {
     "T4_inter2048": (dict(hidden=512, moe_inter=2048, shared_inter=2048), 4, "int4", "zipf"),
     "T4_k16": (dict(n_routed_experts=64, n_group=4, topk_group=4, top_k=16), 4, "int4", "normal0.1"),
     "T3_uneven_shared": (dict(moe_inter=64, shared_inter=96), 3, "int4", "normal0.1"),
+    # the small-batch down kernel's rows per wave (2048 waves): two with some
+    # waves holding one (hidden 2080), four with most holding three (6176),
+    # four everywhere (8192)
+    "T3_h2080": (dict(hidden=2080, moe_inter=96, shared_inter=96), 3, "int4", "normal0.1"),
+    "T2_h6176_nvfp4": (dict(hidden=6176, moe_inter=64, shared_inter=64), 2, "nvfp4", "normal0.1"),
+    "T4_h8192": (dict(hidden=8192, moe_inter=128, shared_inter=128), 4, "int4", "zipf"),
     "nvfp4_T4": (dict(), 4, "nvfp4", "zipf"),
     # K a multiple of 512: thin units read their scales through LDS
     "lds_scales": (dict(hidden=512, moe_inter=512, shared_inter=512), 9, "int4", "normal0.1"),
