@@ -4,9 +4,8 @@
 // dequant-on-use, batch-union MoE; NVFP4 per page "NVIDIA stellt neues
 // GLM-5.2 NVFP4 Modell vor", section "Technische Details").
 //
-// Work unit = (m tile of up to 192 tokens of one expert, 32 in the thin
-// launch; n tile of weight
-// rows).  Each wave dequantises its own weight rows straight from HBM into
+// Work unit = (m tile of up to 192 tokens of one expert (32 in the thin
+// launch), n tile of weight rows).  Each wave dequantises its own weight rows straight from HBM into
 // fp16 A operands (scale folded in, one rounding) and multiplies them against
 // the unit's activations, staged in LDS as fp16, with
 // v_mfma_f32_16x16x32_f16 (fp32 accumulate).
@@ -477,7 +476,7 @@ __global__ void __launch_bounds__(256, (gemm_wgs_per_cu<FMT, BM>())) moe_gemm_ke
         mfmas(A[ks & 1], B[ks & 1]);
         interleave();
       }
-      // block kb + 1 landed in every wave (blocks kb + 2, kb + 3 may be in flight)
+      // block kb + 1 landed in every wave (blocks up to kb + NS - 1 may be in flight)
       kblock_handover<WAITN, thin>();
       read_b(xs[sn], 0, B[0]);
       dequant_ks(ic<sn>{}, 0, A[0]);
