@@ -5,9 +5,9 @@
 // GLM-5.2 NVFP4 Modell vor", section "Technische Details").
 //
 // Work unit = (m tile of up to 192 tokens of one expert (32 in the thin
-// launch), n tile of weight rows).  Each wave dequantises its own weight rows straight from HBM into
-// fp16 A operands (scale folded in, one rounding) and multiplies them against
-// the unit's activations, staged in LDS as fp16, with
+// launch), n tile of weight rows).  Each wave dequantises its own weight rows
+// straight from HBM into fp16 A operands (scale folded in, one rounding) and
+// multiplies them against the unit's activations, staged in LDS as fp16, with
 // v_mfma_f32_16x16x32_f16 (fp32 accumulate).
 //   gate/up: 128 row pairs per unit; each wave holds 32 gate rows and the 32
 //            matching up rows, so the SwiGLU epilogue pairs them in registers
